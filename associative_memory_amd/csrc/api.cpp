@@ -1,0 +1,209 @@
+// C ABI of libkata: argument validation, launch planning, workspace sizing
+// and status codes.  Declarations and the contract live in include/kata.h.
+#include "kata.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+#include "plan.h"
+
+namespace {
+
+using kata::ForwardPlan;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+  const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+size_t elem_size(kata_dtype_t t) { return t == KATA_BF16 ? 2 : 4; }
+
+bool dtype_ok(kata_dtype_t t) { return t == KATA_F32 || t == KATA_BF16; }
+bool head_dim_ok(int d) { return d == 16 || d == 32; }
+bool value_dim_ok(int dv) { return dv == 16 || dv == 32 || dv == 64; }
+bool chunk_ok(int c) { return c == 32 || c == 64 || c == 128; }
+
+kata_status_t from_hip(hipError_t e) { return e == hipSuccess ? KATA_OK : KATA_ERR_DEVICE; }
+
+// Shape/value checks shared by the forward, its workspace query and its plan.
+kata_status_t check_forward_shape(int B, int H, int64_t T, int d, int dv, int chunk,
+                                  kata_dtype_t dtype, kata_scan_t scan) {
+  if (B <= 0 || H <= 0 || T <= 0) return KATA_ERR_INVALID_VALUE;
+  if (scan != KATA_SCAN_AUTO && scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)
+    return KATA_ERR_INVALID_VALUE;
+  if (!dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!head_dim_ok(d) || !value_dim_ok(dv) || !chunk_ok(chunk)) return KATA_ERR_UNSUPPORTED;
+  // every element index must fit comfortably in int64 and every grid in 2^31
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (T > (INT64_C(1) << 40) / BH) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kata_status_string(kata_status_t status) {
+  switch (status) {
+    case KATA_OK: return "KATA_OK";
+    case KATA_ERR_INVALID_VALUE: return "KATA_ERR_INVALID_VALUE";
+    case KATA_ERR_UNSUPPORTED: return "KATA_ERR_UNSUPPORTED";
+    case KATA_ERR_WORKSPACE: return "KATA_ERR_WORKSPACE";
+    case KATA_ERR_DEVICE: return "KATA_ERR_DEVICE";
+  }
+  return "KATA_ERR_UNKNOWN";
+}
+
+int64_t kata_feature_dim(int d) { return d <= 0 ? -1 : static_cast<int64_t>(d) * (d + 1) / 2; }
+
+kata_status_t kata_feature_map(const void* x, void* phi, int64_t rows, int d,
+                               kata_dtype_t x_dtype, kata_dtype_t phi_dtype, void* stream) {
+  if (x == nullptr || phi == nullptr) return KATA_ERR_INVALID_VALUE;
+  if (rows <= 0 || d <= 0) return KATA_ERR_INVALID_VALUE;
+  if (!dtype_ok(x_dtype) || !dtype_ok(phi_dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(x) || !aligned16(phi)) return KATA_ERR_INVALID_VALUE;
+  if (d > 64) return KATA_ERR_UNSUPPORTED;
+  if (rows > (INT64_C(1) << 36)) return KATA_ERR_UNSUPPORTED;
+  const int64_t D = kata_feature_dim(d);
+  if (overlaps(x, rows * d * elem_size(x_dtype), phi, rows * D * elem_size(phi_dtype)))
+    return KATA_ERR_INVALID_VALUE;
+  return from_hip(kata::launch_feature_map(x, phi, rows, d, x_dtype == KATA_BF16,
+                                           phi_dtype == KATA_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t kata_forward_workspace_bytes(int B, int H, int64_t T, int d, int dv, int chunk,
+                                    kata_scan_t scan) {
+  // dtype does not change the workspace; plan with the larger-footprint path
+  if (check_forward_shape(B, H, T, d, dv, chunk, KATA_BF16, scan) != KATA_OK) return 0;
+  const ForwardPlan pb = kata::plan_forward(B, H, T, d, dv, chunk, KATA_BF16, scan);
+  const ForwardPlan pf = kata::plan_forward(B, H, T, d, dv, chunk, KATA_F32, scan);
+  return pb.ws_bytes > pf.ws_bytes ? pb.ws_bytes : pf.ws_bytes;
+}
+
+kata_status_t kata_forward_plan(int B, int H, int64_t T, int d, int dv, int chunk,
+                                kata_dtype_t dtype, kata_scan_t scan, char* buf,
+                                size_t buf_len) {
+  const kata_status_t st = check_forward_shape(B, H, T, d, dv, chunk, dtype, scan);
+  if (st != KATA_OK) return st;
+  if (buf == nullptr || buf_len == 0) return KATA_ERR_INVALID_VALUE;
+  const ForwardPlan p = kata::plan_forward(B, H, T, d, dv, chunk, dtype, scan);
+  kata::describe_plan(p, buf, buf_len);
+  return KATA_OK;
+}
+
+kata_status_t kata_forward_chunked(const void* q, const void* k, const void* v, void* out,
+                                   int B, int H, int64_t T, int d, int dv, int chunk,
+                                   float eps, kata_dtype_t dtype, kata_scan_t scan,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return kata_forward_chunked_profiled(q, k, v, out, B, H, T, d, dv, chunk, eps, dtype, scan,
+                                       workspace, workspace_bytes, nullptr, stream);
+}
+
+kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const void* v,
+                                            void* out, int B, int H, int64_t T, int d, int dv,
+                                            int chunk, float eps, kata_dtype_t dtype,
+                                            kata_scan_t scan, void* workspace,
+                                            size_t workspace_bytes,
+                                            const kata_stage_events_t* events, void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;
+  const kata_status_t st = check_forward_shape(B, H, T, d, dv, chunk, dtype, scan);
+  if (st != KATA_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return KATA_ERR_INVALID_VALUE;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  const size_t es = elem_size(dtype);
+  const size_t qk_bytes = static_cast<size_t>(BH * T * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
+  if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
+      overlaps(out, v_bytes, v, v_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  const ForwardPlan p = kata::plan_forward(B, H, T, d, dv, chunk, dtype, scan);
+  if (p.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < p.ws_bytes) return KATA_ERR_WORKSPACE;
+    if (overlaps(workspace, p.ws_bytes, out, v_bytes) ||
+        overlaps(workspace, p.ws_bytes, q, qk_bytes) ||
+        overlaps(workspace, p.ws_bytes, k, qk_bytes) ||
+        overlaps(workspace, p.ws_bytes, v, v_bytes))
+      return KATA_ERR_INVALID_VALUE;
+  }
+  return from_hip(kata::run_forward(p, q, k, v, out, eps, static_cast<float*>(workspace),
+                                    events, static_cast<hipStream_t>(stream)));
+}
+
+kata_status_t kata_prefill_state(const void* k, const void* v, float* S, float* z, int B,
+                                 int H, int64_t T, int d, int dv, kata_dtype_t dtype,
+                                 void* stream) {
+  if (k == nullptr || v == nullptr || S == nullptr || z == nullptr) return KATA_ERR_INVALID_VALUE;
+  if (B <= 0 || H <= 0 || T <= 0 || !dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(S) || !aligned16(z)) return KATA_ERR_INVALID_VALUE;
+  if (!head_dim_ok(d) || !value_dim_ok(dv)) return KATA_ERR_UNSUPPORTED;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (T > (INT64_C(1) << 40) / BH || BH > (INT64_C(1) << 26)) return KATA_ERR_UNSUPPORTED;
+  const int64_t D = kata_feature_dim(d);
+  const size_t es = elem_size(dtype);
+  const size_t s_bytes = static_cast<size_t>(BH * D * dv) * 4;
+  const size_t z_bytes = static_cast<size_t>(BH * D) * 4;
+  const size_t k_bytes = static_cast<size_t>(BH * T * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
+  if (overlaps(S, s_bytes, z, z_bytes) || overlaps(S, s_bytes, k, k_bytes) ||
+      overlaps(S, s_bytes, v, v_bytes) || overlaps(z, z_bytes, k, k_bytes) ||
+      overlaps(z, z_bytes, v, v_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  kata::StateArgs a{};
+  a.k = k;
+  a.v = v;
+  a.S_out = S;
+  a.z_out = z;
+  a.BH = BH;
+  a.T = T;
+  a.d = d;
+  a.dv = dv;
+  a.span = T;
+  a.n_spans = 1;
+  a.s_stride = D * dv;
+  a.z_stride = D;
+  a.bf16 = dtype == KATA_BF16;
+  a.sym = true;
+  a.skip_last = false;
+  return from_hip(kata::launch_state_valu(a, static_cast<hipStream_t>(stream)));
+}
+
+kata_status_t kata_decode_step(float* S, float* z, const void* q, const void* k,
+                               const void* v, void* out, int B, int H, int d, int dv,
+                               float eps, kata_dtype_t dtype, void* stream) {
+  if (S == nullptr || z == nullptr || q == nullptr || k == nullptr || v == nullptr ||
+      out == nullptr)
+    return KATA_ERR_INVALID_VALUE;
+  if (B <= 0 || H <= 0 || !dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(S) || !aligned16(z) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      !aligned16(out))
+    return KATA_ERR_INVALID_VALUE;
+  if (!head_dim_ok(d) || !value_dim_ok(dv)) return KATA_ERR_UNSUPPORTED;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (BH > (INT64_C(1) << 30)) return KATA_ERR_UNSUPPORTED;
+  const int64_t D = kata_feature_dim(d);
+  const size_t es = elem_size(dtype);
+  const size_t s_bytes = static_cast<size_t>(BH * D * dv) * 4;
+  const size_t z_bytes = static_cast<size_t>(BH * D) * 4;
+  const size_t qk_bytes = static_cast<size_t>(BH * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * dv) * es;
+  if (overlaps(out, v_bytes, S, s_bytes) || overlaps(out, v_bytes, z, z_bytes) ||
+      overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
+      overlaps(out, v_bytes, v, v_bytes) || overlaps(S, s_bytes, z, z_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  return from_hip(kata::launch_decode(S, z, q, k, v, out, BH, d, dv, eps, dtype == KATA_BF16,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,157 @@
+// Recurrent decode step (the KATA page, Sec. 2: additive recurrence
+// S_t = S_{t-1} + psi(k_t) v_t^T, Z_t = Z_{t-1} + psi(k_t), normalised read of
+// Eq. 2 taken after the update).
+//
+// One workgroup per head.  The head's state S[D][dv] (fp32, dv contiguous) is
+// streamed once: every thread owns a float4 column group and a strided set of
+// rows, loads all its rows first (so each lane has all its loads in flight),
+// adds phi(k)_r v, stores, and accumulates phi(q)_r S'_r.  Column sums across
+// the row groups and the denominator phi(q).z' are reduced through LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace kata {
+namespace {
+
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    float* __restrict__ S, float* __restrict__ z, const void* __restrict__ q,
+    const void* __restrict__ k, const void* __restrict__ v, void* __restrict__ out,
+    float eps) {
+  constexpr int D = feature_dim(DK);
+  constexpr int TPR = DV / 4;            // threads per state row (float4 each)
+  constexpr int RPP = kThreads / TPR;    // rows per pass
+  constexpr int NR = (D + RPP - 1) / RPP;
+  constexpr int NZ = (D + kThreads - 1) / kThreads;
+
+  __shared__ float xq[DK];
+  __shared__ float xk[DK];
+  __shared__ float pq[D];
+  __shared__ float pk[D];
+  __shared__ float4 red[RPP][TPR];
+  __shared__ float dred[kThreads / 64];
+
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < DK) {
+    xq[tid] = load_elem<BF16>(q, bh * DK + tid);
+    xk[tid] = load_elem<BF16>(k, bh * DK + tid);
+  }
+  __syncthreads();
+  for (int f = tid; f < D; f += kThreads) {
+    int i, j;
+    pair_of(f, DK, i, j);
+    const float w = (i == j) ? 1.0f : kSqrt2;
+    pq[f] = w * xq[i] * xq[j];
+    pk[f] = w * xk[i] * xk[j];
+  }
+
+  const int r0 = tid / TPR;
+  const int c4 = tid - r0 * TPR;
+  float4 vv;
+  vv.x = load_elem<BF16>(v, bh * DV + c4 * 4 + 0);
+  vv.y = load_elem<BF16>(v, bh * DV + c4 * 4 + 1);
+  vv.z = load_elem<BF16>(v, bh * DV + c4 * 4 + 2);
+  vv.w = load_elem<BF16>(v, bh * DV + c4 * 4 + 3);
+
+  float4* Sh = reinterpret_cast<float4*>(S + bh * static_cast<int64_t>(D) * DV);
+  float4 s[NR];
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    const int r = r0 + n * RPP;
+    if (r < D) s[n] = Sh[r * TPR + c4];
+  }
+  float* zh = z + bh * D;
+  float zv[NZ];
+#pragma unroll
+  for (int n = 0; n < NZ; ++n) {
+    const int f = tid + n * kThreads;
+    if (f < D) zv[n] = zh[f];
+  }
+  __syncthreads();  // pq / pk ready
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int n = 0; n < NR; ++n) {
+    const int r = r0 + n * RPP;
+    if (r < D) {
+      const float a = pk[r];
+      const float b = pq[r];
+      float4 t = s[n];
+      t.x += a * vv.x;
+      t.y += a * vv.y;
+      t.z += a * vv.z;
+      t.w += a * vv.w;
+      Sh[r * TPR + c4] = t;
+      acc.x += b * t.x;
+      acc.y += b * t.y;
+      acc.z += b * t.z;
+      acc.w += b * t.w;
+    }
+  }
+  float den = 0.f;
+#pragma unroll
+  for (int n = 0; n < NZ; ++n) {
+    const int f = tid + n * kThreads;
+    if (f < D) {
+      const float t = zv[n] + pk[f];
+      zh[f] = t;
+      den += pq[f] * t;
+    }
+  }
+  red[r0][c4] = acc;
+  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+  if ((tid & 63) == 0) dred[tid >> 6] = den;
+  __syncthreads();
+
+  if (tid < DV) {
+    float tot = 0.f;
+    const int cg = tid >> 2;
+    const int lane = tid & 3;
+    for (int r = 0; r < RPP; ++r) {
+      const float4 x = red[r][cg];
+      tot += (lane == 0) ? x.x : (lane == 1) ? x.y : (lane == 2) ? x.z : x.w;
+    }
+    float dd = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) dd += dred[w];
+    store_elem<BF16>(out, bh * DV + tid, tot / (dd + eps));
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_dv(float* S, float* z, const void* q, const void* k, const void* v,
+                     void* out, int64_t BH, float eps, bool bf16, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>(BH));
+  if (bf16) {
+    decode_kernel<DK, DV, true><<<grid, kThreads, 0, s>>>(S, z, q, k, v, out, eps);
+  } else {
+    decode_kernel<DK, DV, false><<<grid, kThreads, 0, s>>>(S, z, q, k, v, out, eps);
+  }
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_d(float* S, float* z, const void* q, const void* k, const void* v,
+                    void* out, int64_t BH, int dv, float eps, bool bf16, hipStream_t s) {
+  switch (dv) {
+    case 16: return launch_dv<DK, 16>(S, z, q, k, v, out, BH, eps, bf16, s);
+    case 32: return launch_dv<DK, 32>(S, z, q, k, v, out, BH, eps, bf16, s);
+    case 64: return launch_dv<DK, 64>(S, z, q, k, v, out, BH, eps, bf16, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode(float* S, float* z, const void* q, const void* k,
+                         const void* v, void* out, int64_t BH, int d, int dv,
+                         float eps, bool bf16, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_d<16>(S, z, q, k, v, out, BH, dv, eps, bf16, stream);
+    case 32: return launch_d<32>(S, z, q, k, v, out, BH, dv, eps, bf16, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kata

@@ -1,0 +1,74 @@
+// Kernel launchers of libkata (internal C++ interface between the C ABI layer
+// and the HIP kernels).  Every launcher assumes its arguments were validated
+// by the caller (api.cpp) and only enqueues work on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kata {
+
+// phi(x) for `rows` vectors of width d (public sqrt(2) packing).
+hipError_t launch_feature_map(const void* x, void* phi, int64_t rows, int d,
+                              bool x_bf16, bool phi_bf16, hipStream_t stream);
+
+// One recurrent step for BH independent heads.
+hipError_t launch_decode(float* S, float* z, const void* q, const void* k,
+                         const void* v, void* out, int64_t BH, int d, int dv,
+                         float eps, bool bf16, hipStream_t stream);
+
+// Sums over spans of tokens:
+//   S_out[(bh*n_spans+sp)*s_stride + f*dv + c] = sum_t w_f k_i k_j v_t[c]
+//   z_out[(bh*n_spans+sp)*z_stride + f]        = sum_t w_f k_i k_j
+// over tokens t in [sp*span, min(T, (sp+1)*span)) of head bh, with
+// w_f = sqrt(2) off the diagonal when `sym`, else 1.  Spans that are the
+// last of their head are skipped when `skip_last` (their sum is not needed
+// by an exclusive prefix).
+struct StateArgs {
+  const void* k;
+  const void* v;
+  float* S_out;
+  float* z_out;
+  int64_t BH;
+  int64_t T;
+  int d;
+  int dv;
+  int64_t span;      // tokens per span
+  int64_t n_spans;   // spans per head
+  int64_t s_stride;  // floats between consecutive (bh, span) S blocks
+  int64_t z_stride;  // floats between consecutive (bh, span) z blocks
+  bool bf16;
+  bool sym;
+  bool skip_last;
+};
+hipError_t launch_state_valu(const StateArgs& a, hipStream_t stream);
+
+// In-place exclusive prefix over the span axis of ws[BH][n_spans][E].
+hipError_t launch_scan_sequential(float* ws, int64_t BH, int64_t n_spans,
+                                  int64_t E, hipStream_t stream);
+hipError_t launch_scan_associative(float* ws, int64_t BH, int64_t n_spans,
+                                   int64_t E, hipStream_t stream);
+
+// Chunked readout with carried state, VALU fp32 arithmetic.  Each workgroup
+// takes one span of `G` chunks of one head (and a slice of dv columns),
+// starts from the exclusive prefix state of that span (or zero when
+// prefix == nullptr), and for each chunk reads out then updates the state.
+struct OutputArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  const float* prefix;  // [BH][n_spans][D*dv + D] or nullptr
+  int64_t BH;
+  int64_t T;
+  int d;
+  int dv;
+  int chunk;
+  int64_t G;        // chunks per span
+  int64_t n_spans;  // spans per head
+  float eps;
+  bool bf16;
+};
+hipError_t launch_output_valu(const OutputArgs& a, hipStream_t stream);
+
+}  // namespace kata

@@ -1,0 +1,135 @@
+#include "plan.h"
+
+#include <cstdio>
+
+#include "kernels.h"
+
+namespace kata {
+namespace {
+
+constexpr int64_t kValuDvTile = 16;
+constexpr int64_t kMaxSpans = 8192;     // the associative scan keeps a head's spans in LDS
+constexpr int64_t kTargetWorkgroups = 2048;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
+                         kata_dtype_t dtype, kata_scan_t scan) {
+  ForwardPlan p;
+  p.BH = static_cast<int64_t>(B) * H;
+  p.T = T;
+  p.d = d;
+  p.dv = dv;
+  p.chunk = chunk;
+  p.D = d * (d + 1) / 2;
+  p.bf16 = dtype == KATA_BF16;
+  p.path = Path::Valu;
+  p.n_chunks = ceil_div(T, chunk);
+  p.E = static_cast<int64_t>(p.D) * dv + p.D;
+
+  const int64_t tiles = dv / kValuDvTile;
+  // enough spans to give the readout ~kTargetWorkgroups workgroups
+  int64_t spans = ceil_div(kTargetWorkgroups, p.BH * tiles);
+  if (spans > p.n_chunks) spans = p.n_chunks;
+  if (spans < 1) spans = 1;
+  p.G = ceil_div(p.n_chunks, spans);
+  if (ceil_div(p.n_chunks, p.G) > kMaxSpans) p.G = ceil_div(p.n_chunks, kMaxSpans);
+  p.n_spans = ceil_div(p.n_chunks, p.G);
+
+  if (scan == KATA_SCAN_AUTO) {
+    scan = p.n_spans >= 64 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;
+  }
+  p.scan = scan;
+  p.wg_output = p.BH * p.n_spans * tiles;
+  if (p.n_spans > 1) {
+    p.wg_state = p.BH * p.n_spans * tiles;
+    p.ws_bytes = static_cast<size_t>(p.BH * p.n_spans * p.E) * sizeof(float);
+  }
+  return p;
+}
+
+void describe_plan(const ForwardPlan& p, char* buf, size_t len) {
+  std::snprintf(buf, len,
+                "path=%s scan=%s D=%d chunk=%d n_chunks=%lld chunks_per_span=%lld "
+                "n_spans=%lld wg_state=%lld wg_output=%lld workspace_bytes=%zu",
+                p.path == Path::Mfma ? "mfma" : "valu",
+                p.scan == KATA_SCAN_ASSOCIATIVE ? "associative" : "sequential", p.D, p.chunk,
+                static_cast<long long>(p.n_chunks), static_cast<long long>(p.G),
+                static_cast<long long>(p.n_spans), static_cast<long long>(p.wg_state),
+                static_cast<long long>(p.wg_output), p.ws_bytes);
+}
+
+namespace {
+
+hipError_t mark(const kata_stage_events_t* ev, bool begin, int stage, hipStream_t stream) {
+  if (ev == nullptr) return hipSuccess;
+  void* h = begin ? ev->stage_begin[stage] : ev->stage_end[stage];
+  if (h == nullptr) return hipSuccess;
+  return hipEventRecord(static_cast<hipEvent_t>(h), stream);
+}
+
+}  // namespace
+
+hipError_t run_forward(const ForwardPlan& p, const void* q, const void* k, const void* v,
+                       void* out, float eps, float* ws, const kata_stage_events_t* ev,
+                       hipStream_t stream) {
+  hipError_t e = hipSuccess;
+#define KATA_TRY(x)                  \
+  do {                               \
+    e = (x);                         \
+    if (e != hipSuccess) return e;   \
+  } while (0)
+  KATA_TRY(mark(ev, true, 0, stream));
+  if (p.n_spans > 1) {
+    StateArgs s{};
+    s.k = k;
+    s.v = v;
+    s.S_out = ws;
+    s.z_out = ws + static_cast<int64_t>(p.D) * p.dv;
+    s.BH = p.BH;
+    s.T = p.T;
+    s.d = p.d;
+    s.dv = p.dv;
+    s.span = p.G * p.chunk;
+    s.n_spans = p.n_spans;
+    s.s_stride = p.E;
+    s.z_stride = p.E;
+    s.bf16 = p.bf16;
+    s.sym = false;
+    s.skip_last = true;
+    KATA_TRY(launch_state_valu(s, stream));
+    KATA_TRY(mark(ev, false, 0, stream));
+    KATA_TRY(mark(ev, true, 1, stream));
+    KATA_TRY((p.scan == KATA_SCAN_ASSOCIATIVE)
+                 ? launch_scan_associative(ws, p.BH, p.n_spans, p.E, stream)
+                 : launch_scan_sequential(ws, p.BH, p.n_spans, p.E, stream));
+  } else {
+    KATA_TRY(mark(ev, false, 0, stream));
+    KATA_TRY(mark(ev, true, 1, stream));
+  }
+  KATA_TRY(mark(ev, false, 1, stream));
+  OutputArgs o{};
+  o.q = q;
+  o.k = k;
+  o.v = v;
+  o.out = out;
+  o.prefix = p.n_spans > 1 ? ws : nullptr;
+  o.BH = p.BH;
+  o.T = p.T;
+  o.d = p.d;
+  o.dv = p.dv;
+  o.chunk = p.chunk;
+  o.G = p.G;
+  o.n_spans = p.n_spans;
+  o.eps = eps;
+  o.bf16 = p.bf16;
+  KATA_TRY(mark(ev, true, 2, stream));
+  KATA_TRY(launch_output_valu(o, stream));
+  KATA_TRY(mark(ev, false, 2, stream));
+#undef KATA_TRY
+  return hipSuccess;
+}
+
+}  // namespace kata

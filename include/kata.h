@@ -1,0 +1,176 @@
+/*
+ * kata.h -- C ABI of libkata: causal kernelized linear attention with the
+ * rank-one PSD feature map, for AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method: "Kernelized Linear Attention: Breaking the Capacity
+ * Wall with Symmetric Cones" (Ghriss & Chakraborty, arXiv 2607.17419), cited
+ * below as "the KATA page".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
+ *    by the caller.  The library never allocates, frees or keeps device
+ *    memory, and keeps no mutable global state; calls are reentrant.
+ *  - Tensors are dense, row-major, with the layouts stated per call.  Every
+ *    pointer must be 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    device work is enqueued on it asynchronously; nothing synchronises.
+ *  - Arguments are validated on the host before anything is enqueued.  On any
+ *    error the call returns a status other than KATA_OK and has launched
+ *    nothing and written nothing.  A failed launch returns KATA_ERR_DEVICE.
+ *    Faults during execution surface at the caller's next synchronisation.
+ *  - NaN/Inf inputs are not checked; they propagate.
+ *  - Feature map: for x in R^d, phi(x) has D = d(d+1)/2 coordinates, the
+ *    row-major upper triangle of x x^T, coordinate (i, j), i <= j, at index
+ *    i*d - i*(i-1)/2 + (j - i), scaled by sqrt(2) when i != j, so that
+ *    phi(q) . phi(k) = (q . k)^2 (the KATA page, Sec. 3.1 rank-one lift and
+ *    Eq. 8 packed count).
+ */
+#ifndef KATA_H_
+#define KATA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KATA_F32 = 0,  /* IEEE binary32 */
+  KATA_BF16 = 1  /* bfloat16 (upper half of binary32), round-to-nearest-even */
+} kata_dtype_t;
+
+typedef enum {
+  KATA_SCAN_AUTO = 0,        /* library picks (measured default per shape) */
+  KATA_SCAN_SEQUENTIAL = 1,  /* linear-depth pass over chunk states */
+  KATA_SCAN_ASSOCIATIVE = 2  /* log-depth parallel scan over chunk states */
+} kata_scan_t;
+
+typedef enum {
+  KATA_OK = 0,
+  KATA_ERR_INVALID_VALUE = 1, /* null pointer, non-positive size, bad eps, aliasing, misalignment */
+  KATA_ERR_UNSUPPORTED = 2,   /* valid but outside the supported set (d, dv, chunk, dtype) */
+  KATA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  KATA_ERR_DEVICE = 4         /* a HIP call or kernel launch failed */
+} kata_status_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kata_status_string(kata_status_t status);
+
+/* Packed feature width D = d(d+1)/2 (the KATA page, Eq. 8); -1 if d <= 0. */
+int64_t kata_feature_dim(int d);
+
+/*
+ * kata_feature_map -- phi(x) for `rows` vectors (the KATA page, Sec. 3.1:
+ * psi(u) = u u^T, packed as described above).
+ *   x   : [rows, d] in x_dtype
+ *   phi : [rows, D] in phi_dtype (fp32 arithmetic, one rounding to phi_dtype)
+ * Supported: 1 <= d <= 64, any rows >= 1.
+ */
+kata_status_t kata_feature_map(const void* x, void* phi, int64_t rows, int d,
+                               kata_dtype_t x_dtype, kata_dtype_t phi_dtype,
+                               void* stream);
+
+/*
+ * Bytes of device workspace kata_forward_chunked needs for this shape and
+ * scan mode (0 on invalid arguments).  The workspace holds one fp32 state
+ * pair (D x dv + D) per span of chunks the inter-chunk prefix runs over.
+ */
+size_t kata_forward_workspace_bytes(int B, int H, int64_t T, int d, int dv,
+                                    int chunk, kata_scan_t scan);
+
+/*
+ * kata_forward_chunked -- causal normalised read with the rank-one PSD kernel,
+ *   o_t = sum_{s<=t} (q_t.k_s)^2 v_s / (sum_{s<=t} (q_t.k_s)^2 + eps),
+ * computed in the exact O(T) chunked-state form of the KATA page, Sec. 4.1
+ * Eqs. 17-20 (per-chunk states phi(K_c)^T V_c and phi(K_c)^T 1, an exclusive
+ * prefix over chunks, and per chunk the readout phi(Q_c) S_prefix plus the
+ * causally masked (Q_c K_c^T)^2 block times V_c, normalised).  The prefix over
+ * chunk states is the vector-space cumulative sum of Sec. 4.2, taken either
+ * sequentially or as a log-depth associative scan (`scan`).
+ *   q, k : [B, H, T, d] in dtype;  v, out : [B, H, T, dv] in dtype
+ *   eps  : finite, >= 0; added once to the accumulated denominator
+ *   chunk: chunk length C; a final partial chunk is zero-padded (App. D.2)
+ * Arithmetic: KATA_F32 uses fp32 throughout; KATA_BF16 uses bf16 operands
+ * with fp32 accumulation and fp32 normalisation, output rounded to bf16.
+ * Supported: d in {16, 32}; dv in {16, 32, 64}; chunk in {32, 64, 128};
+ * T >= 1; out must not overlap q, k or v; workspace_bytes >=
+ * kata_forward_workspace_bytes(...) (workspace may be NULL when that is 0).
+ * Deterministic for fixed arguments, scan mode and device.
+ */
+kata_status_t kata_forward_chunked(const void* q, const void* k, const void* v,
+                                   void* out, int B, int H, int64_t T, int d,
+                                   int dv, int chunk, float eps,
+                                   kata_dtype_t dtype, kata_scan_t scan,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * Optional profiling hook: hipEvent_t handles (as void*) recorded on `stream`
+ * immediately before and after each stage of kata_forward_chunked -- stage 0
+ * the span-state sums, stage 1 the prefix over spans, stage 2 the chunked
+ * readout.  A stage the plan does not run gets its two events recorded back
+ * to back.  NULL entries are skipped.  The events are caller-owned.
+ */
+typedef struct {
+  void* stage_begin[3];
+  void* stage_end[3];
+} kata_stage_events_t;
+
+/*
+ * kata_forward_chunked_profiled -- kata_forward_chunked, additionally
+ * recording the stage events in `events` (may be NULL).  Same contract,
+ * validation and results.
+ */
+kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const void* v,
+                                            void* out, int B, int H, int64_t T, int d,
+                                            int dv, int chunk, float eps,
+                                            kata_dtype_t dtype, kata_scan_t scan,
+                                            void* workspace, size_t workspace_bytes,
+                                            const kata_stage_events_t* events,
+                                            void* stream);
+
+/*
+ * kata_prefill_state -- recurrent state of a history, for decoding:
+ *   S = sum_t phi(k_t) v_t^T   [B*H, D, dv] fp32 (row-major, dv contiguous)
+ *   z = sum_t phi(k_t)         [B*H, D]     fp32
+ * (the KATA page, Sec. 2: S_t and Z_t of Eq. 2), with the sqrt(2)-weighted
+ * packing above.  k : [B, H, T, d], v : [B, H, T, dv] in dtype.  S and z are
+ * overwritten.  Supported: d in {16, 32}; dv in {16, 32, 64}; T >= 1.
+ */
+kata_status_t kata_prefill_state(const void* k, const void* v, float* S,
+                                 float* z, int B, int H, int64_t T, int d,
+                                 int dv, kata_dtype_t dtype, void* stream);
+
+/*
+ * kata_decode_step -- one token of the additive recurrence (the KATA page,
+ * Sec. 2: S_t = S_{t-1} + psi(k_t) v_t^T, Z_t = Z_{t-1} + psi(k_t)), then
+ * the normalised read including that token:
+ *   S += phi(k) v^T;  z += phi(k);  out = phi(q)^T S / (phi(q)^T z + eps).
+ *   S    : [B*H, D, dv] fp32, updated in place (layout as kata_prefill_state)
+ *   z    : [B*H, D]     fp32, updated in place
+ *   q, k : [B*H, d] in dtype;  v, out : [B*H, dv] in dtype
+ * fp32 arithmetic.  Supported: d in {16, 32}; dv in {16, 32, 64}.
+ * out must not overlap S, z, q, k or v.
+ */
+kata_status_t kata_decode_step(float* S, float* z, const void* q,
+                               const void* k, const void* v, void* out,
+                               int B, int H, int d, int dv, float eps,
+                               kata_dtype_t dtype, void* stream);
+
+/*
+ * kata_forward_plan -- describe the launch plan kata_forward_chunked uses for
+ * these arguments as a one-line text (kernels, chunk span per prefix entry,
+ * grid sizes) into buf (NUL-terminated, truncated to buf_len).  Returns the
+ * same status kata_forward_chunked's validation would, minus pointer checks.
+ */
+kata_status_t kata_forward_plan(int B, int H, int64_t T, int d, int dv,
+                                int chunk, kata_dtype_t dtype,
+                                kata_scan_t scan, char* buf, size_t buf_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KATA_H_ */

@@ -9,4 +9,5 @@ from .kata_oracle import (  # noqa: F401
     feature_weights,
     forward_chunked,
     forward_quadratic,
+    forward_rows,
 )

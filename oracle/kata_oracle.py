@@ -114,6 +114,23 @@ def forward_quadratic(q: np.ndarray, k: np.ndarray, v: np.ndarray, eps: float,
     return out.reshape(lead + (T, vf.shape[-1]))
 
 
+def forward_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, eps: float) -> np.ndarray:
+    """The same plain definition as forward_quadratic, for selected query rows
+    of one head only (for spot checks of long sequences).
+
+    q, k: [T, d]; v: [T, dv]; rows: query positions.  Returns [len(rows), dv]:
+    o_t = sum_{s<=t} (q_t.k_s)^2 v_s / (sum_{s<=t} (q_t.k_s)^2 + eps).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((len(rows), v.shape[-1]))
+    for n, t in enumerate(rows):
+        c = (k[: t + 1] @ q[t]) ** 2
+        out[n] = (c @ v[: t + 1]) / (c.sum() + eps)
+    return out
+
+
 def forward_chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int,
                     eps: float) -> np.ndarray:
     """Chunkwise form, Eqs. 17-20 with the sequential inter-chunk prefix.

@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point include/kata.h declares, sizes and plans are consistent, and
+every validation error path returns its status without touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import associative_memory_amd as am
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kata.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(am.LIB_PATH),
+                                reason="libkata.so not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kata_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = am.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 8
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in kata.h but not exported"
+    assert sorted(am.EXPORTED) == syms
+
+
+def test_status_strings_and_feature_dim():
+    assert am.status_string(0) == "KATA_OK"
+    assert am.status_string(3) == "KATA_ERR_WORKSPACE"
+    assert am.status_string(99) == "KATA_ERR_UNKNOWN"
+    assert [am.kata_feature_dim(d) for d in (1, 2, 16, 32, 64)] == [1, 3, 136, 528, 2080]
+    assert am.kata_feature_dim(0) == -1
+
+
+def test_workspace_and_plan_consistent():
+    L = am.lib()
+    for (B, H, T, d, dv, C) in [(1, 1, 256, 16, 16, 32), (4, 8, 2048, 16, 64, 64),
+                                (2, 16, 8192, 32, 64, 64), (1, 8, 131072, 16, 64, 128),
+                                (1, 1, 1, 16, 16, 32), (3, 2, 1000, 32, 32, 128)]:
+        for scan in (0, 1, 2):
+            ws = L.kata_forward_workspace_bytes(B, H, T, d, dv, C, scan)
+            for dt in (F32, BF16):
+                plan = am.kata_forward_plan(B, H, T, d, dv, C, dt, scan)
+                fields = dict(kv.split("=") for kv in plan.split())
+                assert int(fields["workspace_bytes"]) <= ws
+                n_chunks = -(-T // C)
+                assert int(fields["n_chunks"]) == n_chunks
+                G, n_spans = int(fields["chunks_per_span"]), int(fields["n_spans"])
+                assert G * n_spans >= n_chunks > G * (n_spans - 1)
+                if scan == 1:
+                    assert fields["scan"] == "sequential"
+                if scan == 2:
+                    assert fields["scan"] == "associative"
+    assert L.kata_forward_workspace_bytes(0, 1, 16, 16, 16, 32, 0) == 0
+    assert L.kata_forward_workspace_bytes(1, 1, 16, 24, 16, 32, 0) == 0
+
+
+# Fake, aligned, distinct "device" addresses: validation must reject before
+# any use of them.
+P = [ctypes.c_void_p((i + 1) << 36) for i in range(8)]
+NULL = None
+
+
+def fwd(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=64, d=16, dv=16, C=32, eps=1e-6,
+        dt=BF16, scan=0, ws=P[4], wsb=1 << 30, stream=None):
+    return am.lib().kata_forward_chunked(q, k, v, out, B, H, T, d, dv, C, eps, dt, scan, ws, wsb,
+                                         stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), INVALID), (dict(k=NULL), INVALID), (dict(v=NULL), INVALID),
+    (dict(out=NULL), INVALID),
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(T=0), INVALID),
+    (dict(d=24), UNSUPPORTED), (dict(d=64), UNSUPPORTED), (dict(dv=48), UNSUPPORTED),
+    (dict(C=16), UNSUPPORTED), (dict(C=256), UNSUPPORTED),
+    (dict(eps=-1e-6), INVALID), (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
+    (dict(dt=7), INVALID), (dict(scan=5), INVALID),
+    (dict(q=ctypes.c_void_p(P[0].value + 4)), INVALID),     # misaligned
+    (dict(out=P[0]), INVALID),                                # out aliases q
+    (dict(out=ctypes.c_void_p(P[2].value + 16)), INVALID),   # out overlaps v
+    (dict(T=100000, wsb=16), WORKSPACE),                      # workspace too small
+    (dict(T=100000, ws=NULL), WORKSPACE),                     # workspace missing
+    (dict(T=100000, ws=P[3]), INVALID),                       # workspace overlaps out
+])
+def test_forward_error_paths(kw, status):
+    assert fwd(**kw) == status
+
+
+def test_decode_error_paths():
+    L = am.lib()
+    dec = lambda S=P[0], z=P[1], q=P[2], k=P[3], v=P[4], out=P[5], B=1, H=1, d=16, dv=64, eps=1e-6, dt=F32: \
+        L.kata_decode_step(S, z, q, k, v, out, B, H, d, dv, eps, dt, None)
+    assert dec(S=NULL) == INVALID
+    assert dec(out=NULL) == INVALID
+    assert dec(B=0) == INVALID
+    assert dec(d=8) == UNSUPPORTED
+    assert dec(dv=100) == UNSUPPORTED
+    assert dec(eps=-1.0) == INVALID
+    assert dec(out=P[0]) == INVALID           # out aliases S
+    assert dec(z=P[0]) == INVALID             # z aliases S
+    assert dec(q=ctypes.c_void_p(P[2].value + 8)) == INVALID
+    assert dec(dt=3) == INVALID
+
+
+def test_prefill_and_feature_map_error_paths():
+    L = am.lib()
+    assert L.kata_prefill_state(NULL, P[1], P[2], P[3], 1, 1, 8, 16, 16, F32, None) == INVALID
+    assert L.kata_prefill_state(P[0], P[1], P[2], P[3], 1, 1, 0, 16, 16, F32, None) == INVALID
+    assert L.kata_prefill_state(P[0], P[1], P[2], P[3], 1, 1, 8, 12, 16, F32, None) == UNSUPPORTED
+    assert L.kata_prefill_state(P[0], P[1], P[2], P[2], 1, 1, 8, 16, 16, F32, None) == INVALID
+    assert L.kata_feature_map(NULL, P[1], 4, 16, F32, F32, None) == INVALID
+    assert L.kata_feature_map(P[0], P[1], 0, 16, F32, F32, None) == INVALID
+    assert L.kata_feature_map(P[0], P[1], 4, 65, F32, F32, None) == UNSUPPORTED
+    assert L.kata_feature_map(P[0], P[0], 4, 16, F32, F32, None) == INVALID
+    buf = ctypes.create_string_buffer(8)
+    assert L.kata_forward_plan(1, 1, 64, 16, 16, 32, BF16, 0, None, 0) == INVALID
+    assert L.kata_forward_plan(1, 1, 64, 16, 16, 32, BF16, 0, buf, 8) == OK
+    assert len(buf.value) == 7  # truncated, NUL-terminated

@@ -1,0 +1,138 @@
+"""GPU parity of the feature map, the decode-state prefill and the recurrent
+decode step against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import associative_memory_amd as am
+import kata_inputs as ki
+from oracle import kata_oracle as orc
+from gpu_util import check, say, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("d", [1, 3, 16, 32, 64])
+@pytest.mark.parametrize("xd,pd", [(ki.F32, ki.F32), (ki.BF16, ki.F32), (ki.F32, ki.BF16),
+                                   (ki.BF16, ki.BF16)])
+def test_feature_map(d, xd, pd):
+    say(f"feature_map d={d} x={xd} phi={pd}")
+    g = np.random.Generator(np.random.PCG64(d))
+    rows = 1037
+    xs, x64 = ki.as_storage(g.standard_normal((rows, d)), xd)
+    x = to_dev(xs, xd)
+    phi = am.kata_feature_map(x, phi_dtype=torch.bfloat16 if pd == ki.BF16 else torch.float32)
+    torch.cuda.synchronize()
+    got = to_host64(phi)
+    ref = orc.feature_map(x64)
+    # one fp32 product chain then one rounding to the output type
+    rel = 2.0 ** -8 if pd == ki.BF16 else 4 * 2.0 ** -24
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + 1e-30)
+
+
+def _decode_case(heads, prefill, steps, d, dv, seed, eps=1e-6):
+    di = ki.decode_inputs(seed, heads, prefill, steps, d, dv)
+    pk = to_dev(di.pk[:, None], ki.F32)  # [heads, 1, P, d] as B = heads, H = 1
+    pv = to_dev(di.pv[:, None], ki.F32)
+    S, z = am.kata_prefill_state(pk, pv)
+    torch.cuda.synchronize()
+    S0, z0 = orc.decode_state(di.pk.astype(np.float64), di.pv.astype(np.float64))
+    return di, S, z, S0, z0
+
+
+@pytest.mark.parametrize("d,dv", [(16, 64), (16, 16), (32, 32), (32, 64)])
+def test_prefill_state_matches_oracle(d, dv):
+    say(f"prefill d={d} dv={dv}")
+    di, S, z, S0, z0 = _decode_case(5, 300, 0, d, dv, seed=3)
+    Sg, zg = to_host64(S), to_host64(z)
+    # fp32 sums of 300 products of magnitude <= max|v|
+    bound = 300 * 4 * 2.0 ** -24 * (1 + np.abs(di.pv).max())
+    assert np.abs(Sg - S0).max() <= bound
+    assert np.abs(zg - z0).max() <= 300 * 4 * 2.0 ** -24
+
+
+@pytest.mark.parametrize("d,dv,dtype", [(16, 64, ki.F32), (16, 16, ki.F32), (32, 64, ki.F32),
+                                        (16, 64, ki.BF16)])
+def test_decode_steps_match_oracle(d, dv, dtype):
+    say(f"decode d={d} dv={dv} dtype={dtype}")
+    heads, prefill, steps, eps = 7, 200, 24, 1e-6
+    di, S, z, S_ref, z_ref = _decode_case(heads, prefill, steps, d, dv, seed=11)
+    vmax = max(np.abs(di.pv).max(), np.abs(di.sv).max())
+    gots, refs = [], []
+    for s in range(steps):
+        qs, q64 = ki.as_storage(di.sq[s], dtype)
+        ks, k64 = ki.as_storage(di.sk[s], dtype)
+        vs, v64 = ki.as_storage(di.sv[s], dtype)
+        out = am.kata_decode_step(S, z, to_dev(qs, dtype), to_dev(ks, dtype), to_dev(vs, dtype),
+                                  eps=eps)
+        S_ref, z_ref, o = orc.decode_step(S_ref, z_ref, q64, k64, v64, eps)
+        gots.append(to_host64(out))
+        refs.append(o)
+    torch.cuda.synchronize()
+    check(np.stack(gots), np.stack(refs), dtype, vmax, f"decode d={d} dv={dv}")
+    np.testing.assert_allclose(to_host64(S), S_ref, rtol=0, atol=1e-4 * vmax)
+
+
+def test_decode_continues_forward():
+    # history through the forward and the prefill, then decode steps, equals
+    # the forward over the whole sequence at the new positions
+    B, H, T0, n, d, dv = 2, 2, 640, 16, 16, 64
+    inp = ki.forward_inputs(B, H, T0 + n, d, dv, ki.F32, seed=21)
+    q, k, v = (to_dev(a, ki.F32) for a in (inp.q, inp.k, inp.v))
+    full = am.kata_forward_chunked(q, k, v, 64, eps=1e-6)
+    S, z = am.kata_prefill_state(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous())
+    outs = []
+    for t in range(T0, T0 + n):
+        o = am.kata_decode_step(S, z, q[:, :, t].reshape(B * H, d).contiguous(),
+                                k[:, :, t].reshape(B * H, d).contiguous(),
+                                v[:, :, t].reshape(B * H, dv).contiguous(), eps=1e-6)
+        outs.append(o.reshape(B, H, dv))
+    torch.cuda.synchronize()
+    dec = to_host64(torch.stack(outs, dim=2))
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6)[:, :, T0:]
+    vmax = np.abs(inp.v64).max()
+    check(dec, ref, ki.F32, vmax, "decode after prefill")
+    check(to_host64(full)[:, :, T0:], ref, ki.F32, vmax, "forward tail")
+
+
+def test_checkpoint_resume_bitwise():
+    heads, d, dv = 64, 16, 64
+    di = ki.decode_inputs(31, heads, 128, 40, d, dv)
+    pk = to_dev(di.pk[:, None], ki.F32)
+    pv = to_dev(di.pv[:, None], ki.F32)
+    S, z = am.kata_prefill_state(pk, pv)
+    S2, z2 = S.clone(), z.clone()
+    step = lambda S_, z_, s: am.kata_decode_step(S_, z_, to_dev(di.sq[s], ki.F32),
+                                                 to_dev(di.sk[s], ki.F32), to_dev(di.sv[s], ki.F32))
+    a = [step(S, z, s) for s in range(40)]
+    for s in range(20):
+        step(S2, z2, s)
+    S3, z3 = S2.cpu().to("cuda"), z2.cpu().to("cuda")  # round trip through host memory
+    b = [step(S3, z3, s) for s in range(20, 40)]
+    torch.cuda.synchronize()
+    for x, y in zip(a[20:], b):
+        assert torch.equal(x, y)
+    assert torch.equal(S, S3) and torch.equal(z, z3)
+
+
+def test_decode_full_size_sampled_heads():
+    w = ki.DECODE
+    say(f"decode full size {w.name}: drawing inputs on the device")
+    steps = 8
+    pk, pv, sq, sk, sv = ki.decode_inputs_torch(w.seed, w.heads, w.prefill, steps, w.d, w.dv, "cuda")
+    S, z = am.kata_prefill_state(pk[:, None], pv[:, None])
+    outs = [am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps) for s in range(steps)]
+    torch.cuda.synchronize()
+    heads = [0, 1, 17, 1000, 2047, 3333, 4094, 4095]
+    vmax = max(float(pv.abs().max()), float(sv.abs().max()))
+    got = np.stack([to_host64(o[heads]) for o in outs])
+    hk = pk[heads].double().cpu().numpy()
+    hv = pv[heads].double().cpu().numpy()
+    S_ref, z_ref = orc.decode_state(hk, hv)
+    refs = []
+    for s in range(steps):
+        S_ref, z_ref, o = orc.decode_step(S_ref, z_ref, sq[s, heads].double().cpu().numpy(),
+                                          sk[s, heads].double().cpu().numpy(),
+                                          sv[s, heads].double().cpu().numpy(), w.eps)
+        refs.append(o)
+    check(got, np.stack(refs), ki.F32, vmax, "decode full size, sampled heads")

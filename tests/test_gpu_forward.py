@@ -1,0 +1,154 @@
+"""GPU parity of the chunked forward against the fp64 oracle, through the C ABI.
+
+Small workloads are compared element by element over every output; the long
+workloads (T = 8192 at d = 32, T = 131072) in the launch configuration the
+benchmark times are compared on every output of sampled heads (where the
+quadratic oracle takes seconds) and on sampled rows of every head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import associative_memory_amd as am
+import kata_inputs as ki
+from oracle import kata_oracle as orc
+from gpu_util import check, say, to_dev, to_host64
+
+pytestmark = pytest.mark.gpu
+
+SCANS = ("sequential", "associative")
+
+
+def run(inp: ki.ForwardInputs, chunk, eps, scan="auto"):
+    q, k, v = (to_dev(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+    out = am.kata_forward_chunked(q, k, v, chunk, eps=eps, scan=scan)
+    torch.cuda.synchronize()
+    return to_host64(out)
+
+
+@pytest.mark.parametrize("scan", SCANS)
+@pytest.mark.parametrize("w", [ki.TINY, ki.MEDIUM], ids=lambda w: w.name)
+def test_full_parity_small_workloads(w, scan):
+    say(f"forward {w.name} scan={scan}")
+    inp = ki.workload_inputs(w)
+    got = run(inp, w.chunk, w.eps, scan)
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, w.eps)
+    check(got, ref, w.dtype, np.abs(inp.v64).max(), w.name)
+
+
+def _sampled_rows(T, chunk, g, n=24):
+    rows = {0, 1, chunk - 1, chunk, chunk + 1, T // 2, T - 2, T - 1}
+    rows.update(int(x) for x in g.integers(0, T, n))
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+@pytest.mark.parametrize("scan", SCANS)
+@pytest.mark.parametrize("w", [ki.WIDE, ki.LONG], ids=lambda w: w.name)
+def test_sampled_parity_long_workloads(w, scan):
+    say(f"forward {w.name} scan={scan} plan: "
+        + am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk, am.KATA_BF16, scan))
+    inp = ki.workload_inputs(w)
+    got = run(inp, w.chunk, w.eps, scan)
+    vmax = np.abs(inp.v64).max()
+    g = np.random.Generator(np.random.PCG64(w.seed + 100))
+    # every output of one head at the two ends of the (b, h) range, where the
+    # quadratic oracle finishes in seconds
+    if w.T <= 8192:
+        for (b, h) in ((0, 0), (w.B - 1, w.H - 1)):
+            ref = orc.forward_quadratic(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], w.eps)
+            check(got[b, h], ref, w.dtype, vmax, f"{w.name} head ({b},{h}) all rows")
+    # sampled rows of every head
+    refs, gots = [], []
+    for b in range(w.B):
+        for h in range(w.H):
+            rows = _sampled_rows(w.T, w.chunk, g)
+            refs.append(orc.forward_rows(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], rows, w.eps))
+            gots.append(got[b, h, rows])
+    check(np.concatenate(gots), np.concatenate(refs), w.dtype, vmax, f"{w.name} sampled rows")
+
+
+RAGGED = [
+    # (B, H, T, d, dv, chunk, dtype)
+    (1, 1, 1, 16, 16, 32, ki.F32),
+    (1, 2, 77, 16, 64, 128, ki.BF16),
+    (2, 3, 1000, 16, 64, 64, ki.BF16),
+    (3, 2, 1000, 32, 32, 128, ki.BF16),
+    (2, 1, 333, 32, 16, 32, ki.F32),
+    (1, 3, 4099, 16, 32, 64, ki.F32),
+    (1, 1, 5000, 32, 64, 64, ki.BF16),
+]
+
+
+@pytest.mark.parametrize("scan", SCANS)
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "B{}H{}T{}d{}dv{}C{}{}".format(*c))
+def test_ragged_and_edge_shapes(case, scan):
+    B, H, T, d, dv, chunk, dtype = case
+    say(f"forward ragged {case} scan={scan}")
+    inp = ki.forward_inputs(B, H, T, d, dv, dtype, seed=T + d + dv)
+    got = run(inp, chunk, 1e-6, scan)
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6)
+    check(got, ref, dtype, np.abs(inp.v64).max(), str(case))
+
+
+def test_deterministic_run_to_run():
+    w = ki.MEDIUM
+    inp = ki.workload_inputs(w)
+    q, k, v = (to_dev(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+    for scan in SCANS:
+        a = am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan)
+        b = am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_chunk_size_invariance_and_guard_bands():
+    B, H, T, d, dv = 2, 2, 1500, 16, 64
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.F32, seed=77)
+    q, k, v = (to_dev(a, ki.F32) for a in (inp.q, inp.k, inp.v))
+    outs = []
+    for chunk in (32, 64, 128):
+        # out inside a larger buffer with canaries on both sides
+        pad = 1024
+        buf = torch.full((pad + B * H * T * dv + pad,), 12345.0, device="cuda")
+        out = buf[pad:pad + B * H * T * dv].view(B, H, T, dv)
+        am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, out=out)
+        torch.cuda.synchronize()
+        assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0)
+        outs.append(to_host64(out))
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6)
+    for o in outs:
+        check(o, ref, ki.F32, np.abs(inp.v64).max(), "chunk invariance")
+    assert np.abs(outs[0] - outs[2]).max() <= 2e-4 * np.abs(inp.v64).max()
+
+
+def test_symmetries_on_device():
+    # sign flips of q/k rows and a common rotation leave the read unchanged
+    B, H, T, d, dv = 1, 2, 700, 16, 32
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.F32, seed=5)
+    g = np.random.Generator(np.random.PCG64(6))
+    U, _ = np.linalg.qr(g.standard_normal((d, d)))
+    sgn = g.choice([-1.0, 1.0], size=(B, H, T, 1))
+    q2 = (inp.q64 * sgn) @ U.T
+    k2 = (inp.k64 * sgn[..., ::-1, :]) @ U.T
+    base = run(inp, 64, 1e-6)
+    alt = ki.ForwardInputs(q2.astype(np.float32), k2.astype(np.float32), inp.v, q2, k2, inp.v64, ki.F32)
+    rot = run(alt, 64, 1e-6)
+    ref = orc.forward_quadratic(q2.astype(np.float32).astype(np.float64),
+                                k2.astype(np.float32).astype(np.float64), inp.v64, 1e-6)
+    check(rot, ref, ki.F32, np.abs(inp.v64).max(), "rotated")
+    assert np.abs(rot - base).max() <= 2e-4 * np.abs(inp.v64).max()
+
+
+def test_constant_values_reproduced():
+    # constant v: o_t = c D_t / (D_t + eps); with unit q, k and T >= 64 the
+    # factor is 1 to ~1e-6, an O(1) output the long-T bar can see.
+    B, H, T, d, dv = 1, 1, 4096, 16, 64
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.BF16, seed=12)
+    v = np.zeros_like(inp.v64) + np.linspace(-2, 2, dv)
+    vb, v64 = ki.as_storage(v, ki.BF16)
+    alt = ki.ForwardInputs(inp.q, inp.k, vb, inp.q64, inp.k64, v64, ki.BF16)
+    got = run(alt, 128, 1e-6)
+    ref = orc.forward_quadratic(inp.q64, inp.k64, v64, 1e-6)
+    check(got, ref, ki.BF16, np.abs(v64).max(), "constant v")
+    # beyond the first few tokens the read equals v to bf16 rounding
+    assert np.abs(got[0, 0, 64:] - v64[0, 0, 64:]).max() <= 2 ** -7 * 2

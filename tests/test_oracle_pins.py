@@ -174,6 +174,19 @@ def test_bruteforce_exact_rationals_tiny():
         np.testing.assert_allclose(got, f(want)[0, 0], rtol=1e-13, atol=1e-15)
 
 
+def test_forward_rows_matches_worked_values_and_full_form():
+    ex, q, k, v = _example("three_token_example")
+    got = orc.forward_rows(q[0, 0], k[0, 0], v[0, 0], [2, 0], eps=0.0)
+    np.testing.assert_allclose(got, _f64(ex["out"])[[2, 0]], rtol=0, atol=1e-14)
+    g = np.random.Generator(np.random.PCG64(9))
+    T = 300
+    q, k = _unit(g, (T, 16)), _unit(g, (T, 16))
+    v = g.standard_normal((T, 8))
+    rows = [0, 1, 63, 64, 150, 299]
+    full = orc.forward_quadratic(q[None], k[None], v[None], eps=1e-6)[0]
+    np.testing.assert_allclose(orc.forward_rows(q, k, v, rows, 1e-6), full[rows], rtol=1e-12, atol=1e-14)
+
+
 # ------------------------------------------------------------------ chunked == quadratic
 
 @pytest.mark.parametrize("T", [1, 2, 3, 257])
