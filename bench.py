@@ -1,0 +1,316 @@
+#!/usr/bin/env python3
+"""Benchmark of libkata on one MI355X.
+
+A step is one chunked forward (feature map, intra-chunk block, span states,
+prefix over spans, readout -- the whole forward path) over the long-context
+workload B=1, H=8, T=131072, d=16, dv=64, chunk=128, bf16, with inputs already
+resident in HBM.  `value` is sequence tokens per second, B*T / t_step.  Both
+prefix variants (sequential and associative) are timed and reported; `value`
+is the library's default (auto) choice.  The recurrent decode workload
+(4096 heads, D=136, dv=64, fp32 state, 1024 steps) is timed in the same run
+and reported under "decode" with its own roofline.
+
+The fp64 oracle's timing on the host (a bounded sample, extrapolated to the
+whole workload) is reported as cpu_baseline: a baseline, not the target.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ HIP events
+
+class Hip:
+    """Minimal HIP runtime access for events on the stream the library uses."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.h.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float()
+        assert self.h.hipEventSynchronize(b) == 0
+        assert self.h.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(e)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "associative_memory_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except Exception:
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ forward
+
+def bench_forward(args, hip, am, ki, torch):
+    w = ki.LONG
+    inp = ki.workload_inputs(w)
+
+    def dev(a):
+        return torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    out = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    results = {}
+    for scan in ("sequential", "associative", "auto"):
+        ws_bytes = am.kata_forward_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, w.chunk, scan)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        # timed region: K whole forwards, bracketed by events on the library's stream
+        e0, e1 = hip.event(), hip.event()
+        t_wall = time.perf_counter()
+        hip.record(e0, stream)
+        for _ in range(args.steps):
+            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan, out=out, workspace=ws)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        ms_step = hip.ms(e0, e1) / args.steps
+        # per-stage kernel durations, same launches, one event set per step
+        sets = []
+        for _ in range(args.steps):
+            ev = am.StageEvents()
+            hs = [hip.event() for _ in range(6)]
+            for i in range(3):
+                ev.stage_begin[i] = hs[2 * i]
+                ev.stage_end[i] = hs[2 * i + 1]
+            am.kata_forward_chunked_profiled(q, k, v, w.chunk, ev, eps=w.eps, scan=scan, out=out,
+                                             workspace=ws)
+            sets.append(hs)
+        torch.cuda.synchronize()
+        stage_ms = [0.0, 0.0, 0.0]
+        for hs in sets:
+            for i in range(3):
+                stage_ms[i] += hip.ms(hs[2 * i], hs[2 * i + 1]) / args.steps
+            for h in hs:
+                hip.destroy(h)
+        results[scan] = {
+            "ms_per_step": ms_step,
+            "wall_ms_per_step": 1e3 * t_wall / args.steps,
+            "tokens_per_s": w.B * w.T / (ms_step * 1e-3),
+            "stage_ms": {"span_states": stage_ms[0], "prefix": stage_ms[1], "readout": stage_ms[2]},
+            "plan": am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk, am.KATA_BF16, scan),
+        }
+        hip.destroy(e0)
+        hip.destroy(e1)
+        del ws
+    return w, inp, results
+
+
+# ------------------------------------------------------------------ decode
+
+def bench_decode(args, hip, am, ki, torch):
+    w = ki.DECODE
+    steps = args.decode_steps
+    pk, pv, sq, sk, sv = ki.decode_inputs_torch(w.seed, w.heads, w.prefill, steps, w.d, w.dv, "cuda")
+    S, z = am.kata_prefill_state(pk[:, None], pv[:, None])
+    del pk, pv
+    out = torch.empty((w.heads, w.dv), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for s in range(min(args.warmup, steps)):
+        am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for s in range(steps):
+        am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps, out=out)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    loop_ms = hip.ms(e0, e1)
+    # per-launch kernel durations
+    n = min(steps, 256)
+    evs = [(hip.event(), hip.event()) for _ in range(n)]
+    for s in range(n):
+        hip.record(evs[s][0], stream)
+        am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps, out=out)
+        hip.record(evs[s][1], stream)
+    torch.cuda.synchronize()
+    kern_ms = sum(hip.ms(a, b) for a, b in evs) / n
+    for a, b in evs:
+        hip.destroy(a)
+        hip.destroy(b)
+    hip.destroy(e0)
+    hip.destroy(e1)
+    D = w.d * (w.d + 1) // 2
+    bytes_per_head = 2 * (D * w.dv + D) * 4 + (2 * w.d + 2 * w.dv) * 4
+    alg_bytes = w.heads * bytes_per_head
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    return {
+        "workload": w.name,
+        "heads": w.heads,
+        "steps": steps,
+        "ms_per_step": loop_ms / steps,
+        "kernel_ms": kern_ms,
+        "tokens_per_s": w.seqs * steps / (loop_ms * 1e-3),
+        "head_tokens_per_s": w.heads * steps / (loop_ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("decode"),
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "note": "state (%.1f MB) fits the 256 MB Infinity Cache" % (w.heads * (D * w.dv + D) * 4 / 1e6),
+    }
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(w, inp):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import kata_oracle as orc
+
+    Ts = 65536
+    t = time.perf_counter()
+    orc.forward_quadratic(inp.q64[0, 0, :Ts], inp.k64[0, 0, :Ts], inp.v64[0, 0, :Ts], w.eps)
+    dt = time.perf_counter() - t
+    # the quadratic form's work grows as T^2 per head: scale to all heads at full T
+    full = dt * (w.T / Ts) ** 2 * (w.B * w.H)
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(w.B * w.T / full, 1), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"fp64 quadratic oracle on head (0,0), first {Ts} of {w.T} tokens "
+                      f"({dt:.1f} s), scaled by (T/{Ts})^2 x {w.B * w.H} heads",
+            "sample_seconds": round(dt, 2)}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import associative_memory_amd as am
+    import kata_inputs as ki
+
+    am.lib()  # fails loudly when libkata.so is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    hip = Hip()
+
+    if args.calib_copy:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+
+    w, inp, fwd = bench_forward(args, hip, am, ki, torch)
+    main_r = fwd["auto"]
+    D = w.d * (w.d + 1) // 2
+    BHT = w.B * w.H * w.T
+    flop_per_tok = 2 * ((w.chunk + 1) / 2 * (w.d + w.dv) + 2 * D * w.dv + 2 * D)
+    bytes_per_tok = 2 * (2 * w.d + w.dv) + 2 * w.dv
+    readout_ms = main_r["stage_ms"]["readout"]
+    achieved = bytes_per_tok * BHT / (readout_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "tokens/s + % bf16 MFMA peak, KATA chunked fwd T=131072; decode % HBM BW",
+        "value": round(main_r["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_r["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded unit-norm Gaussian q,k; Gaussian v)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d": w.d, "dv": w.dv,
+                   "chunk": w.chunk, "plan": main_r["plan"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("forward_readout"), "kernel": "readout",
+                     "algorithmic_bytes_per_launch": bytes_per_tok * BHT},
+        "mfma": {"useful_tflops": round(flop_per_tok * BHT / (main_r["ms_per_step"] * 1e-3) / 1e12, 2),
+                 "peak_tflops": BF16_PEAK_TFLOPS,
+                 "frac": round(flop_per_tok * BHT / (main_r["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
+        "head_tokens_per_s": round(BHT / (main_r["ms_per_step"] * 1e-3), 1),
+        "scan_variants": {s: {"tokens_per_s": round(fwd[s]["tokens_per_s"], 1),
+                              "ms_per_step": round(fwd[s]["ms_per_step"], 4),
+                              "stage_ms": {kk: round(vv, 4) for kk, vv in fwd[s]["stage_ms"].items()},
+                              "plan": fwd[s]["plan"]}
+                          for s in ("sequential", "associative")},
+    }
+    if not args.no_decode:
+        rec["decode"] = bench_decode(args, hip, am, ki, torch)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
