@@ -3,6 +3,7 @@
 #include <cstdio>
 
 #include "kernels.h"
+#include "plan_mfma.h"
 
 namespace kata {
 namespace {
@@ -10,6 +11,7 @@ namespace {
 constexpr int64_t kValuDvTile = 16;
 constexpr int64_t kMaxSpans = 8192;     // the associative scan keeps a head's spans in LDS
 constexpr int64_t kTargetWorkgroups = 2048;
+constexpr int64_t kMfmaTargetWorkgroups = 512;  // two resident readout workgroups per CU
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -25,13 +27,14 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.chunk = chunk;
   p.D = d * (d + 1) / 2;
   p.bf16 = dtype == KATA_BF16;
-  p.path = Path::Valu;
   p.n_chunks = ceil_div(T, chunk);
-  p.E = static_cast<int64_t>(p.D) * dv + p.D;
+  const bool mfma = mfma_supported(p.bf16, d, dv, chunk);
+  p.path = mfma ? Path::Mfma : Path::Valu;
+  p.E = mfma ? kMfmaStateFloats : static_cast<int64_t>(p.D) * dv + p.D;
 
-  const int64_t tiles = dv / kValuDvTile;
-  // enough spans to give the readout ~kTargetWorkgroups workgroups
-  int64_t spans = ceil_div(kTargetWorkgroups, p.BH * tiles);
+  const int64_t tiles = mfma ? 1 : dv / kValuDvTile;
+  // enough spans to give the readout about the target number of workgroups
+  int64_t spans = ceil_div(mfma ? kMfmaTargetWorkgroups : kTargetWorkgroups, p.BH * tiles);
   if (spans > p.n_chunks) spans = p.n_chunks;
   if (spans < 1) spans = 1;
   p.G = ceil_div(p.n_chunks, spans);
@@ -44,7 +47,7 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.scan = scan;
   p.wg_output = p.BH * p.n_spans * tiles;
   if (p.n_spans > 1) {
-    p.wg_state = p.BH * p.n_spans * tiles;
+    p.wg_state = p.BH * (mfma ? p.n_spans - 1 : p.n_spans) * tiles;
     p.ws_bytes = static_cast<size_t>(p.BH * p.n_spans * p.E) * sizeof(float);
   }
   return p;
@@ -82,6 +85,33 @@ hipError_t run_forward(const ForwardPlan& p, const void* q, const void* k, const
     if (e != hipSuccess) return e;   \
   } while (0)
   KATA_TRY(mark(ev, true, 0, stream));
+  if (p.path == Path::Mfma) {
+    MfmaArgs m{};
+    m.q = q;
+    m.k = k;
+    m.v = v;
+    m.out = out;
+    m.ws = ws;
+    m.BH = p.BH;
+    m.T = p.T;
+    m.chunk = p.chunk;
+    m.G = p.G;
+    m.n_spans = p.n_spans;
+    m.eps = eps;
+    if (p.n_spans > 1) KATA_TRY(launch_span_state_mfma(m, stream));
+    KATA_TRY(mark(ev, false, 0, stream));
+    KATA_TRY(mark(ev, true, 1, stream));
+    if (p.n_spans > 1) {
+      KATA_TRY((p.scan == KATA_SCAN_ASSOCIATIVE)
+                   ? launch_scan_associative(ws, p.BH, p.n_spans, p.E, stream)
+                   : launch_scan_sequential(ws, p.BH, p.n_spans, p.E, stream));
+    }
+    KATA_TRY(mark(ev, false, 1, stream));
+    KATA_TRY(mark(ev, true, 2, stream));
+    KATA_TRY(launch_readout_mfma(m, stream));
+    KATA_TRY(mark(ev, false, 2, stream));
+    return hipSuccess;
+  }
   if (p.n_spans > 1) {
     StateArgs s{};
     s.k = k;

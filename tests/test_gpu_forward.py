@@ -76,6 +76,10 @@ RAGGED = [
     (2, 1, 333, 32, 16, 32, ki.F32),
     (1, 3, 4099, 16, 32, 64, ki.F32),
     (1, 1, 5000, 32, 64, 64, ki.BF16),
+    (1, 1, 129, 16, 64, 128, ki.BF16),
+    (3, 5, 2500, 16, 64, 128, ki.BF16),
+    (2, 2, 8191, 16, 64, 64, ki.BF16),
+    (1, 3, 40000, 16, 64, 128, ki.BF16),
 ]
 
 
