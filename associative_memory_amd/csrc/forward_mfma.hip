@@ -131,57 +131,62 @@ __device__ __forceinline__ int group_pos(int tg) {
   return (tg >> 3) * 32 + ((a < 4) ? 8 * a : 8 * (a - 4) + 4);
 }
 
+// LDS tiles.  Row strides are padded so that the 16-byte operand reads of 16
+// consecutive lanes (consecutive rows) land on distinct bank groups, and
+// every row starts 16-byte aligned so the reads stay single b128 accesses.
+constexpr int QF_LD = DK + 4;  // fp32 row stride of Q (80 B)
+constexpr int KB_LD = DK + 8;  // bf16 row stride of K (48 B)
+
 template <int C>
-struct Smem {
-  static constexpr int LDT = C + 8;  // bf16 row stride of Vt
-  static constexpr int LDK = C + 4;  // fp32 row stride of Kt
-  uint16_t Vt[VROWS * LDT];          // [value row][token position], rows 64.. = ones, zeros
-  float Kt[DK * LDK];                // [d][token position] fp32
+struct alignas(16) Smem {
+  static constexpr int LDT = C + 8;       // bf16 row stride of Vt (C=128: 272 B)
+  static constexpr int LDK = C + 4;       // fp32 row stride of Kt
+  alignas(16) uint16_t Vt[DV * LDT];      // [value column][token position]
+  alignas(16) float Kt[DK * LDK];         // [d][token position] fp32
 };
 
 template <int C>
-struct SmemOut : Smem<C> {
-  uint16_t Kb[C * DK];               // [token][d] bf16 (score operand)
-  float Qf[C * DK];                  // [token][d] fp32
-  uint16_t Sb[VROWS * SB_LD];        // [value row][feature position] bf16 state copy
+struct alignas(16) SmemOut : Smem<C> {
+  alignas(16) uint16_t Kb[C * KB_LD];     // [token][d] bf16 (score operand)
+  alignas(16) float Qf[C * QF_LD];        // [token][d] fp32
+  alignas(16) uint16_t Sb[VROWS * SB_LD]; // [value row][feature position] bf16 state copy
 };
 
 // ------------------------------------------------------------ chunk staging
 //
 // Global -> registers -> LDS for one chunk.  V: groups of 4 tokens x 8
-// columns (16 B per token), K and Q: groups of 4 tokens x 4 dims (8 B per
-// token).  Tokens at or past T read as zero.
+// columns (16 B per token), written transposed; K and Q: one token row
+// (32 B) per thread.  Tokens at or past T read as zero.
 template <int C, bool WITH_Q>
 struct Stage {
   static constexpr int NVG = (C / 4) * (DV / 8);
-  static constexpr int NKG = (C / 4) * (DK / 4);
   uint4 v[4];
-  uint2 k[4];
-  uint2 q[4];
+  uint4 kq[2];  // one K row (threads [0, C)) or one Q row (threads [C, 2C))
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
                                        const uint16_t* __restrict__ vg, int64_t tok0, int64_t c0,
                                        int64_t T, int tid) {
+    const bool full = c0 + C <= T;
     if (tid < NVG) {
       const int tg = tid % (C / 4), cg = tid / (C / 4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t t = c0 + 4 * tg + r;
-        v[r] = (t < T) ? *reinterpret_cast<const uint4*>(vg + (tok0 + t) * DV + 8 * cg)
-                       : make_uint4(0, 0, 0, 0);
+        v[r] = (full || t < T) ? *reinterpret_cast<const uint4*>(vg + (tok0 + t) * DV + 8 * cg)
+                               : make_uint4(0, 0, 0, 0);
       }
     }
-    if (tid < NKG) {
-      const int tg = tid % (C / 4), dg = tid / (C / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = c0 + 4 * tg + r;
-        k[r] = (t < T) ? *reinterpret_cast<const uint2*>(kg + (tok0 + t) * DK + 4 * dg)
-                       : make_uint2(0, 0);
-        if constexpr (WITH_Q) {
-          q[r] = (t < T) ? *reinterpret_cast<const uint2*>(qg + (tok0 + t) * DK + 4 * dg)
-                         : make_uint2(0, 0);
-        }
+    const int nrows = WITH_Q ? 2 * C : C;
+    if (tid < nrows) {
+      const bool is_q = WITH_Q && tid >= C;
+      const int64_t t = c0 + (is_q ? tid - C : tid);
+      const uint16_t* src = (is_q ? qg : kg) + (tok0 + t) * DK;
+      if (full || t < T) {
+        kq[0] = *reinterpret_cast<const uint4*>(src);
+        kq[1] = *reinterpret_cast<const uint4*>(src + 8);
+      } else {
+        kq[0] = make_uint4(0, 0, 0, 0);
+        kq[1] = make_uint4(0, 0, 0, 0);
       }
     }
   }
@@ -209,41 +214,42 @@ struct Stage {
         *reinterpret_cast<uint2*>(&sm.Vt[(8 * cg + x) * LDT + pos]) = o;
       }
     }
-    if (tid < NKG) {
-      const int tg = tid % (C / 4), dg = tid / (C / 4);
-      const int pos = group_pos(tg);
+    if (tid < C) {
+      // K row: fp32 transposed copy (key features) and, with Q, a bf16 row copy (scores)
+      const int t = tid;
+      const int pos = group_pos(t >> 2) + (t & 3);
+      const uint32_t w[8] = {kq[0].x, kq[0].y, kq[0].z, kq[0].w, kq[1].x, kq[1].y, kq[1].z, kq[1].w};
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        float4 f;
-        f.x = (x & 1) ? hi_bf16((x < 2) ? k[0].x : k[0].y) : lo_bf16((x < 2) ? k[0].x : k[0].y);
-        f.y = (x & 1) ? hi_bf16((x < 2) ? k[1].x : k[1].y) : lo_bf16((x < 2) ? k[1].x : k[1].y);
-        f.z = (x & 1) ? hi_bf16((x < 2) ? k[2].x : k[2].y) : lo_bf16((x < 2) ? k[2].x : k[2].y);
-        f.w = (x & 1) ? hi_bf16((x < 2) ? k[3].x : k[3].y) : lo_bf16((x < 2) ? k[3].x : k[3].y);
-        *reinterpret_cast<float4*>(&sm.Kt[(4 * dg + x) * LDK + pos]) = f;
+      for (int x = 0; x < DK; ++x) {
+        sm.Kt[x * LDK + pos] = (x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]);
       }
       if constexpr (WITH_Q) {
+        *reinterpret_cast<uint4*>(&sm.Kb[t * KB_LD]) = kq[0];
+        *reinterpret_cast<uint4*>(&sm.Kb[t * KB_LD + 8]) = kq[1];
+      }
+    } else if (WITH_Q && tid < 2 * C) {
+      if constexpr (WITH_Q) {
+        const int t = tid - C;
+        const uint32_t w[8] = {kq[0].x, kq[0].y, kq[0].z, kq[0].w, kq[1].x, kq[1].y, kq[1].z, kq[1].w};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          *reinterpret_cast<uint2*>(&sm.Kb[(4 * tg + r) * DK + 4 * dg]) = k[r];
+        for (int c = 0; c < 4; ++c) {
           float4 f;
-          f.x = lo_bf16(q[r].x);
-          f.y = hi_bf16(q[r].x);
-          f.z = lo_bf16(q[r].y);
-          f.w = hi_bf16(q[r].y);
-          *reinterpret_cast<float4*>(&sm.Qf[(4 * tg + r) * DK + 4 * dg]) = f;
+          f.x = lo_bf16(w[2 * c]);
+          f.y = hi_bf16(w[2 * c]);
+          f.z = lo_bf16(w[2 * c + 1]);
+          f.w = hi_bf16(w[2 * c + 1]);
+          *reinterpret_cast<float4*>(&sm.Qf[t * QF_LD + 4 * c]) = f;
         }
       }
     }
   }
 };
 
-// constant rows of Vt: row 64 = 1.0 (bf16 0x3f80), rows 65..79 = 0
-template <int C, class S>
-__device__ __forceinline__ void init_vt_const_rows(S& sm, int tid) {
-  constexpr int LDT = Smem<C>::LDT;
-  for (int e = tid; e < 16 * LDT; e += kThreads) {
-    sm.Vt[64 * LDT + e] = (e < LDT) ? static_cast<uint16_t>(0x3f80) : static_cast<uint16_t>(0);
-  }
+// The ones column of [V | 1 | 0]: value tile 4 holds 1.0 in its first column
+// (lane r == 0 of every lane group) and zeros elsewhere, for every token slot.
+__device__ __forceinline__ u32x4 ones_frag(int r) {
+  const uint32_t one2 = 0x3f803f80u;  // two bf16 1.0
+  return (r == 0) ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
 }
 
 // ------------------------------------------------------------ state update
@@ -271,16 +277,17 @@ __device__ __forceinline__ KeyPairs key_pairs(int w, int r) {
 
 template <int C, class S>
 __device__ __forceinline__ void state_update(f32x4 (&acc)[3][NDT], const S& sm, int w, int lane,
-                                             const KeyPairs& kp) {
+                                             const KeyPairs& kp, const u32x4& ones) {
   constexpr int LDT = Smem<C>::LDT, LDK = Smem<C>::LDK;
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int ks = 0; ks < C / 32; ++ks) {
     u32x4 bv[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    for (int dt = 0; dt < NDT - 1; ++dt) {
       bv[dt] = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * dt + r) * LDT + 32 * ks + 8 * g]);
     }
+    bv[NDT - 1] = ones;
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
       if (w + 4 * m >= NFT) continue;  // uniform per wave
@@ -303,34 +310,48 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[3][NDT], const S& sm, 
   }
 }
 
-// fp32 state tiles <-> workspace, tile-native order ((ft*NDT + dt)*64 + lane)*4 + j
+// fp32 state tiles <-> workspace.  Value tiles 0..3 in tile-native order
+// ((ft*4 + dt)*64 + lane)*4 + j; the ones-column tile only carries z in its
+// column 0 (lanes r == 0), stored as 16 floats per feature tile.
+constexpr int kZOffset = NFT * (NDT - 1) * 256;
+
 __device__ __forceinline__ void load_state(f32x4 (&acc)[3][NDT], const float* __restrict__ P,
                                            int w, int lane) {
+  const int g = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
     const int ft = w + 4 * m;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      if (P != nullptr && ft < NFT) {
-        const float4 x = *reinterpret_cast<const float4*>(P + ((ft * NDT + dt) * 64 + lane) * 4);
-        acc[m][dt] = f32x4{x.x, x.y, x.z, x.w};
-      } else {
-        acc[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+    for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (P == nullptr || ft >= NFT) continue;
+#pragma unroll
+    for (int dt = 0; dt < NDT - 1; ++dt) {
+      const float4 x = *reinterpret_cast<const float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4);
+      acc[m][dt] = f32x4{x.x, x.y, x.z, x.w};
+    }
+    if (r == 0) {
+      const float4 x = *reinterpret_cast<const float4*>(P + kZOffset + ft * 16 + 4 * g);
+      acc[m][NDT - 1] = f32x4{x.x, x.y, x.z, x.w};
     }
   }
 }
 
 __device__ __forceinline__ void store_state(const f32x4 (&acc)[3][NDT], float* __restrict__ P,
                                             int w, int lane) {
+  const int g = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int m = 0; m < 3; ++m) {
     const int ft = w + 4 * m;
     if (ft >= NFT) continue;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      *reinterpret_cast<float4*>(P + ((ft * NDT + dt) * 64 + lane) * 4) =
+    for (int dt = 0; dt < NDT - 1; ++dt) {
+      *reinterpret_cast<float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4) =
           make_float4(acc[m][dt][0], acc[m][dt][1], acc[m][dt][2], acc[m][dt][3]);
+    }
+    if (r == 0) {
+      *reinterpret_cast<float4*>(P + kZOffset + ft * 16 + 4 * g) =
+          make_float4(acc[m][NDT - 1][0], acc[m][NDT - 1][1], acc[m][NDT - 1][2],
+                      acc[m][NDT - 1][3]);
     }
   }
 }
@@ -366,21 +387,30 @@ __global__ __launch_bounds__(kThreads) void span_state_mfma_kernel(MfmaArgs a) {
   const uint16_t* kg = static_cast<const uint16_t*>(a.k);
   const uint16_t* vg = static_cast<const uint16_t*>(a.v);
 
-  init_vt_const_rows<C>(sm, tid);
   const KeyPairs kp = key_pairs(w, lane & 15);
+  const u32x4 ones = ones_frag(lane & 15);
   f32x4 acc[3][NDT];
   load_state(acc, nullptr, w, lane);
 
-  Stage<C, false> st;
-  int64_t c0 = sp * a.G * C;
-  st.load(nullptr, kg, vg, tok0, c0, a.T, tid);
-  for (int64_t gi = 0; gi < a.G; ++gi, c0 += C) {
-    if (c0 >= a.T) break;
+  // two register stages: chunk i+2 is in flight while chunk i is consumed
+  const int64_t first = sp * a.G * C;
+  int64_t end = first + a.G * C;
+  if (end > a.T) end = a.T;
+  Stage<C, false> st0, st1;
+  st0.load(nullptr, kg, vg, tok0, first, a.T, tid);
+  if (first + C < end) st1.load(nullptr, kg, vg, tok0, first + C, a.T, tid);
+  for (int64_t c0 = first; c0 < end; c0 += 2 * C) {
     __syncthreads();
-    st.store(sm, tid);
-    if (gi + 1 < a.G && c0 + C < a.T) st.load(nullptr, kg, vg, tok0, c0 + C, a.T, tid);
+    st0.store(sm, tid);
+    if (c0 + 2 * C < end) st0.load(nullptr, kg, vg, tok0, c0 + 2 * C, a.T, tid);
     __syncthreads();
-    state_update<C>(acc, sm, w, lane, kp);
+    state_update<C>(acc, sm, w, lane, kp, ones);
+    if (c0 + C >= end) break;
+    __syncthreads();
+    st1.store(sm, tid);
+    if (c0 + 3 * C < end) st1.load(nullptr, kg, vg, tok0, c0 + 3 * C, a.T, tid);
+    __syncthreads();
+    state_update<C>(acc, sm, w, lane, kp, ones);
   }
   store_state(acc, a.ws + (bh * a.n_spans + sp) * kMfmaStateFloats, w, lane);
 }
@@ -413,14 +443,20 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
   const uint16_t* vg = static_cast<const uint16_t*>(a.v);
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
-  init_vt_const_rows<C>(sm, tid);
   // feature positions 144..159 hold no feature: keep their state copy zero
   for (int e = tid; e < VROWS * 16; e += kThreads) sm.Sb[(e >> 4) * SB_LD + 144 + (e & 15)] = 0;
   const KeyPairs kp = key_pairs(w, r);
+  const u32x4 ones = ones_frag(r);
   f32x4 acc[3][NDT];
   load_state(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * kMfmaStateFloats : nullptr, w,
              lane);
   write_sb(sm, acc, w, lane);
+
+  int qt[NSLOT];
+#pragma unroll
+  for (int slot = 0; slot < NSLOT; ++slot) qt[slot] = query_tile<C>(w, slot);
+  const int qt_max = qt[NSLOT - 1] > qt[0] ? qt[NSLOT - 1] : qt[0];
+  const float keep2 = (g < 2) ? 1.0f : 0.0f;
 
   Stage<C, true> st;
   int64_t c0 = sp * a.G * C;
@@ -432,28 +468,35 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
     if (gi + 1 < a.G && c0 + C < a.T) st.load(qg, kg, vg, tok0, c0 + C, a.T, tid);
     __syncthreads();
 
-    // ---- readout of this chunk's queries (state = prefix before the chunk)
+    // ---- readout of this chunk's queries (state = prefix before the chunk).
+    // Computed transposed, O^T = [S|z]^T phi_q(Q)^T + [V|1]^T P^T, so a lane
+    // ends up holding 4 consecutive value columns of one query.
+    f32x4 o[NSLOT][NDT];
+    float qr[NSLOT][DK];  // this lane's query row (query 16 qt + r), rotated by 4g
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
-      const int qt = query_tile<C>(w, slot);
-      f32x4 o[NDT];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-      // query row of this lane (query 16 qt + r), read rotated by 4g
-      float qr[DK];
+      for (int dt = 0; dt < NDT; ++dt) o[slot][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const float4 x = *reinterpret_cast<const float4*>(&sm.Qf[(16 * qt + r) * DK + 4 * ((c + g) & 3)]);
-        qr[4 * c + 0] = x.x;
-        qr[4 * c + 1] = x.y;
-        qr[4 * c + 2] = x.z;
-        qr[4 * c + 3] = x.w;
+        const float4 x =
+            *reinterpret_cast<const float4*>(&sm.Qf[(16 * qt[slot] + r) * QF_LD + 4 * ((c + g) & 3)]);
+        qr[slot][4 * c + 0] = x.x;
+        qr[slot][4 * c + 1] = x.y;
+        qr[slot][4 * c + 2] = x.z;
+        qr[slot][4 * c + 3] = x.w;
       }
-      const float keep2 = (g < 2) ? 1.0f : 0.0f;
-      // inter-chunk term: phi_q(Q) [S | z]
+    }
+    // inter-chunk term
 #pragma unroll
-      for (int ks = 0; ks < NKS_F; ++ks) {
+    for (int ks = 0; ks < NKS_F; ++ks) {
+      u32x4 bs[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        bs[dt] = *reinterpret_cast<const u32x4*>(&sm.Sb[(16 * dt + r) * SB_LD + 32 * ks + 8 * g]);
+      }
+#pragma unroll
+      for (int slot = 0; slot < NSLOT; ++slot) {
         float f[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -462,70 +505,84 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
             f[i] = 0.f;
           } else {
             const int pa = kSched.a[e], pb = kSched.b[e];
-            const float x = (pa == pb) ? qr[pa] * qr[pa] : 2.0f * qr[pa] * qr[pb];
+            const float x = (pa == pb) ? qr[slot][pa] * qr[slot][pa]
+                                       : (2.0f * qr[slot][pa]) * qr[slot][pb];
             f[i] = kSched.pair2[e] ? x * keep2 : x;
           }
         }
-        const u32x4 af = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+        const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const u32x4 bs = *reinterpret_cast<const u32x4*>(&sm.Sb[(16 * dt + r) * SB_LD + 32 * ks + 8 * g]);
-          o[dt] = mfma(af, bs, o[dt]);
-        }
+        for (int dt = 0; dt < NDT; ++dt) o[slot][dt] = mfma(bs[dt], qfeat, o[slot][dt]);
       }
-      // intra-chunk term: squared causal scores times [V | 1]
-      u32x4 qf = {0u, 0u, 0u, 0u};
+    }
+    // intra-chunk term: squared causal scores
+    u32x4 qf[NSLOT];
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) {
+      qf[slot] = u32x4{0u, 0u, 0u, 0u};
       if (g < 2) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&sm.Qf[(16 * qt + r) * DK + 8 * g]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&sm.Qf[(16 * qt + r) * DK + 8 * g + 4]);
-        qf = u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
+        const float* qrow = &sm.Qf[(16 * qt[slot] + r) * QF_LD + 8 * g];
+        const float4 x0 = *reinterpret_cast<const float4*>(qrow);
+        const float4 x1 = *reinterpret_cast<const float4*>(qrow + 4);
+        qf[slot] = u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
       }
+    }
 #pragma unroll
-      for (int s = 0; s < C / 32; ++s) {
-        if (2 * s > qt) break;
+    for (int s = 0; s < C / 32; ++s) {
+      if (2 * s > qt_max) break;
+      u32x4 kf[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        kf[h] = u32x4{0u, 0u, 0u, 0u};
+        if (g < 2) kf[h] = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * (2 * s + h) + r) * KB_LD + 8 * g]);
+      }
+      u32x4 bv[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT - 1; ++dt) {
+        bv[dt] = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * dt + r) * LDT + 32 * s + 8 * g]);
+      }
+      bv[NDT - 1] = ones;
+#pragma unroll
+      for (int slot = 0; slot < NSLOT; ++slot) {
+        if (2 * s > qt[slot]) continue;  // uniform per wave
         float p[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int kt = 2 * s + h;
+          const f32x4 sc = mfma(kf[h], qf[slot], f32x4{0.f, 0.f, 0.f, 0.f});  // [key 4g+j][query r]
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
-          if (kt <= qt) {
-            u32x4 kf = {0u, 0u, 0u, 0u};
-            if (g < 2) kf = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * kt + r) * DK + 8 * g]);
-            const f32x4 sc = mfma(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});  // [key 4g+j][query r]
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float x = sc[j] * sc[j];
-              p[h][j] = (kt == qt && 4 * g + j > r) ? 0.f : x;
-            }
+          for (int j = 0; j < 4; ++j) {
+            const float x = sc[j] * sc[j];
+            p[h][j] = (kt > qt[slot] || (kt == qt[slot] && 4 * g + j > r)) ? 0.f : x;
           }
         }
         const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
                           pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const u32x4 bv = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * dt + r) * LDT + 32 * s + 8 * g]);
-          o[dt] = mfma(pf, bv, o[dt]);
-        }
+        for (int dt = 0; dt < NDT; ++dt) o[slot][dt] = mfma(bv[dt], pf, o[slot][dt]);
       }
-      // normalise: the denominator of row 4g+j sits in column 0 of tile 4,
-      // held by lane 16g
+    }
+    // normalise and store: lane r of group 0 holds the denominator of query r
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float den = __shfl(o[NDT - 1][j], lane & ~15);
-        const float inv = 1.0f / (den + a.eps);
-        const int64_t t = c0 + 16 * qt + 4 * g + j;
-        if (t < a.T) {
-          uint16_t* dst = og + (tok0 + t) * DV + r;
+    for (int slot = 0; slot < NSLOT; ++slot) {
+      const float den = __shfl(o[slot][NDT - 1][0], r);
+      const float inv = __builtin_amdgcn_rcpf(den + a.eps);
+      const int64_t t = c0 + 16 * qt[slot] + r;
+      if (t < a.T) {
+        uint16_t* dst = og + (tok0 + t) * DV + 4 * g;
 #pragma unroll
-          for (int dt = 0; dt < NDT - 1; ++dt) dst[16 * dt] = f32_to_bf16_bits(o[dt][j] * inv);
+        for (int dt = 0; dt < NDT - 1; ++dt) {
+          uint2 ob;
+          ob.x = pack2(o[slot][dt][0] * inv, o[slot][dt][1] * inv);
+          ob.y = pack2(o[slot][dt][2] * inv, o[slot][dt][3] * inv);
+          *reinterpret_cast<uint2*>(dst + 16 * dt) = ob;
         }
       }
     }
 
     // ---- carry the state across the chunk
     if (gi + 1 < a.G && c0 + C < a.T) {
-      state_update<C>(acc, sm, w, lane, kp);
+      state_update<C>(acc, sm, w, lane, kp, ones);
       __syncthreads();  // every wave done reading Sb for this chunk
       write_sb(sm, acc, w, lane);
     }

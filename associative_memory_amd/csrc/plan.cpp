@@ -42,7 +42,11 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.n_spans = ceil_div(p.n_chunks, p.G);
 
   if (scan == KATA_SCAN_AUTO) {
-    scan = p.n_spans >= 64 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;
+    // measured on MI355X: with the span counts this planner produces (<= 8192
+    // per head, typically 16..64) the sequential pass is the faster prefix
+    // (e.g. 11 us vs 47 us at 8 heads x 64 spans of 46 KB states); the
+    // log-depth scan only pays off for very long span axes
+    scan = p.n_spans >= 1024 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;
   }
   p.scan = scan;
   p.wg_output = p.BH * p.n_spans * tiles;

@@ -9,8 +9,10 @@ namespace kata {
 
 constexpr int kMfmaValueTiles = 5;    // 4 tiles of 16 value columns + the ones-column tile
 constexpr int kMfmaFeatureTiles = 9;  // feature tiles of 16 holding the 136 features
-// floats of one span state in the workspace (fp32 accumulator tiles)
-constexpr int64_t kMfmaStateFloats = int64_t(kMfmaFeatureTiles) * kMfmaValueTiles * 256;
+// floats of one span state in the workspace: the fp32 accumulator tiles of
+// the 4 value tiles, then the denominator column z (16 floats per feature tile)
+constexpr int64_t kMfmaStateFloats = int64_t(kMfmaFeatureTiles) * (kMfmaValueTiles - 1) * 256 +
+                                     int64_t(kMfmaFeatureTiles) * 16;
 
 struct MfmaArgs {
   const void* q;
