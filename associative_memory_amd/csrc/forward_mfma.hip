@@ -1,31 +1,33 @@
 // Matrix-core (bf16 MFMA, fp32 accumulate) kernels of the chunked forward for
-// d = 16 (D = 136), dv = 64, chunk 64 or 128 -- the KATA page, Sec. 4.1
-// Eqs. 17-20: per chunk c of a span,
+// dv = 64 and head dim d = 16 (D = 136) or d = 32 (D = 528) -- the KATA page,
+// Sec. 4.1 Eqs. 17-20: per chunk c of a span,
 //   O_c = [phi_q(Q_c) S + ((Q_c K_c^T)^2 * M) V_c] / [phi_q(Q_c) z + ((Q_c K_c^T)^2 * M) 1 + eps]
 //   S  += phi_k(K_c)^T V_c,   z += phi_k(K_c)^T 1
 // with the incoming (S, z) of the span taken from the exclusive prefix over
 // span sums (App. E.1 three-stage pipeline).
 //
 // Layout decisions (all private to the forward):
-//  * Features.  The 136 products x_a x_b (a <= b) are placed on 160 feature
+//  * Features.  The D products x_a x_b (a <= b) are placed on feature
 //    positions p = 32*ks + 8*g + i (ks: 32-wide MFMA k-step, g: lane group of
 //    the 16x16x32 operand layout, i: slot).  Group g holds the pairs of group
-//    0 shifted by 4g (mod 16) in both indices: every pair orbit under that
-//    shift has 4 members, except the 4 orbits {(x, x+8), (x+4, x+12)} of 2.
-//    A lane can then build its query-feature operand from its own query row
-//    read rotated by 4g, with compile-time pair indices: phi(Q) never goes
+//    0 shifted by g*d/4 (mod d) in both indices: every orbit of that shift
+//    has 4 pairs, except the d/4 orbits {(x, x+d/2), (x+d/4, x+3d/4)} of 2.
+//    A lane then builds its query-feature operand from its own query row read
+//    rotated by g*d/4, with compile-time pair indices: phi(Q) never goes
 //    through LDS.  Query features carry the off-diagonal factor 2, key
-//    features none, so phi_q . phi_k = (q.k)^2.
-//  * Denominators ride through the MFMAs: V gets a column of ones (tile 4 of
-//    the value tiles), so P.1 and phi_q.z come out of the same products as
-//    the numerators, and z is column 64 of the fp32 state.
+//    features none, so phi_q . phi_k = (q.k)^2 without rounding sqrt(2).
+//  * Denominators ride through the MFMAs: V gets a column of ones (value tile
+//    4, built in registers), so P.1 and phi_q.z come out of the same products
+//    as the numerators, and z is column 64 of the fp32 state.
 //  * Tokens inside each 32-token k-step are stored in the order in which a
-//    16x16 score accumulator hands them to the next product (the two 16-key
-//    halves interleaved in groups of 4), so the squared scores feed P.V
+//    pair of 16x16 score accumulators hands keys to the next product (the two
+//    16-key halves interleaved in groups of 4), so squared scores feed P.V
 //    straight from registers.
-//  * The fp32 state S (feature tiles x 5 value tiles) lives in registers,
-//    feature tiles split across the 4 waves; a bf16 copy in LDS is the
-//    operand of the readout, which is split across waves by query tiles.
+//  * The fp32 state (feature tiles x 5 value tiles) lives in registers, split
+//    across the waves by feature tile; a bf16 copy in LDS is the operand of
+//    the readout, which is split across waves by query tile (and, for d = 32,
+//    by value tiles) and computed transposed, O^T = [S|z]^T phi_q^T + [V|1]^T P^T,
+//    so a lane holds 4 consecutive value columns of one query.
 #include "common.h"
 #include "kernels.h"
 #include "plan_mfma.h"
@@ -38,33 +40,35 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int DK = 16;
 constexpr int DV = 64;
-constexpr int NDT = kMfmaValueTiles;     // 4 value tiles + the ones-column tile
-constexpr int VROWS = 16 * NDT;          // 80
-constexpr int DP = 160;                  // feature positions (5 k-steps of 32)
-constexpr int NKS_F = DP / 32;           // feature k-steps of the readout
-constexpr int NFT = kMfmaFeatureTiles;   // 9 feature tiles hold the 136 features
-constexpr int SB_LD = DP + 8;            // LDS row stride of the bf16 state copy
+constexpr int NDT = kMfmaValueTiles;  // 4 value tiles + the ones-column tile
+constexpr int VROWS = 16 * NDT;       // 80
 
 // ------------------------------------------------------------ feature schedule
 
+template <int DK>
 struct Schedule {
-  int8_t a[40];
-  int8_t b[40];
-  bool pair2[40];  // orbit of size 2: only lane groups 0 and 1 carry it
+  static constexpr int SH = DK / 4;                                     // index shift per lane group
+  static constexpr int NE = (DK * (DK + 1) / 2 - DK / 2) / 4 + DK / 4;  // orbit representatives
+  static constexpr int NKS = (NE + 7) / 8;                              // 32-wide feature k-steps
+  static constexpr int NPOS = 32 * NKS;                                 // feature positions
+  int8_t a[8 * NKS];
+  int8_t b[8 * NKS];
+  bool pair2[8 * NKS];  // orbit of size 2: only lane groups 0 and 1 carry it
 };
 
-constexpr Schedule make_schedule() {
-  Schedule s{};
-  bool used[16][16] = {};
-  int n4 = 0, n2 = 32;
-  for (int i = 0; i < 16; ++i) {
-    for (int j = i; j < 16; ++j) {
+template <int DK>
+constexpr Schedule<DK> make_schedule() {
+  Schedule<DK> s{};
+  constexpr int SH = Schedule<DK>::SH;
+  bool used[DK][DK] = {};
+  int n4 = 0, n2 = (DK * (DK + 1) / 2 - DK / 2) / 4;
+  for (int i = 0; i < DK; ++i) {
+    for (int j = i; j < DK; ++j) {
       if (used[i][j]) continue;
       int size = 0;
       for (int g = 0; g < 4; ++g) {
-        int x = (i + 4 * g) & 15, y = (j + 4 * g) & 15;
+        int x = (i + SH * g) % DK, y = (j + SH * g) % DK;
         if (x > y) { int t = x; x = y; y = t; }
         if (!used[x][y]) { used[x][y] = true; ++size; }
       }
@@ -75,37 +79,124 @@ constexpr Schedule make_schedule() {
       }
     }
   }
-  for (int e = 36; e < 40; ++e) { s.a[e] = -1; s.b[e] = -1; s.pair2[e] = false; }
+  for (int e = Schedule<DK>::NE; e < 8 * Schedule<DK>::NKS; ++e) {
+    s.a[e] = -1; s.b[e] = -1; s.pair2[e] = false;
+  }
   return s;
 }
 
-constexpr Schedule kSched = make_schedule();
-__constant__ Schedule kSchedDev = make_schedule();
+template <int DK>
+constexpr Schedule<DK> kSched = make_schedule<DK>();
 
+__constant__ Schedule<16> kSchedDev16 = make_schedule<16>();
+__constant__ Schedule<32> kSchedDev32 = make_schedule<32>();
+
+template <int DK>
 constexpr bool schedule_ok() {
-  // 32 orbits of 4 and 4 of 2 cover the 136 pairs exactly once
-  bool seen[16][16] = {};
+  // every pair (a <= b) covered exactly once by the orbits
+  bool seen[DK][DK] = {};
   int n = 0;
-  for (int e = 0; e < 36; ++e) {
-    for (int g = 0; g < (kSched.pair2[e] ? 2 : 4); ++g) {
-      int x = (kSched.a[e] + 4 * g) & 15, y = (kSched.b[e] + 4 * g) & 15;
+  for (int e = 0; e < Schedule<DK>::NE; ++e) {
+    const int a = kSched<DK>.a[e], b = kSched<DK>.b[e];
+    if (a < 0 || b < 0) return false;
+    for (int g = 0; g < (kSched<DK>.pair2[e] ? 2 : 4); ++g) {
+      int x = (a + Schedule<DK>::SH * g) % DK, y = (b + Schedule<DK>::SH * g) % DK;
       if (x > y) { int t = x; x = y; y = t; }
       if (seen[x][y]) return false;
       seen[x][y] = true;
       ++n;
     }
   }
-  return n == 136;
+  return n == DK * (DK + 1) / 2;
 }
-static_assert(schedule_ok(), "feature schedule must cover every pair once");
+static_assert(schedule_ok<16>(), "d = 16 feature schedule must cover every pair once");
+static_assert(schedule_ok<32>(), "d = 32 feature schedule must cover every pair once");
+
+// number of 16-position feature tiles holding at least one feature
+template <int DK>
+constexpr int feature_tiles() {
+  int last = 0;
+  for (int p = 0; p < Schedule<DK>::NPOS; ++p) {
+    const int ks = p / 32, g = (p % 32) / 8, i = p % 8, e = 8 * ks + i;
+    if (e < Schedule<DK>::NE && !(kSched<DK>.pair2[e] && g >= 2)) last = p;
+  }
+  return last / 16 + 1;
+}
+static_assert(feature_tiles<16>() == mfma_feature_tiles(16), "feature tile count (d = 16)");
+static_assert(feature_tiles<32>() == mfma_feature_tiles(32), "feature tile count (d = 32)");
+
+template <int DK>
+__device__ __forceinline__ const Schedule<DK>& sched_dev() {
+  if constexpr (DK == 16) {
+    return kSchedDev16;
+  } else {
+    return kSchedDev32;
+  }
+}
 
 // pair (a, b) on feature position p, or a = -1 for an empty position
+template <int DK>
 __device__ __forceinline__ void pair_at(int p, int& a, int& b) {
+  const Schedule<DK>& s = sched_dev<DK>();
   const int ks = p >> 5, o = p & 31, g = o >> 3, i = o & 7;
   const int e = 8 * ks + i;
-  if (e >= 36 || (kSchedDev.pair2[e] && g >= 2)) { a = -1; b = -1; return; }
-  a = (kSchedDev.a[e] + 4 * g) & 15;
-  b = (kSchedDev.b[e] + 4 * g) & 15;
+  if (e >= Schedule<DK>::NE || (s.pair2[e] && g >= 2)) { a = -1; b = -1; return; }
+  a = (s.a[e] + Schedule<DK>::SH * g) % DK;
+  b = (s.b[e] + Schedule<DK>::SH * g) % DK;
+}
+
+// ------------------------------------------------------------ configuration
+
+template <int DK_, int C_>
+struct Cfg {
+  static constexpr int DK = DK_;
+  static constexpr int C = C_;
+  static constexpr int NW = mfma_waves(DK_);  // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int NKS = Schedule<DK>::NKS;
+  static constexpr int NPOS = Schedule<DK>::NPOS;
+  static constexpr int NFT = mfma_feature_tiles(DK_);
+  static constexpr int MFT = (NFT + NW - 1) / NW;   // feature tiles per wave (max)
+  static constexpr int SB_LD = NPOS + 8;            // bf16 row stride of the state copy
+  static constexpr int QF_LD = DK + 4;              // fp32 row stride of Q
+  static constexpr int KB_LD = DK + 8;              // bf16 row stride of K
+  static constexpr int LDT = C + 8;                 // bf16 row stride of V^T
+  static constexpr int LDK = C + 4;                 // fp32 row stride of K^T
+  // readout split: 4 waves take 1 or 2 query tiles each with all value tiles;
+  // 8 waves take one query tile each, at chunk 64 sharing it between two
+  // waves that split the value tiles
+  static constexpr int NSLOT = (NW == 4 && C == 128) ? 2 : 1;  // query tiles per wave
+  static constexpr int NDW = (NW == 8 && C == 64) ? 3 : NDT;   // value tiles per wave
+  static constexpr int NSTAGE = (DK == 16) ? 2 : 1;  // register stages in the span kernel
+  static constexpr int ZOFF = NFT * (NDT - 1) * 256;  // z column offset in a span state
+  static_assert(NT >= 2 * C, "one thread per K row and per Q row");
+  static_assert((NW == 4 || NW == 8) && (C == 64 || C == 128), "tiling");
+};
+
+// query tile of a wave's slot, balanced for the causal work
+template <class CF>
+__device__ __forceinline__ int query_tile(int w, int slot) {
+  if constexpr (CF::NW == 4) {
+    if constexpr (CF::C == 128) {
+      constexpr int t[4][2] = {{0, 1}, {2, 7}, {3, 6}, {4, 5}};
+      return t[w][slot];
+    } else {
+      return w;
+    }
+  } else {
+    return CF::C == 64 ? (w & 3) : w;
+  }
+}
+
+// value tile of a wave's readout index: all five tiles, or for two waves
+// sharing a query tile {0, 1, 4} and {2, 3, 4} (both carry the denominator)
+template <class CF>
+__device__ __forceinline__ int value_tile(int w, int idx) {
+  if constexpr (CF::NDW == NDT) {
+    return idx;
+  } else {
+    return idx == 2 ? 4 : idx + ((w >> 2) << 1);
+  }
 }
 
 // ------------------------------------------------------------ small helpers
@@ -125,43 +216,49 @@ __device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u 
 
 // position of the first of 4 consecutive tokens (group tg) inside a chunk:
 // within each 32-token block, token groups 0..3 sit at 8a, groups 4..7 at
-// 8(a-4)+4, matching the key order of a 16x16 accumulator pair.
+// 8(a-4)+4, matching the key order of a pair of 16x16 accumulators.
 __device__ __forceinline__ int group_pos(int tg) {
   const int a = tg & 7;
   return (tg >> 3) * 32 + ((a < 4) ? 8 * a : 8 * (a - 4) + 4);
 }
 
-// LDS tiles.  Row strides are padded so that the 16-byte operand reads of 16
-// consecutive lanes (consecutive rows) land on distinct bank groups, and
-// every row starts 16-byte aligned so the reads stay single b128 accesses.
-constexpr int QF_LD = DK + 4;  // fp32 row stride of Q (80 B)
-constexpr int KB_LD = DK + 8;  // bf16 row stride of K (48 B)
+// The ones column of [V | 1 | 0]: value tile 4 holds 1.0 in its first column
+// (lane r == 0 of every lane group) and zeros elsewhere, for every token slot.
+__device__ __forceinline__ u32x4 ones_frag(int r) {
+  const uint32_t one2 = 0x3f803f80u;  // two bf16 1.0
+  return (r == 0) ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
+}
 
-template <int C>
+// ------------------------------------------------------------ LDS tiles
+//
+// Row strides are padded so the 16-byte operand reads of 16 consecutive
+// lanes (consecutive rows) land on distinct bank groups; every row starts
+// 16-byte aligned so the reads stay single b128 accesses.
+template <class CF>
 struct alignas(16) Smem {
-  static constexpr int LDT = C + 8;       // bf16 row stride of Vt (C=128: 272 B)
-  static constexpr int LDK = C + 4;       // fp32 row stride of Kt
-  alignas(16) uint16_t Vt[DV * LDT];      // [value column][token position]
-  alignas(16) float Kt[DK * LDK];         // [d][token position] fp32
+  alignas(16) uint16_t Vt[DV * CF::LDT];   // [value column][token position]
+  alignas(16) float Kt[CF::DK * CF::LDK];  // [d][token position] fp32
 };
 
-template <int C>
-struct alignas(16) SmemOut : Smem<C> {
-  alignas(16) uint16_t Kb[C * KB_LD];     // [token][d] bf16 (score operand)
-  alignas(16) float Qf[C * QF_LD];        // [token][d] fp32
-  alignas(16) uint16_t Sb[VROWS * SB_LD]; // [value row][feature position] bf16 state copy
+template <class CF>
+struct alignas(16) SmemOut : Smem<CF> {
+  alignas(16) uint16_t Kb[CF::C * CF::KB_LD];  // [token][d] bf16 (score operand)
+  alignas(16) float Qf[CF::C * CF::QF_LD];     // [token][d] fp32
+  alignas(16) uint16_t Sb[VROWS * CF::SB_LD];  // [value row][feature position] bf16 state
 };
 
 // ------------------------------------------------------------ chunk staging
 //
 // Global -> registers -> LDS for one chunk.  V: groups of 4 tokens x 8
-// columns (16 B per token), written transposed; K and Q: one token row
-// (32 B) per thread.  Tokens at or past T read as zero.
-template <int C, bool WITH_Q>
+// columns (16 B per token), written transposed; K and Q: one token row per
+// thread.  Tokens at or past T read as zero.
+template <class CF, bool WITH_Q>
 struct Stage {
+  static constexpr int C = CF::C, DK = CF::DK;
   static constexpr int NVG = (C / 4) * (DV / 8);
+  static constexpr int RW = DK / 8;  // 16-byte words per K/Q row
   uint4 v[4];
-  uint4 kq[2];  // one K row (threads [0, C)) or one Q row (threads [C, 2C))
+  uint4 kq[RW];  // one K row (threads [0, C)) or one Q row (threads [C, 2C))
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
                                        const uint16_t* __restrict__ vg, int64_t tok0, int64_t c0,
@@ -181,19 +278,16 @@ struct Stage {
       const bool is_q = WITH_Q && tid >= C;
       const int64_t t = c0 + (is_q ? tid - C : tid);
       const uint16_t* src = (is_q ? qg : kg) + (tok0 + t) * DK;
-      if (full || t < T) {
-        kq[0] = *reinterpret_cast<const uint4*>(src);
-        kq[1] = *reinterpret_cast<const uint4*>(src + 8);
-      } else {
-        kq[0] = make_uint4(0, 0, 0, 0);
-        kq[1] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < RW; ++u) {
+        kq[u] = (full || t < T) ? *reinterpret_cast<const uint4*>(src + 8 * u) : make_uint4(0, 0, 0, 0);
       }
     }
   }
 
   template <class S>
   __device__ __forceinline__ void store(S& sm, int tid) const {
-    constexpr int LDT = Smem<C>::LDT, LDK = Smem<C>::LDK;
+    constexpr int LDT = CF::LDT, LDK = CF::LDK;
     if (tid < NVG) {
       const int tg = tid % (C / 4), cg = tid / (C / 4);
       const int pos = group_pos(tg);
@@ -214,74 +308,75 @@ struct Stage {
         *reinterpret_cast<uint2*>(&sm.Vt[(8 * cg + x) * LDT + pos]) = o;
       }
     }
+    uint32_t w[4 * RW];
+#pragma unroll
+    for (int u = 0; u < RW; ++u) {
+      w[4 * u + 0] = kq[u].x;
+      w[4 * u + 1] = kq[u].y;
+      w[4 * u + 2] = kq[u].z;
+      w[4 * u + 3] = kq[u].w;
+    }
     if (tid < C) {
       // K row: fp32 transposed copy (key features) and, with Q, a bf16 row copy (scores)
       const int t = tid;
       const int pos = group_pos(t >> 2) + (t & 3);
-      const uint32_t w[8] = {kq[0].x, kq[0].y, kq[0].z, kq[0].w, kq[1].x, kq[1].y, kq[1].z, kq[1].w};
 #pragma unroll
       for (int x = 0; x < DK; ++x) {
         sm.Kt[x * LDK + pos] = (x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]);
       }
       if constexpr (WITH_Q) {
-        *reinterpret_cast<uint4*>(&sm.Kb[t * KB_LD]) = kq[0];
-        *reinterpret_cast<uint4*>(&sm.Kb[t * KB_LD + 8]) = kq[1];
+#pragma unroll
+        for (int u = 0; u < RW; ++u) *reinterpret_cast<uint4*>(&sm.Kb[t * CF::KB_LD + 8 * u]) = kq[u];
       }
     } else if (WITH_Q && tid < 2 * C) {
       if constexpr (WITH_Q) {
         const int t = tid - C;
-        const uint32_t w[8] = {kq[0].x, kq[0].y, kq[0].z, kq[0].w, kq[1].x, kq[1].y, kq[1].z, kq[1].w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < DK / 4; ++c) {
           float4 f;
           f.x = lo_bf16(w[2 * c]);
           f.y = hi_bf16(w[2 * c]);
           f.z = lo_bf16(w[2 * c + 1]);
           f.w = hi_bf16(w[2 * c + 1]);
-          *reinterpret_cast<float4*>(&sm.Qf[t * QF_LD + 4 * c]) = f;
+          *reinterpret_cast<float4*>(&sm.Qf[t * CF::QF_LD + 4 * c]) = f;
         }
       }
     }
   }
 };
 
-// The ones column of [V | 1 | 0]: value tile 4 holds 1.0 in its first column
-// (lane r == 0 of every lane group) and zeros elsewhere, for every token slot.
-__device__ __forceinline__ u32x4 ones_frag(int r) {
-  const uint32_t one2 = 0x3f803f80u;  // two bf16 1.0
-  return (r == 0) ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
-}
-
 // ------------------------------------------------------------ state update
 //
-// acc[m][dt] += phi_k(K_c)^T [V_c | 1 | 0] for the feature tiles ft = w + 4m
+// acc[m][dt] += phi_k(K_c)^T [V_c | 1 | 0] for the feature tiles ft = w + NW m
 // this wave owns.  The key-feature operand (position 16 ft + r, 8 token
 // slots) is built from two fp32 rows of K^T.
+template <class CF>
 struct KeyPairs {
-  int a[3];
-  int b[3];
+  int a[CF::MFT];
+  int b[CF::MFT];
 };
 
-__device__ __forceinline__ KeyPairs key_pairs(int w, int r) {
-  KeyPairs kp;
+template <class CF>
+__device__ __forceinline__ KeyPairs<CF> key_pairs(int w, int r) {
+  KeyPairs<CF> kp;
 #pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    const int ft = w + 4 * m;
+  for (int m = 0; m < CF::MFT; ++m) {
+    const int ft = w + CF::NW * m;
     int a = -1, b = -1;
-    if (ft < NFT) pair_at(16 * ft + r, a, b);
+    if (ft < CF::NFT) pair_at<CF::DK>(16 * ft + r, a, b);
     kp.a[m] = a;
     kp.b[m] = b;
   }
   return kp;
 }
 
-template <int C, class S>
-__device__ __forceinline__ void state_update(f32x4 (&acc)[3][NDT], const S& sm, int w, int lane,
-                                             const KeyPairs& kp, const u32x4& ones) {
-  constexpr int LDT = Smem<C>::LDT, LDK = Smem<C>::LDK;
+template <class CF, class S>
+__device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S& sm, int w, int lane,
+                                             const KeyPairs<CF>& kp, const u32x4& ones) {
+  constexpr int LDT = CF::LDT, LDK = CF::LDK;
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int ks = 0; ks < C / 32; ++ks) {
+  for (int ks = 0; ks < CF::C / 32; ++ks) {
     u32x4 bv[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT - 1; ++dt) {
@@ -289,8 +384,8 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[3][NDT], const S& sm, 
     }
     bv[NDT - 1] = ones;
 #pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      if (w + 4 * m >= NFT) continue;  // uniform per wave
+    for (int m = 0; m < CF::MFT; ++m) {
+      if (w + CF::NW * m >= CF::NFT) continue;  // uniform per wave
       u32x4 af = {0u, 0u, 0u, 0u};
       if (kp.a[m] >= 0) {
         const float* ra = &sm.Kt[kp.a[m] * LDK + 32 * ks + 8 * g];
@@ -313,43 +408,43 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[3][NDT], const S& sm, 
 // fp32 state tiles <-> workspace.  Value tiles 0..3 in tile-native order
 // ((ft*4 + dt)*64 + lane)*4 + j; the ones-column tile only carries z in its
 // column 0 (lanes r == 0), stored as 16 floats per feature tile.
-constexpr int kZOffset = NFT * (NDT - 1) * 256;
-
-__device__ __forceinline__ void load_state(f32x4 (&acc)[3][NDT], const float* __restrict__ P,
+template <class CF>
+__device__ __forceinline__ void load_state(f32x4 (&acc)[CF::MFT][NDT], const float* __restrict__ P,
                                            int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    const int ft = w + 4 * m;
+  for (int m = 0; m < CF::MFT; ++m) {
+    const int ft = w + CF::NW * m;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (P == nullptr || ft >= NFT) continue;
+    if (P == nullptr || ft >= CF::NFT) continue;
 #pragma unroll
     for (int dt = 0; dt < NDT - 1; ++dt) {
       const float4 x = *reinterpret_cast<const float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4);
       acc[m][dt] = f32x4{x.x, x.y, x.z, x.w};
     }
     if (r == 0) {
-      const float4 x = *reinterpret_cast<const float4*>(P + kZOffset + ft * 16 + 4 * g);
+      const float4 x = *reinterpret_cast<const float4*>(P + CF::ZOFF + ft * 16 + 4 * g);
       acc[m][NDT - 1] = f32x4{x.x, x.y, x.z, x.w};
     }
   }
 }
 
-__device__ __forceinline__ void store_state(const f32x4 (&acc)[3][NDT], float* __restrict__ P,
+template <class CF>
+__device__ __forceinline__ void store_state(const f32x4 (&acc)[CF::MFT][NDT], float* __restrict__ P,
                                             int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    const int ft = w + 4 * m;
-    if (ft >= NFT) continue;
+  for (int m = 0; m < CF::MFT; ++m) {
+    const int ft = w + CF::NW * m;
+    if (ft >= CF::NFT) continue;
 #pragma unroll
     for (int dt = 0; dt < NDT - 1; ++dt) {
       *reinterpret_cast<float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4) =
           make_float4(acc[m][dt][0], acc[m][dt][1], acc[m][dt][2], acc[m][dt][3]);
     }
     if (r == 0) {
-      *reinterpret_cast<float4*>(P + kZOffset + ft * 16 + 4 * g) =
+      *reinterpret_cast<float4*>(P + CF::ZOFF + ft * 16 + 4 * g) =
           make_float4(acc[m][NDT - 1][0], acc[m][NDT - 1][1], acc[m][NDT - 1][2],
                       acc[m][NDT - 1][3]);
     }
@@ -357,28 +452,29 @@ __device__ __forceinline__ void store_state(const f32x4 (&acc)[3][NDT], float* _
 }
 
 // bf16 copy of the owned state tiles into Sb[value row][feature position]
-template <class S>
-__device__ __forceinline__ void write_sb(S& sm, const f32x4 (&acc)[3][NDT], int w, int lane) {
+template <class CF, class S>
+__device__ __forceinline__ void write_sb(S& sm, const f32x4 (&acc)[CF::MFT][NDT], int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    const int ft = w + 4 * m;
-    if (ft >= NFT) continue;
+  for (int m = 0; m < CF::MFT; ++m) {
+    const int ft = w + CF::NW * m;
+    if (ft >= CF::NFT) continue;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 o;
       o.x = pack2(acc[m][dt][0], acc[m][dt][1]);
       o.y = pack2(acc[m][dt][2], acc[m][dt][3]);
-      *reinterpret_cast<uint2*>(&sm.Sb[(16 * dt + r) * SB_LD + 16 * ft + 4 * g]) = o;
+      *reinterpret_cast<uint2*>(&sm.Sb[(16 * dt + r) * CF::SB_LD + 16 * ft + 4 * g]) = o;
     }
   }
 }
 
 // ------------------------------------------------------------ span sums
 
-template <int C>
-__global__ __launch_bounds__(kThreads) void span_state_mfma_kernel(MfmaArgs a) {
-  __shared__ Smem<C> sm;
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
+  constexpr int C = CF::C;
+  __shared__ Smem<CF> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int64_t nsp_work = a.n_spans - 1;  // the last span's sum is never read
   const int64_t bh = blockIdx.x / nsp_work;
@@ -387,52 +483,54 @@ __global__ __launch_bounds__(kThreads) void span_state_mfma_kernel(MfmaArgs a) {
   const uint16_t* kg = static_cast<const uint16_t*>(a.k);
   const uint16_t* vg = static_cast<const uint16_t*>(a.v);
 
-  const KeyPairs kp = key_pairs(w, lane & 15);
+  const KeyPairs<CF> kp = key_pairs<CF>(w, lane & 15);
   const u32x4 ones = ones_frag(lane & 15);
-  f32x4 acc[3][NDT];
-  load_state(acc, nullptr, w, lane);
+  f32x4 acc[CF::MFT][NDT];
+  load_state<CF>(acc, nullptr, w, lane);
 
-  // two register stages: chunk i+2 is in flight while chunk i is consumed
   const int64_t first = sp * a.G * C;
   int64_t end = first + a.G * C;
   if (end > a.T) end = a.T;
-  Stage<C, false> st0, st1;
-  st0.load(nullptr, kg, vg, tok0, first, a.T, tid);
-  if (first + C < end) st1.load(nullptr, kg, vg, tok0, first + C, a.T, tid);
-  for (int64_t c0 = first; c0 < end; c0 += 2 * C) {
-    __syncthreads();
-    st0.store(sm, tid);
-    if (c0 + 2 * C < end) st0.load(nullptr, kg, vg, tok0, c0 + 2 * C, a.T, tid);
-    __syncthreads();
-    state_update<C>(acc, sm, w, lane, kp, ones);
-    if (c0 + C >= end) break;
-    __syncthreads();
-    st1.store(sm, tid);
-    if (c0 + 3 * C < end) st1.load(nullptr, kg, vg, tok0, c0 + 3 * C, a.T, tid);
-    __syncthreads();
-    state_update<C>(acc, sm, w, lane, kp, ones);
+  if constexpr (CF::NSTAGE == 2) {
+    // two register stages: chunk i+2 is in flight while chunk i is consumed
+    Stage<CF, false> st0, st1;
+    st0.load(nullptr, kg, vg, tok0, first, a.T, tid);
+    if (first + C < end) st1.load(nullptr, kg, vg, tok0, first + C, a.T, tid);
+    for (int64_t c0 = first; c0 < end; c0 += 2 * C) {
+      __syncthreads();
+      st0.store(sm, tid);
+      if (c0 + 2 * C < end) st0.load(nullptr, kg, vg, tok0, c0 + 2 * C, a.T, tid);
+      __syncthreads();
+      state_update<CF>(acc, sm, w, lane, kp, ones);
+      if (c0 + C >= end) break;
+      __syncthreads();
+      st1.store(sm, tid);
+      if (c0 + 3 * C < end) st1.load(nullptr, kg, vg, tok0, c0 + 3 * C, a.T, tid);
+      __syncthreads();
+      state_update<CF>(acc, sm, w, lane, kp, ones);
+    }
+  } else {
+    Stage<CF, false> st;
+    st.load(nullptr, kg, vg, tok0, first, a.T, tid);
+    for (int64_t c0 = first; c0 < end; c0 += C) {
+      __syncthreads();
+      st.store(sm, tid);
+      if (c0 + C < end) st.load(nullptr, kg, vg, tok0, c0 + C, a.T, tid);
+      __syncthreads();
+      state_update<CF>(acc, sm, w, lane, kp, ones);
+    }
   }
-  store_state(acc, a.ws + (bh * a.n_spans + sp) * kMfmaStateFloats, w, lane);
+  store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(CF::DK), w, lane);
 }
 
 // ------------------------------------------------------------ readout
 
-// query tiles of each wave, balanced for the causal work: {slot0, slot1}
-template <int C>
-__device__ __forceinline__ int query_tile(int w, int slot) {
-  if constexpr (C == 128) {
-    constexpr int t[4][2] = {{0, 1}, {2, 7}, {3, 6}, {4, 5}};
-    return t[w][slot];
-  } else {
-    return slot == 0 ? w : -1;
-  }
-}
-
-template <int C>
-__global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
-  __shared__ SmemOut<C> sm;
-  constexpr int LDT = Smem<C>::LDT;
-  constexpr int NSLOT = (C == 128) ? 2 : 1;
+template <class CF>
+__global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
+  constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
+  constexpr int LDT = CF::LDT, SB_LD = CF::SB_LD, QF_LD = CF::QF_LD, KB_LD = CF::KB_LD;
+  constexpr int SH = Schedule<DK>::SH;
+  __shared__ SmemOut<CF> sm;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
   const int64_t bh = blockIdx.x / a.n_spans;
@@ -443,22 +541,28 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
   const uint16_t* vg = static_cast<const uint16_t*>(a.v);
   uint16_t* og = static_cast<uint16_t*>(a.out);
 
-  // feature positions 144..159 hold no feature: keep their state copy zero
-  for (int e = tid; e < VROWS * 16; e += kThreads) sm.Sb[(e >> 4) * SB_LD + 144 + (e & 15)] = 0;
-  const KeyPairs kp = key_pairs(w, r);
+  // feature positions past the last feature tile hold no feature: zero once
+  constexpr int ZPOS = CF::NPOS - 16 * CF::NFT;
+  for (int e = tid; e < VROWS * ZPOS; e += CF::NT) {
+    sm.Sb[(e / ZPOS) * SB_LD + 16 * CF::NFT + (e % ZPOS)] = 0;
+  }
+  const KeyPairs<CF> kp = key_pairs<CF>(w, r);
   const u32x4 ones = ones_frag(r);
-  f32x4 acc[3][NDT];
-  load_state(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * kMfmaStateFloats : nullptr, w,
-             lane);
-  write_sb(sm, acc, w, lane);
+  f32x4 acc[CF::MFT][NDT];
+  load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
+                 w, lane);
+  write_sb<CF>(sm, acc, w, lane);
 
   int qt[NSLOT];
 #pragma unroll
-  for (int slot = 0; slot < NSLOT; ++slot) qt[slot] = query_tile<C>(w, slot);
+  for (int slot = 0; slot < NSLOT; ++slot) qt[slot] = query_tile<CF>(w, slot);
   const int qt_max = qt[NSLOT - 1] > qt[0] ? qt[NSLOT - 1] : qt[0];
+  int vt[NDW];
+#pragma unroll
+  for (int i = 0; i < NDW; ++i) vt[i] = value_tile<CF>(w, i);
   const float keep2 = (g < 2) ? 1.0f : 0.0f;
 
-  Stage<C, true> st;
+  Stage<CF, true> st;
   int64_t c0 = sp * a.G * C;
   st.load(qg, kg, vg, tok0, c0, a.T, tid);
   for (int64_t gi = 0; gi < a.G; ++gi, c0 += C) {
@@ -468,19 +572,17 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
     if (gi + 1 < a.G && c0 + C < a.T) st.load(qg, kg, vg, tok0, c0 + C, a.T, tid);
     __syncthreads();
 
-    // ---- readout of this chunk's queries (state = prefix before the chunk).
-    // Computed transposed, O^T = [S|z]^T phi_q(Q)^T + [V|1]^T P^T, so a lane
-    // ends up holding 4 consecutive value columns of one query.
-    f32x4 o[NSLOT][NDT];
-    float qr[NSLOT][DK];  // this lane's query row (query 16 qt + r), rotated by 4g
+    // ---- readout of this chunk's queries (state = prefix before the chunk)
+    f32x4 o[NSLOT][NDW];
+    float qr[NSLOT][DK];  // this lane's query row (query 16 qt + r), rotated by g*SH
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[slot][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < NDW; ++i) o[slot][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 x =
-            *reinterpret_cast<const float4*>(&sm.Qf[(16 * qt[slot] + r) * QF_LD + 4 * ((c + g) & 3)]);
+      for (int c = 0; c < DK / 4; ++c) {
+        const int src = (c + g * (SH / 4)) % (DK / 4);
+        const float4 x = *reinterpret_cast<const float4*>(&sm.Qf[(16 * qt[slot] + r) * QF_LD + 4 * src]);
         qr[slot][4 * c + 0] = x.x;
         qr[slot][4 * c + 1] = x.y;
         qr[slot][4 * c + 2] = x.z;
@@ -489,11 +591,11 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
     }
     // inter-chunk term
 #pragma unroll
-    for (int ks = 0; ks < NKS_F; ++ks) {
-      u32x4 bs[NDT];
+    for (int ks = 0; ks < CF::NKS; ++ks) {
+      u32x4 bs[NDW];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        bs[dt] = *reinterpret_cast<const u32x4*>(&sm.Sb[(16 * dt + r) * SB_LD + 32 * ks + 8 * g]);
+      for (int i = 0; i < NDW; ++i) {
+        bs[i] = *reinterpret_cast<const u32x4*>(&sm.Sb[(16 * vt[i] + r) * SB_LD + 32 * ks + 8 * g]);
       }
 #pragma unroll
       for (int slot = 0; slot < NSLOT; ++slot) {
@@ -501,18 +603,18 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int e = 8 * ks + i;
-          if (e >= 36) {
+          if (e >= Schedule<DK>::NE) {
             f[i] = 0.f;
           } else {
-            const int pa = kSched.a[e], pb = kSched.b[e];
+            const int pa = kSched<DK>.a[e], pb = kSched<DK>.b[e];
             const float x = (pa == pb) ? qr[slot][pa] * qr[slot][pa]
                                        : (2.0f * qr[slot][pa]) * qr[slot][pb];
-            f[i] = kSched.pair2[e] ? x * keep2 : x;
+            f[i] = kSched<DK>.pair2[e] ? x * keep2 : x;
           }
         }
         const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[slot][dt] = mfma(bs[dt], qfeat, o[slot][dt]);
+        for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bs[i], qfeat, o[slot][i]);
       }
     }
     // intra-chunk term: squared causal scores
@@ -520,7 +622,7 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
       qf[slot] = u32x4{0u, 0u, 0u, 0u};
-      if (g < 2) {
+      if (8 * g < DK) {
         const float* qrow = &sm.Qf[(16 * qt[slot] + r) * QF_LD + 8 * g];
         const float4 x0 = *reinterpret_cast<const float4*>(qrow);
         const float4 x1 = *reinterpret_cast<const float4*>(qrow + 4);
@@ -534,14 +636,17 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         kf[h] = u32x4{0u, 0u, 0u, 0u};
-        if (g < 2) kf[h] = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * (2 * s + h) + r) * KB_LD + 8 * g]);
+        if (8 * g < DK) {
+          kf[h] = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * (2 * s + h) + r) * KB_LD + 8 * g]);
+        }
       }
-      u32x4 bv[NDT];
+      u32x4 bv[NDW];
 #pragma unroll
-      for (int dt = 0; dt < NDT - 1; ++dt) {
-        bv[dt] = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * dt + r) * LDT + 32 * s + 8 * g]);
+      for (int i = 0; i < NDW; ++i) {
+        bv[i] = (vt[i] == NDT - 1)
+                    ? ones
+                    : *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * vt[i] + r) * LDT + 32 * s + 8 * g]);
       }
-      bv[NDT - 1] = ones;
 #pragma unroll
       for (int slot = 0; slot < NSLOT; ++slot) {
         if (2 * s > qt[slot]) continue;  // uniform per wave
@@ -559,57 +664,70 @@ __global__ __launch_bounds__(kThreads, 2) void readout_mfma_kernel(MfmaArgs a) {
         const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
                           pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[slot][dt] = mfma(bv[dt], pf, o[slot][dt]);
+        for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
       }
     }
     // normalise and store: lane r of group 0 holds the denominator of query r
+    // (the last readout value tile of every wave is the ones-column tile)
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
-      const float den = __shfl(o[slot][NDT - 1][0], r);
+      const float den = __shfl(o[slot][NDW - 1][0], r);
       const float inv = __builtin_amdgcn_rcpf(den + a.eps);
       const int64_t t = c0 + 16 * qt[slot] + r;
       if (t < a.T) {
         uint16_t* dst = og + (tok0 + t) * DV + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < NDT - 1; ++dt) {
+        for (int i = 0; i < NDW - 1; ++i) {
           uint2 ob;
-          ob.x = pack2(o[slot][dt][0] * inv, o[slot][dt][1] * inv);
-          ob.y = pack2(o[slot][dt][2] * inv, o[slot][dt][3] * inv);
-          *reinterpret_cast<uint2*>(dst + 16 * dt) = ob;
+          ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
+          ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
+          *reinterpret_cast<uint2*>(dst + 16 * vt[i]) = ob;
         }
       }
     }
 
     // ---- carry the state across the chunk
     if (gi + 1 < a.G && c0 + C < a.T) {
-      state_update<C>(acc, sm, w, lane, kp, ones);
+      state_update<CF>(acc, sm, w, lane, kp, ones);
       __syncthreads();  // every wave done reading Sb for this chunk
-      write_sb(sm, acc, w, lane);
+      write_sb<CF>(sm, acc, w, lane);
     }
   }
+}
+
+template <int DK, int C>
+hipError_t launch_span(const MfmaArgs& a, hipStream_t stream) {
+  using CF = Cfg<DK, C>;
+  dim3 grid(static_cast<unsigned>(a.BH * (a.n_spans - 1)));
+  span_state_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int DK, int C>
+hipError_t launch_readout(const MfmaArgs& a, hipStream_t stream) {
+  using CF = Cfg<DK, C>;
+  dim3 grid(static_cast<unsigned>(a.BH * a.n_spans));
+  readout_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.n_spans < 2) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(a.BH * (a.n_spans - 1)));
-  switch (a.chunk) {
-    case 64: span_state_mfma_kernel<64><<<grid, kThreads, 0, stream>>>(a); break;
-    case 128: span_state_mfma_kernel<128><<<grid, kThreads, 0, stream>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.d == 16 && a.chunk == 64) return launch_span<16, 64>(a, stream);
+  if (a.d == 16 && a.chunk == 128) return launch_span<16, 128>(a, stream);
+  if (a.d == 32 && a.chunk == 64) return launch_span<32, 64>(a, stream);
+  if (a.d == 32 && a.chunk == 128) return launch_span<32, 128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(a.BH * a.n_spans));
-  switch (a.chunk) {
-    case 64: readout_mfma_kernel<64><<<grid, kThreads, 0, stream>>>(a); break;
-    case 128: readout_mfma_kernel<128><<<grid, kThreads, 0, stream>>>(a); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  if (a.d == 16 && a.chunk == 64) return launch_readout<16, 64>(a, stream);
+  if (a.d == 16 && a.chunk == 128) return launch_readout<16, 128>(a, stream);
+  if (a.d == 32 && a.chunk == 64) return launch_readout<32, 64>(a, stream);
+  if (a.d == 32 && a.chunk == 128) return launch_readout<32, 128>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kata

@@ -11,7 +11,8 @@ namespace {
 constexpr int64_t kValuDvTile = 16;
 constexpr int64_t kMaxSpans = 8192;     // the associative scan keeps a head's spans in LDS
 constexpr int64_t kTargetWorkgroups = 2048;
-constexpr int64_t kMfmaTargetWorkgroups = 512;  // two resident readout workgroups per CU
+// resident readout workgroups per CU: two of 4 waves at d = 16, one of 8 at d = 32
+constexpr int64_t mfma_target_workgroups(int d) { return d == 16 ? 512 : 256; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -30,11 +31,11 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.n_chunks = ceil_div(T, chunk);
   const bool mfma = mfma_supported(p.bf16, d, dv, chunk);
   p.path = mfma ? Path::Mfma : Path::Valu;
-  p.E = mfma ? kMfmaStateFloats : static_cast<int64_t>(p.D) * dv + p.D;
+  p.E = mfma ? mfma_state_floats(d) : static_cast<int64_t>(p.D) * dv + p.D;
 
   const int64_t tiles = mfma ? 1 : dv / kValuDvTile;
   // enough spans to give the readout about the target number of workgroups
-  int64_t spans = ceil_div(mfma ? kMfmaTargetWorkgroups : kTargetWorkgroups, p.BH * tiles);
+  int64_t spans = ceil_div(mfma ? mfma_target_workgroups(d) : kTargetWorkgroups, p.BH * tiles);
   if (spans > p.n_chunks) spans = p.n_chunks;
   if (spans < 1) spans = 1;
   p.G = ceil_div(p.n_chunks, spans);
@@ -98,6 +99,7 @@ hipError_t run_forward(const ForwardPlan& p, const void* q, const void* k, const
     m.ws = ws;
     m.BH = p.BH;
     m.T = p.T;
+    m.d = p.d;
     m.chunk = p.chunk;
     m.G = p.G;
     m.n_spans = p.n_spans;

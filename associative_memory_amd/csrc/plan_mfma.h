@@ -1,5 +1,5 @@
-// Interface of the matrix-core chunked forward (d = 16, dv = 64, bf16,
-// chunk 64 or 128).  See forward_mfma.hip for the kernel design.
+// Interface of the matrix-core chunked forward (bf16, dv = 64, head dim 16 or
+// 32, chunk 64 or 128).  See forward_mfma.hip for the kernel design.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,21 +7,30 @@
 
 namespace kata {
 
-constexpr int kMfmaValueTiles = 5;    // 4 tiles of 16 value columns + the ones-column tile
-constexpr int kMfmaFeatureTiles = 9;  // feature tiles of 16 holding the 136 features
+constexpr int kMfmaValueTiles = 5;  // 4 tiles of 16 value columns + the ones-column tile
+
+// waves per workgroup: the d = 32 state (33 feature tiles) is spread over 8
+__host__ __device__ constexpr int mfma_waves(int d) { return d == 16 ? 4 : 8; }
+
+// feature tiles of 16 positions holding the d(d+1)/2 features
+__host__ __device__ constexpr int mfma_feature_tiles(int d) { return d == 16 ? 9 : 33; }
+
 // floats of one span state in the workspace: the fp32 accumulator tiles of
 // the 4 value tiles, then the denominator column z (16 floats per feature tile)
-constexpr int64_t kMfmaStateFloats = int64_t(kMfmaFeatureTiles) * (kMfmaValueTiles - 1) * 256 +
-                                     int64_t(kMfmaFeatureTiles) * 16;
+__host__ __device__ constexpr int64_t mfma_state_floats(int d) {
+  return int64_t(mfma_feature_tiles(d)) * (kMfmaValueTiles - 1) * 256 +
+         int64_t(mfma_feature_tiles(d)) * 16;
+}
 
 struct MfmaArgs {
   const void* q;
   const void* k;
   const void* v;
   void* out;
-  float* ws;        // [BH][n_spans][kMfmaStateFloats]
+  float* ws;        // [BH][n_spans][mfma_state_floats(d)]
   int64_t BH;
   int64_t T;
+  int d;
   int chunk;
   int64_t G;        // chunks per span
   int64_t n_spans;  // spans per head
@@ -29,7 +38,7 @@ struct MfmaArgs {
 };
 
 inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
-  return bf16 && d == 16 && dv == 64 && (chunk == 64 || chunk == 128);
+  return bf16 && (d == 16 || d == 32) && dv == 64 && (chunk == 64 || chunk == 128);
 }
 
 // span sums of spans 0 .. n_spans-2 of every head into ws

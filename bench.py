@@ -41,6 +41,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other", action="store_true", help="skip the other forward workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -161,6 +162,50 @@ def bench_forward(args, hip, am, ki, torch):
         hip.destroy(e1)
         del ws
     return w, inp, results
+
+
+def bench_other_workloads(args, hip, am, ki, torch):
+    """The other forward workloads (parity-test shapes), library default plan."""
+    res = {}
+    for w in (ki.MEDIUM, ki.WIDE, ki.TINY):
+        inp = ki.workload_inputs(w)
+        if w.dtype == ki.BF16:
+            dev = lambda a: torch.from_numpy(a.view("int16")).view(torch.bfloat16).cuda()
+        else:
+            dev = lambda a: torch.from_numpy(a).cuda()
+        q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+        out = torch.empty((w.B, w.H, w.T, w.dv), dtype=q.dtype, device="cuda")
+        ws_bytes = am.kata_forward_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, w.chunk, "auto")
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        for _ in range(args.warmup):
+            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(args.steps):
+            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, out=out, workspace=ws)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(e0, e1) / args.steps
+        hip.destroy(e0)
+        hip.destroy(e1)
+        D = w.d * (w.d + 1) // 2
+        BHT = w.B * w.H * w.T
+        es = 2 if w.dtype == ki.BF16 else 4
+        flops = 2 * ((w.chunk + 1) / 2 * (w.d + w.dv) + 2 * D * w.dv + 2 * D) * BHT
+        bytes_ = (es * (2 * w.d + w.dv) + es * w.dv) * BHT
+        res[w.name] = {
+            "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "hbm_gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "plan": am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk,
+                                         am.KATA_BF16 if w.dtype == ki.BF16 else am.KATA_F32, "auto"),
+        }
+    return res
 
 
 # ------------------------------------------------------------------ decode
@@ -303,6 +348,8 @@ def main():
                               "plan": fwd[s]["plan"]}
                           for s in ("sequential", "associative")},
     }
+    if not args.no_other:
+        rec["other_workloads"] = bench_other_workloads(args, hip, am, ki, torch)
     if not args.no_decode:
         rec["decode"] = bench_decode(args, hip, am, ki, torch)
     if not args.no_cpu_baseline:

@@ -67,6 +67,9 @@ def test_workspace_and_plan_consistent():
     assert "path=mfma" in am.kata_forward_plan(4, 8, 2048, 16, 64, 64, BF16, 0)
     assert "path=valu" in am.kata_forward_plan(1, 8, 131072, 16, 64, 128, F32, 0)
     assert "path=valu" in am.kata_forward_plan(1, 8, 4096, 16, 64, 32, BF16, 0)
+    assert "path=mfma" in am.kata_forward_plan(2, 16, 8192, 32, 64, 64, BF16, 0)
+    assert "path=mfma" in am.kata_forward_plan(2, 16, 8192, 32, 64, 128, BF16, 0)
+    assert "path=valu" in am.kata_forward_plan(2, 16, 8192, 32, 32, 64, BF16, 0)
     assert L.kata_forward_workspace_bytes(0, 1, 16, 16, 16, 32, 0) == 0
     assert L.kata_forward_workspace_bytes(1, 1, 16, 24, 16, 32, 0) == 0
 

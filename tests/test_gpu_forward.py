@@ -80,6 +80,9 @@ RAGGED = [
     (3, 5, 2500, 16, 64, 128, ki.BF16),
     (2, 2, 8191, 16, 64, 64, ki.BF16),
     (1, 3, 40000, 16, 64, 128, ki.BF16),
+    (2, 3, 3000, 32, 64, 128, ki.BF16),
+    (1, 2, 9000, 32, 64, 64, ki.BF16),
+    (3, 1, 65, 32, 64, 64, ki.BF16),
 ]
 
 
