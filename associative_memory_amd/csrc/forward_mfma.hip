@@ -214,6 +214,34 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// Score products Sc^T[key][query] = K Q^T with K = d.  At d = 16 the
+// 16x16x16 form takes 4 bf16 per lane (k = 4g + i); at d = 32 the 16x16x32
+// form takes 8 (k = 8g + i).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int DK>
+struct ScoreOpT;
+template <>
+struct ScoreOpT<16> {
+  using type = uint2;
+};
+template <>
+struct ScoreOpT<32> {
+  using type = u32x4;
+};
+template <int DK>
+using ScoreOp = typename ScoreOpT<DK>::type;
+
+template <int DK>
+__device__ __forceinline__ f32x4 score_mfma(const ScoreOp<DK>& a, const ScoreOp<DK>& b) {
+  if constexpr (DK == 16) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                     __builtin_bit_cast(s16x4, b),
+                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  } else {
+    return mfma(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+}
+
 // position of the first of 4 consecutive tokens (group tg) inside a chunk:
 // within each 32-token block, token groups 0..3 sit at 8a, groups 4..7 at
 // 8(a-4)+4, matching the key order of a pair of 16x16 accumulators.
@@ -237,15 +265,42 @@ __device__ __forceinline__ u32x4 ones_frag(int r) {
 template <class CF>
 struct alignas(16) Smem {
   alignas(16) uint16_t Vt[DV * CF::LDT];   // [value column][token position]
-  alignas(16) float Kt[CF::DK * CF::LDK];  // [d][token position] fp32
+  alignas(16) float Kt[(CF::DK + 1) * CF::LDK];  // [d][token position] fp32; row d is zero
 };
 
 template <class CF>
-struct alignas(16) SmemOut : Smem<CF> {
+struct alignas(16) Tiles : Smem<CF> {
   alignas(16) uint16_t Kb[CF::C * CF::KB_LD];  // [token][d] bf16 (score operand)
   alignas(16) float Qf[CF::C * CF::QF_LD];     // [token][d] fp32
+};
+
+template <class CF>
+struct alignas(16) SmemOut : Tiles<CF> {
   alignas(16) uint16_t Sb[VROWS * CF::SB_LD];  // [value row][feature position] bf16 state
 };
+
+// score operand of row `row` from the fp32 Q tile / the bf16 K tile
+template <class CF>
+__device__ __forceinline__ ScoreOp<CF::DK> score_operand(const float* Qf, int row, int g) {
+  if constexpr (CF::DK == 16) {
+    const float4 x = *reinterpret_cast<const float4*>(&Qf[row * CF::QF_LD + 4 * g]);
+    return uint2{pack2(x.x, x.y), pack2(x.z, x.w)};
+  } else {
+    const float* q = &Qf[row * CF::QF_LD + 8 * g];
+    const float4 x0 = *reinterpret_cast<const float4*>(q);
+    const float4 x1 = *reinterpret_cast<const float4*>(q + 4);
+    return u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
+  }
+}
+
+template <class CF>
+__device__ __forceinline__ ScoreOp<CF::DK> score_operand_bf16(const uint16_t* Kb, int row, int g) {
+  if constexpr (CF::DK == 16) {
+    return *reinterpret_cast<const uint2*>(&Kb[row * CF::KB_LD + 4 * g]);
+  } else {
+    return *reinterpret_cast<const u32x4*>(&Kb[row * CF::KB_LD + 8 * g]);
+  }
+}
 
 // ------------------------------------------------------------ chunk staging
 //
@@ -345,6 +400,12 @@ struct Stage {
   }
 };
 
+// the zero row of K^T read by empty feature positions
+template <class CF, class S>
+__device__ __forceinline__ void zero_kt_row(S& sm, int tid) {
+  for (int e = tid; e < CF::LDK; e += CF::NT) sm.Kt[CF::DK * CF::LDK + e] = 0.f;
+}
+
 // ------------------------------------------------------------ state update
 //
 // acc[m][dt] += phi_k(K_c)^T [V_c | 1 | 0] for the feature tiles ft = w + NW m
@@ -364,8 +425,9 @@ __device__ __forceinline__ KeyPairs<CF> key_pairs(int w, int r) {
     const int ft = w + CF::NW * m;
     int a = -1, b = -1;
     if (ft < CF::NFT) pair_at<CF::DK>(16 * ft + r, a, b);
-    kp.a[m] = a;
-    kp.b[m] = b;
+    // an empty position reads the zero row of K^T: its features are 0
+    kp.a[m] = a < 0 ? CF::DK : a;
+    kp.b[m] = b < 0 ? CF::DK : b;
   }
   return kp;
 }
@@ -386,19 +448,17 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S
 #pragma unroll
     for (int m = 0; m < CF::MFT; ++m) {
       if (w + CF::NW * m >= CF::NFT) continue;  // uniform per wave
-      u32x4 af = {0u, 0u, 0u, 0u};
-      if (kp.a[m] >= 0) {
-        const float* ra = &sm.Kt[kp.a[m] * LDK + 32 * ks + 8 * g];
-        const float* rb = &sm.Kt[kp.b[m] * LDK + 32 * ks + 8 * g];
-        const float4 a0 = *reinterpret_cast<const float4*>(ra);
-        const float4 a1 = *reinterpret_cast<const float4*>(ra + 4);
-        const float4 b0 = *reinterpret_cast<const float4*>(rb);
-        const float4 b1 = *reinterpret_cast<const float4*>(rb + 4);
-        af.x = pack2(a0.x * b0.x, a0.y * b0.y);
-        af.y = pack2(a0.z * b0.z, a0.w * b0.w);
-        af.z = pack2(a1.x * b1.x, a1.y * b1.y);
-        af.w = pack2(a1.z * b1.z, a1.w * b1.w);
-      }
+      const float* ra = &sm.Kt[kp.a[m] * LDK + 32 * ks + 8 * g];
+      const float* rb = &sm.Kt[kp.b[m] * LDK + 32 * ks + 8 * g];
+      const float4 a0 = *reinterpret_cast<const float4*>(ra);
+      const float4 a1 = *reinterpret_cast<const float4*>(ra + 4);
+      const float4 b0 = *reinterpret_cast<const float4*>(rb);
+      const float4 b1 = *reinterpret_cast<const float4*>(rb + 4);
+      u32x4 af;
+      af.x = pack2(a0.x * b0.x, a0.y * b0.y);
+      af.y = pack2(a0.z * b0.z, a0.w * b0.w);
+      af.z = pack2(a1.x * b1.x, a1.y * b1.y);
+      af.w = pack2(a1.z * b1.z, a1.w * b1.w);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = mfma(af, bv[dt], acc[m][dt]);
     }
@@ -452,8 +512,9 @@ __device__ __forceinline__ void store_state(const f32x4 (&acc)[CF::MFT][NDT], fl
 }
 
 // bf16 copy of the owned state tiles into Sb[value row][feature position]
-template <class CF, class S>
-__device__ __forceinline__ void write_sb(S& sm, const f32x4 (&acc)[CF::MFT][NDT], int w, int lane) {
+template <class CF>
+__device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 (&acc)[CF::MFT][NDT],
+                                         int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int m = 0; m < CF::MFT; ++m) {
@@ -464,7 +525,7 @@ __device__ __forceinline__ void write_sb(S& sm, const f32x4 (&acc)[CF::MFT][NDT]
       uint2 o;
       o.x = pack2(acc[m][dt][0], acc[m][dt][1]);
       o.y = pack2(acc[m][dt][2], acc[m][dt][3]);
-      *reinterpret_cast<uint2*>(&sm.Sb[(16 * dt + r) * CF::SB_LD + 16 * ft + 4 * g]) = o;
+      *reinterpret_cast<uint2*>(&Sb[(16 * dt + r) * CF::SB_LD + 16 * ft + 4 * g]) = o;
     }
   }
 }
@@ -475,7 +536,10 @@ template <class CF>
 __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
   constexpr int C = CF::C;
   __shared__ Smem<CF> sm;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave: keep it scalar so every
+  // wave-dependent branch is a scalar branch, not an exec-mask region
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nsp_work = a.n_spans - 1;  // the last span's sum is never read
   const int64_t bh = blockIdx.x / nsp_work;
   const int64_t sp = blockIdx.x - bh * nsp_work;
@@ -483,6 +547,7 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
   const uint16_t* kg = static_cast<const uint16_t*>(a.k);
   const uint16_t* vg = static_cast<const uint16_t*>(a.v);
 
+  zero_kt_row<CF>(sm, tid);
   const KeyPairs<CF> kp = key_pairs<CF>(w, lane & 15);
   const u32x4 ones = ones_frag(lane & 15);
   f32x4 acc[CF::MFT][NDT];
@@ -525,14 +590,144 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
 
 // ------------------------------------------------------------ readout
 
+// Readout of one chunk by readout wave `w` (of 4, or of 8 at d = 32): the
+// chunk's queries against the state copy Sb (the prefix before the chunk)
+// plus the squared causal scores of the chunk, normalised and stored.
+template <class CF>
+__device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_t* __restrict__ Sb,
+                                              int w, int lane, int64_t c0, int64_t tok0, int64_t T,
+                                              float eps, uint16_t* __restrict__ og) {
+  constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
+  constexpr int LDT = CF::LDT, SB_LD = CF::SB_LD, QF_LD = CF::QF_LD;
+  constexpr int SH = Schedule<DK>::SH;
+  const int g = lane >> 4, r = lane & 15;
+  const u32x4 ones = ones_frag(r);
+  const float keep2 = (g < 2) ? 1.0f : 0.0f;
+  int qt[NSLOT];
+#pragma unroll
+  for (int slot = 0; slot < NSLOT; ++slot) qt[slot] = query_tile<CF>(w, slot);
+  const int qt_max = qt[NSLOT - 1] > qt[0] ? qt[NSLOT - 1] : qt[0];
+  int vt[NDW];
+#pragma unroll
+  for (int i = 0; i < NDW; ++i) vt[i] = value_tile<CF>(w, i);
+
+  f32x4 o[NSLOT][NDW];
+  float qr[NSLOT][DK];  // this lane's query row (query 16 qt + r), rotated by g*SH
+#pragma unroll
+  for (int slot = 0; slot < NSLOT; ++slot) {
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) o[slot][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DK / 4; ++c) {
+      const int src = (c + g * (SH / 4)) % (DK / 4);
+      const float4 x = *reinterpret_cast<const float4*>(&tl.Qf[(16 * qt[slot] + r) * QF_LD + 4 * src]);
+      qr[slot][4 * c + 0] = x.x;
+      qr[slot][4 * c + 1] = x.y;
+      qr[slot][4 * c + 2] = x.z;
+      qr[slot][4 * c + 3] = x.w;
+    }
+  }
+  // inter-chunk term
+#pragma unroll
+  for (int ks = 0; ks < CF::NKS; ++ks) {
+    u32x4 bs[NDW];
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) {
+      bs[i] = *reinterpret_cast<const u32x4*>(&Sb[(16 * vt[i] + r) * SB_LD + 32 * ks + 8 * g]);
+    }
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) {
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = 8 * ks + i;
+        if (e >= Schedule<DK>::NE) {
+          f[i] = 0.f;
+        } else {
+          const int pa = kSched<DK>.a[e], pb = kSched<DK>.b[e];
+          const float x = (pa == pb) ? qr[slot][pa] * qr[slot][pa]
+                                     : (2.0f * qr[slot][pa]) * qr[slot][pb];
+          f[i] = kSched<DK>.pair2[e] ? x * keep2 : x;
+        }
+      }
+      const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+#pragma unroll
+      for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bs[i], qfeat, o[slot][i]);
+    }
+  }
+  // intra-chunk term: squared causal scores.  The score product has K = d:
+  // one 16x16x16 product at d = 16, one 16x16x32 product at d = 32.
+  ScoreOp<DK> qf[NSLOT];
+#pragma unroll
+  for (int slot = 0; slot < NSLOT; ++slot) qf[slot] = score_operand<CF>(tl.Qf, 16 * qt[slot] + r, g);
+#pragma unroll
+  for (int s = 0; s < C / 32; ++s) {
+    if (2 * s > qt_max) break;
+    ScoreOp<DK> kf[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kf[h] = score_operand_bf16<CF>(tl.Kb, 16 * (2 * s + h) + r, g);
+    u32x4 bv[NDW];
+#pragma unroll
+    for (int i = 0; i < NDW; ++i) {
+      bv[i] = (vt[i] == NDT - 1)
+                  ? ones
+                  : *reinterpret_cast<const u32x4*>(&tl.Vt[(16 * vt[i] + r) * LDT + 32 * s + 8 * g]);
+    }
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) {
+      if (2 * s > qt[slot]) continue;  // uniform per wave
+      float p[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kt = 2 * s + h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
+        if (kt > qt[slot]) continue;  // fully masked tile: uniform per wave
+        const f32x4 sc = score_mfma<DK>(kf[h], qf[slot]);  // [key 4g+j][query r]
+        if (kt < qt[slot]) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[h][j] = sc[j] * sc[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[h][j] = (4 * g + j > r) ? 0.f : sc[j] * sc[j];
+        }
+      }
+      const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
+                        pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
+#pragma unroll
+      for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
+    }
+  }
+  // normalise and store: lane r of group 0 holds the denominator of query r
+  // (the last readout value tile of every wave is the ones-column tile)
+#pragma unroll
+  for (int slot = 0; slot < NSLOT; ++slot) {
+    const float den = __shfl(o[slot][NDW - 1][0], r);
+    const float inv = __builtin_amdgcn_rcpf(den + eps);
+    const int64_t t = c0 + 16 * qt[slot] + r;
+    if (t < T) {
+      uint16_t* dst = og + (tok0 + t) * DV + 4 * g;
+#pragma unroll
+      for (int i = 0; i < NDW - 1; ++i) {
+        uint2 ob;
+        ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
+        ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
+        *reinterpret_cast<uint2*>(dst + 16 * vt[i]) = ob;
+      }
+    }
+  }
+}
+
+// every wave reads out and carries its share of the state
 template <class CF>
 __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
-  constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
-  constexpr int LDT = CF::LDT, SB_LD = CF::SB_LD, QF_LD = CF::QF_LD, KB_LD = CF::KB_LD;
-  constexpr int SH = Schedule<DK>::SH;
+  constexpr int C = CF::C, DK = CF::DK, SB_LD = CF::SB_LD;
   __shared__ SmemOut<CF> sm;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave: keep it scalar so every
+  // wave-dependent branch is a scalar branch, not an exec-mask region
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15;
   const int64_t bh = blockIdx.x / a.n_spans;
   const int64_t sp = blockIdx.x - bh * a.n_spans;
   const int64_t tok0 = bh * a.T;
@@ -546,21 +741,13 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
   for (int e = tid; e < VROWS * ZPOS; e += CF::NT) {
     sm.Sb[(e / ZPOS) * SB_LD + 16 * CF::NFT + (e % ZPOS)] = 0;
   }
+  zero_kt_row<CF>(sm, tid);
   const KeyPairs<CF> kp = key_pairs<CF>(w, r);
   const u32x4 ones = ones_frag(r);
   f32x4 acc[CF::MFT][NDT];
   load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
                  w, lane);
-  write_sb<CF>(sm, acc, w, lane);
-
-  int qt[NSLOT];
-#pragma unroll
-  for (int slot = 0; slot < NSLOT; ++slot) qt[slot] = query_tile<CF>(w, slot);
-  const int qt_max = qt[NSLOT - 1] > qt[0] ? qt[NSLOT - 1] : qt[0];
-  int vt[NDW];
-#pragma unroll
-  for (int i = 0; i < NDW; ++i) vt[i] = value_tile<CF>(w, i);
-  const float keep2 = (g < 2) ? 1.0f : 0.0f;
+  write_sb<CF>(sm.Sb, acc, w, lane);
 
   Stage<CF, true> st;
   int64_t c0 = sp * a.G * C;
@@ -571,126 +758,12 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
     st.store(sm, tid);
     if (gi + 1 < a.G && c0 + C < a.T) st.load(qg, kg, vg, tok0, c0 + C, a.T, tid);
     __syncthreads();
-
-    // ---- readout of this chunk's queries (state = prefix before the chunk)
-    f32x4 o[NSLOT][NDW];
-    float qr[NSLOT][DK];  // this lane's query row (query 16 qt + r), rotated by g*SH
-#pragma unroll
-    for (int slot = 0; slot < NSLOT; ++slot) {
-#pragma unroll
-      for (int i = 0; i < NDW; ++i) o[slot][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < DK / 4; ++c) {
-        const int src = (c + g * (SH / 4)) % (DK / 4);
-        const float4 x = *reinterpret_cast<const float4*>(&sm.Qf[(16 * qt[slot] + r) * QF_LD + 4 * src]);
-        qr[slot][4 * c + 0] = x.x;
-        qr[slot][4 * c + 1] = x.y;
-        qr[slot][4 * c + 2] = x.z;
-        qr[slot][4 * c + 3] = x.w;
-      }
-    }
-    // inter-chunk term
-#pragma unroll
-    for (int ks = 0; ks < CF::NKS; ++ks) {
-      u32x4 bs[NDW];
-#pragma unroll
-      for (int i = 0; i < NDW; ++i) {
-        bs[i] = *reinterpret_cast<const u32x4*>(&sm.Sb[(16 * vt[i] + r) * SB_LD + 32 * ks + 8 * g]);
-      }
-#pragma unroll
-      for (int slot = 0; slot < NSLOT; ++slot) {
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int e = 8 * ks + i;
-          if (e >= Schedule<DK>::NE) {
-            f[i] = 0.f;
-          } else {
-            const int pa = kSched<DK>.a[e], pb = kSched<DK>.b[e];
-            const float x = (pa == pb) ? qr[slot][pa] * qr[slot][pa]
-                                       : (2.0f * qr[slot][pa]) * qr[slot][pb];
-            f[i] = kSched<DK>.pair2[e] ? x * keep2 : x;
-          }
-        }
-        const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
-#pragma unroll
-        for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bs[i], qfeat, o[slot][i]);
-      }
-    }
-    // intra-chunk term: squared causal scores
-    u32x4 qf[NSLOT];
-#pragma unroll
-    for (int slot = 0; slot < NSLOT; ++slot) {
-      qf[slot] = u32x4{0u, 0u, 0u, 0u};
-      if (8 * g < DK) {
-        const float* qrow = &sm.Qf[(16 * qt[slot] + r) * QF_LD + 8 * g];
-        const float4 x0 = *reinterpret_cast<const float4*>(qrow);
-        const float4 x1 = *reinterpret_cast<const float4*>(qrow + 4);
-        qf[slot] = u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < C / 32; ++s) {
-      if (2 * s > qt_max) break;
-      u32x4 kf[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        kf[h] = u32x4{0u, 0u, 0u, 0u};
-        if (8 * g < DK) {
-          kf[h] = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * (2 * s + h) + r) * KB_LD + 8 * g]);
-        }
-      }
-      u32x4 bv[NDW];
-#pragma unroll
-      for (int i = 0; i < NDW; ++i) {
-        bv[i] = (vt[i] == NDT - 1)
-                    ? ones
-                    : *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * vt[i] + r) * LDT + 32 * s + 8 * g]);
-      }
-#pragma unroll
-      for (int slot = 0; slot < NSLOT; ++slot) {
-        if (2 * s > qt[slot]) continue;  // uniform per wave
-        float p[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kt = 2 * s + h;
-          const f32x4 sc = mfma(kf[h], qf[slot], f32x4{0.f, 0.f, 0.f, 0.f});  // [key 4g+j][query r]
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = sc[j] * sc[j];
-            p[h][j] = (kt > qt[slot] || (kt == qt[slot] && 4 * g + j > r)) ? 0.f : x;
-          }
-        }
-        const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
-                          pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
-#pragma unroll
-        for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
-      }
-    }
-    // normalise and store: lane r of group 0 holds the denominator of query r
-    // (the last readout value tile of every wave is the ones-column tile)
-#pragma unroll
-    for (int slot = 0; slot < NSLOT; ++slot) {
-      const float den = __shfl(o[slot][NDW - 1][0], r);
-      const float inv = __builtin_amdgcn_rcpf(den + a.eps);
-      const int64_t t = c0 + 16 * qt[slot] + r;
-      if (t < a.T) {
-        uint16_t* dst = og + (tok0 + t) * DV + 4 * g;
-#pragma unroll
-        for (int i = 0; i < NDW - 1; ++i) {
-          uint2 ob;
-          ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
-          ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
-          *reinterpret_cast<uint2*>(dst + 16 * vt[i]) = ob;
-        }
-      }
-    }
-
-    // ---- carry the state across the chunk
+    readout_chunk<CF>(sm, sm.Sb, w, lane, c0, tok0, a.T, a.eps, og);
+    // carry the state across the chunk
     if (gi + 1 < a.G && c0 + C < a.T) {
       state_update<CF>(acc, sm, w, lane, kp, ones);
       __syncthreads();  // every wave done reading Sb for this chunk
-      write_sb<CF>(sm, acc, w, lane);
+      write_sb<CF>(sm.Sb, acc, w, lane);
     }
   }
 }
