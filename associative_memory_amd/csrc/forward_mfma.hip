@@ -14,8 +14,10 @@
 //    has 4 pairs, except the d/4 orbits {(x, x+d/2), (x+d/4, x+3d/4)} of 2.
 //    A lane then builds its query-feature operand from its own query row read
 //    rotated by g*d/4, with compile-time pair indices: phi(Q) never goes
-//    through LDS.  Query features carry the off-diagonal factor 2, key
-//    features none, so phi_q . phi_k = (q.k)^2 without rounding sqrt(2).
+//    through LDS.  Key features are built from sqrt(2) k (fp32), so every
+//    key feature carries weight 2; query features carry 1 off the diagonal
+//    and 1/2 on it, so phi_q . phi_k = (q.k)^2 and only the few diagonal
+//    query features pay an extra multiply.
 //  * Denominators ride through the MFMAs: V gets a column of ones (value tile
 //    4, built in registers), so P.1 and phi_q.z come out of the same products
 //    as the numerators, and z is column 64 of the fp32 state.
@@ -28,6 +30,8 @@
 //    the readout, which is split across waves by query tile (and, for d = 32,
 //    by value tiles) and computed transposed, O^T = [S|z]^T phi_q^T + [V|1]^T P^T,
 //    so a lane holds 4 consecutive value columns of one query.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 #include "plan_mfma.h"
@@ -61,21 +65,35 @@ template <int DK>
 constexpr Schedule<DK> make_schedule() {
   Schedule<DK> s{};
   constexpr int SH = Schedule<DK>::SH;
-  bool used[DK][DK] = {};
-  int n4 = 0, n2 = (DK * (DK + 1) / 2 - DK / 2) / 4;
-  for (int i = 0; i < DK; ++i) {
-    for (int j = i; j < DK; ++j) {
-      if (used[i][j]) continue;
-      int size = 0;
-      for (int g = 0; g < 4; ++g) {
-        int x = (i + SH * g) % DK, y = (j + SH * g) % DK;
-        if (x > y) { int t = x; x = y; y = t; }
-        if (!used[x][y]) { used[x][y] = true; ++size; }
+  if constexpr (DK == 16) {
+    // entry 4 j + x is the pair (x, x + j): lane group g then holds the pairs
+    // (4 g + x, 4 g + x + j), the rows 4 g + x of the key-feature tile j
+    // built by lane rotation (state update, d = 16), so a run of 4 entries
+    // is one 8-byte store of the state copy.  j = 8 is the size-2 orbit.
+    for (int j = 0; j <= 8; ++j) {
+      for (int x = 0; x < 4; ++x) {
+        s.a[4 * j + x] = static_cast<int8_t>(x);
+        s.b[4 * j + x] = static_cast<int8_t>(x + j);
+        s.pair2[4 * j + x] = (j == 8);
       }
-      if (size == 4) {
-        s.a[n4] = static_cast<int8_t>(i); s.b[n4] = static_cast<int8_t>(j); s.pair2[n4] = false; ++n4;
-      } else {
-        s.a[n2] = static_cast<int8_t>(i); s.b[n2] = static_cast<int8_t>(j); s.pair2[n2] = true; ++n2;
+    }
+  } else {
+    bool used[DK][DK] = {};
+    int n4 = 0, n2 = (DK * (DK + 1) / 2 - DK / 2) / 4;
+    for (int i = 0; i < DK; ++i) {
+      for (int j = i; j < DK; ++j) {
+        if (used[i][j]) continue;
+        int size = 0;
+        for (int g = 0; g < 4; ++g) {
+          int x = (i + SH * g) % DK, y = (j + SH * g) % DK;
+          if (x > y) { int t = x; x = y; y = t; }
+          if (!used[x][y]) { used[x][y] = true; ++size; }
+        }
+        if (size == 4) {
+          s.a[n4] = static_cast<int8_t>(i); s.b[n4] = static_cast<int8_t>(j); s.pair2[n4] = false; ++n4;
+        } else {
+          s.a[n2] = static_cast<int8_t>(i); s.b[n2] = static_cast<int8_t>(j); s.pair2[n2] = true; ++n2;
+        }
       }
     }
   }
@@ -250,11 +268,25 @@ __device__ __forceinline__ int group_pos(int tg) {
   return (tg >> 3) * 32 + ((a < 4) ? 8 * a : 8 * (a - 4) + 4);
 }
 
-// The ones column of [V | 1 | 0]: value tile 4 holds 1.0 in its first column
-// (lane r == 0 of every lane group) and zeros elsewhere, for every token slot.
-__device__ __forceinline__ u32x4 ones_frag(int r) {
-  const uint32_t one2 = 0x3f803f80u;  // two bf16 1.0
-  return (r == 0) ? u32x4{one2, one2, one2, one2} : u32x4{0u, 0u, 0u, 0u};
+// Buffer resource over `rows` rows of `row_bytes` starting at row `row0` of
+// `base`.  Buffer reads past the last row return 0 and writes past it are
+// dropped by the hardware range check, which is how the ragged last chunk of
+// a sequence is read and written.  The resource is uniform (scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t row0, int64_t rows,
+                                                           int row_bytes) {
+  char* p = const_cast<char*>(static_cast<const char*>(base)) + row0 * row_bytes;
+  const int n = rows > 0 ? static_cast<int>(rows) * row_bytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0), n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, uint2 x) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{x.x, x.y}, r, off, 0, 0);
 }
 
 // ------------------------------------------------------------ LDS tiles
@@ -264,7 +296,9 @@ __device__ __forceinline__ u32x4 ones_frag(int r) {
 // 16-byte aligned so the reads stay single b128 accesses.
 template <class CF>
 struct alignas(16) Smem {
-  alignas(16) uint16_t Vt[DV * CF::LDT];   // [value column][token position]
+  // [value column][token position]; rows 64..79 hold the ones-column tile
+  // [1 | 0] (row 64 all ones, the rest zero), written once per kernel
+  alignas(16) uint16_t Vt[VROWS * CF::LDT];
   alignas(16) float Kt[(CF::DK + 1) * CF::LDK];  // [d][token position] fp32; row d is zero
 };
 
@@ -306,7 +340,19 @@ __device__ __forceinline__ ScoreOp<CF::DK> score_operand_bf16(const uint16_t* Kb
 //
 // Global -> registers -> LDS for one chunk.  V: groups of 4 tokens x 8
 // columns (16 B per token), written transposed; K and Q: one token row per
-// thread.  Tokens at or past T read as zero.
+// thread.  Tokens at or past T read as zero (buffer range check).
+struct ChunkSrc {
+  __amdgpu_buffer_rsrc_t q, k, v;
+};
+
+template <int DK, int C>
+__device__ __forceinline__ ChunkSrc chunk_src(const void* q, const void* k, const void* v, int64_t tok0,
+                                              int64_t c0, int64_t T) {
+  const int64_t n = (T - c0 < C) ? T - c0 : C;
+  return ChunkSrc{rows_rsrc(q, tok0 + c0, n, 2 * DK), rows_rsrc(k, tok0 + c0, n, 2 * DK),
+                  rows_rsrc(v, tok0 + c0, n, 2 * DV)};
+}
+
 template <class CF, bool WITH_Q>
 struct Stage {
   static constexpr int C = CF::C, DK = CF::DK;
@@ -315,28 +361,18 @@ struct Stage {
   uint4 v[4];
   uint4 kq[RW];  // one K row (threads [0, C)) or one Q row (threads [C, 2C))
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ qg, const uint16_t* __restrict__ kg,
-                                       const uint16_t* __restrict__ vg, int64_t tok0, int64_t c0,
-                                       int64_t T, int tid) {
-    const bool full = c0 + C <= T;
+  __device__ __forceinline__ void load(const ChunkSrc& src, int tid) {
     if (tid < NVG) {
       const int tg = tid % (C / 4), cg = tid / (C / 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = c0 + 4 * tg + r;
-        v[r] = (full || t < T) ? *reinterpret_cast<const uint4*>(vg + (tok0 + t) * DV + 8 * cg)
-                               : make_uint4(0, 0, 0, 0);
-      }
+      for (int r = 0; r < 4; ++r) v[r] = buf_load16(src.v, (4 * tg + r) * (2 * DV) + 16 * cg);
     }
     const int nrows = WITH_Q ? 2 * C : C;
     if (tid < nrows) {
       const bool is_q = WITH_Q && tid >= C;
-      const int64_t t = c0 + (is_q ? tid - C : tid);
-      const uint16_t* src = (is_q ? qg : kg) + (tok0 + t) * DK;
+      const int t = is_q ? tid - C : tid;
 #pragma unroll
-      for (int u = 0; u < RW; ++u) {
-        kq[u] = (full || t < T) ? *reinterpret_cast<const uint4*>(src + 8 * u) : make_uint4(0, 0, 0, 0);
-      }
+      for (int u = 0; u < RW; ++u) kq[u] = buf_load16(is_q ? src.q : src.k, t * (2 * DK) + 16 * u);
     }
   }
 
@@ -348,18 +384,16 @@ struct Stage {
       const int pos = group_pos(tg);
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
-        const uint32_t w0 = (x < 2) ? v[0].x : (x < 4) ? v[0].y : (x < 6) ? v[0].z : v[0].w;
-        const uint32_t w1 = (x < 2) ? v[1].x : (x < 4) ? v[1].y : (x < 6) ? v[1].z : v[1].w;
-        const uint32_t w2 = (x < 2) ? v[2].x : (x < 4) ? v[2].y : (x < 6) ? v[2].z : v[2].w;
-        const uint32_t w3 = (x < 2) ? v[3].x : (x < 4) ? v[3].y : (x < 6) ? v[3].z : v[3].w;
+        const int c = x >> 1;
+        const uint32_t w0 = c == 0 ? v[0].x : c == 1 ? v[0].y : c == 2 ? v[0].z : v[0].w;
+        const uint32_t w1 = c == 0 ? v[1].x : c == 1 ? v[1].y : c == 2 ? v[1].z : v[1].w;
+        const uint32_t w2 = c == 0 ? v[2].x : c == 1 ? v[2].y : c == 2 ? v[2].z : v[2].w;
+        const uint32_t w3 = c == 0 ? v[3].x : c == 1 ? v[3].y : c == 2 ? v[3].z : v[3].w;
+        // column x of the 4 tokens: low (even x) or high (odd x) halves
+        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
         uint2 o;
-        if (x & 1) {
-          o.x = (w0 >> 16) | (w1 & 0xffff0000u);
-          o.y = (w2 >> 16) | (w3 & 0xffff0000u);
-        } else {
-          o.x = (w0 & 0xffffu) | (w1 << 16);
-          o.y = (w2 & 0xffffu) | (w3 << 16);
-        }
+        o.x = __builtin_amdgcn_perm(w1, w0, sel);
+        o.y = __builtin_amdgcn_perm(w3, w2, sel);
         *reinterpret_cast<uint2*>(&sm.Vt[(8 * cg + x) * LDT + pos]) = o;
       }
     }
@@ -372,12 +406,13 @@ struct Stage {
       w[4 * u + 3] = kq[u].w;
     }
     if (tid < C) {
-      // K row: fp32 transposed copy (key features) and, with Q, a bf16 row copy (scores)
+      // K row: fp32 transposed copy scaled by sqrt(2) (key features) and,
+      // with Q, a bf16 row copy (scores)
       const int t = tid;
       const int pos = group_pos(t >> 2) + (t & 3);
 #pragma unroll
       for (int x = 0; x < DK; ++x) {
-        sm.Kt[x * LDK + pos] = (x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]);
+        sm.Kt[x * LDK + pos] = kSqrt2 * ((x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]));
       }
       if constexpr (WITH_Q) {
 #pragma unroll
@@ -400,10 +435,14 @@ struct Stage {
   }
 };
 
-// the zero row of K^T read by empty feature positions
+// constant LDS rows written once per kernel: the zero row of K^T read by empty
+// feature positions, and the ones-column tile of V^T
 template <class CF, class S>
-__device__ __forceinline__ void zero_kt_row(S& sm, int tid) {
+__device__ __forceinline__ void init_const_rows(S& sm, int tid) {
   for (int e = tid; e < CF::LDK; e += CF::NT) sm.Kt[CF::DK * CF::LDK + e] = 0.f;
+  for (int e = tid; e < 16 * CF::LDT; e += CF::NT) {
+    sm.Vt[DV * CF::LDT + e] = (e < CF::LDT) ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
+  }
 }
 
 // ------------------------------------------------------------ state update
@@ -432,35 +471,78 @@ __device__ __forceinline__ KeyPairs<CF> key_pairs(int w, int r) {
   return kp;
 }
 
+// lane r of each 16-lane row receives the value of lane (r + J) mod 16
+template <int J>
+__device__ __forceinline__ float row_rotate(float x) {
+  if constexpr (J == 0) {
+    return x;
+  } else {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x),
+                                                              0x120 + (16 - J), 0xF, 0xF, true));
+  }
+}
+
+// d = 16: key-feature tile J (J = 0..8) holds on row R the pair (R, R + J mod
+// 16).  Lane (g, r) loads its own dimension r of its 8 tokens once per
+// k-step and takes the partner dimension from lane r + J of its row, so the
+// features of every tile come from one 32-byte read per lane and k-step.
+// Rows 8..15 of tile 8 repeat rows 0..7; the state copy drops them.
+template <class CF, int J>
+__device__ __forceinline__ void state_tile16(f32x4 (&acc)[CF::MFT][NDT], const float (&kr)[8],
+                                             const u32x4 (&bv)[NDT], int w) {
+  if (J % CF::NW != w) return;  // uniform per wave
+  constexpr int m = J / CF::NW;
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = kr[i] * row_rotate<J>(kr[i]);
+  const u32x4 af = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = mfma(af, bv[dt], acc[m][dt]);
+}
+
+template <class CF, int... J>
+__device__ __forceinline__ void state_tiles16(f32x4 (&acc)[CF::MFT][NDT], const float (&kr)[8],
+                                              const u32x4 (&bv)[NDT], int w,
+                                              std::integer_sequence<int, J...>) {
+  (state_tile16<CF, J>(acc, kr, bv, w), ...);
+}
+
 template <class CF, class S>
 __device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S& sm, int w, int lane,
-                                             const KeyPairs<CF>& kp, const u32x4& ones) {
+                                             const KeyPairs<CF>& kp) {
   constexpr int LDT = CF::LDT, LDK = CF::LDK;
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int ks = 0; ks < CF::C / 32; ++ks) {
     u32x4 bv[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT - 1; ++dt) {
+    for (int dt = 0; dt < NDT; ++dt) {
       bv[dt] = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * dt + r) * LDT + 32 * ks + 8 * g]);
     }
-    bv[NDT - 1] = ones;
+    if constexpr (CF::DK == 16) {
+      const float* rk = &sm.Kt[r * LDK + 32 * ks + 8 * g];
+      const float4 k0 = *reinterpret_cast<const float4*>(rk);
+      const float4 k1 = *reinterpret_cast<const float4*>(rk + 4);
+      const float kr[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      state_tiles16<CF>(acc, kr, bv, w, std::make_integer_sequence<int, CF::NFT>{});
+    } else {
 #pragma unroll
-    for (int m = 0; m < CF::MFT; ++m) {
-      if (w + CF::NW * m >= CF::NFT) continue;  // uniform per wave
-      const float* ra = &sm.Kt[kp.a[m] * LDK + 32 * ks + 8 * g];
-      const float* rb = &sm.Kt[kp.b[m] * LDK + 32 * ks + 8 * g];
-      const float4 a0 = *reinterpret_cast<const float4*>(ra);
-      const float4 a1 = *reinterpret_cast<const float4*>(ra + 4);
-      const float4 b0 = *reinterpret_cast<const float4*>(rb);
-      const float4 b1 = *reinterpret_cast<const float4*>(rb + 4);
-      u32x4 af;
-      af.x = pack2(a0.x * b0.x, a0.y * b0.y);
-      af.y = pack2(a0.z * b0.z, a0.w * b0.w);
-      af.z = pack2(a1.x * b1.x, a1.y * b1.y);
-      af.w = pack2(a1.z * b1.z, a1.w * b1.w);
+      for (int m = 0; m < CF::MFT; ++m) {
+        if (w + CF::NW * m >= CF::NFT) continue;  // uniform per wave
+        const float* ra = &sm.Kt[kp.a[m] * LDK + 32 * ks + 8 * g];
+        const float* rb = &sm.Kt[kp.b[m] * LDK + 32 * ks + 8 * g];
+        const float4 a0 = *reinterpret_cast<const float4*>(ra);
+        const float4 a1 = *reinterpret_cast<const float4*>(ra + 4);
+        const float4 b0 = *reinterpret_cast<const float4*>(rb);
+        const float4 b1 = *reinterpret_cast<const float4*>(rb + 4);
+        u32x4 af;
+        af.x = pack2(a0.x * b0.x, a0.y * b0.y);
+        af.y = pack2(a0.z * b0.z, a0.w * b0.w);
+        af.z = pack2(a1.x * b1.x, a1.y * b1.y);
+        af.w = pack2(a1.z * b1.z, a1.w * b1.w);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = mfma(af, bv[dt], acc[m][dt]);
+        for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = mfma(af, bv[dt], acc[m][dt]);
+      }
     }
   }
 }
@@ -511,6 +593,25 @@ __device__ __forceinline__ void store_state(const f32x4 (&acc)[CF::MFT][NDT], fl
   }
 }
 
+// Column of the state copy holding rows 4g..4g+3 of feature tile ft.  At
+// d = 16 tile J's row R is the pair (R, R + J), which the query schedule puts
+// on k-step J/2, lane group R/4, slots 4(J%2) + R%4; otherwise tile ft covers
+// columns 16 ft .. 16 ft + 15.
+template <class CF>
+__host__ __device__ constexpr int sb_col(int ft, int g) {
+  return CF::DK == 16 ? 32 * (ft / 2) + 8 * g + 4 * (ft % 2) : 16 * ft + 4 * g;
+}
+
+// true if no feature tile writes column c of the state copy (zeroed once)
+template <class CF>
+__host__ __device__ constexpr bool sb_col_unused(int c) {
+  if constexpr (CF::DK == 16) {
+    return 2 * (c / 32) + (c % 8) / 4 >= CF::NFT;
+  } else {
+    return c >= 16 * CF::NFT;
+  }
+}
+
 // bf16 copy of the owned state tiles into Sb[value row][feature position]
 template <class CF>
 __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 (&acc)[CF::MFT][NDT],
@@ -520,12 +621,14 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
   for (int m = 0; m < CF::MFT; ++m) {
     const int ft = w + CF::NW * m;
     if (ft >= CF::NFT) continue;
+    // d = 16, tile 8: rows 8..15 repeat rows 0..7 and are stored as zero
+    const bool dup = CF::DK == 16 && ft == 8 && g >= 2;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       uint2 o;
-      o.x = pack2(acc[m][dt][0], acc[m][dt][1]);
-      o.y = pack2(acc[m][dt][2], acc[m][dt][3]);
-      *reinterpret_cast<uint2*>(&Sb[(16 * dt + r) * CF::SB_LD + 16 * ft + 4 * g]) = o;
+      o.x = dup ? 0u : pack2(acc[m][dt][0], acc[m][dt][1]);
+      o.y = dup ? 0u : pack2(acc[m][dt][2], acc[m][dt][3]);
+      *reinterpret_cast<uint2*>(&Sb[(16 * dt + r) * CF::SB_LD + sb_col<CF>(ft, g)]) = o;
     }
   }
 }
@@ -534,7 +637,7 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
 
 template <class CF>
 __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
-  constexpr int C = CF::C;
+  constexpr int C = CF::C, DK = CF::DK;
   __shared__ Smem<CF> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across the wave: keep it scalar so every
@@ -544,12 +647,9 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
   const int64_t bh = blockIdx.x / nsp_work;
   const int64_t sp = blockIdx.x - bh * nsp_work;
   const int64_t tok0 = bh * a.T;
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
 
-  zero_kt_row<CF>(sm, tid);
+  init_const_rows<CF>(sm, tid);
   const KeyPairs<CF> kp = key_pairs<CF>(w, lane & 15);
-  const u32x4 ones = ones_frag(lane & 15);
   f32x4 acc[CF::MFT][NDT];
   load_state<CF>(acc, nullptr, w, lane);
 
@@ -559,57 +659,71 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
   if constexpr (CF::NSTAGE == 2) {
     // two register stages: chunk i+2 is in flight while chunk i is consumed
     Stage<CF, false> st0, st1;
-    st0.load(nullptr, kg, vg, tok0, first, a.T, tid);
-    if (first + C < end) st1.load(nullptr, kg, vg, tok0, first + C, a.T, tid);
+    st0.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, first, a.T), tid);
+    if (first + C < end) st1.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, first + C, a.T), tid);
     for (int64_t c0 = first; c0 < end; c0 += 2 * C) {
       __syncthreads();
       st0.store(sm, tid);
-      if (c0 + 2 * C < end) st0.load(nullptr, kg, vg, tok0, c0 + 2 * C, a.T, tid);
+      if (c0 + 2 * C < end) st0.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + 2 * C, a.T), tid);
       __syncthreads();
-      state_update<CF>(acc, sm, w, lane, kp, ones);
+      state_update<CF>(acc, sm, w, lane, kp);
       if (c0 + C >= end) break;
       __syncthreads();
       st1.store(sm, tid);
-      if (c0 + 3 * C < end) st1.load(nullptr, kg, vg, tok0, c0 + 3 * C, a.T, tid);
+      if (c0 + 3 * C < end) st1.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + 3 * C, a.T), tid);
       __syncthreads();
-      state_update<CF>(acc, sm, w, lane, kp, ones);
+      state_update<CF>(acc, sm, w, lane, kp);
     }
   } else {
     Stage<CF, false> st;
-    st.load(nullptr, kg, vg, tok0, first, a.T, tid);
+    st.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, first, a.T), tid);
     for (int64_t c0 = first; c0 < end; c0 += C) {
       __syncthreads();
       st.store(sm, tid);
-      if (c0 + C < end) st.load(nullptr, kg, vg, tok0, c0 + C, a.T, tid);
+      if (c0 + C < end) st.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + C, a.T), tid);
       __syncthreads();
-      state_update<CF>(acc, sm, w, lane, kp, ones);
+      state_update<CF>(acc, sm, w, lane, kp);
     }
   }
-  store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(CF::DK), w, lane);
+  store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), w, lane);
 }
 
 // ------------------------------------------------------------ readout
 
-// Readout of one chunk by readout wave `w` (of 4, or of 8 at d = 32): the
-// chunk's queries against the state copy Sb (the prefix before the chunk)
-// plus the squared causal scores of the chunk, normalised and stored.
+// per-lane constants of the readout: query and value tiles of the wave and
+// the causal mask of the diagonal score tile (key 4g + j against query r)
+template <class CF>
+struct ReadoutLane {
+  int qt[CF::NSLOT];
+  int vt[CF::NDW];
+  bool keep[4];
+};
+
+template <class CF>
+__device__ __forceinline__ ReadoutLane<CF> readout_lane(int w, int lane) {
+  ReadoutLane<CF> L;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int slot = 0; slot < CF::NSLOT; ++slot) L.qt[slot] = query_tile<CF>(w, slot);
+#pragma unroll
+  for (int i = 0; i < CF::NDW; ++i) L.vt[i] = value_tile<CF>(w, i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) L.keep[j] = 4 * g + j <= r;
+  return L;
+}
+
+// Readout of one chunk by wave `w`: the chunk's queries against the state
+// copy Sb (the prefix before the chunk) plus the squared causal scores of the
+// chunk, normalised and stored through `dst` (rows of this chunk).
 template <class CF>
 __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_t* __restrict__ Sb,
-                                              int w, int lane, int64_t c0, int64_t tok0, int64_t T,
-                                              float eps, uint16_t* __restrict__ og) {
+                                              const ReadoutLane<CF>& L, int lane, float eps,
+                                              __amdgpu_buffer_rsrc_t dst) {
   constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
   constexpr int LDT = CF::LDT, SB_LD = CF::SB_LD, QF_LD = CF::QF_LD;
   constexpr int SH = Schedule<DK>::SH;
   const int g = lane >> 4, r = lane & 15;
-  const u32x4 ones = ones_frag(r);
-  const float keep2 = (g < 2) ? 1.0f : 0.0f;
-  int qt[NSLOT];
-#pragma unroll
-  for (int slot = 0; slot < NSLOT; ++slot) qt[slot] = query_tile<CF>(w, slot);
-  const int qt_max = qt[NSLOT - 1] > qt[0] ? qt[NSLOT - 1] : qt[0];
-  int vt[NDW];
-#pragma unroll
-  for (int i = 0; i < NDW; ++i) vt[i] = value_tile<CF>(w, i);
+  const int qt_max = L.qt[NSLOT - 1] > L.qt[0] ? L.qt[NSLOT - 1] : L.qt[0];
 
   f32x4 o[NSLOT][NDW];
   float qr[NSLOT][DK];  // this lane's query row (query 16 qt + r), rotated by g*SH
@@ -620,20 +734,22 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
 #pragma unroll
     for (int c = 0; c < DK / 4; ++c) {
       const int src = (c + g * (SH / 4)) % (DK / 4);
-      const float4 x = *reinterpret_cast<const float4*>(&tl.Qf[(16 * qt[slot] + r) * QF_LD + 4 * src]);
+      const float4 x = *reinterpret_cast<const float4*>(&tl.Qf[(16 * L.qt[slot] + r) * QF_LD + 4 * src]);
       qr[slot][4 * c + 0] = x.x;
       qr[slot][4 * c + 1] = x.y;
       qr[slot][4 * c + 2] = x.z;
       qr[slot][4 * c + 3] = x.w;
     }
   }
-  // inter-chunk term
+  // inter-chunk term.  Positions of a size-2 orbit in lane groups 2 and 3
+  // and positions past the last feature hold zero state, so the query
+  // feature there is left unmasked.
 #pragma unroll
   for (int ks = 0; ks < CF::NKS; ++ks) {
     u32x4 bs[NDW];
 #pragma unroll
     for (int i = 0; i < NDW; ++i) {
-      bs[i] = *reinterpret_cast<const u32x4*>(&Sb[(16 * vt[i] + r) * SB_LD + 32 * ks + 8 * g]);
+      bs[i] = *reinterpret_cast<const u32x4*>(&Sb[(16 * L.vt[i] + r) * SB_LD + 32 * ks + 8 * g]);
     }
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
@@ -645,9 +761,7 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
           f[i] = 0.f;
         } else {
           const int pa = kSched<DK>.a[e], pb = kSched<DK>.b[e];
-          const float x = (pa == pb) ? qr[slot][pa] * qr[slot][pa]
-                                     : (2.0f * qr[slot][pa]) * qr[slot][pb];
-          f[i] = kSched<DK>.pair2[e] ? x * keep2 : x;
+          f[i] = (pa == pb) ? (0.5f * qr[slot][pa]) * qr[slot][pa] : qr[slot][pa] * qr[slot][pb];
         }
       }
       const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
@@ -659,7 +773,7 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
   // one 16x16x16 product at d = 16, one 16x16x32 product at d = 32.
   ScoreOp<DK> qf[NSLOT];
 #pragma unroll
-  for (int slot = 0; slot < NSLOT; ++slot) qf[slot] = score_operand<CF>(tl.Qf, 16 * qt[slot] + r, g);
+  for (int slot = 0; slot < NSLOT; ++slot) qf[slot] = score_operand<CF>(tl.Qf, 16 * L.qt[slot] + r, g);
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
     if (2 * s > qt_max) break;
@@ -669,27 +783,25 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
     u32x4 bv[NDW];
 #pragma unroll
     for (int i = 0; i < NDW; ++i) {
-      bv[i] = (vt[i] == NDT - 1)
-                  ? ones
-                  : *reinterpret_cast<const u32x4*>(&tl.Vt[(16 * vt[i] + r) * LDT + 32 * s + 8 * g]);
+      bv[i] = *reinterpret_cast<const u32x4*>(&tl.Vt[(16 * L.vt[i] + r) * LDT + 32 * s + 8 * g]);
     }
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
-      if (2 * s > qt[slot]) continue;  // uniform per wave
+      if (2 * s > L.qt[slot]) continue;  // uniform per wave
       float p[2][4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int kt = 2 * s + h;
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
-        if (kt > qt[slot]) continue;  // fully masked tile: uniform per wave
+        if (kt > L.qt[slot]) continue;  // fully masked tile: uniform per wave
         const f32x4 sc = score_mfma<DK>(kf[h], qf[slot]);  // [key 4g+j][query r]
-        if (kt < qt[slot]) {
+        if (kt < L.qt[slot]) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) p[h][j] = sc[j] * sc[j];
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[h][j] = (4 * g + j > r) ? 0.f : sc[j] * sc[j];
+          for (int j = 0; j < 4; ++j) p[h][j] = L.keep[j] ? sc[j] * sc[j] : 0.f;
         }
       }
       const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
@@ -699,21 +811,19 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
     }
   }
   // normalise and store: lane r of group 0 holds the denominator of query r
-  // (the last readout value tile of every wave is the ones-column tile)
+  // (the last readout value tile of every wave is the ones-column tile);
+  // rows past T fall outside `dst` and are dropped
 #pragma unroll
   for (int slot = 0; slot < NSLOT; ++slot) {
     const float den = __shfl(o[slot][NDW - 1][0], r);
     const float inv = __builtin_amdgcn_rcpf(den + eps);
-    const int64_t t = c0 + 16 * qt[slot] + r;
-    if (t < T) {
-      uint16_t* dst = og + (tok0 + t) * DV + 4 * g;
+    const int row = 16 * L.qt[slot] + r;
 #pragma unroll
-      for (int i = 0; i < NDW - 1; ++i) {
-        uint2 ob;
-        ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
-        ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
-        *reinterpret_cast<uint2*>(dst + 16 * vt[i]) = ob;
-      }
+    for (int i = 0; i < NDW - 1; ++i) {
+      uint2 ob;
+      ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
+      ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
+      buf_store8(dst, row * (2 * DV) + 2 * (16 * L.vt[i] + 4 * g), ob);
     }
   }
 }
@@ -727,23 +837,18 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
   // the wave index is uniform across the wave: keep it scalar so every
   // wave-dependent branch is a scalar branch, not an exec-mask region
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 15;
   const int64_t bh = blockIdx.x / a.n_spans;
   const int64_t sp = blockIdx.x - bh * a.n_spans;
   const int64_t tok0 = bh * a.T;
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
-  uint16_t* og = static_cast<uint16_t*>(a.out);
 
-  // feature positions past the last feature tile hold no feature: zero once
-  constexpr int ZPOS = CF::NPOS - 16 * CF::NFT;
-  for (int e = tid; e < VROWS * ZPOS; e += CF::NT) {
-    sm.Sb[(e / ZPOS) * SB_LD + 16 * CF::NFT + (e % ZPOS)] = 0;
+  // feature positions no tile writes hold no feature: zero once
+  for (int e = tid; e < VROWS * CF::NPOS; e += CF::NT) {
+    const int c = e % CF::NPOS;
+    if (sb_col_unused<CF>(c)) sm.Sb[(e / CF::NPOS) * SB_LD + c] = 0;
   }
-  zero_kt_row<CF>(sm, tid);
-  const KeyPairs<CF> kp = key_pairs<CF>(w, r);
-  const u32x4 ones = ones_frag(r);
+  init_const_rows<CF>(sm, tid);
+  const KeyPairs<CF> kp = key_pairs<CF>(w, lane & 15);
+  const ReadoutLane<CF> L = readout_lane<CF>(w, lane);
   f32x4 acc[CF::MFT][NDT];
   load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
                  w, lane);
@@ -751,17 +856,19 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
 
   Stage<CF, true> st;
   int64_t c0 = sp * a.G * C;
-  st.load(qg, kg, vg, tok0, c0, a.T, tid);
+  st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0, a.T), tid);
   for (int64_t gi = 0; gi < a.G; ++gi, c0 += C) {
     if (c0 >= a.T) break;
     __syncthreads();  // previous chunk: all reads of the staged tiles done, Sb written
     st.store(sm, tid);
-    if (gi + 1 < a.G && c0 + C < a.T) st.load(qg, kg, vg, tok0, c0 + C, a.T, tid);
+    const bool more = gi + 1 < a.G && c0 + C < a.T;
+    if (more) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + C, a.T), tid);
     __syncthreads();
-    readout_chunk<CF>(sm, sm.Sb, w, lane, c0, tok0, a.T, a.eps, og);
+    const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
+    readout_chunk<CF>(sm, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV));
     // carry the state across the chunk
-    if (gi + 1 < a.G && c0 + C < a.T) {
-      state_update<CF>(acc, sm, w, lane, kp, ones);
+    if (more) {
+      state_update<CF>(acc, sm, w, lane, kp);
       __syncthreads();  // every wave done reading Sb for this chunk
       write_sb<CF>(sm.Sb, acc, w, lane);
     }
