@@ -185,7 +185,6 @@ struct Cfg {
   // waves that split the value tiles
   static constexpr int NSLOT = (NW == 4 && C == 128) ? 2 : 1;  // query tiles per wave
   static constexpr int NDW = (NW == 8 && C == 64) ? 3 : NDT;   // value tiles per wave
-  static constexpr int NSTAGE = (DK == 16) ? 2 : 1;  // register stages in the span kernel
   static constexpr int ZOFF = NFT * (NDT - 1) * 256;  // z column offset in a span state
   static_assert(NT >= 2 * C, "one thread per K row and per Q row");
   static_assert((NW == 4 || NW == 8) && (C == 64 || C == 128), "tiling");
@@ -218,6 +217,34 @@ __device__ __forceinline__ int value_tile(int w, int idx) {
 }
 
 // ------------------------------------------------------------ small helpers
+
+// Calls f(std::integral_constant<int, W>) for the wave index w (uniform per
+// wave): each wave runs a body specialised for its index, so the per-wave
+// work split (query tiles, feature tiles, lane rotations) is resolved at
+// compile time and the chunk body has no wave-dependent branches.
+template <int NW, class F>
+__device__ __forceinline__ void with_wave(int w, F&& f) {
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  switch (w) {
+    case 0: f(std::integral_constant<int, 0>{}); break;
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    default:
+      if constexpr (NW == 8) {
+        switch (w) {
+          case 4: f(std::integral_constant<int, 4>{}); break;
+          case 5: f(std::integral_constant<int, 5>{}); break;
+          case 6: f(std::integral_constant<int, 6>{}); break;
+          default: f(std::integral_constant<int, 7>{}); break;
+        }
+      }
+      break;
+  }
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt unconstrained
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -638,7 +665,9 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
 template <class CF>
 __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
   constexpr int C = CF::C, DK = CF::DK;
-  __shared__ Smem<CF> sm;
+  // two LDS tile buffers: chunk i is staged into buffer i % 2 while the
+  // other buffer may still be read for chunk i - 1, so one barrier per chunk
+  __shared__ Smem<CF> sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across the wave: keep it scalar so every
   // wave-dependent branch is a scalar branch, not an exec-mask region
@@ -648,44 +677,28 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
   const int64_t sp = blockIdx.x - bh * nsp_work;
   const int64_t tok0 = bh * a.T;
 
-  init_const_rows<CF>(sm, tid);
-  const KeyPairs<CF> kp = key_pairs<CF>(w, lane & 15);
-  f32x4 acc[CF::MFT][NDT];
-  load_state<CF>(acc, nullptr, w, lane);
+  init_const_rows<CF>(sm[0], tid);
+  init_const_rows<CF>(sm[1], tid);
+  with_wave<CF::NW>(w, [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    const KeyPairs<CF> kp = key_pairs<CF>(W, lane & 15);
+    f32x4 acc[CF::MFT][NDT];
+    load_state<CF>(acc, nullptr, W, lane);
 
-  const int64_t first = sp * a.G * C;
-  int64_t end = first + a.G * C;
-  if (end > a.T) end = a.T;
-  if constexpr (CF::NSTAGE == 2) {
-    // two register stages: chunk i+2 is in flight while chunk i is consumed
-    Stage<CF, false> st0, st1;
-    st0.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, first, a.T), tid);
-    if (first + C < end) st1.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, first + C, a.T), tid);
-    for (int64_t c0 = first; c0 < end; c0 += 2 * C) {
-      __syncthreads();
-      st0.store(sm, tid);
-      if (c0 + 2 * C < end) st0.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + 2 * C, a.T), tid);
-      __syncthreads();
-      state_update<CF>(acc, sm, w, lane, kp);
-      if (c0 + C >= end) break;
-      __syncthreads();
-      st1.store(sm, tid);
-      if (c0 + 3 * C < end) st1.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + 3 * C, a.T), tid);
-      __syncthreads();
-      state_update<CF>(acc, sm, w, lane, kp);
-    }
-  } else {
+    const int64_t first = sp * a.G * C;
+    int64_t end = first + a.G * C;
+    if (end > a.T) end = a.T;
     Stage<CF, false> st;
     st.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, first, a.T), tid);
-    for (int64_t c0 = first; c0 < end; c0 += C) {
-      __syncthreads();
-      st.store(sm, tid);
+    int buf = 0;
+    for (int64_t c0 = first; c0 < end; c0 += C, buf ^= 1) {
+      st.store(sm[buf], tid);
       if (c0 + C < end) st.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + C, a.T), tid);
       __syncthreads();
-      state_update<CF>(acc, sm, w, lane, kp);
+      state_update<CF>(acc, sm[buf], W, lane, kp);
     }
-  }
-  store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), w, lane);
+    store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
+  });
 }
 
 // ------------------------------------------------------------ readout
@@ -847,32 +860,43 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
     if (sb_col_unused<CF>(c)) sm.Sb[(e / CF::NPOS) * SB_LD + c] = 0;
   }
   init_const_rows<CF>(sm, tid);
-  const KeyPairs<CF> kp = key_pairs<CF>(w, lane & 15);
-  const ReadoutLane<CF> L = readout_lane<CF>(w, lane);
-  f32x4 acc[CF::MFT][NDT];
-  load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
-                 w, lane);
-  write_sb<CF>(sm.Sb, acc, w, lane);
+  with_wave<CF::NW>(w, [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    const KeyPairs<CF> kp = key_pairs<CF>(W, lane & 15);
+    const ReadoutLane<CF> L = readout_lane<CF>(W, lane);
+    f32x4 acc[CF::MFT][NDT];
+    load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
+                   W, lane);
+    write_sb<CF>(sm.Sb, acc, W, lane);
+    // An unconditional vmcnt(0) retires the state loads for the wait-count
+    // analysis, which would otherwise keep them pending into the chunk loop
+    // and stall its MFMAs on the in-order count of the chunk prefetches.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  Stage<CF, true> st;
-  int64_t c0 = sp * a.G * C;
-  st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0, a.T), tid);
-  for (int64_t gi = 0; gi < a.G; ++gi, c0 += C) {
-    if (c0 >= a.T) break;
-    __syncthreads();  // previous chunk: all reads of the staged tiles done, Sb written
+    // chunk i is read from LDS while chunk i+1 waits in registers; after the
+    // chunk's reads a single phase writes the next state copy and stages the
+    // next chunk (disjoint LDS regions), so each chunk costs two barriers
+    Stage<CF, true> st;
+    const int64_t first = sp * a.G * C;
+    int64_t end = first + a.G * C;
+    if (end > a.T) end = a.T;
+    st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, first, a.T), tid);
     st.store(sm, tid);
-    const bool more = gi + 1 < a.G && c0 + C < a.T;
-    if (more) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + C, a.T), tid);
+    if (first + C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, first + C, a.T), tid);
     __syncthreads();
-    const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
-    readout_chunk<CF>(sm, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV));
-    // carry the state across the chunk
-    if (more) {
-      state_update<CF>(acc, sm, w, lane, kp);
-      __syncthreads();  // every wave done reading Sb for this chunk
-      write_sb<CF>(sm.Sb, acc, w, lane);
+    for (int64_t c0 = first; c0 < end; c0 += C) {
+      const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
+      readout_chunk<CF>(sm, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV));
+      if (c0 + C >= end) break;
+      // carry the state across the chunk
+      state_update<CF>(acc, sm, W, lane, kp);
+      __syncthreads();  // every wave done reading the tiles and Sb of this chunk
+      write_sb<CF>(sm.Sb, acc, W, lane);
+      st.store(sm, tid);
+      if (c0 + 2 * C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + 2 * C, a.T), tid);
+      __syncthreads();
     }
-  }
+  });
 }
 
 template <int DK, int C>
