@@ -8,7 +8,11 @@ resident in HBM.  `value` is sequence tokens per second, B*T / t_step.  Both
 prefix variants (sequential and associative) are timed and reported; `value`
 is the library's default (auto) choice.  The recurrent decode workload
 (4096 heads, D=136, dv=64, fp32 state, 1024 steps) is timed in the same run
-and reported under "decode" with its own roofline.
+and reported under "decode" with its own roofline: the eager launch loop, the
+kernel alone, and the loop captured in one HIP graph.  The same decode over
+512 sequences (290 MB of state, beyond the 256 MB Infinity Cache) is reported
+under "decode_beyond_cache".  "attainable" gives the whole step against the
+larger of its HBM time (minimal bytes) and its MFMA time (useful FLOPs).
 
 The fp64 oracle's timing on the host (a bounded sample, extrapolated to the
 whole workload) is reported as cpu_baseline: a baseline, not the target.
@@ -41,6 +45,7 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured decode timing")
     ap.add_argument("--no-other", action="store_true", help="skip the other forward workloads")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
@@ -210,8 +215,11 @@ def bench_other_workloads(args, hip, am, ki, torch):
 
 # ------------------------------------------------------------------ decode
 
-def bench_decode(args, hip, am, ki, torch):
-    w = ki.DECODE
+def bench_decode(args, hip, am, ki, torch, w):
+    """Recurrent decode: `steps` consecutive kata_decode_step launches over
+    every head, timed three ways on the library's stream: the eager launch
+    loop, each launch alone (kernel duration), and the whole loop captured in
+    one HIP graph and replayed."""
     steps = args.decode_steps
     pk, pv, sq, sk, sv = ki.decode_inputs_torch(w.seed, w.heads, w.prefill, steps, w.d, w.dv, "cuda")
     S, z = am.kata_prefill_state(pk[:, None], pv[:, None])
@@ -240,26 +248,55 @@ def bench_decode(args, hip, am, ki, torch):
     for a, b in evs:
         hip.destroy(a)
         hip.destroy(b)
+    # the same loop captured in one graph (launch overhead removed)
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for s in range(steps):
+                    am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps, out=out)
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 3
+        hip.record(e0, stream)
+        for _ in range(reps):
+            g.replay()
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        graph_ms = hip.ms(e0, e1) / (reps * steps)
+        del g
     hip.destroy(e0)
     hip.destroy(e1)
     D = w.d * (w.d + 1) // 2
     bytes_per_head = 2 * (D * w.dv + D) * 4 + (2 * w.d + 2 * w.dv) * 4
     alg_bytes = w.heads * bytes_per_head
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
-    return {
+    state_mb = w.heads * (D * w.dv + D) * 4 / 1e6
+    res = {
         "workload": w.name,
         "heads": w.heads,
         "steps": steps,
         "ms_per_step": loop_ms / steps,
         "kernel_ms": kern_ms,
+        "graph_ms_per_step": graph_ms,
         "tokens_per_s": w.seqs * steps / (loop_ms * 1e-3),
         "head_tokens_per_s": w.heads * steps / (loop_ms * 1e-3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for("decode"),
+                     "traffic": traffic_for("decode" if w is ki.DECODE else "decode_512"),
                      "algorithmic_bytes_per_launch": alg_bytes},
-        "note": "state (%.1f MB) fits the 256 MB Infinity Cache" % (w.heads * (D * w.dv + D) * 4 / 1e6),
+        "note": "state %.1f MB %s the 256 MB Infinity Cache" % (state_mb, "fits" if state_mb < 256 else "exceeds"),
     }
+    if graph_ms:
+        res["graph_tokens_per_s"] = w.seqs / (graph_ms * 1e-3)
+        res["graph_roofline_frac"] = round(alg_bytes / (graph_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    del S, z, sq, sk, sv, out
+    torch.cuda.empty_cache()
+    return res
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -342,6 +379,16 @@ def main():
                  "peak_tflops": BF16_PEAK_TFLOPS,
                  "frac": round(flop_per_tok * BHT / (main_r["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)},
         "head_tokens_per_s": round(BHT / (main_r["ms_per_step"] * 1e-3), 1),
+        # max(time at HBM peak on the minimal bytes, time at bf16 MFMA peak on
+        # the useful FLOPs) over the measured step: the fraction of the
+        # attainable roofline the whole step reaches
+        "attainable": {
+            "t_hbm_us": round(bytes_per_tok * BHT / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+            "t_mfma_us": round(flop_per_tok * BHT / (BF16_PEAK_TFLOPS * 1e12) * 1e6, 2),
+            "t_step_us": round(main_r["ms_per_step"] * 1e3, 2),
+            "frac": round(max(bytes_per_tok * BHT / (HBM_PEAK_GBS * 1e9),
+                              flop_per_tok * BHT / (BF16_PEAK_TFLOPS * 1e12))
+                          / (main_r["ms_per_step"] * 1e-3), 4)},
         "scan_variants": {s: {"tokens_per_s": round(fwd[s]["tokens_per_s"], 1),
                               "ms_per_step": round(fwd[s]["ms_per_step"], 4),
                               "stage_ms": {kk: round(vv, 4) for kk, vv in fwd[s]["stage_ms"].items()},
@@ -351,7 +398,8 @@ def main():
     if not args.no_other:
         rec["other_workloads"] = bench_other_workloads(args, hip, am, ki, torch)
     if not args.no_decode:
-        rec["decode"] = bench_decode(args, hip, am, ki, torch)
+        rec["decode"] = bench_decode(args, hip, am, ki, torch, ki.DECODE)
+        rec["decode_beyond_cache"] = bench_decode(args, hip, am, ki, torch, ki.DECODE_512)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp)
     else:

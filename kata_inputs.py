@@ -67,6 +67,10 @@ WIDE = ForwardWorkload("B2_H16_T8192_d32_dv64_C64_bf16", 2, 16, 8192, 32, 64, 64
 LONG = ForwardWorkload("B1_H8_T131072_d16_dv64_C128_bf16", 1, 8, 131072, 16, 64, 128, BF16, 3)
 DECODE = DecodeWorkload("decode_256seq_H16_d16_dv64_prefill4096_1024steps_f32",
                         256, 16, 16, 64, 4096, 1024, F32, 4)
+# the same decode with twice the sequences: 290 MB of state, more than the
+# 256 MB Infinity Cache holds, so each step streams the state from HBM
+DECODE_512 = DecodeWorkload("decode_512seq_H16_d16_dv64_prefill4096_1024steps_f32",
+                            512, 16, 16, 64, 4096, 1024, F32, 5)
 
 FORWARD_WORKLOADS = (TINY, MEDIUM, WIDE, LONG)
 

@@ -136,3 +136,38 @@ def test_decode_full_size_sampled_heads():
                                           sv[s, heads].double().cpu().numpy(), w.eps)
         refs.append(o)
     check(got, np.stack(refs), ki.F32, vmax, "decode full size, sampled heads")
+
+
+def test_decode_graph_replay_matches_eager():
+    # a run of decode steps captured in one HIP graph: every replay (state
+    # restored by eager work between replays) equals the eager launches bitwise
+    heads, d, dv, n = 96, 16, 64, 12
+    say(f"decode graph replay heads={heads} steps={n}")
+    di = ki.decode_inputs(41, heads, 64, n, d, dv)
+    S0, z0 = am.kata_prefill_state(to_dev(di.pk[:, None], ki.F32), to_dev(di.pv[:, None], ki.F32))
+    sq, sk, sv = (to_dev(x, ki.F32) for x in (di.sq, di.sk, di.sv))
+    S, z = S0.clone(), z0.clone()
+    eager = [am.kata_decode_step(S, z, sq[s], sk[s], sv[s]).clone() for s in range(n)]
+    S_e, z_e = S.clone(), z.clone()
+    torch.cuda.synchronize()
+
+    S, z = S0.clone(), z0.clone()
+    outs = torch.zeros((n, heads, dv), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=cap):
+        for s in range(n):
+            am.kata_decode_step(S, z, sq[s], sk[s], sv[s], out=outs[s])
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        S.copy_(S0)
+        z.copy_(z0)
+        outs.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for s in range(n):
+            assert torch.equal(outs[s], eager[s]), (rep, s)
+        assert torch.equal(S, S_e) and torch.equal(z, z_e), rep
