@@ -46,7 +46,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int DV = 64;
 constexpr int NDT = kMfmaValueTiles;  // 4 value tiles + the ones-column tile
-constexpr int VROWS = 16 * NDT;       // 80
+// LDS rows of V^T and of the state copy: 64 value rows, then row 64 (ones
+// for V, z for the state) and row 65 (zeros).  Operand rows 65..79 of the
+// ones-column tile are all zero, so every lane past the first reads row 65.
+constexpr int VROWS = DV + 2;
+__device__ __forceinline__ int vrow(int vt, int r) { return vt == NDT - 1 ? DV + (r > 0) : 16 * vt + r; }
 
 // ------------------------------------------------------------ feature schedule
 
@@ -323,8 +327,8 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, ui
 // 16-byte aligned so the reads stay single b128 accesses.
 template <class CF>
 struct alignas(16) Smem {
-  // [value column][token position]; rows 64..79 hold the ones-column tile
-  // [1 | 0] (row 64 all ones, the rest zero), written once per kernel
+  // [value column][token position]; row 64 all ones and row 65 all zeros
+  // (the ones-column tile [1 | 0]), written once per kernel
   alignas(16) uint16_t Vt[VROWS * CF::LDT];
   alignas(16) float Kt[(CF::DK + 1) * CF::LDK];  // [d][token position] fp32; row d is zero
 };
@@ -335,9 +339,14 @@ struct alignas(16) Tiles : Smem<CF> {
   alignas(16) float Qf[CF::C * CF::QF_LD];     // [token][d] fp32
 };
 
+constexpr int OB_LD = DV + 8;  // bf16 row stride of a wave's output staging tile
+
 template <class CF>
 struct alignas(16) SmemOut : Tiles<CF> {
   alignas(16) uint16_t Sb[VROWS * CF::SB_LD];  // [value row][feature position] bf16 state
+  // per-wave 16 x 64 output tile, staged so the chunk's rows leave as
+  // contiguous 16-byte stores (used when a wave owns whole output rows)
+  alignas(16) uint16_t Ob[CF::NDW == NDT ? CF::NW : 1][16 * OB_LD];
 };
 
 // score operand of row `row` from the fp32 Q tile / the bf16 K tile
@@ -467,7 +476,7 @@ struct Stage {
 template <class CF, class S>
 __device__ __forceinline__ void init_const_rows(S& sm, int tid) {
   for (int e = tid; e < CF::LDK; e += CF::NT) sm.Kt[CF::DK * CF::LDK + e] = 0.f;
-  for (int e = tid; e < 16 * CF::LDT; e += CF::NT) {
+  for (int e = tid; e < 2 * CF::LDT; e += CF::NT) {
     sm.Vt[DV * CF::LDT + e] = (e < CF::LDT) ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
   }
 }
@@ -544,7 +553,7 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S
     u32x4 bv[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      bv[dt] = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * dt + r) * LDT + 32 * ks + 8 * g]);
+      bv[dt] = *reinterpret_cast<const u32x4*>(&sm.Vt[vrow(dt, r) * LDT + 32 * ks + 8 * g]);
     }
     if constexpr (CF::DK == 16) {
       const float* rk = &sm.Kt[r * LDK + 32 * ks + 8 * g];
@@ -652,10 +661,12 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
     const bool dup = CF::DK == 16 && ft == 8 && g >= 2;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
+      // ones-column tile: column 0 is z (row 64), the rest are zero (row 65)
+      if (dt == NDT - 1 && r > 1) continue;
       uint2 o;
       o.x = dup ? 0u : pack2(acc[m][dt][0], acc[m][dt][1]);
       o.y = dup ? 0u : pack2(acc[m][dt][2], acc[m][dt][3]);
-      *reinterpret_cast<uint2*>(&Sb[(16 * dt + r) * CF::SB_LD + sb_col<CF>(ft, g)]) = o;
+      *reinterpret_cast<uint2*>(&Sb[vrow(dt, r) * CF::SB_LD + sb_col<CF>(ft, g)]) = o;
     }
   }
 }
@@ -731,7 +742,7 @@ __device__ __forceinline__ ReadoutLane<CF> readout_lane(int w, int lane) {
 template <class CF>
 __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_t* __restrict__ Sb,
                                               const ReadoutLane<CF>& L, int lane, float eps,
-                                              __amdgpu_buffer_rsrc_t dst) {
+                                              __amdgpu_buffer_rsrc_t dst, uint16_t* __restrict__ ob_tile) {
   constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
   constexpr int LDT = CF::LDT, SB_LD = CF::SB_LD, QF_LD = CF::QF_LD;
   constexpr int SH = Schedule<DK>::SH;
@@ -762,7 +773,7 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
     u32x4 bs[NDW];
 #pragma unroll
     for (int i = 0; i < NDW; ++i) {
-      bs[i] = *reinterpret_cast<const u32x4*>(&Sb[(16 * L.vt[i] + r) * SB_LD + 32 * ks + 8 * g]);
+      bs[i] = *reinterpret_cast<const u32x4*>(&Sb[vrow(L.vt[i], r) * SB_LD + 32 * ks + 8 * g]);
     }
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
@@ -796,7 +807,7 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
     u32x4 bv[NDW];
 #pragma unroll
     for (int i = 0; i < NDW; ++i) {
-      bv[i] = *reinterpret_cast<const u32x4*>(&tl.Vt[(16 * L.vt[i] + r) * LDT + 32 * s + 8 * g]);
+      bv[i] = *reinterpret_cast<const u32x4*>(&tl.Vt[vrow(L.vt[i], r) * LDT + 32 * s + 8 * g]);
     }
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
@@ -830,13 +841,32 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
   for (int slot = 0; slot < NSLOT; ++slot) {
     const float den = __shfl(o[slot][NDW - 1][0], r);
     const float inv = __builtin_amdgcn_rcpf(den + eps);
-    const int row = 16 * L.qt[slot] + r;
+    if constexpr (NDW == NDT) {
+      // whole rows: stage the 16 x 64 tile in the wave's LDS tile, then
+      // write it back as 1 KB contiguous stores (16 bytes per lane)
 #pragma unroll
-    for (int i = 0; i < NDW - 1; ++i) {
-      uint2 ob;
-      ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
-      ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
-      buf_store8(dst, row * (2 * DV) + 2 * (16 * L.vt[i] + 4 * g), ob);
+      for (int i = 0; i < NDW - 1; ++i) {
+        uint2 ob;
+        ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
+        ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
+        *reinterpret_cast<uint2*>(&ob_tile[r * OB_LD + 16 * L.vt[i] + 4 * g]) = ob;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * h + (lane >> 3);
+        const uint4 x = *reinterpret_cast<const uint4*>(&ob_tile[row * OB_LD + 8 * (lane & 7)]);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, dst,
+                                               (16 * L.qt[slot] + row) * (2 * DV) + 16 * (lane & 7), 0, 0);
+      }
+    } else {
+      const int row = 16 * L.qt[slot] + r;
+#pragma unroll
+      for (int i = 0; i < NDW - 1; ++i) {
+        uint2 ob;
+        ob.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
+        ob.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
+        buf_store8(dst, row * (2 * DV) + 2 * (16 * L.vt[i] + 4 * g), ob);
+      }
     }
   }
 }
@@ -886,7 +916,8 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
     __syncthreads();
     for (int64_t c0 = first; c0 < end; c0 += C) {
       const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
-      readout_chunk<CF>(sm, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV));
+      readout_chunk<CF>(sm, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV),
+                        sm.Ob[CF::NDW == NDT ? W : 0]);
       if (c0 + C >= end) break;
       // carry the state across the chunk
       state_update<CF>(acc, sm, W, lane, kp);
