@@ -903,18 +903,19 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
     // and stall its MFMAs on the in-order count of the chunk prefetches.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-    // chunk i is read from LDS while chunk i+1 waits in registers; after the
-    // chunk's reads a single phase writes the next state copy and stages the
-    // next chunk (disjoint LDS regions), so each chunk costs two barriers
+    // chunk i is read from LDS while chunk i+1 arrives in registers; after
+    // the chunk's reads a single phase writes the next state copy and stages
+    // the next chunk (disjoint LDS regions), so each chunk costs two barriers
     Stage<CF, true> st;
     const int64_t first = sp * a.G * C;
     int64_t end = first + a.G * C;
     if (end > a.T) end = a.T;
     st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, first, a.T), tid);
     st.store(sm, tid);
-    if (first + C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, first + C, a.T), tid);
     __syncthreads();
     for (int64_t c0 = first; c0 < end; c0 += C) {
+      // the next chunk's loads go out first, to overlap this chunk's compute
+      if (c0 + C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + C, a.T), tid);
       const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
       readout_chunk<CF>(sm, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV),
                         sm.Ob[CF::NDW == NDT ? W : 0]);
@@ -924,7 +925,6 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
       __syncthreads();  // every wave done reading the tiles and Sb of this chunk
       write_sb<CF>(sm.Sb, acc, W, lane);
       st.store(sm, tid);
-      if (c0 + 2 * C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + 2 * C, a.T), tid);
       __syncthreads();
     }
   });
