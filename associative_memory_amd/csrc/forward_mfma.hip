@@ -395,7 +395,17 @@ struct Stage {
   static constexpr int NVG = (C / 4) * (DV / 8);
   static constexpr int RW = DK / 8;  // 16-byte words per K/Q row
   uint4 v[4];
-  uint4 kq[RW];  // one K row (threads [0, C)) or one Q row (threads [C, 2C))
+  uint4 kq[RW];  // one K row or, with Q, one Q row (threads [C, 2C))
+
+  // K row staged by thread tid, or -1: threads [0, C) with Q; without Q the
+  // last C threads, away from wave 0, which reduces the extra feature tile
+  static __device__ __forceinline__ int krow(int tid) {
+    if constexpr (WITH_Q) {
+      return tid < C ? tid : -1;
+    } else {
+      return tid >= CF::NT - C ? tid - (CF::NT - C) : -1;
+    }
+  }
 
   __device__ __forceinline__ void load(const ChunkSrc& src, int tid) {
     if (tid < NVG) {
@@ -403,12 +413,19 @@ struct Stage {
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = buf_load16(src.v, (4 * tg + r) * (2 * DV) + 16 * cg);
     }
-    const int nrows = WITH_Q ? 2 * C : C;
-    if (tid < nrows) {
-      const bool is_q = WITH_Q && tid >= C;
-      const int t = is_q ? tid - C : tid;
+    if constexpr (WITH_Q) {
+      if (tid < 2 * C) {
+        const bool is_q = tid >= C;
+        const int t = is_q ? tid - C : tid;
 #pragma unroll
-      for (int u = 0; u < RW; ++u) kq[u] = buf_load16(is_q ? src.q : src.k, t * (2 * DK) + 16 * u);
+        for (int u = 0; u < RW; ++u) kq[u] = buf_load16(is_q ? src.q : src.k, t * (2 * DK) + 16 * u);
+      }
+    } else {
+      const int t = krow(tid);
+      if (t >= 0) {
+#pragma unroll
+        for (int u = 0; u < RW; ++u) kq[u] = buf_load16(src.k, t * (2 * DK) + 16 * u);
+      }
     }
   }
 
@@ -441,10 +458,10 @@ struct Stage {
       w[4 * u + 2] = kq[u].z;
       w[4 * u + 3] = kq[u].w;
     }
-    if (tid < C) {
+    if (krow(tid) >= 0) {
       // K row: fp32 transposed copy scaled by sqrt(2) (key features) and,
       // with Q, a bf16 row copy (scores)
-      const int t = tid;
+      const int t = krow(tid);
       const int pos = group_pos(t >> 2) + (t & 3);
 #pragma unroll
       for (int x = 0; x < DK; ++x) {
