@@ -302,7 +302,6 @@ def bench_decode(args, hip, am, ki, torch, w):
 # ------------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(w, inp):
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import kata_oracle as orc
