@@ -540,17 +540,21 @@ __device__ __forceinline__ float row_rotate(float x) {
 // k-step and takes the partner dimension from lane r + J of its row, so the
 // features of every tile come from one 32-byte read per lane and k-step.
 // Rows 8..15 of tile 8 repeat rows 0..7; the state copy drops them.
-template <class CF, int J>
-__device__ __forceinline__ void state_tile16(f32x4 (&acc)[CF::MFT][NDT], const float (&kr)[8],
-                                             const u32x4 (&bv)[NDT], int w) {
-  if (J % CF::NW != w) return;  // uniform per wave
-  constexpr int m = J / CF::NW;
+template <int J>
+__device__ __forceinline__ void tile16_into(f32x4 (&dst)[NDT], const float (&kr)[8], const u32x4 (&bv)[NDT]) {
   float f[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = kr[i] * row_rotate<J>(kr[i]);
   const u32x4 af = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = mfma(af, bv[dt], acc[m][dt]);
+  for (int dt = 0; dt < NDT; ++dt) dst[dt] = mfma(af, bv[dt], dst[dt]);
+}
+
+template <class CF, int J>
+__device__ __forceinline__ void state_tile16(f32x4 (&acc)[CF::MFT][NDT], const float (&kr)[8],
+                                             const u32x4 (&bv)[NDT], int w) {
+  if (J % CF::NW != w) return;  // uniform per wave
+  tile16_into<J>(acc[J / CF::NW], kr, bv);
 }
 
 template <class CF, int... J>
@@ -724,6 +728,226 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
       if (c0 + C < end) st.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + C, a.T), tid);
       __syncthreads();
       state_update<CF>(acc, sm[buf], W, lane, kp);
+    }
+    store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
+  });
+}
+
+// ------------------------------------------------------------ span sums, d = 16, LDS DMA
+//
+// The chunk goes from HBM straight into LDS (`buffer_load ... lds`, no
+// registers, no VALU): raw V rows (128 B, 16-byte chunks XOR-swizzled by
+// (row >> 1) & 7 against bank conflicts) and raw K rows (32 B).  The MFMA
+// operands are read back with the transposing LDS read `ds_read_b64_tr_b16`:
+// in each 16-lane group, lane i receives element i % 4 of the 8 bytes
+// addressed by lanes 4m + i/4 (m = 0..3), so when lane s addresses row m = s/4,
+// columns 4(s % 4)..+3 of a row-major tile, lane i gets column i of 4
+// consecutive rows.  The two buffers are distinct LDS variables and the loop
+// is unrolled over them, so the compiler's wait counts see that a chunk
+// arriving in one buffer does not alias reads of the other.
+template <int C>
+struct alignas(16) DmaTile16 {
+  alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
+  alignas(16) uint16_t k[C * 16];  // [token][dimension]
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define KATA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+
+__device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(uint2, x);
+}
+
+// wave W's share of the chunk's DMA: V in 1 KB pieces of 8 rows, K in 1 KB
+// pieces of 32 rows; rows past the buffer resource's end arrive as zero
+template <int C, int W, int NW>
+__device__ __forceinline__ void dma_chunk16(DmaTile16<C>& b, const ChunkSrc& src, int lane) {
+#pragma unroll
+  for (int j = W; j < C / 8; j += NW) {
+    const int t = 8 * j + (lane >> 3);
+    const int cg = (lane & 7) ^ vswz(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, KATA_LDS(&b.v[8 * j * DV]), 16, t * (2 * DV) + 16 * cg, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = W; j < C / 32; j += NW) {
+    const int t = 32 * j + (lane >> 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
+  }
+}
+
+// Per-lane element offsets of the transposing reads.  Lane (g, s) addresses
+// row 4g + s/4 (+ 32 ks + 16 h), columns 4(s % 4)..+3 of the 16-column block;
+// within a 32-row k-step the V swizzle (row >> 1) & 7 reduces to
+// (2g + s/8) & 7, so the offsets are lane constants and k-step / half are
+// immediate offsets.
+struct TrOffsets {
+  int v[NDT - 1];  // V, per value tile
+  int k;           // K
+};
+
+__device__ __forceinline__ TrOffsets tr_offsets(int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = 4 * g + (s >> 2);
+  const int z = (2 * g + (s >> 3)) & 7;
+  TrOffsets o;
+#pragma unroll
+  for (int dt = 0; dt < NDT - 1; ++dt) {
+    const int chunk = (2 * dt + ((s & 3) >> 1)) ^ z;
+    o.v[dt] = row * DV + 8 * chunk + 4 * (s & 1);
+  }
+  o.k = row * 16 + 4 * (s & 3);
+  return o;
+}
+
+// operand of k-step ks: lane (g, r) gets column r of the block of tokens
+// 32 ks + 4g + m and 32 ks + 16 + 4g + m (m = 0..3), the key order of a pair
+// of 16x16 score accumulators
+template <int LD>
+__device__ __forceinline__ u32x4 tr_operand(const uint16_t* t, int off, int ks) {
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint2 x = tr_read(&t[off + (32 * ks + 16 * h) * LD]);
+    out[2 * h] = x.x;
+    out[2 * h + 1] = x.y;
+  }
+  return out;
+}
+
+// Span-sum update: wave W reduces feature tiles W and W + 4 over every k-step
+// and the last tile (8) over the k-steps ks % 4 == W into acc8, so the waves
+// carry equal work; the partial acc8 of the waves are added once per span.
+template <class CF, int W>
+__device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f32x4 (&acc8)[NDT],
+                                                   const DmaTile16<CF::C>& b, const u32x4& bones,
+                                                   const TrOffsets& to) {
+  static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
+#pragma unroll
+  for (int ks = 0; ks < CF::C / 32; ++ks) {
+    u32x4 bv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], ks);
+    bv[NDT - 1] = bones;
+    const u32x4 kb = tr_operand<16>(b.k, to.k, ks);
+    float kr[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[2 * i] = kSqrt2 * lo_bf16(kb[i]);
+      kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
+    }
+    tile16_into<W>(acc[0], kr, bv);
+    tile16_into<W + 4>(acc[1], kr, bv);
+    if (ks % CF::NW == W) tile16_into<8>(acc8, kr, bv);  // compile-time per wave
+  }
+}
+
+// s_waitcnt immediate with vmcnt = n (gfx9 encoding), expcnt and lgkmcnt free
+constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+
+// Workgroup barrier that leaves vector-memory loads in flight: LDS reads and
+// writes of this wave complete first (lgkmcnt), global loads and LDS DMA do
+// not.  The memory clobber keeps the compiler from moving memory operations
+// across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// DMA instructions one wave issues per chunk
+template <int C, int W, int NW>
+constexpr int dma_count16() {
+  int n = 0;
+  for (int j = W; j < C / 8; j += NW) ++n;
+  for (int j = W; j < C / 32; j += NW) ++n;
+  return n;
+}
+
+// Three LDS buffers: chunk i is reduced while chunks i+1 and i+2 are in
+// flight.  Before each chunk a wave waits for its own share of that chunk
+// (vmcnt: the later chunk's transfers may stay outstanding) and the barrier
+// then publishes every wave's share.  Chunks at or past the span's end read
+// as zero; their reduction is skipped.
+template <int C>
+__global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
+  using CF = Cfg<16, C>;
+  constexpr int DK = 16;
+  __shared__ DmaTile16<C> b0;
+  __shared__ DmaTile16<C> b1;
+  __shared__ DmaTile16<C> b2;
+  __shared__ alignas(16) uint16_t ones[128];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nsp_work = a.n_spans - 1;  // the last span's sum is never read
+  const int64_t bh = blockIdx.x / nsp_work;
+  const int64_t sp = blockIdx.x - bh * nsp_work;
+  const int64_t tok0 = bh * a.T;
+  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
+  __syncthreads();  // the ones rows
+
+  with_wave<CF::NW>(w, [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    constexpr int NPC = dma_count16<C, W, CF::NW>();  // this wave's transfers per chunk
+    f32x4 acc[CF::MFT][NDT];
+    load_state<CF>(acc, nullptr, W, lane);
+    f32x4 acc8[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc8[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const TrOffsets to = tr_offsets(lane);
+    // the ones-column tile: row 0 of `ones` is all ones, row 1 all zeros
+    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[((lane & 15) > 0 ? 64 : 0) + 8 * (lane >> 4)]);
+    const int64_t first = sp * a.G * C;
+    int64_t end = first + a.G * C;
+    if (end > a.T) end = a.T;
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, end); };
+    dma_chunk16<C, W, CF::NW>(b0, src(first), lane);
+    dma_chunk16<C, W, CF::NW>(b1, src(first + C), lane);
+    for (int64_t c0 = first; c0 < end; c0 += 3 * C) {
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
+      barrier_lds();
+      dma_chunk16<C, W, CF::NW>(b2, src(c0 + 2 * C), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      state_update_dma16<CF, W>(acc, acc8, b0, bones, to);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
+      barrier_lds();
+      dma_chunk16<C, W, CF::NW>(b0, src(c0 + 3 * C), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + C < end) state_update_dma16<CF, W>(acc, acc8, b1, bones, to);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
+      barrier_lds();
+      dma_chunk16<C, W, CF::NW>(b1, src(c0 + 4 * C), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + 2 * C < end) state_update_dma16<CF, W>(acc, acc8, b2, bones, to);
+    }
+    // drain the transfers still in flight, then add the waves' parts of tile 8
+    // through LDS (4 x 64 lanes x 5 x 16 bytes = 20 KB over the tile buffers)
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    __syncthreads();
+    constexpr int RED_BYTES = NDT * 16 * 64;  // one wave's part
+    static_assert(3 * sizeof(DmaTile16<C>) >= 4 * RED_BYTES, "reduction space");
+    auto red = [&](int wv) -> f32x4* {
+      const int off = wv * RED_BYTES;
+      char* base = off < int(sizeof(DmaTile16<C>)) ? reinterpret_cast<char*>(&b0)
+                 : off < int(2 * sizeof(DmaTile16<C>)) ? reinterpret_cast<char*>(&b1)
+                                                       : reinterpret_cast<char*>(&b2);
+      return reinterpret_cast<f32x4*>(base + off % int(sizeof(DmaTile16<C>)));
+    };
+    static_assert(sizeof(DmaTile16<C>) % RED_BYTES == 0, "parts do not straddle buffers");
+    if constexpr (W != 0) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) red(W)[dt * 64 + lane] = acc8[dt];
+    }
+    __syncthreads();
+    if constexpr (W == 0) {
+#pragma unroll
+      for (int wv = 1; wv < CF::NW; ++wv) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc8[dt] += red(wv)[dt * 64 + lane];
+      }
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[2][dt] = acc8[dt];
     }
     store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
   });
@@ -951,7 +1175,11 @@ template <int DK, int C>
 hipError_t launch_span(const MfmaArgs& a, hipStream_t stream) {
   using CF = Cfg<DK, C>;
   dim3 grid(static_cast<unsigned>(a.BH * (a.n_spans - 1)));
-  span_state_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
+  if constexpr (DK == 16) {
+    span_state_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
+  } else {
+    span_state_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
