@@ -980,12 +980,42 @@ __device__ __forceinline__ ReadoutLane<CF> readout_lane(int w, int lane) {
 // Readout of one chunk by wave `w`: the chunk's queries against the state
 // copy Sb (the prefix before the chunk) plus the squared causal scores of the
 // chunk, normalised and stored through `dst` (rows of this chunk).
+//
+// The chunk's operands come from `src`: register-staged LDS tiles (TileSrc)
+// or the raw tiles of the DMA path (DmaSrc16).  A source gives the fp32
+// values of 4 consecutive dimensions of a query row, the score operands of a
+// query / key row, and the V operand of a value tile and 32-key block.
 template <class CF>
-__device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_t* __restrict__ Sb,
+struct TileSrc {
+  const Tiles<CF>& tl;
+  __device__ __forceinline__ float4 qrow4(int row, int c4) const {
+    return *reinterpret_cast<const float4*>(&tl.Qf[row * CF::QF_LD + 4 * c4]);
+  }
+  __device__ __forceinline__ ScoreOp<CF::DK> score_q(int row, int g) const {
+    return score_operand<CF>(tl.Qf, row, g);
+  }
+  __device__ __forceinline__ ScoreOp<CF::DK> score_k(int row, int g) const {
+    return score_operand_bf16<CF>(tl.Kb, row, g);
+  }
+  __device__ __forceinline__ u32x4 v_op(int vt, int s, int lane) const {
+    const int g = lane >> 4, r = lane & 15;
+    return *reinterpret_cast<const u32x4*>(&tl.Vt[vrow(vt, r) * CF::LDT + 32 * s + 8 * g]);
+  }
+};
+
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// `after_q` runs once the query rows are in registers (the DMA readout issues
+// the next chunk's transfer there)
+template <class CF, class S, class H = NoHook>
+__device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __restrict__ Sb,
                                               const ReadoutLane<CF>& L, int lane, float eps,
-                                              __amdgpu_buffer_rsrc_t dst, uint16_t* __restrict__ ob_tile) {
+                                              __amdgpu_buffer_rsrc_t dst, uint16_t* __restrict__ ob_tile,
+                                              const H& after_q = H{}) {
   constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
-  constexpr int LDT = CF::LDT, SB_LD = CF::SB_LD, QF_LD = CF::QF_LD;
+  constexpr int SB_LD = CF::SB_LD;
   constexpr int SH = Schedule<DK>::SH;
   const int g = lane >> 4, r = lane & 15;
   const int qt_max = L.qt[NSLOT - 1] > L.qt[0] ? L.qt[NSLOT - 1] : L.qt[0];
@@ -998,14 +1028,15 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
     for (int i = 0; i < NDW; ++i) o[slot][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < DK / 4; ++c) {
-      const int src = (c + g * (SH / 4)) % (DK / 4);
-      const float4 x = *reinterpret_cast<const float4*>(&tl.Qf[(16 * L.qt[slot] + r) * QF_LD + 4 * src]);
+      const int c4 = (c + g * (SH / 4)) % (DK / 4);
+      const float4 x = src.qrow4(16 * L.qt[slot] + r, c4);
       qr[slot][4 * c + 0] = x.x;
       qr[slot][4 * c + 1] = x.y;
       qr[slot][4 * c + 2] = x.z;
       qr[slot][4 * c + 3] = x.w;
     }
   }
+  after_q();
   // inter-chunk term.  Positions of a size-2 orbit in lane groups 2 and 3
   // and positions past the last feature hold zero state, so the query
   // feature there is left unmasked.
@@ -1038,18 +1069,16 @@ __device__ __forceinline__ void readout_chunk(const Tiles<CF>& tl, const uint16_
   // one 16x16x16 product at d = 16, one 16x16x32 product at d = 32.
   ScoreOp<DK> qf[NSLOT];
 #pragma unroll
-  for (int slot = 0; slot < NSLOT; ++slot) qf[slot] = score_operand<CF>(tl.Qf, 16 * L.qt[slot] + r, g);
+  for (int slot = 0; slot < NSLOT; ++slot) qf[slot] = src.score_q(16 * L.qt[slot] + r, g);
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
     if (2 * s > qt_max) break;
     ScoreOp<DK> kf[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) kf[h] = score_operand_bf16<CF>(tl.Kb, 16 * (2 * s + h) + r, g);
+    for (int h = 0; h < 2; ++h) kf[h] = src.score_k(16 * (2 * s + h) + r, g);
     u32x4 bv[NDW];
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) {
-      bv[i] = *reinterpret_cast<const u32x4*>(&tl.Vt[vrow(L.vt[i], r) * LDT + 32 * s + 8 * g]);
-    }
+    for (int i = 0; i < NDW; ++i) bv[i] = src.v_op(L.vt[i], s, lane);
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
       if (2 * s > L.qt[slot]) continue;  // uniform per wave
@@ -1158,7 +1187,7 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
       // the next chunk's loads go out first, to overlap this chunk's compute
       if (c0 + C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + C, a.T), tid);
       const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
-      readout_chunk<CF>(sm, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV),
+      readout_chunk<CF>(TileSrc<CF>{sm}, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV),
                         sm.Ob[CF::NDW == NDT ? W : 0]);
       if (c0 + C >= end) break;
       // carry the state across the chunk
@@ -1168,6 +1197,158 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
       st.store(sm, tid);
       __syncthreads();
     }
+  });
+}
+
+// ------------------------------------------------------------ readout, d = 16, LDS DMA
+//
+// The chunk's V, K and Q arrive raw by LDS DMA into one of two buffers while
+// the other is read.  Query rows and score operands are plain row reads; V and
+// K operands come from transposing reads, as in the span sums.
+template <int C>
+struct alignas(16) DmaTileQ16 {
+  alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
+  alignas(16) uint16_t k[C * 16];  // [token][dimension]
+  alignas(16) uint16_t q[C * 16];  // [token][dimension]
+};
+
+template <int C, int W, int NW>
+__device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C>& b, const ChunkSrc& src, int lane) {
+#pragma unroll
+  for (int j = W; j < C / 8; j += NW) {
+    const int t = 8 * j + (lane >> 3);
+    const int cg = (lane & 7) ^ vswz(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, KATA_LDS(&b.v[8 * j * DV]), 16, t * (2 * DV) + 16 * cg, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = W; j < C / 32; j += NW) {
+    const int t = 32 * j + (lane >> 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.q, KATA_LDS(&b.q[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
+  }
+}
+
+template <int C>
+struct DmaSrc16 {
+  const DmaTileQ16<C>& b;
+  const TrOffsets& to;
+  const u32x4& bones;
+  __device__ __forceinline__ float4 qrow4(int row, int c4) const {
+    const uint2 x = *reinterpret_cast<const uint2*>(&b.q[row * 16 + 4 * c4]);
+    return make_float4(lo_bf16(x.x), hi_bf16(x.x), lo_bf16(x.y), hi_bf16(x.y));
+  }
+  __device__ __forceinline__ uint2 score_q(int row, int g) const {
+    return *reinterpret_cast<const uint2*>(&b.q[row * 16 + 4 * g]);
+  }
+  __device__ __forceinline__ uint2 score_k(int row, int g) const {
+    return *reinterpret_cast<const uint2*>(&b.k[row * 16 + 4 * g]);
+  }
+  __device__ __forceinline__ u32x4 v_op(int vt, int s, int lane) const {
+    return vt == NDT - 1 ? bones : tr_operand<DV>(b.v, to.v[vt], s);
+  }
+};
+
+// state carry of the readout: wave W owns feature tiles W, W + 4 (and 8 for
+// wave 0), the whole state being needed for the next chunk's state copy
+template <class CF, int W>
+__device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], const DmaTileQ16<CF::C>& b,
+                                                  const u32x4& bones, const TrOffsets& to) {
+  static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
+#pragma unroll
+  for (int ks = 0; ks < CF::C / 32; ++ks) {
+    u32x4 bv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], ks);
+    bv[NDT - 1] = bones;
+    const u32x4 kb = tr_operand<16>(b.k, to.k, ks);
+    float kr[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kr[2 * i] = kSqrt2 * lo_bf16(kb[i]);
+      kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
+    }
+    tile16_into<W>(acc[0], kr, bv);
+    tile16_into<W + 4>(acc[1], kr, bv);
+    if constexpr (W == 0) tile16_into<8>(acc[2], kr, bv);
+  }
+}
+
+template <int C>
+__global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
+  using CF = Cfg<16, C>;
+  constexpr int DK = 16, SB_LD = CF::SB_LD;
+  static_assert(CF::NDW == NDT, "whole output rows per wave");
+  __shared__ DmaTileQ16<C> x0;
+  __shared__ DmaTileQ16<C> x1;
+  __shared__ alignas(16) uint16_t ones[128];
+  __shared__ alignas(16) uint16_t Sb[VROWS * SB_LD];
+  __shared__ alignas(16) uint16_t Ob[CF::NW][16 * OB_LD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / a.n_spans;
+  const int64_t sp = blockIdx.x - bh * a.n_spans;
+  const int64_t tok0 = bh * a.T;
+
+  // feature positions no tile writes hold no feature: zero once
+  for (int e = tid; e < VROWS * CF::NPOS; e += CF::NT) {
+    const int c = e % CF::NPOS;
+    if (sb_col_unused<CF>(c)) Sb[(e / CF::NPOS) * SB_LD + c] = 0;
+  }
+  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
+  with_wave<CF::NW>(w, [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    // output stores a wave issues per chunk: two 1 KB stores per query tile
+    constexpr int NSTORE = 2 * CF::NSLOT;
+    const ReadoutLane<CF> L = readout_lane<CF>(W, lane);
+    const TrOffsets to = tr_offsets(lane);
+    f32x4 acc[CF::MFT][NDT];
+    load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
+                   W, lane);
+    write_sb<CF>(Sb, acc, W, lane);
+    const int64_t first = sp * a.G * C;
+    int64_t end = first + a.G * C;
+    if (end > a.T) end = a.T;
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end); };
+    dma_chunkq16<C, W, CF::NW>(x0, src(first), lane);
+    // the state loads and the first chunk; an unconditional vmcnt(0) also
+    // retires the state loads for the compiler's wait-count analysis
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    // the ones-column tile: row 0 of `ones` is all ones, row 1 all zeros
+    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[((lane & 15) > 0 ? 64 : 0) + 8 * (lane >> 4)]);
+
+    // one chunk: prefetch the next into the other buffer, read out, and
+    // (unless it is the span's last) carry the state and refresh Sb
+    auto chunk = [&](DmaTileQ16<C>& cur, DmaTileQ16<C>& nxt, int64_t c) {
+      const int64_t n = (a.T - c < C) ? a.T - c : C;
+      // the next chunk's transfer goes out right after the query rows are
+      // read (zeros past the span's end); issued any earlier, the compiler's
+      // wait counts make those row reads wait for it
+      auto prefetch = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_chunkq16<C, W, CF::NW>(nxt, src(c + C), lane);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      readout_chunk<CF>(DmaSrc16<C>{cur, to, bones}, Sb, L, lane, a.eps,
+                        rows_rsrc(a.out, tok0 + c, n, 2 * DV), Ob[W], prefetch);
+      const bool more = c + C < end;
+      if (more) state_update_ro16<CF, W>(acc, cur, bones, to);
+      // this wave's share of the next chunk has landed (the output stores
+      // issued after it may still be in flight).  Unconditional, so that on
+      // every path the compiler's wait counts see the transfer retired.
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NSTORE));
+      if (more) {
+        // every wave is done reading `cur` and Sb, and the next chunk is visible
+        barrier_lds();
+        write_sb<CF>(Sb, acc, W, lane);
+        barrier_lds();
+      }
+    };
+    for (int64_t c0 = first; c0 < end; c0 += 2 * C) {
+      chunk(x0, x1, c0);
+      if (c0 + C < end) chunk(x1, x0, c0 + C);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   });
 }
 
@@ -1187,7 +1368,11 @@ template <int DK, int C>
 hipError_t launch_readout(const MfmaArgs& a, hipStream_t stream) {
   using CF = Cfg<DK, C>;
   dim3 grid(static_cast<unsigned>(a.BH * a.n_spans));
-  readout_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
+  if constexpr (DK == 16) {
+    readout_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
+  } else {
+    readout_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
