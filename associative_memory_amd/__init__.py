@@ -37,6 +37,7 @@ EXPORTED = (
     "kata_decode_step",
     "kata_forward_plan",
     "kata_forward_chunked_profiled",
+    "kata_forward_quadratic",
 )
 
 
@@ -77,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_chunked_profiled.restype = i32
     L.kata_forward_chunked_profiled.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32,
                                                 i32, i32, vp, sz, vp, vp]
+    L.kata_forward_quadratic.restype = i32
+    L.kata_forward_quadratic.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, vp]
     L.kata_forward_plan.restype = i32
     L.kata_forward_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]
     _lib = L
@@ -191,6 +194,24 @@ def kata_forward_chunked(q, k, v, chunk: int, eps: float = 1e-6, scan="auto", ou
     st = lib().kata_forward_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv, chunk,
                                     float(eps), _dtype_code(q), sc, wptr, wbytes, _stream(stream))
     _check(st, "kata_forward_chunked")
+    return out
+
+
+def kata_forward_quadratic(q, k, v, eps: float = 1e-6, out=None, stream=None):
+    """The same causal read as kata_forward_chunked in its direct O(T^2) form
+    (no state, no workspace).  q, k: [B, H, T, d]; v: [B, H, T, dv]; bf16,
+    contiguous, on the device.  Returns out [B, H, T, dv] bf16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _device_tensor(t, n)
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
+    _device_tensor(out, "out")
+    st = lib().kata_forward_quadratic(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv,
+                                      float(eps), _dtype_code(q), _stream(stream))
+    _check(st, "kata_forward_quadratic")
     return out
 
 

@@ -1352,6 +1352,200 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
   });
 }
 
+// ------------------------------------------------------------ quadratic forward
+//
+// The O(T^2) form of the read, Eq. 2 of the KATA page evaluated directly (its
+// flash-style "quadratic" operating point, Sec. 4): per block of 128 queries,
+// the key blocks up to the diagonal stream through LDS (DMA, two buffers);
+// each gives the squared scores (QK^T)^2 on the matrix cores, masked only on
+// the diagonal block, and adds P [V | 1] to fp32 accumulators that stay in
+// registers.  No state, no workspace.  Wave W owns query tiles W and 7 - W.
+constexpr int QB = 128;
+
+template <int DK>
+struct alignas(16) QuadTile {
+  alignas(16) uint16_t v[QB * DV];  // [key][value column], swizzled
+  alignas(16) uint16_t k[QB * DK];  // [key][dimension]
+};
+
+template <int DK, int W>
+__device__ __forceinline__ void dma_quad(QuadTile<DK>& b, const ChunkSrc& src, int lane) {
+#pragma unroll
+  for (int j = W; j < QB / 8; j += 4) {
+    const int t = 8 * j + (lane >> 3);
+    const int cg = (lane & 7) ^ vswz(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, KATA_LDS(&b.v[8 * j * DV]), 16, t * (2 * DV) + 16 * cg, 0, 0, 0);
+  }
+  constexpr int PPR = 2 * DK / 16;  // 16-byte pieces per K row
+  constexpr int RPI = 64 / PPR;     // K rows per 1 KB transfer
+#pragma unroll
+  for (int j = W; j < QB / RPI; j += 4) {
+    const int t = RPI * j + lane / PPR;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[RPI * j * DK]), 16,
+                                             t * (2 * DK) + 16 * (lane % PPR), 0, 0, 0);
+  }
+}
+
+template <int DK>
+__device__ __forceinline__ ScoreOp<DK> quad_key_op(const QuadTile<DK>& b, int row, int g) {
+  if constexpr (DK == 16) {
+    return *reinterpret_cast<const uint2*>(&b.k[row * 16 + 4 * g]);
+  } else {
+    return *reinterpret_cast<const u32x4*>(&b.k[row * 32 + 8 * g]);
+  }
+}
+
+// one key block against the wave's two query tiles; DIAG: the block holding
+// the queries themselves (causal mask, fully masked tiles skipped)
+// `after_k` runs once the block's key operands are in registers (the next
+// block's transfer is issued there: any earlier, the compiler's wait counts
+// make these reads wait for it)
+template <int DK, int W, bool DIAG, class H>
+__device__ __forceinline__ void quad_block(f32x4 (&o)[2][NDT], const QuadTile<DK>& b,
+                                           const ScoreOp<DK> (&qf)[2], const bool (&keep)[4],
+                                           const TrOffsets& to, const u32x4& bones, int lane,
+                                           const H& after_k) {
+  constexpr int qt[2] = {W, 7 - W};
+  constexpr int qt_max = qt[0] > qt[1] ? qt[0] : qt[1];
+  constexpr int NS = DIAG ? qt_max / 2 + 1 : QB / 32;  // 32-key steps read
+  const int g = lane >> 4, r = lane & 15;
+  ScoreOp<DK> kall[NS][2];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) kall[s][h] = quad_key_op<DK>(b, 16 * (2 * s + h) + r, g);
+  }
+  after_k();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const ScoreOp<DK> (&kf)[2] = kall[s];
+    u32x4 bv[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], s);
+    bv[NDT - 1] = bones;
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+      if (DIAG && 2 * s > qt[slot]) continue;
+      float p[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kt = 2 * s + h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
+        if (DIAG && kt > qt[slot]) continue;
+        const f32x4 sc = score_mfma<DK>(kf[h], qf[slot]);  // [key 4g+j][query r]
+        if (DIAG && kt == qt[slot]) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[h][j] = keep[j] ? sc[j] * sc[j] : 0.f;
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[h][j] = sc[j] * sc[j];
+        }
+      }
+      const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
+                        pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
+    }
+  }
+}
+
+template <int DK>
+__global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
+  __shared__ QuadTile<DK> x0;
+  __shared__ QuadTile<DK> x1;
+  __shared__ alignas(16) uint16_t ones[128];
+  __shared__ alignas(16) uint16_t Ob[4][16 * OB_LD];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nqb = (a.T + QB - 1) / QB;
+  const int64_t bh = blockIdx.x / nqb;
+  const int64_t qb = nqb - 1 - (blockIdx.x - bh * nqb);  // the longest rows of blocks first
+  const int64_t tok0 = bh * a.T;
+  const int64_t q0 = qb * QB;
+  const int64_t kend = (a.T < q0 + QB) ? a.T : q0 + QB;  // keys [0, kend) are read
+  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
+
+  with_wave<4>(w, [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    constexpr int qt[2] = {W, 7 - W};
+    const int g = lane >> 4, r = lane & 15;
+    bool keep[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) keep[j] = 4 * g + j <= r;
+    const TrOffsets to = tr_offsets(lane);
+    // the wave's query score operands, straight from HBM (rows past T read 0)
+    const __amdgpu_buffer_rsrc_t qsrc = rows_rsrc(a.q, tok0 + q0, a.T - q0 < QB ? a.T - q0 : QB, 2 * DK);
+    ScoreOp<DK> qf[2];
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+      const int off = (16 * qt[slot] + r) * (2 * DK);
+      if constexpr (DK == 16) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(qsrc, off + 8 * g, 0, 0);
+        qf[slot] = uint2{x[0], x[1]};
+      } else {
+        qf[slot] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, off + 16 * g, 0, 0);
+      }
+    }
+    f32x4 o[2][NDT];
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+#pragma unroll
+      for (int i = 0; i < NDT; ++i) o[slot][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto src = [&](int64_t kb) { return chunk_src<DK, QB>(nullptr, a.k, a.v, tok0, kb * QB, kend); };
+    dma_quad<DK, W>(x0, src(0), lane);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[(r > 0 ? 64 : 0) + 8 * g]);
+    auto prefetch = [&](QuadTile<DK>& nxt, int64_t kb) {
+      return [&src, lane, kb, p = &nxt]() {
+        __builtin_amdgcn_sched_barrier(0);
+        dma_quad<DK, W>(*p, src(kb), lane);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+    };
+    for (int64_t kb = 0; kb < qb; kb += 2) {
+      quad_block<DK, W, false>(o, x0, qf, keep, to, bones, lane, prefetch(x1, kb + 1));
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      barrier_lds();
+      if (kb + 1 < qb) {
+        quad_block<DK, W, false>(o, x1, qf, keep, to, bones, lane, prefetch(x0, kb + 2));
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        barrier_lds();
+      }
+    }
+    // the diagonal block: in x0 when qb is even, in x1 when odd
+    if (qb & 1) {
+      quad_block<DK, W, true>(o, x1, qf, keep, to, bones, lane, NoHook{});
+    } else {
+      quad_block<DK, W, true>(o, x0, qf, keep, to, bones, lane, NoHook{});
+    }
+    // normalise; stage each 16 x 64 tile and store it as 1 KB contiguous rows
+    const __amdgpu_buffer_rsrc_t dst = rows_rsrc(a.out, tok0 + q0, a.T - q0 < QB ? a.T - q0 : QB, 2 * DV);
+    uint16_t* ob = Ob[W];
+#pragma unroll
+    for (int slot = 0; slot < 2; ++slot) {
+      const float den = __shfl(o[slot][NDT - 1][0], r);
+      const float inv = __builtin_amdgcn_rcpf(den + a.eps);
+#pragma unroll
+      for (int i = 0; i < NDT - 1; ++i) {
+        uint2 x;
+        x.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
+        x.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
+        *reinterpret_cast<uint2*>(&ob[r * OB_LD + 16 * i + 4 * g]) = x;
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * h + (lane >> 3);
+        const uint4 x = *reinterpret_cast<const uint4*>(&ob[row * OB_LD + 8 * (lane & 7)]);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, dst,
+                                               (16 * qt[slot] + row) * (2 * DV) + 16 * (lane & 7), 0, 0);
+      }
+    }
+  });
+}
+
 template <int DK, int C>
 hipError_t launch_span(const MfmaArgs& a, hipStream_t stream) {
   using CF = Cfg<DK, C>;
@@ -1385,6 +1579,19 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 32 && a.chunk == 64) return launch_span<32, 64>(a, stream);
   if (a.d == 32 && a.chunk == 128) return launch_span<32, 128>(a, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_forward_quadratic_mfma(const QuadArgs& a, hipStream_t stream) {
+  const int64_t nqb = (a.T + QB - 1) / QB;
+  dim3 grid(static_cast<unsigned>(a.BH * nqb));
+  if (a.d == 16) {
+    quad_kernel<16><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 32) {
+    quad_kernel<32><<<grid, 256, 0, stream>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream) {

@@ -37,6 +37,22 @@ struct MfmaArgs {
   float eps;
 };
 
+struct QuadArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int64_t BH;
+  int64_t T;
+  int d;
+  float eps;
+};
+
+inline bool quadratic_supported(bool bf16, int d, int dv) { return bf16 && (d == 16 || d == 32) && dv == 64; }
+
+// the O(T^2) form: one workgroup per (head, 128-query block)
+hipError_t launch_forward_quadratic_mfma(const QuadArgs& a, hipStream_t stream);
+
 inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
   return bf16 && (d == 16 || d == 32) && dv == 64 && (chunk == 64 || chunk == 128);
 }

@@ -210,7 +210,33 @@ def bench_other_workloads(args, hip, am, ki, torch):
             "plan": am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk,
                                          am.KATA_BF16 if w.dtype == ki.BF16 else am.KATA_F32, "auto"),
         }
+        if w.dtype == ki.BF16 and w.dv == 64:
+            res[w.name]["quadratic"] = bench_quadratic(args, hip, am, torch, w, q, k, v, out)
     return res
+
+
+def bench_quadratic(args, hip, am, torch, w, q, k, v, out):
+    """The direct O(T^2) form on the same inputs.  Useful FLOPs: the causal
+    triangle of (d + dv + 1)-wide products, 2 * (T+1)/2 * (d + dv) per
+    token-head as for the intra-chunk block, with the chunk as long as the
+    sequence."""
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        am.kata_forward_quadratic(q, k, v, eps=w.eps, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        am.kata_forward_quadratic(q, k, v, eps=w.eps, out=out)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / args.steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    flops = 2 * (w.T + 1) / 2 * (w.d + w.dv) * w.B * w.H * w.T
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
 
 # ------------------------------------------------------------------ decode

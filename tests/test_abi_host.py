@@ -135,3 +135,21 @@ def test_prefill_and_feature_map_error_paths():
     assert L.kata_forward_plan(1, 1, 64, 16, 16, 32, BF16, 0, None, 0) == INVALID
     assert L.kata_forward_plan(1, 1, 64, 16, 16, 32, BF16, 0, buf, 8) == OK
     assert len(buf.value) == 7  # truncated, NUL-terminated
+
+
+def quad(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=300, d=16, dv=64, eps=1e-6, dt=BF16):
+    return am.lib().kata_forward_quadratic(q, k, v, out, B, H, T, d, dv, eps, dt, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), INVALID), (dict(out=NULL), INVALID),
+    (dict(B=0), INVALID), (dict(T=0), INVALID), (dict(d=0), INVALID),
+    (dict(dt=F32), UNSUPPORTED), (dict(d=24), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
+    (dict(eps=-1.0), INVALID), (dict(eps=float("nan")), INVALID), (dict(dt=9), INVALID),
+    (dict(k=ctypes.c_void_p(P[1].value + 2)), INVALID),      # misaligned
+    (dict(out=P[1]), INVALID),                                # out aliases k
+    (dict(out=ctypes.c_void_p(P[2].value + 64)), INVALID),   # out overlaps v
+    (dict(B=1 << 20, H=1 << 10, T=1 << 20), UNSUPPORTED),     # grid too large
+])
+def test_quadratic_error_paths(kw, status):
+    assert quad(**kw) == status
