@@ -79,7 +79,7 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_chunked_profiled.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32,
                                                 i32, i32, vp, sz, vp, vp]
     L.kata_forward_quadratic.restype = i32
-    L.kata_forward_quadratic.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, f32, i32, vp]
+    L.kata_forward_quadratic.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, i32, vp]
     L.kata_forward_plan.restype = i32
     L.kata_forward_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]
     _lib = L
@@ -197,10 +197,11 @@ def kata_forward_chunked(q, k, v, chunk: int, eps: float = 1e-6, scan="auto", ou
     return out
 
 
-def kata_forward_quadratic(q, k, v, eps: float = 1e-6, out=None, stream=None):
-    """The same causal read as kata_forward_chunked in its direct O(T^2) form
-    (no state, no workspace).  q, k: [B, H, T, d]; v: [B, H, T, dv]; bf16,
-    contiguous, on the device.  Returns out [B, H, T, dv] bf16."""
+def kata_forward_quadratic(q, k, v, eps: float = 1e-6, g: int = 1, out=None, stream=None):
+    """The causal read in its direct O(T^2) form (no state, no workspace),
+    with the KATA-Mg score sum_a (q_a . k_a)^2 over g blocks of q and k
+    (g = 1: the full map's (q . k)^2).  q, k: [B, H, T, d]; v: [B, H, T, dv];
+    bf16, contiguous, on the device.  Returns out [B, H, T, dv] bf16."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _device_tensor(t, n)
@@ -210,7 +211,7 @@ def kata_forward_quadratic(q, k, v, eps: float = 1e-6, out=None, stream=None):
         out = torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
     _device_tensor(out, "out")
     st = lib().kata_forward_quadratic(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv,
-                                      float(eps), _dtype_code(q), _stream(stream))
+                                      int(g), float(eps), _dtype_code(q), _stream(stream))
     _check(st, "kata_forward_quadratic")
     return out
 

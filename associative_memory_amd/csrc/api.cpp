@@ -110,14 +110,15 @@ kata_status_t kata_forward_chunked(const void* q, const void* k, const void* v, 
 }
 
 kata_status_t kata_forward_quadratic(const void* q, const void* k, const void* v, void* out,
-                                     int B, int H, int64_t T, int d, int dv, float eps,
+                                     int B, int H, int64_t T, int d, int dv, int g, float eps,
                                      kata_dtype_t dtype, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;
-  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0) return KATA_ERR_INVALID_VALUE;
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0 || g <= 0) return KATA_ERR_INVALID_VALUE;
+  if (d % g != 0) return KATA_ERR_INVALID_VALUE;
   if (!dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
   if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KATA_ERR_INVALID_VALUE;
-  if (!kata::quadratic_supported(dtype == KATA_BF16, d, dv)) return KATA_ERR_UNSUPPORTED;
+  if (!kata::quadratic_supported(dtype == KATA_BF16, d, dv, g)) return KATA_ERR_UNSUPPORTED;
   const int64_t BH = static_cast<int64_t>(B) * H;
   // one workgroup per (head, 128-query block): the grid must fit 2^31 - 1
   if (T > (INT64_C(1) << 40) / BH || BH * ((T + 127) / 128) > INT64_C(0x7fffffff))
@@ -128,7 +129,7 @@ kata_status_t kata_forward_quadratic(const void* q, const void* k, const void* v
   if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
       overlaps(out, v_bytes, v, v_bytes))
     return KATA_ERR_INVALID_VALUE;
-  kata::QuadArgs a{q, k, v, out, BH, T, d, eps};
+  kata::QuadArgs a{q, k, v, out, BH, T, d, g, eps};
   return from_hip(kata::launch_forward_quadratic_mfma(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -1357,15 +1357,60 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
 // The O(T^2) form of the read, Eq. 2 of the KATA page evaluated directly (its
 // flash-style "quadratic" operating point, Sec. 4): per block of 128 queries,
 // the key blocks up to the diagonal stream through LDS (DMA, two buffers);
-// each gives the squared scores (QK^T)^2 on the matrix cores, masked only on
-// the diagonal block, and adds P [V | 1] to fp32 accumulators that stay in
+// each gives the squared scores on the matrix cores, masked only on the
+// diagonal block, and adds P [V | 1] to fp32 accumulators that stay in
 // registers.  No state, no workspace.  Wave W owns query tiles W and 7 - W.
+//
+// Scores follow the KATA-Mg block family of Sec. 4.1: the d dimensions split
+// into g = DK / M blocks of width M and the score is sum_a (q_a . k_a)^2
+// (g = 1: the full map's (q . k)^2).  A score operand is a set of pieces:
+// at M = 16 one 16x16x16 product per block (4 dimensions per lane), otherwise
+// 16x16x32 products over 32-dimension pieces, chained within a block.
 constexpr int QB = 128;
+
+template <int DK, int M>
+struct QkOp {
+  static constexpr bool K16 = (M == 16);
+  static constexpr int NP = K16 ? DK / 16 : DK / 32;  // pieces per operand
+  static constexpr int PPB = K16 ? 1 : M / 32;         // pieces per block
+  using Piece = typename ScoreOpT<K16 ? 16 : 32>::type;
+  Piece p[NP];
+  // first dimension of piece i held by lane group g
+  static constexpr __device__ int col(int i, int g) { return K16 ? 16 * i + 4 * g : 32 * i + 8 * g; }
+};
+
+// sum over blocks of the squared score tile [key 4g + j][query r]
+template <int DK, int M>
+__device__ __forceinline__ void block_sq_scores(const QkOp<DK, M>& k, const QkOp<DK, M>& q, float (&p)[4]) {
+  using Op = QkOp<DK, M>;
+#pragma unroll
+  for (int b = 0; b < Op::NP / Op::PPB; ++b) {
+    f32x4 sc;
+    if constexpr (Op::K16) {
+      sc = score_mfma<16>(k.p[b], q.p[b]);
+    } else {
+      sc = mfma(k.p[b * Op::PPB], q.p[b * Op::PPB], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int j = 1; j < Op::PPB; ++j) sc = mfma(k.p[b * Op::PPB + j], q.p[b * Op::PPB + j], sc);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p[j] = b == 0 ? sc[j] * sc[j] : __builtin_fmaf(sc[j], sc[j], p[j]);
+  }
+}
+
+// K rows in LDS hold their 16-byte pieces XOR-swizzled by the row, so that
+// the 16 rows one operand read touches fall in distinct banks:
+// piece c of row r sits at c ^ ksw(r).
+template <int DK>
+__device__ __forceinline__ int ksw(int r) {
+  constexpr int SH = DK == 16 ? 3 : (DK == 32 ? 2 : 1);  // log2(128 / DK)
+  return (r >> SH) & (DK / 8 - 1);
+}
 
 template <int DK>
 struct alignas(16) QuadTile {
   alignas(16) uint16_t v[QB * DV];  // [key][value column], swizzled
-  alignas(16) uint16_t k[QB * DK];  // [key][dimension]
+  alignas(16) uint16_t k[QB * DK];  // [key][dimension], swizzled
 };
 
 template <int DK, int W>
@@ -1381,18 +1426,23 @@ __device__ __forceinline__ void dma_quad(QuadTile<DK>& b, const ChunkSrc& src, i
 #pragma unroll
   for (int j = W; j < QB / RPI; j += 4) {
     const int t = RPI * j + lane / PPR;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[RPI * j * DK]), 16,
-                                             t * (2 * DK) + 16 * (lane % PPR), 0, 0, 0);
+    const int c = (lane % PPR) ^ ksw<DK>(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[RPI * j * DK]), 16, t * (2 * DK) + 16 * c,
+                                             0, 0, 0);
   }
 }
 
-template <int DK>
-__device__ __forceinline__ ScoreOp<DK> quad_key_op(const QuadTile<DK>& b, int row, int g) {
-  if constexpr (DK == 16) {
-    return *reinterpret_cast<const uint2*>(&b.k[row * 16 + 4 * g]);
-  } else {
-    return *reinterpret_cast<const u32x4*>(&b.k[row * 32 + 8 * g]);
+template <int DK, int M>
+__device__ __forceinline__ QkOp<DK, M> quad_key_op(const QuadTile<DK>& b, int row, int g) {
+  using Op = QkOp<DK, M>;
+  Op op;
+#pragma unroll
+  for (int i = 0; i < Op::NP; ++i) {
+    const int col = Op::col(i, g);
+    const uint16_t* at = &b.k[row * DK + 8 * ((col >> 3) ^ ksw<DK>(row)) + (col & 7)];
+    op.p[i] = *reinterpret_cast<const typename Op::Piece*>(at);
   }
+  return op;
 }
 
 // one key block against the wave's two query tiles; DIAG: the block holding
@@ -1400,25 +1450,24 @@ __device__ __forceinline__ ScoreOp<DK> quad_key_op(const QuadTile<DK>& b, int ro
 // `after_k` runs once the block's key operands are in registers (the next
 // block's transfer is issued there: any earlier, the compiler's wait counts
 // make these reads wait for it)
-template <int DK, int W, bool DIAG, class H>
+template <int DK, int M, int W, bool DIAG, class H>
 __device__ __forceinline__ void quad_block(f32x4 (&o)[2][NDT], const QuadTile<DK>& b,
-                                           const ScoreOp<DK> (&qf)[2], const bool (&keep)[4],
+                                           const QkOp<DK, M> (&qf)[2], const bool (&keep)[4],
                                            const TrOffsets& to, const u32x4& bones, int lane,
                                            const H& after_k) {
   constexpr int qt[2] = {W, 7 - W};
   constexpr int qt_max = qt[0] > qt[1] ? qt[0] : qt[1];
   constexpr int NS = DIAG ? qt_max / 2 + 1 : QB / 32;  // 32-key steps read
   const int g = lane >> 4, r = lane & 15;
-  ScoreOp<DK> kall[NS][2];
+  QkOp<DK, M> kall[NS][2];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) kall[s][h] = quad_key_op<DK>(b, 16 * (2 * s + h) + r, g);
+    for (int h = 0; h < 2; ++h) kall[s][h] = quad_key_op<DK, M>(b, 16 * (2 * s + h) + r, g);
   }
   after_k();
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const ScoreOp<DK> (&kf)[2] = kall[s];
     u32x4 bv[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], s);
@@ -1433,13 +1482,10 @@ __device__ __forceinline__ void quad_block(f32x4 (&o)[2][NDT], const QuadTile<DK
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
         if (DIAG && kt > qt[slot]) continue;
-        const f32x4 sc = score_mfma<DK>(kf[h], qf[slot]);  // [key 4g+j][query r]
+        block_sq_scores<DK, M>(kall[s][h], qf[slot], p[h]);
         if (DIAG && kt == qt[slot]) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[h][j] = keep[j] ? sc[j] * sc[j] : 0.f;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p[h][j] = sc[j] * sc[j];
+          for (int j = 0; j < 4; ++j) p[h][j] = keep[j] ? p[h][j] : 0.f;
         }
       }
       const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
@@ -1450,8 +1496,9 @@ __device__ __forceinline__ void quad_block(f32x4 (&o)[2][NDT], const QuadTile<DK
   }
 }
 
-template <int DK>
+template <int DK, int M>
 __global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
+  using Op = QkOp<DK, M>;
   __shared__ QuadTile<DK> x0;
   __shared__ QuadTile<DK> x1;
   __shared__ alignas(16) uint16_t ones[128];
@@ -1476,15 +1523,18 @@ __global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
     const TrOffsets to = tr_offsets(lane);
     // the wave's query score operands, straight from HBM (rows past T read 0)
     const __amdgpu_buffer_rsrc_t qsrc = rows_rsrc(a.q, tok0 + q0, a.T - q0 < QB ? a.T - q0 : QB, 2 * DK);
-    ScoreOp<DK> qf[2];
+    Op qf[2];
 #pragma unroll
     for (int slot = 0; slot < 2; ++slot) {
-      const int off = (16 * qt[slot] + r) * (2 * DK);
-      if constexpr (DK == 16) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(qsrc, off + 8 * g, 0, 0);
-        qf[slot] = uint2{x[0], x[1]};
-      } else {
-        qf[slot] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, off + 16 * g, 0, 0);
+#pragma unroll
+      for (int i = 0; i < Op::NP; ++i) {
+        const int off = (16 * qt[slot] + r) * (2 * DK) + 2 * Op::col(i, g);
+        if constexpr (Op::K16) {
+          const auto x = __builtin_amdgcn_raw_buffer_load_b64(qsrc, off, 0, 0);
+          qf[slot].p[i] = uint2{x[0], x[1]};
+        } else {
+          qf[slot].p[i] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, off, 0, 0);
+        }
       }
     }
     f32x4 o[2][NDT];
@@ -1506,20 +1556,20 @@ __global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
       };
     };
     for (int64_t kb = 0; kb < qb; kb += 2) {
-      quad_block<DK, W, false>(o, x0, qf, keep, to, bones, lane, prefetch(x1, kb + 1));
+      quad_block<DK, M, W, false>(o, x0, qf, keep, to, bones, lane, prefetch(x1, kb + 1));
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
       barrier_lds();
       if (kb + 1 < qb) {
-        quad_block<DK, W, false>(o, x1, qf, keep, to, bones, lane, prefetch(x0, kb + 2));
+        quad_block<DK, M, W, false>(o, x1, qf, keep, to, bones, lane, prefetch(x0, kb + 2));
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         barrier_lds();
       }
     }
     // the diagonal block: in x0 when qb is even, in x1 when odd
     if (qb & 1) {
-      quad_block<DK, W, true>(o, x1, qf, keep, to, bones, lane, NoHook{});
+      quad_block<DK, M, W, true>(o, x1, qf, keep, to, bones, lane, NoHook{});
     } else {
-      quad_block<DK, W, true>(o, x0, qf, keep, to, bones, lane, NoHook{});
+      quad_block<DK, M, W, true>(o, x0, qf, keep, to, bones, lane, NoHook{});
     }
     // normalise; stage each 16 x 64 tile and store it as 1 KB contiguous rows
     const __amdgpu_buffer_rsrc_t dst = rows_rsrc(a.out, tok0 + q0, a.T - q0 < QB ? a.T - q0 : QB, 2 * DV);
@@ -1584,10 +1634,19 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
 hipError_t launch_forward_quadratic_mfma(const QuadArgs& a, hipStream_t stream) {
   const int64_t nqb = (a.T + QB - 1) / QB;
   dim3 grid(static_cast<unsigned>(a.BH * nqb));
-  if (a.d == 16) {
-    quad_kernel<16><<<grid, 256, 0, stream>>>(a);
-  } else if (a.d == 32) {
-    quad_kernel<32><<<grid, 256, 0, stream>>>(a);
+  const int m = a.g > 0 ? a.d / a.g : 0;
+  if (a.d == 16 && m == 16) {
+    quad_kernel<16, 16><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 32 && m == 32) {
+    quad_kernel<32, 32><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 32 && m == 16) {
+    quad_kernel<32, 16><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 64 && m == 64) {
+    quad_kernel<64, 64><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 64 && m == 32) {
+    quad_kernel<64, 32><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 64 && m == 16) {
+    quad_kernel<64, 16><<<grid, 256, 0, stream>>>(a);
   } else {
     return hipErrorInvalidValue;
   }

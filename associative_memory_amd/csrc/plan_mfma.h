@@ -45,10 +45,17 @@ struct QuadArgs {
   int64_t BH;
   int64_t T;
   int d;
+  int g;  // feature blocks (KATA-Mg); 1 = the full rank-one map
   float eps;
 };
 
-inline bool quadratic_supported(bool bf16, int d, int dv) { return bf16 && (d == 16 || d == 32) && dv == 64; }
+// bf16, dv = 64, d in {16, 32, 64} split into g blocks of width 16, 32 or 64
+inline bool quadratic_supported(bool bf16, int d, int dv, int g) {
+  if (!bf16 || dv != 64 || g < 1 || d % g != 0) return false;
+  if (d != 16 && d != 32 && d != 64) return false;
+  const int m = d / g;
+  return m == 16 || m == 32 || m == 64;
+}
 
 // the O(T^2) form: one workgroup per (head, 128-query block)
 hipError_t launch_forward_quadratic_mfma(const QuadArgs& a, hipStream_t stream);

@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured decode timing")
     ap.add_argument("--no-other", action="store_true", help="skip the other forward workloads")
+    ap.add_argument("--no-table8", action="store_true",
+                    help="skip the quadratic block-map timings on the d = 64 shape")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -217,17 +219,17 @@ def bench_other_workloads(args, hip, am, ki, torch):
 
 def bench_quadratic(args, hip, am, torch, w, q, k, v, out):
     """The direct O(T^2) form on the same inputs.  Useful FLOPs: the causal
-    triangle of (d + dv + 1)-wide products, 2 * (T+1)/2 * (d + dv) per
+    triangle of (d + dv)-wide products, 2 * (T+1)/2 * (d + dv) per
     token-head as for the intra-chunk block, with the chunk as long as the
-    sequence."""
+    sequence (the KATA-Mg score costs the same 2d per pair for any g)."""
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(args.warmup):
-        am.kata_forward_quadratic(q, k, v, eps=w.eps, out=out)
+        am.kata_forward_quadratic(q, k, v, eps=w.eps, g=w.g, out=out)
     torch.cuda.synchronize()
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, stream)
     for _ in range(args.steps):
-        am.kata_forward_quadratic(q, k, v, eps=w.eps, out=out)
+        am.kata_forward_quadratic(q, k, v, eps=w.eps, g=w.g, out=out)
     hip.record(e1, stream)
     torch.cuda.synchronize()
     ms = hip.ms(e0, e1) / args.steps
@@ -237,6 +239,27 @@ def bench_quadratic(args, hip, am, torch, w, q, k, v, out):
     return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+
+# forward latency of the quadratic KATA-M1 / KATA-M2 kernels on one H100, in
+# ms, from Table 8 of the KATA page (B = 8, H = 16, d_head = 64, bf16):
+# context for the same shapes here, not a target on this hardware
+PAGE_TABLE8_QUAD_MS = {(1024, 1): 0.07, (4096, 1): 0.58, (16384, 1): 8.92,
+                       (1024, 2): 0.07, (4096, 2): 0.72, (16384, 2): 10.62}
+
+
+def bench_table8(args, hip, am, ki, torch):
+    """The quadratic form with the KATA-Mg block maps (g = 1, 2, 4) on the
+    page's Table 8 shape, inputs drawn on the device."""
+    res = {}
+    for w in ki.TABLE8_QUAD:
+        q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
+        out = torch.empty_like(v)
+        r = bench_quadratic(args, hip, am, torch, w, q, k, v, out)
+        r["page_h100_ms"] = PAGE_TABLE8_QUAD_MS.get((w.T, w.g))
+        res[w.name] = r
+        del q, k, v, out
+    return res
 
 
 # ------------------------------------------------------------------ decode
@@ -422,6 +445,8 @@ def main():
     }
     if not args.no_other:
         rec["other_workloads"] = bench_other_workloads(args, hip, am, ki, torch)
+    if not args.no_table8:
+        rec["quadratic_block_maps_d64"] = bench_table8(args, hip, am, ki, torch)
     if not args.no_decode:
         rec["decode"] = bench_decode(args, hip, am, ki, torch, ki.DECODE)
         rec["decode_beyond_cache"] = bench_decode(args, hip, am, ki, torch, ki.DECODE_512)

@@ -107,25 +107,32 @@ kata_status_t kata_forward_chunked(const void* q, const void* k, const void* v,
                                    void* stream);
 
 /*
- * kata_forward_quadratic -- the same causal read as kata_forward_chunked,
- *   o_t = sum_{s<=t} (q_t.k_s)^2 v_s / (sum_{s<=t} (q_t.k_s)^2 + eps),
- * evaluated in its direct O(T^2) form: the read of the KATA page, Eq. 2, with
- * the rank-one lift's kernel (q.k)^2 (Sec. 3.1), which the page runs as its
- * quadratic operating point beside the chunked one (Sec. 4, Table 8).  Per
+ * kata_forward_quadratic -- the causal read of kata_forward_chunked,
+ *   o_t = sum_{s<=t} c_{t,s} v_s / (sum_{s<=t} c_{t,s} + eps),
+ * evaluated in its direct O(T^2) form: the read of the KATA page, Eq. 2, which
+ * the page runs as its quadratic operating point beside the chunked one
+ * (Sec. 4, Table 8).  The score is that of the KATA-Mg block maps (Sec. 4.1):
+ * q and k split into g equal blocks of width m = d/g and
+ *   c_{t,s} = sum_a (q_{t,a} . k_{s,a})^2,
+ * which at g = 1 is the full rank-one lift's (q_t . k_s)^2 (Sec. 3.1).  Per
  * block of 128 queries, every key block up to the diagonal contributes its
- * causally masked squared scores times [V | 1]; there is no state and no
- * workspace.  The work grows as T^2: it is the faster form for short T.
+ * causally masked scores times [V | 1]; there is no state and no workspace.
+ * The work grows as T^2: it is the faster form for short T.
  *   q, k : [B, H, T, d] bf16;  v, out : [B, H, T, dv] bf16
+ *   g    : feature blocks, >= 1, dividing d (1 = the full map)
  *   eps  : finite, >= 0; added once to the accumulated denominator
- * Arithmetic: bf16 operands, fp32 accumulation and normalisation, output
- * rounded to bf16.
- * Supported: KATA_BF16; d in {16, 32}; dv = 64; T >= 1 (other shapes and
- * KATA_F32 return KATA_ERR_UNSUPPORTED).  Pointers 16-byte aligned; out must
- * not overlap q, k or v.  Deterministic for fixed arguments and device.
+ * Arithmetic: bf16 operands, fp32 scores, squares and accumulation, scores
+ * rounded to bf16 before they weight V, fp32 normalisation, output rounded to
+ * bf16.
+ * Supported: KATA_BF16; dv = 64; d in {16, 32, 64} with block width d/g in
+ * {16, 32, 64} (M1, M2, M4 at d = 64); T >= 1 (other shapes and KATA_F32
+ * return KATA_ERR_UNSUPPORTED; g < 1 or g not dividing d is
+ * KATA_ERR_INVALID_VALUE).  Pointers 16-byte aligned; out must not overlap q,
+ * k or v.  Deterministic for fixed arguments and device.
  */
 kata_status_t kata_forward_quadratic(const void* q, const void* k, const void* v,
                                      void* out, int B, int H, int64_t T, int d,
-                                     int dv, float eps, kata_dtype_t dtype,
+                                     int dv, int g, float eps, kata_dtype_t dtype,
                                      void* stream);
 
 /*

@@ -39,6 +39,7 @@ class ForwardWorkload:
     dtype: str
     seed: int
     eps: float = 1e-6
+    g: int = 1  # feature blocks of the KATA-Mg maps (1: the full map)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -73,6 +74,17 @@ DECODE_512 = DecodeWorkload("decode_512seq_H16_d16_dv64_prefill4096_1024steps_f3
                             512, 16, 16, 64, 4096, 1024, F32, 5)
 
 FORWARD_WORKLOADS = (TINY, MEDIUM, WIDE, LONG)
+
+
+def table8(T: int, g: int, seed: int) -> ForwardWorkload:
+    """The KATA page's forward-latency shape (Table 8: B = 8, H = 16,
+    d_head = 64, bf16; dv = d_head) with the KATA-Mg map of g blocks."""
+    return ForwardWorkload(f"B8_H16_T{T}_d64_dv64_M{g}_bf16", 8, 16, T, 64, 64, 64, BF16, seed, g=g)
+
+
+# quadratic-form measurements on that shape: M1, M2, M4 at 1K, 4K and 16K tokens
+TABLE8_QUAD = tuple(table8(T, g, 6 + 3 * i + j)
+                    for i, T in enumerate((1024, 4096, 16384)) for j, g in enumerate((1, 2, 4)))
 
 
 # ---------------------------------------------------------------- rounding
@@ -218,3 +230,22 @@ def decode_inputs_torch(seed: int, heads: int, prefill: int, steps: int, d: int,
     sk = unit((steps, heads, d))
     sv = torch.randn((steps, heads, dv), generator=gen, device=device, dtype=torch.float32)
     return pk, pv, sq, sk, sv
+
+
+def forward_inputs_torch(B: int, H: int, T: int, d: int, dv: int, seed: int, device):
+    """bf16 q, k (unit rows) and v (Gaussian) drawn on the device with
+    torch's seeded generator, for timing large shapes (same distributions as
+    forward_inputs, not the same numbers)."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def unit(shape):
+        x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+        return (x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    q = unit((B, H, T, d))
+    k = unit((B, H, T, d))
+    v = torch.randn((B, H, T, dv), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v

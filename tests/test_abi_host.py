@@ -137,8 +137,8 @@ def test_prefill_and_feature_map_error_paths():
     assert len(buf.value) == 7  # truncated, NUL-terminated
 
 
-def quad(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=300, d=16, dv=64, eps=1e-6, dt=BF16):
-    return am.lib().kata_forward_quadratic(q, k, v, out, B, H, T, d, dv, eps, dt, None)
+def quad(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=300, d=16, dv=64, g=1, eps=1e-6, dt=BF16):
+    return am.lib().kata_forward_quadratic(q, k, v, out, B, H, T, d, dv, g, eps, dt, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -150,6 +150,9 @@ def quad(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=300, d=16, dv=64, eps=1e-
     (dict(out=P[1]), INVALID),                                # out aliases k
     (dict(out=ctypes.c_void_p(P[2].value + 64)), INVALID),   # out overlaps v
     (dict(B=1 << 20, H=1 << 10, T=1 << 20), UNSUPPORTED),     # grid too large
+    (dict(g=0), INVALID), (dict(g=-2), INVALID), (dict(d=64, g=3), INVALID),  # g must divide d
+    (dict(d=16, g=2), UNSUPPORTED), (dict(d=64, g=8), UNSUPPORTED),  # block width 8
+    (dict(d=48, g=3), UNSUPPORTED), (dict(d=128, g=2), UNSUPPORTED),
 ])
 def test_quadratic_error_paths(kw, status):
     assert quad(**kw) == status

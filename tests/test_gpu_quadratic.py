@@ -1,7 +1,8 @@
 """GPU parity of the quadratic (O(T^2)) forward against the fp64 oracle,
 through the C ABI: full outputs at the T = 2048 workload and on ragged shapes,
-sampled rows at T = 8192 (d = 32), agreement with the chunked form, and
-run-to-run determinism."""
+sampled rows at T = 8192 (d = 32), the KATA-Mg block maps at d = 64 (full
+outputs on ragged shapes, sampled rows at the page's Table 8 shape),
+agreement with the chunked form, and run-to-run determinism."""
 import numpy as np
 import pytest
 import torch
@@ -14,9 +15,9 @@ from gpu_util import check, say, to_dev, to_host64
 pytestmark = pytest.mark.gpu
 
 
-def run(inp, eps):
+def run(inp, eps, g=1):
     q, k, v = (to_dev(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
-    out = am.kata_forward_quadratic(q, k, v, eps=eps)
+    out = am.kata_forward_quadratic(q, k, v, eps=eps, g=g)
     torch.cuda.synchronize()
     return to_host64(out)
 
@@ -60,6 +61,40 @@ def test_sampled_rows_wide():
             refs.append(orc.forward_rows(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], rows, w.eps))
             gots.append(got[b, h, rows])
     check(np.concatenate(gots), np.concatenate(refs), w.dtype, np.abs(inp.v64).max(), "quadratic wide rows")
+
+
+BLOCK_CASES = [
+    # (B, H, T, d, g): block width d/g in {16, 32, 64}
+    (1, 1, 1, 64, 1), (1, 2, 77, 64, 2), (2, 1, 300, 64, 4), (1, 1, 1000, 64, 1),
+    (1, 2, 2049, 64, 2), (2, 2, 513, 64, 4), (1, 1, 4097, 64, 4), (2, 1, 700, 32, 2),
+    (1, 1, 3000, 32, 2), (2, 4, 1024, 64, 2),
+]
+
+
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=lambda c: "B{}H{}T{}d{}g{}".format(*c))
+def test_block_maps(case):
+    B, H, T, d, g = case
+    say(f"quadratic block map {case}")
+    inp = ki.forward_inputs(B, H, T, d, 64, ki.BF16, seed=T + 7 * g)
+    got = run(inp, 1e-6, g)
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6, g=g)
+    check(got, ref, ki.BF16, np.abs(inp.v64).max(), f"quadratic {case}")
+
+
+@pytest.mark.parametrize("g", [1, 2, 4])
+def test_table8_shape_sampled_rows(g):
+    w = ki.table8(4096, g, 40 + g)
+    say(f"quadratic {w.name} sampled rows")
+    inp = ki.workload_inputs(w)
+    got = run(inp, w.eps, g)
+    rng = np.random.Generator(np.random.PCG64(w.seed + 300))
+    refs, gots = [], []
+    for b in range(w.B):
+        for h in rng.choice(w.H, 4, replace=False):
+            rows = sorted({0, 127, 128, w.T - 1} | {int(x) for x in rng.integers(0, w.T, 6)})
+            refs.append(orc.forward_rows(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], rows, w.eps, g=g))
+            gots.append(got[b, h, rows])
+    check(np.concatenate(gots), np.concatenate(refs), w.dtype, np.abs(inp.v64).max(), w.name + " rows")
 
 
 def test_matches_chunked_form():
