@@ -38,6 +38,8 @@ EXPORTED = (
     "kata_forward_plan",
     "kata_forward_chunked_profiled",
     "kata_forward_quadratic",
+    "kata_forward_linear_workspace_bytes",
+    "kata_forward_linear",
 )
 
 
@@ -80,6 +82,11 @@ def lib() -> ctypes.CDLL:
                                                 i32, i32, vp, sz, vp, vp]
     L.kata_forward_quadratic.restype = i32
     L.kata_forward_quadratic.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, i32, vp]
+    L.kata_forward_linear_workspace_bytes.restype = sz
+    L.kata_forward_linear_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.kata_forward_linear.restype = i32
+    L.kata_forward_linear.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, f32, f32, i32,
+                                      vp, sz, vp]
     L.kata_forward_plan.restype = i32
     L.kata_forward_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]
     _lib = L
@@ -278,4 +285,42 @@ def kata_decode_step(S, z, q, k, v, eps: float = 1e-6, out=None, B: Optional[int
     st = lib().kata_decode_step(_ptr(S), _ptr(z), _ptr(q), _ptr(k), _ptr(v), _ptr(out), b,
                                 BH // b, d, dv, float(eps), _dtype_code(q), _stream(stream))
     _check(st, "kata_decode_step")
+    return out
+
+
+KATA_FEATURE_ORTHANT = 0
+KATA_FEATURE_LORENTZ = 1
+_FEATURES = {"orthant": KATA_FEATURE_ORTHANT, "lorentz": KATA_FEATURE_LORENTZ}
+
+
+def kata_forward_linear_workspace_bytes(B, H, T, d, dv, chunk=64) -> int:
+    return int(lib().kata_forward_linear_workspace_bytes(B, H, T, d, dv, chunk))
+
+
+def kata_forward_linear(q, k, v, feature: str = "orthant", shift: float = 1e-6, eps: float = 1e-6,
+                        chunk: int = 64, out=None, workspace=None, stream=None):
+    """Causal normalised read with a linear cone feature,
+    o_t = sum_{s<=t} (psi(q_t).psi(k_s)) v_s / (sum + eps), psi the orthant
+    (ReLU(x) + shift) or Lorentz ((y, |y|(1 + s^2))) map.  q, k: [B, H, T, d];
+    v: [B, H, T, dv]; bf16, contiguous, on the device.  Returns out
+    [B, H, T, dv] bf16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _device_tensor(t, n)
+    if feature not in _FEATURES:
+        raise ValueError(f"feature must be one of {sorted(_FEATURES)}, got {feature!r}")
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
+    _device_tensor(out, "out")
+    need = kata_forward_linear_workspace_bytes(B, H, T, d, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = _ptr(workspace) if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().kata_forward_linear(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv, chunk,
+                                   _FEATURES[feature], float(shift), float(eps), _dtype_code(q), wptr,
+                                   wbytes, _stream(stream))
+    _check(st, "kata_forward_linear")
     return out

@@ -48,6 +48,33 @@ kata_status_t check_forward_shape(int B, int H, int64_t T, int d, int dv, int ch
   return KATA_OK;
 }
 
+// Span plan of the linear-feature forward: about 512 readout workgroups.
+struct LinPlan {
+  int64_t n_chunks, G, n_spans;
+  size_t ws_bytes;
+};
+
+LinPlan plan_linear(int64_t BH, int64_t T) {
+  LinPlan p;
+  p.n_chunks = (T + kata::kLinChunk - 1) / kata::kLinChunk;
+  const int64_t spans = (512 + BH - 1) / BH;
+  p.G = (p.n_chunks + spans - 1) / spans;
+  p.n_spans = (p.n_chunks + p.G - 1) / p.G;
+  p.ws_bytes = p.n_spans > 1 ? static_cast<size_t>(BH * p.n_spans * kata::kLinStateFloats) * sizeof(float) : 0;
+  return p;
+}
+
+kata_status_t check_linear_shape(int B, int H, int64_t T, int d, int dv, int chunk,
+                                 kata_feature_t feature, kata_dtype_t dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0 || chunk <= 0) return KATA_ERR_INVALID_VALUE;
+  if (!dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (feature != KATA_FEATURE_ORTHANT && feature != KATA_FEATURE_LORENTZ) return KATA_ERR_INVALID_VALUE;
+  if (!kata::linear_supported(dtype == KATA_BF16, d, dv, chunk)) return KATA_ERR_UNSUPPORTED;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (T > (INT64_C(1) << 40) / BH) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +158,49 @@ kata_status_t kata_forward_quadratic(const void* q, const void* k, const void* v
     return KATA_ERR_INVALID_VALUE;
   kata::QuadArgs a{q, k, v, out, BH, T, d, g, eps};
   return from_hip(kata::launch_forward_quadratic_mfma(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t kata_forward_linear_workspace_bytes(int B, int H, int64_t T, int d, int dv, int chunk) {
+  if (check_linear_shape(B, H, T, d, dv, chunk, KATA_FEATURE_ORTHANT, KATA_BF16) != KATA_OK) return 0;
+  return plan_linear(static_cast<int64_t>(B) * H, T).ws_bytes;
+}
+
+kata_status_t kata_forward_linear(const void* q, const void* k, const void* v, void* out, int B,
+                                  int H, int64_t T, int d, int dv, int chunk,
+                                  kata_feature_t feature, float shift, float eps,
+                                  kata_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;
+  const kata_status_t st = check_linear_shape(B, H, T, d, dv, chunk, feature, dtype);
+  if (st != KATA_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
+  if (!std::isfinite(shift) || shift < 0.f) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return KATA_ERR_INVALID_VALUE;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  const size_t es = elem_size(dtype);
+  const size_t qk_bytes = static_cast<size_t>(BH * T * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
+  if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
+      overlaps(out, v_bytes, v, v_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  const LinPlan p = plan_linear(BH, T);
+  if (p.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < p.ws_bytes) return KATA_ERR_WORKSPACE;
+    if (overlaps(workspace, p.ws_bytes, out, v_bytes) || overlaps(workspace, p.ws_bytes, q, qk_bytes) ||
+        overlaps(workspace, p.ws_bytes, k, qk_bytes) || overlaps(workspace, p.ws_bytes, v, v_bytes))
+      return KATA_ERR_INVALID_VALUE;
+  }
+  if (BH * p.n_spans > INT64_C(0x7fffffff)) return KATA_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  kata::LinArgs a{q, k, v, out, static_cast<float*>(workspace), BH, T, static_cast<int>(feature),
+                  shift, p.G, p.n_spans, eps};
+  if (p.n_spans > 1) {
+    hipError_t e = kata::launch_linear_span_state(a, s);
+    if (e == hipSuccess) e = kata::launch_scan_sequential(a.ws, BH, p.n_spans, kata::kLinStateFloats, s);
+    if (e != hipSuccess) return KATA_ERR_DEVICE;
+  }
+  return from_hip(kata::launch_linear_readout(a, s));
 }
 
 kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const void* v,

@@ -60,6 +60,40 @@ inline bool quadratic_supported(bool bf16, int d, int dv, int g) {
 // the O(T^2) form: one workgroup per (head, 128-query block)
 hipError_t launch_forward_quadratic_mfma(const QuadArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------------ linear cone features
+// (D = d = 64, chunk 64): orthant psi(x) = ReLU(x) + shift, Lorentz
+// psi(x) = (y, |y| (1 + s^2))
+constexpr int kLinFeatOrthant = 0;
+constexpr int kLinFeatLorentz = 1;
+constexpr int kLinChunk = 64;
+// floats of one span state: 4 feature tiles x 5 value tiles of accumulator
+// tiles (the ones-column tile holds z in its first column)
+constexpr int64_t kLinStateFloats = int64_t(4) * kMfmaValueTiles * 256;
+
+struct LinArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* ws;  // [BH][n_spans][kLinStateFloats]
+  int64_t BH;
+  int64_t T;
+  int feature;
+  float shift;
+  int64_t G;        // chunks per span
+  int64_t n_spans;  // spans per head
+  float eps;
+};
+
+inline bool linear_supported(bool bf16, int d, int dv, int chunk) {
+  return bf16 && d == 64 && dv == 64 && chunk == kLinChunk;
+}
+
+// span sums psi(K)^T [V | 1] of spans 0 .. n_spans-2 of every head into ws
+hipError_t launch_linear_span_state(const LinArgs& a, hipStream_t stream);
+// readout of every span from the exclusive prefix in ws
+hipError_t launch_linear_readout(const LinArgs& a, hipStream_t stream);
+
 inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
   return bf16 && (d == 16 || d == 32) && dv == 64 && (chunk == 64 || chunk == 128);
 }

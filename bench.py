@@ -47,6 +47,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured decode timing")
     ap.add_argument("--no-other", action="store_true", help="skip the other forward workloads")
+    ap.add_argument("--no-linear", action="store_true", help="skip the linear-feature timings")
     ap.add_argument("--no-table8", action="store_true",
                     help="skip the quadratic block-map timings on the d = 64 shape")
     ap.add_argument("--calib-copy", action="store_true",
@@ -262,6 +263,60 @@ def bench_table8(args, hip, am, ki, torch):
     return res
 
 
+# throughput of linear-feature kernels on one H100, Mtok/s, from the KATA page:
+# Table 11 (B = 1, H = 16, d_head = 64, bf16, psi(x) = x, chunk 128: its
+# tree-scan kernel) and the orthant/Lorentz table of Sec. 4.2 (B = 4, H = 12,
+# dv = 64, chunk 32, tree scan): context for the same shapes, not targets
+PAGE_LINEAR_MTOKS = {(1, 16, 131072, "orthant"): 69.4, (1, 16, 131072, "lorentz"): 69.4,
+                     (4, 12, 1024, "orthant"): 25.6, (4, 12, 1024, "lorentz"): 25.6,
+                     (4, 12, 2048, "orthant"): 30.3, (4, 12, 2048, "lorentz"): 30.3,
+                     (4, 12, 4096, "orthant"): 33.5}
+
+
+def bench_linear(args, hip, am, ki, torch):
+    """The linear-feature chunked forward (orthant, Lorentz; D = d = 64) on
+    the page's Table 11 shape and its Sec. 4.2 table shapes, inputs drawn on
+    the device.  Algorithmic bytes: q, k, v read and out written once,
+    2 (2d + dv) + 2 dv = 512 B per token-head; useful FLOPs
+    2 [(C+1)/2 (d + dv) + 2 d dv + 2 d] per token-head."""
+    res = {}
+    shapes = [(1, 16, 131072), (4, 12, 1024), (4, 12, 2048), (4, 12, 4096)]
+    d = dv = 64
+    C = 64
+    stream = torch.cuda.current_stream().cuda_stream
+    for (B, H, T) in shapes:
+        q, k, v = ki.forward_inputs_torch(B, H, T, d, dv, 80 + T % 97, "cuda")
+        out = torch.empty_like(v)
+        need = am.kata_forward_linear_workspace_bytes(B, H, T, d, dv, C)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        for feature in ("orthant", "lorentz"):
+            for _ in range(args.warmup):
+                am.kata_forward_linear(q, k, v, feature=feature, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(args.steps):
+                am.kata_forward_linear(q, k, v, feature=feature, out=out, workspace=ws)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            ms = hip.ms(e0, e1) / args.steps
+            hip.destroy(e0)
+            hip.destroy(e1)
+            BHT = B * H * T
+            bytes_ = (2 * (2 * d + dv) + 2 * dv) * BHT
+            flops = 2 * ((C + 1) / 2 * (d + dv) + 2 * d * dv + 2 * d) * BHT
+            res[f"B{B}_H{H}_T{T}_d64_dv64_{feature}_bf16"] = {
+                "ms_per_step": round(ms, 4),
+                "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                "hbm_gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                "page_h100_mtoks": PAGE_LINEAR_MTOKS.get((B, H, T, feature)),
+            }
+        del q, k, v, out, ws
+    return res
+
+
 # ------------------------------------------------------------------ decode
 
 def bench_decode(args, hip, am, ki, torch, w):
@@ -447,6 +502,8 @@ def main():
         rec["other_workloads"] = bench_other_workloads(args, hip, am, ki, torch)
     if not args.no_table8:
         rec["quadratic_block_maps_d64"] = bench_table8(args, hip, am, ki, torch)
+    if not args.no_linear:
+        rec["linear_features_d64"] = bench_linear(args, hip, am, ki, torch)
     if not args.no_decode:
         rec["decode"] = bench_decode(args, hip, am, ki, torch, ki.DECODE)
         rec["decode_beyond_cache"] = bench_decode(args, hip, am, ki, torch, ki.DECODE_512)

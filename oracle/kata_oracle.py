@@ -33,7 +33,7 @@ Capacity Wall with Symmetric Cones" (Ghriss & Chakraborty, arXiv 2607.17419):
       blocks of width m = d/g, psi_Mg(u) = (u_1 u_1^T, ..., u_g u_g^T), whose
       inner products are sum_a (q_a . k_a)^2; g = 1 is the full map.
   feature_orthant / feature_lorentz / forward_linear_quadratic /
-  forward_linear_chunked
+  forward_linear_rows / forward_linear_chunked
       the linear (D = d) cone features: KATA-Orthant psi(x) = ReLU(x) + shift,
       KATA-Lorentz psi(x) = (y, |y|_2 (1 + s^2)) with y = x_{1:d-1}, s = x_d
       (App. F.4; Sec. 2.3 names both cone families), read with the same
@@ -284,6 +284,20 @@ def forward_linear_quadratic(q: np.ndarray, k: np.ndarray, v: np.ndarray, featur
             c = np.where(cols <= rows, c, 0.0)
             out[h, t0:t1] = (c @ vf[h, :t1]) / (c.sum(axis=1, keepdims=True) + eps)
     return out.reshape(lead + (T, vf.shape[-1]))
+
+
+def forward_linear_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows, feature: str,
+                        eps: float, shift: float = 1e-6) -> np.ndarray:
+    """forward_linear_quadratic for selected query rows of one head:
+    q, k: [T, d]; v: [T, dv]; returns [len(rows), dv]."""
+    psi = linear_feature(feature, shift)
+    pk = psi(np.asarray(k, dtype=np.float64))
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((len(rows), v.shape[-1]))
+    for n, t in enumerate(rows):
+        c = pk[: t + 1] @ psi(np.asarray(q[t], dtype=np.float64))
+        out[n] = (c @ v[: t + 1]) / (c.sum() + eps)
+    return out
 
 
 def forward_linear_chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int,

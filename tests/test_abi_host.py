@@ -156,3 +156,33 @@ def quad(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=300, d=16, dv=64, g=1, ep
 ])
 def test_quadratic_error_paths(kw, status):
     assert quad(**kw) == status
+
+
+def lin(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=300, d=64, dv=64, chunk=64, feat=0, shift=1e-6,
+        eps=1e-6, dt=BF16, ws=None, wsb=0):
+    return am.lib().kata_forward_linear(q, k, v, out, B, H, T, d, dv, chunk, feat, shift, eps, dt, ws,
+                                        wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), INVALID), (dict(v=NULL), INVALID), (dict(B=0), INVALID), (dict(T=-1), INVALID),
+    (dict(feat=2), INVALID), (dict(feat=-1), INVALID), (dict(dt=7), INVALID),
+    (dict(dt=F32), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
+    (dict(chunk=128), UNSUPPORTED),
+    (dict(shift=-1.0), INVALID), (dict(shift=float("inf")), INVALID), (dict(eps=float("nan")), INVALID),
+    (dict(out=ctypes.c_void_p(P[3].value + 8)), INVALID),  # misaligned
+    (dict(out=P[0]), INVALID),                              # out aliases q
+    (dict(T=1 << 20), WORKSPACE),                           # several spans, no workspace
+])
+def test_linear_error_paths(kw, status):
+    assert lin(**kw) == status
+
+
+def test_linear_workspace_sizes():
+    L = am.lib()
+    # one span per head: no workspace
+    assert L.kata_forward_linear_workspace_bytes(64, 16, 64, 64, 64, 64) == 0
+    # B=1, H=16, T=131072: 2048 chunks per head in 32 spans of 64 chunks
+    n = L.kata_forward_linear_workspace_bytes(1, 16, 131072, 64, 64, 64)
+    assert n == 16 * 32 * 4 * 5 * 256 * 4
+    assert L.kata_forward_linear_workspace_bytes(1, 16, 131072, 32, 64, 64) == 0  # unsupported

@@ -185,6 +185,17 @@ def test_linear_chunked_equals_quadratic(feature, T):
 
 
 @pytest.mark.parametrize("feature", ["orthant", "lorentz"])
+def test_linear_rows_match_the_full_form(feature):
+    rng = np.random.Generator(np.random.PCG64(20))
+    T = 70
+    q, k, v = _unit(rng, (T, 8)), _unit(rng, (T, 8)), rng.standard_normal((T, 3))
+    rows = [0, 5, 31, 69]
+    np.testing.assert_allclose(orc.forward_linear_rows(q, k, v, rows, feature, 1e-6),
+                               orc.forward_linear_quadratic(q, k, v, feature, 1e-6)[rows], rtol=1e-13,
+                               atol=1e-15)
+
+
+@pytest.mark.parametrize("feature", ["orthant", "lorentz"])
 def test_linear_reads_are_convex_combinations(feature):
     # cone features give nonnegative scores, so (D+eps)/D o_t lies inside the visible v's range
     rng = np.random.Generator(np.random.PCG64(12))
