@@ -40,6 +40,8 @@ EXPORTED = (
     "kata_forward_quadratic",
     "kata_forward_linear_workspace_bytes",
     "kata_forward_linear",
+    "kata_forward_gated_workspace_bytes",
+    "kata_forward_gated",
 )
 
 
@@ -87,6 +89,10 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_linear.restype = i32
     L.kata_forward_linear.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, f32, f32, i32,
                                       vp, sz, vp]
+    L.kata_forward_gated_workspace_bytes.restype = sz
+    L.kata_forward_gated_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+    L.kata_forward_gated.restype = i32
+    L.kata_forward_gated.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, sz, vp]
     L.kata_forward_plan.restype = i32
     L.kata_forward_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]
     _lib = L
@@ -323,4 +329,34 @@ def kata_forward_linear(q, k, v, feature: str = "orthant", shift: float = 1e-6, 
                                    _FEATURES[feature], float(shift), float(eps), _dtype_code(q), wptr,
                                    wbytes, _stream(stream))
     _check(st, "kata_forward_linear")
+    return out
+
+
+def kata_forward_gated_workspace_bytes(B, H, T, d, dv, chunk=64) -> int:
+    return int(lib().kata_forward_gated_workspace_bytes(B, H, T, d, dv, chunk))
+
+
+def kata_forward_gated(q, k, v, log_gamma, chunk: int = 64, out=None, workspace=None, stream=None):
+    """GatedKATA read o_t = phi(q_t)^T S_t with S_t = gamma_t S_{t-1} +
+    phi(k_t) v_t^T (no denominator).  q, k: [B, H, T, d]; v: [B, H, T, dv];
+    bf16; log_gamma: [B, H, T] float32; all contiguous on the device.
+    Returns out [B, H, T, dv] bf16."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma")):
+        _device_tensor(t, n)
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    if tuple(log_gamma.shape) != (B, H, T) or log_gamma.dtype != torch.float32:
+        raise ValueError("log_gamma must be a float32 tensor of shape [B, H, T]")
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
+    _device_tensor(out, "out")
+    need = kata_forward_gated_workspace_bytes(B, H, T, d, dv, chunk)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = _ptr(workspace) if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().kata_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(out), B, H, T, d, dv,
+                                  chunk, _dtype_code(q), wptr, wbytes, _stream(stream))
+    _check(st, "kata_forward_gated")
     return out

@@ -75,6 +75,33 @@ kata_status_t check_linear_shape(int B, int H, int64_t T, int d, int dv, int chu
   return KATA_OK;
 }
 
+// Workspace of the gated read: span states (when there are several spans),
+// then the running gate sums [BH*T], then the chunk totals [BH][n_chunks].
+struct GatedLayout {
+  ForwardPlan p;
+  size_t gb_off = 0, ctot_off = 0, bytes = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+GatedLayout plan_gated(int B, int H, int64_t T, int d, int dv, int chunk) {
+  GatedLayout l;
+  l.p = kata::plan_forward(B, H, T, d, dv, chunk, KATA_BF16, KATA_SCAN_SEQUENTIAL);
+  l.gb_off = align256(l.p.ws_bytes);
+  l.ctot_off = align256(l.gb_off + static_cast<size_t>(l.p.BH * T) * sizeof(float));
+  l.bytes = l.ctot_off + static_cast<size_t>(l.p.BH * l.p.n_chunks) * sizeof(float);
+  return l;
+}
+
+kata_status_t check_gated_shape(int B, int H, int64_t T, int d, int dv, int chunk, kata_dtype_t dtype) {
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0 || chunk <= 0) return KATA_ERR_INVALID_VALUE;
+  if (!dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!kata::gated_supported(dtype == KATA_BF16, d, dv, chunk)) return KATA_ERR_UNSUPPORTED;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (T > (INT64_C(1) << 40) / BH) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -201,6 +228,66 @@ kata_status_t kata_forward_linear(const void* q, const void* k, const void* v, v
     if (e != hipSuccess) return KATA_ERR_DEVICE;
   }
   return from_hip(kata::launch_linear_readout(a, s));
+}
+
+size_t kata_forward_gated_workspace_bytes(int B, int H, int64_t T, int d, int dv, int chunk) {
+  if (check_gated_shape(B, H, T, d, dv, chunk, KATA_BF16) != KATA_OK) return 0;
+  return plan_gated(B, H, T, d, dv, chunk).bytes;
+}
+
+kata_status_t kata_forward_gated(const void* q, const void* k, const void* v, const float* log_gamma,
+                                 void* out, int B, int H, int64_t T, int d, int dv, int chunk,
+                                 kata_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || log_gamma == nullptr || out == nullptr)
+    return KATA_ERR_INVALID_VALUE;
+  const kata_status_t st = check_gated_shape(B, H, T, d, dv, chunk, dtype);
+  if (st != KATA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_gamma) || !aligned16(out) ||
+      !aligned16(workspace))
+    return KATA_ERR_INVALID_VALUE;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  const size_t es = elem_size(dtype);
+  const size_t qk_bytes = static_cast<size_t>(BH * T * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
+  const size_t g_bytes = static_cast<size_t>(BH * T) * sizeof(float);
+  if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
+      overlaps(out, v_bytes, v, v_bytes) || overlaps(out, v_bytes, log_gamma, g_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  const GatedLayout l = plan_gated(B, H, T, d, dv, chunk);
+  if (workspace == nullptr || workspace_bytes < l.bytes) return KATA_ERR_WORKSPACE;
+  if (overlaps(workspace, l.bytes, out, v_bytes) || overlaps(workspace, l.bytes, q, qk_bytes) ||
+      overlaps(workspace, l.bytes, k, qk_bytes) || overlaps(workspace, l.bytes, v, v_bytes) ||
+      overlaps(workspace, l.bytes, log_gamma, g_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  const ForwardPlan& p = l.p;
+  if (BH * p.n_spans > INT64_C(0x7fffffff) || BH * p.n_chunks > (INT64_C(1) << 33))
+    return KATA_ERR_UNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* wsb = static_cast<char*>(workspace);
+  float* gb = reinterpret_cast<float*>(wsb + l.gb_off);
+  float* ctot = reinterpret_cast<float*>(wsb + l.ctot_off);
+  kata::MfmaArgs m{};
+  m.q = q;
+  m.k = k;
+  m.v = v;
+  m.out = out;
+  m.ws = reinterpret_cast<float*>(wsb);
+  m.BH = BH;
+  m.T = T;
+  m.d = d;
+  m.chunk = chunk;
+  m.G = p.G;
+  m.n_spans = p.n_spans;
+  m.eps = 0.f;
+  m.gb = gb;
+  hipError_t e = kata::launch_gate_prep(log_gamma, gb, ctot, BH, T, chunk, s);
+  if (e == hipSuccess && p.n_spans > 1) {
+    e = kata::launch_span_state_gated(m, s);
+    if (e == hipSuccess) e = kata::launch_scan_affine(m.ws, ctot, BH, p.n_spans, p.E, p.G, p.n_chunks, s);
+  }
+  if (e == hipSuccess) e = kata::launch_readout_gated(m, s);
+  return from_hip(e);
 }
 
 kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const void* v,

@@ -379,14 +379,15 @@ __device__ __forceinline__ ScoreOp<CF::DK> score_operand_bf16(const uint16_t* Kb
 // thread.  Tokens at or past T read as zero (buffer range check).
 struct ChunkSrc {
   __amdgpu_buffer_rsrc_t q, k, v;
+  __amdgpu_buffer_rsrc_t g;  // per-token gate sums (gated read only)
 };
 
 template <int DK, int C>
 __device__ __forceinline__ ChunkSrc chunk_src(const void* q, const void* k, const void* v, int64_t tok0,
-                                              int64_t c0, int64_t T) {
+                                              int64_t c0, int64_t T, const float* gb = nullptr) {
   const int64_t n = (T - c0 < C) ? T - c0 : C;
   return ChunkSrc{rows_rsrc(q, tok0 + c0, n, 2 * DK), rows_rsrc(k, tok0 + c0, n, 2 * DK),
-                  rows_rsrc(v, tok0 + c0, n, 2 * DV)};
+                  rows_rsrc(v, tok0 + c0, n, 2 * DV), rows_rsrc(gb, tok0 + c0, n, 4)};
 }
 
 template <class CF, bool WITH_Q>
@@ -745,8 +746,18 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
 // consecutive rows.  The two buffers are distinct LDS variables and the loop
 // is unrolled over them, so the compiler's wait counts see that a chunk
 // arriving in one buffer does not alias reads of the other.
-template <int C>
-struct alignas(16) DmaTile16 {
+// Gated read only: the chunk's running gate sums beta_t (log2 units, see
+// gate_prep_kernel), 1 KB so one DMA instruction fills it (entries past the
+// chunk read as 0).  The ungated tiles carry nothing (empty base).
+template <bool G>
+struct GateRows {};
+template <>
+struct GateRows<true> {
+  alignas(16) float gb[256];
+};
+
+template <int C, bool G = false>
+struct alignas(16) DmaTile16 : GateRows<G> {
   alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
   alignas(16) uint16_t k[C * 16];  // [token][dimension]
 };
@@ -764,8 +775,16 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
 
 // wave W's share of the chunk's DMA: V in 1 KB pieces of 8 rows, K in 1 KB
 // pieces of 32 rows; rows past the buffer resource's end arrive as zero
-template <int C, int W, int NW>
-__device__ __forceinline__ void dma_chunk16(DmaTile16<C>& b, const ChunkSrc& src, int lane) {
+// the gate sums of a chunk: one DMA by the last wave
+template <bool G, int W, int NW, class B>
+__device__ __forceinline__ void dma_gate(B& b, const ChunkSrc& src, int lane) {
+  if constexpr (G && W == NW - 1) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.g, KATA_LDS(&b.gb[0]), 16, 16 * lane, 0, 0, 0);
+  }
+}
+
+template <int C, int W, int NW, bool G = false>
+__device__ __forceinline__ void dma_chunk16(DmaTile16<C, G>& b, const ChunkSrc& src, int lane) {
 #pragma unroll
   for (int j = W; j < C / 8; j += NW) {
     const int t = 8 * j + (lane >> 3);
@@ -777,6 +796,7 @@ __device__ __forceinline__ void dma_chunk16(DmaTile16<C>& b, const ChunkSrc& src
     const int t = 32 * j + (lane >> 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
   }
+  dma_gate<G, W, NW>(b, src, lane);
 }
 
 // Per-lane element offsets of the transposing reads.  Lane (g, s) addresses
@@ -821,11 +841,43 @@ __device__ __forceinline__ u32x4 tr_operand(const uint16_t* t, int off, int ks) 
 // Span-sum update: wave W reduces feature tiles W and W + 4 over every k-step
 // and the last tile (8) over the k-steps ks % 4 == W into acc8, so the waves
 // carry equal work; the partial acc8 of the waves are added once per span.
-template <class CF, int W>
+// Gated read (GatedKATA, S_t = gamma_t S_{t-1} + phi(k_t) v_t^T): over a
+// chunk with running gate sums beta_t (log2 units) and total beta_C,
+//   S <- 2^beta_C S + sum_s 2^(beta_C - beta_s) phi(k_s) v_s^T.
+// phi is quadratic in k, so token s's key row is scaled by
+// 2^((beta_C - beta_s) / 2); the lane's 8 tokens are those of its transposed
+// K operand (32 ks + 4g + m and 32 ks + 16 + 4g + m).
+template <int NA, int NB>
+__device__ __forceinline__ void gate_decay(f32x4 (&acc)[NA][NB], float f) {
+#pragma unroll
+  for (int m = 0; m < NA; ++m) {
+#pragma unroll
+    for (int dt = 0; dt < NB; ++dt) acc[m][dt] *= f;
+  }
+}
+
+__device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gb, float beta_c, int ks) {
+  const int g = __lane_id() >> 4;
+  const float4 b0 = *reinterpret_cast<const float4*>(&gb[32 * ks + 4 * g]);
+  const float4 b1 = *reinterpret_cast<const float4*>(&gb[32 * ks + 16 + 4 * g]);
+  const float bs[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kr[i] *= __builtin_amdgcn_exp2f(0.5f * (beta_c - bs[i]));
+}
+
+template <class CF, int W, bool G = false>
 __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f32x4 (&acc8)[NDT],
-                                                   const DmaTile16<CF::C>& b, const u32x4& bones,
+                                                   const DmaTile16<CF::C, G>& b, const u32x4& bones,
                                                    const TrOffsets& to) {
   static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
+  float beta_c = 0.f;
+  if constexpr (G) {
+    beta_c = b.gb[CF::C - 1];
+    const float f = __builtin_amdgcn_exp2f(beta_c);
+    gate_decay(acc, f);
+    f32x4(&a8)[1][NDT] = *reinterpret_cast<f32x4(*)[1][NDT]>(&acc8);
+    gate_decay(a8, f);
+  }
 #pragma unroll
   for (int ks = 0; ks < CF::C / 32; ++ks) {
     u32x4 bv[NDT];
@@ -839,6 +891,7 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
       kr[2 * i] = kSqrt2 * lo_bf16(kb[i]);
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
+    if constexpr (G) gate_keys(kr, b.gb, beta_c, ks);
     tile16_into<W>(acc[0], kr, bv);
     tile16_into<W + 4>(acc[1], kr, bv);
     if (ks % CF::NW == W) tile16_into<8>(acc8, kr, bv);  // compile-time per wave
@@ -857,11 +910,12 @@ __device__ __forceinline__ void barrier_lds() {
 }
 
 // DMA instructions one wave issues per chunk
-template <int C, int W, int NW>
+template <int C, int W, int NW, bool G = false>
 constexpr int dma_count16() {
   int n = 0;
   for (int j = W; j < C / 8; j += NW) ++n;
   for (int j = W; j < C / 32; j += NW) ++n;
+  if (G && W == NW - 1) ++n;
   return n;
 }
 
@@ -870,13 +924,13 @@ constexpr int dma_count16() {
 // (vmcnt: the later chunk's transfers may stay outstanding) and the barrier
 // then publishes every wave's share.  Chunks at or past the span's end read
 // as zero; their reduction is skipped.
-template <int C>
+template <int C, bool G = false>
 __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
   using CF = Cfg<16, C>;
   constexpr int DK = 16;
-  __shared__ DmaTile16<C> b0;
-  __shared__ DmaTile16<C> b1;
-  __shared__ DmaTile16<C> b2;
+  __shared__ DmaTile16<C, G> b0;
+  __shared__ DmaTile16<C, G> b1;
+  __shared__ DmaTile16<C, G> b2;
   __shared__ alignas(16) uint16_t ones[128];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -889,7 +943,7 @@ __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
 
   with_wave<CF::NW>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    constexpr int NPC = dma_count16<C, W, CF::NW>();  // this wave's transfers per chunk
+    constexpr int NPC = dma_count16<C, W, CF::NW, G>();  // this wave's transfers per chunk
     f32x4 acc[CF::MFT][NDT];
     load_state<CF>(acc, nullptr, W, lane);
     f32x4 acc8[NDT];
@@ -901,40 +955,49 @@ __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
     const int64_t first = sp * a.G * C;
     int64_t end = first + a.G * C;
     if (end > a.T) end = a.T;
-    auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, end); };
-    dma_chunk16<C, W, CF::NW>(b0, src(first), lane);
-    dma_chunk16<C, W, CF::NW>(b1, src(first + C), lane);
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, end, a.gb); };
+    dma_chunk16<C, W, CF::NW, G>(b0, src(first), lane);
+    dma_chunk16<C, W, CF::NW, G>(b1, src(first + C), lane);
     for (int64_t c0 = first; c0 < end; c0 += 3 * C) {
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
-      dma_chunk16<C, W, CF::NW>(b2, src(c0 + 2 * C), lane);
+      dma_chunk16<C, W, CF::NW, G>(b2, src(c0 + 2 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      state_update_dma16<CF, W>(acc, acc8, b0, bones, to);
+      state_update_dma16<CF, W, G>(acc, acc8, b0, bones, to);
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
-      dma_chunk16<C, W, CF::NW>(b0, src(c0 + 3 * C), lane);
+      dma_chunk16<C, W, CF::NW, G>(b0, src(c0 + 3 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (c0 + C < end) state_update_dma16<CF, W>(acc, acc8, b1, bones, to);
+      if (c0 + C < end) state_update_dma16<CF, W, G>(acc, acc8, b1, bones, to);
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
-      dma_chunk16<C, W, CF::NW>(b1, src(c0 + 4 * C), lane);
+      dma_chunk16<C, W, CF::NW, G>(b1, src(c0 + 4 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (c0 + 2 * C < end) state_update_dma16<CF, W>(acc, acc8, b2, bones, to);
+      if (c0 + 2 * C < end) state_update_dma16<CF, W, G>(acc, acc8, b2, bones, to);
     }
     // drain the transfers still in flight, then add the waves' parts of tile 8
     // through LDS (4 x 64 lanes x 5 x 16 bytes = 20 KB over the tile buffers)
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     __syncthreads();
     constexpr int RED_BYTES = NDT * 16 * 64;  // one wave's part
-    static_assert(3 * sizeof(DmaTile16<C>) >= 4 * RED_BYTES, "reduction space");
+    using Tile = DmaTile16<C, G>;
+    static_assert(3 * sizeof(Tile) >= 4 * RED_BYTES, "reduction space");
     auto red = [&](int wv) -> f32x4* {
-      const int off = wv * RED_BYTES;
-      char* base = off < int(sizeof(DmaTile16<C>)) ? reinterpret_cast<char*>(&b0)
-                 : off < int(2 * sizeof(DmaTile16<C>)) ? reinterpret_cast<char*>(&b1)
-                                                       : reinterpret_cast<char*>(&b2);
-      return reinterpret_cast<f32x4*>(base + off % int(sizeof(DmaTile16<C>)));
+      if constexpr (G) {
+        // gated tiles: waves 1, 2, 3 each use the start of one buffer
+        static_assert(sizeof(Tile) >= RED_BYTES, "reduction space");
+        return reinterpret_cast<f32x4*>(wv == 1 ? reinterpret_cast<char*>(&b0)
+                                        : wv == 2 ? reinterpret_cast<char*>(&b1)
+                                                  : reinterpret_cast<char*>(&b2));
+      } else {
+        const int off = wv * RED_BYTES;
+        char* base = off < int(sizeof(Tile)) ? reinterpret_cast<char*>(&b0)
+                   : off < int(2 * sizeof(Tile)) ? reinterpret_cast<char*>(&b1)
+                                                 : reinterpret_cast<char*>(&b2);
+        return reinterpret_cast<f32x4*>(base + off % int(sizeof(Tile)));
+      }
     };
-    static_assert(sizeof(DmaTile16<C>) % RED_BYTES == 0, "parts do not straddle buffers");
+    static_assert(G || sizeof(Tile) % RED_BYTES == 0, "parts do not straddle buffers");
     if constexpr (W != 0) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) red(W)[dt * 64 + lane] = acc8[dt];
@@ -1009,7 +1072,12 @@ struct NoHook {
 
 // `after_q` runs once the query rows are in registers (the DMA readout issues
 // the next chunk's transfer there)
-template <class CF, class S, class H = NoHook>
+//
+// G (gated read): the source also gives the chunk's running gate sums beta_t
+// (log2 units).  The inter term of query t is 2^beta_t phi(q_t) S, so the
+// query row is scaled by 2^(beta_t / 2); the intra score of key s is weighted
+// by 2^(beta_t - beta_s); there is no denominator.
+template <class CF, class S, class H = NoHook, bool G = false>
 __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __restrict__ Sb,
                                               const ReadoutLane<CF>& L, int lane, float eps,
                                               __amdgpu_buffer_rsrc_t dst, uint16_t* __restrict__ ob_tile,
@@ -1034,6 +1102,16 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
       qr[slot][4 * c + 1] = x.y;
       qr[slot][4 * c + 2] = x.z;
       qr[slot][4 * c + 3] = x.w;
+    }
+  }
+  float bq[NSLOT];  // gate sum of the lane's query (gated read)
+  if constexpr (G) {
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) {
+      bq[slot] = src.gate(16 * L.qt[slot] + r);
+      const float f = __builtin_amdgcn_exp2f(0.5f * bq[slot]);
+#pragma unroll
+      for (int c = 0; c < DK; ++c) qr[slot][c] *= f;
     }
   }
   after_q();
@@ -1089,7 +1167,15 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
         if (kt > L.qt[slot]) continue;  // fully masked tile: uniform per wave
-        const f32x4 sc = score_mfma<DK>(kf[h], qf[slot]);  // [key 4g+j][query r]
+        f32x4 sc = score_mfma<DK>(kf[h], qf[slot]);  // [key 4g+j][query r]
+        if constexpr (G) {
+          // p = sc^2 2^(beta_q - beta_k): fold the root of the weight into sc
+          const float4 bk = src.gate4(16 * kt + 4 * g);
+          sc[0] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.x));
+          sc[1] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.y));
+          sc[2] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.z));
+          sc[3] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.w));
+        }
         if (kt < L.qt[slot]) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) p[h][j] = sc[j] * sc[j];
@@ -1109,8 +1195,11 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
   // rows past T fall outside `dst` and are dropped
 #pragma unroll
   for (int slot = 0; slot < NSLOT; ++slot) {
-    const float den = __shfl(o[slot][NDW - 1][0], r);
-    const float inv = __builtin_amdgcn_rcpf(den + eps);
+    float inv = 1.f;  // the gated read has no denominator
+    if constexpr (!G) {
+      const float den = __shfl(o[slot][NDW - 1][0], r);
+      inv = __builtin_amdgcn_rcpf(den + eps);
+    }
     if constexpr (NDW == NDT) {
       // whole rows: stage the 16 x 64 tile in the wave's LDS tile, then
       // write it back as 1 KB contiguous stores (16 bytes per lane)
@@ -1205,15 +1294,15 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
 // The chunk's V, K and Q arrive raw by LDS DMA into one of two buffers while
 // the other is read.  Query rows and score operands are plain row reads; V and
 // K operands come from transposing reads, as in the span sums.
-template <int C>
-struct alignas(16) DmaTileQ16 {
+template <int C, bool G = false>
+struct alignas(16) DmaTileQ16 : GateRows<G> {
   alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
   alignas(16) uint16_t k[C * 16];  // [token][dimension]
   alignas(16) uint16_t q[C * 16];  // [token][dimension]
 };
 
-template <int C, int W, int NW>
-__device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C>& b, const ChunkSrc& src, int lane) {
+template <int C, int W, int NW, bool G = false>
+__device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C, G>& b, const ChunkSrc& src, int lane) {
 #pragma unroll
   for (int j = W; j < C / 8; j += NW) {
     const int t = 8 * j + (lane >> 3);
@@ -1226,11 +1315,12 @@ __device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C>& b, const ChunkSrc& s
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.q, KATA_LDS(&b.q[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
   }
+  dma_gate<G, W, NW>(b, src, lane);
 }
 
-template <int C>
+template <int C, bool G = false>
 struct DmaSrc16 {
-  const DmaTileQ16<C>& b;
+  const DmaTileQ16<C, G>& b;
   const TrOffsets& to;
   const u32x4& bones;
   __device__ __forceinline__ float4 qrow4(int row, int c4) const {
@@ -1246,14 +1336,23 @@ struct DmaSrc16 {
   __device__ __forceinline__ u32x4 v_op(int vt, int s, int lane) const {
     return vt == NDT - 1 ? bones : tr_operand<DV>(b.v, to.v[vt], s);
   }
+  __device__ __forceinline__ float gate(int row) const { return b.gb[row]; }
+  __device__ __forceinline__ float4 gate4(int row) const {
+    return *reinterpret_cast<const float4*>(&b.gb[row]);
+  }
 };
 
 // state carry of the readout: wave W owns feature tiles W, W + 4 (and 8 for
 // wave 0), the whole state being needed for the next chunk's state copy
-template <class CF, int W>
-__device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], const DmaTileQ16<CF::C>& b,
+template <class CF, int W, bool G = false>
+__device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], const DmaTileQ16<CF::C, G>& b,
                                                   const u32x4& bones, const TrOffsets& to) {
   static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
+  float beta_c = 0.f;
+  if constexpr (G) {
+    beta_c = b.gb[CF::C - 1];
+    gate_decay(acc, __builtin_amdgcn_exp2f(beta_c));
+  }
 #pragma unroll
   for (int ks = 0; ks < CF::C / 32; ++ks) {
     u32x4 bv[NDT];
@@ -1267,19 +1366,20 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], co
       kr[2 * i] = kSqrt2 * lo_bf16(kb[i]);
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
+    if constexpr (G) gate_keys(kr, b.gb, beta_c, ks);
     tile16_into<W>(acc[0], kr, bv);
     tile16_into<W + 4>(acc[1], kr, bv);
     if constexpr (W == 0) tile16_into<8>(acc[2], kr, bv);
   }
 }
 
-template <int C>
+template <int C, bool G = false>
 __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
   using CF = Cfg<16, C>;
   constexpr int DK = 16, SB_LD = CF::SB_LD;
   static_assert(CF::NDW == NDT, "whole output rows per wave");
-  __shared__ DmaTileQ16<C> x0;
-  __shared__ DmaTileQ16<C> x1;
+  __shared__ DmaTileQ16<C, G> x0;
+  __shared__ DmaTileQ16<C, G> x1;
   __shared__ alignas(16) uint16_t ones[128];
   __shared__ alignas(16) uint16_t Sb[VROWS * SB_LD];
   __shared__ alignas(16) uint16_t Ob[CF::NW][16 * OB_LD];
@@ -1308,8 +1408,8 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
     const int64_t first = sp * a.G * C;
     int64_t end = first + a.G * C;
     if (end > a.T) end = a.T;
-    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end); };
-    dma_chunkq16<C, W, CF::NW>(x0, src(first), lane);
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb); };
+    dma_chunkq16<C, W, CF::NW, G>(x0, src(first), lane);
     // the state loads and the first chunk; an unconditional vmcnt(0) also
     // retires the state loads for the compiler's wait-count analysis
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -1319,20 +1419,21 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
 
     // one chunk: prefetch the next into the other buffer, read out, and
     // (unless it is the span's last) carry the state and refresh Sb
-    auto chunk = [&](DmaTileQ16<C>& cur, DmaTileQ16<C>& nxt, int64_t c) {
+    auto chunk = [&](DmaTileQ16<C, G>& cur, DmaTileQ16<C, G>& nxt, int64_t c) {
       const int64_t n = (a.T - c < C) ? a.T - c : C;
       // the next chunk's transfer goes out right after the query rows are
       // read (zeros past the span's end); issued any earlier, the compiler's
       // wait counts make those row reads wait for it
       auto prefetch = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        dma_chunkq16<C, W, CF::NW>(nxt, src(c + C), lane);
+        dma_chunkq16<C, W, CF::NW, G>(nxt, src(c + C), lane);
         __builtin_amdgcn_sched_barrier(0);
       };
-      readout_chunk<CF>(DmaSrc16<C>{cur, to, bones}, Sb, L, lane, a.eps,
-                        rows_rsrc(a.out, tok0 + c, n, 2 * DV), Ob[W], prefetch);
+      readout_chunk<CF, DmaSrc16<C, G>, decltype(prefetch), G>(
+          DmaSrc16<C, G>{cur, to, bones}, Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c, n, 2 * DV), Ob[W],
+          prefetch);
       const bool more = c + C < end;
-      if (more) state_update_ro16<CF, W>(acc, cur, bones, to);
+      if (more) state_update_ro16<CF, W, G>(acc, cur, bones, to);
       // this wave's share of the next chunk has landed (the output stores
       // issued after it may still be in flight).  Unconditional, so that on
       // every path the compiler's wait counts see the transfer retired.
@@ -2005,6 +2106,31 @@ hipError_t launch_linear_readout(const LinArgs& a, hipStream_t stream) {
     lin_readout_kernel<kLinFeatOrthant><<<grid, 256, 0, stream>>>(a);
   } else if (a.feature == kLinFeatLorentz) {
     lin_readout_kernel<kLinFeatLorentz><<<grid, 256, 0, stream>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_span_state_gated(const MfmaArgs& a, hipStream_t stream) {
+  if (a.n_spans < 2) return hipSuccess;
+  dim3 grid(static_cast<unsigned>(a.BH * (a.n_spans - 1)));
+  if (a.d == 16 && a.chunk == 64) {
+    span_state_dma16_kernel<64, true><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 16 && a.chunk == 128) {
+    span_state_dma16_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_readout_gated(const MfmaArgs& a, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(a.BH * a.n_spans));
+  if (a.d == 16 && a.chunk == 64) {
+    readout_dma16_kernel<64, true><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 16 && a.chunk == 128) {
+    readout_dma16_kernel<128, true><<<grid, 256, 0, stream>>>(a);
   } else {
     return hipErrorInvalidValue;
   }

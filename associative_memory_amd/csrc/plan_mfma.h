@@ -35,6 +35,7 @@ struct MfmaArgs {
   int64_t G;        // chunks per span
   int64_t n_spans;  // spans per head
   float eps;
+  const float* gb = nullptr;  // gated read: running gate sums per token, log2 units
 };
 
 struct QuadArgs {
@@ -102,5 +103,13 @@ inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
 hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream);
 // readout of every span, starting from the exclusive prefix in ws
 hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream);
+
+// The gated read (GatedKATA) on the d = 16 path, chunk 64 or 128: span sums
+// and readout with the running gate sums a.gb (no denominator).
+inline bool gated_supported(bool bf16, int d, int dv, int chunk) {
+  return bf16 && d == 16 && dv == 64 && (chunk == 64 || chunk == 128);
+}
+hipError_t launch_span_state_gated(const MfmaArgs& a, hipStream_t stream);
+hipError_t launch_readout_gated(const MfmaArgs& a, hipStream_t stream);
 
 }  // namespace kata

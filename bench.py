@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured decode timing")
     ap.add_argument("--no-other", action="store_true", help="skip the other forward workloads")
     ap.add_argument("--no-linear", action="store_true", help="skip the linear-feature timings")
+    ap.add_argument("--no-gated", action="store_true", help="skip the gated-read timings")
     ap.add_argument("--no-table8", action="store_true",
                     help="skip the quadratic block-map timings on the d = 64 shape")
     ap.add_argument("--calib-copy", action="store_true",
@@ -317,6 +318,45 @@ def bench_linear(args, hip, am, ki, torch):
     return res
 
 
+def bench_gated(args, hip, am, ki, torch):
+    """The gated read (GatedKATA, d = 16) on the T = 131072 and T = 2048
+    forward shapes at both chunk lengths, gates from the seeded recipe.
+    Algorithmic bytes: q, k, v, the fp32 gate read and out written,
+    2 (2d + dv) + 4 + 2 dv = 324 B per token-head."""
+    res = {}
+    stream = torch.cuda.current_stream().cuda_stream
+    for w in (ki.LONG, ki.MEDIUM):
+        q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
+        lg = torch.from_numpy(ki.draw_log_gamma(w.B, w.H, w.T, w.seed)).cuda()
+        out = torch.empty_like(v)
+        for C in (64, 128):
+            need = am.kata_forward_gated_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, C)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            for _ in range(args.warmup):
+                am.kata_forward_gated(q, k, v, lg, chunk=C, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(args.steps):
+                am.kata_forward_gated(q, k, v, lg, chunk=C, out=out, workspace=ws)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            ms = hip.ms(e0, e1) / args.steps
+            hip.destroy(e0)
+            hip.destroy(e1)
+            BHT = w.B * w.H * w.T
+            bytes_ = (2 * (2 * w.d + w.dv) + 4 + 2 * w.dv) * BHT
+            res[f"{w.name.replace('_C128', '').replace('_C64', '')}_gated_C{C}"] = {
+                "ms_per_step": round(ms, 4),
+                "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+                "hbm_gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
+                "hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            }
+            del ws
+        del q, k, v, lg, out
+    return res
+
+
 # ------------------------------------------------------------------ decode
 
 def bench_decode(args, hip, am, ki, torch, w):
@@ -504,6 +544,8 @@ def main():
         rec["quadratic_block_maps_d64"] = bench_table8(args, hip, am, ki, torch)
     if not args.no_linear:
         rec["linear_features_d64"] = bench_linear(args, hip, am, ki, torch)
+    if not args.no_gated:
+        rec["gated"] = bench_gated(args, hip, am, ki, torch)
     if not args.no_decode:
         rec["decode"] = bench_decode(args, hip, am, ki, torch, ki.DECODE)
         rec["decode_beyond_cache"] = bench_decode(args, hip, am, ki, torch, ki.DECODE_512)

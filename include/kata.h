@@ -135,6 +135,37 @@ kata_status_t kata_forward_quadratic(const void* q, const void* k, const void* v
                                      int dv, int g, float eps, kata_dtype_t dtype,
                                      void* stream);
 
+/*
+ * kata_forward_gated -- the gated read of the KATA page's GatedKATA (App.
+ * F.4): the state decays by a per-token scalar gate before each write,
+ *   S_t = gamma_t S_{t-1} + phi(k_t) v_t^T,   o_t = phi(q_t)^T S_t,
+ * with no denominator, i.e. o_t = sum_{s<=t} (prod_{r=s+1..t} gamma_r)
+ * (q_t.k_s)^2 v_s (the unrolled form of Sec. 5.2), phi the rank-one lift.
+ * Computed chunkwise like kata_forward_chunked: per chunk the running sums
+ * b_t of log gamma from the chunk start weight the intra-chunk scores by
+ * exp(b_t - b_s), the incoming state by exp(b_t), and the keys written to the
+ * state by exp(b_C - b_s); the prefix over span states is affine (each span's
+ * state scaled by its gate product before the next is added).
+ *   q, k      : [B, H, T, d] bf16;  v, out : [B, H, T, dv] bf16
+ *   log_gamma : [B, H, T] fp32, log of the gate (expected <= 0: the page's
+ *               gate is a sigmoid; larger values can overflow)
+ *   chunk     : chunk length, 64 or 128
+ * Arithmetic: gate sums in fp32 (log2 units), bf16 operands, fp32 scores,
+ * states and accumulation, bf16 output.
+ * Supported: KATA_BF16, d = 16, dv = 64, T >= 1 (other shapes and KATA_F32
+ * return KATA_ERR_UNSUPPORTED).  The workspace is always needed:
+ * workspace_bytes >= kata_forward_gated_workspace_bytes(...).  Pointers
+ * 16-byte aligned; out and the workspace must not overlap each other or the
+ * inputs.  Deterministic for fixed arguments and device.
+ */
+size_t kata_forward_gated_workspace_bytes(int B, int H, int64_t T, int d, int dv,
+                                          int chunk);
+kata_status_t kata_forward_gated(const void* q, const void* k, const void* v,
+                                 const float* log_gamma, void* out, int B, int H,
+                                 int64_t T, int d, int dv, int chunk,
+                                 kata_dtype_t dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Linear (D = d) cone features of kata_forward_linear. */
 typedef enum {
   KATA_FEATURE_ORTHANT = 0, /* psi(x) = ReLU(x) + shift, every coordinate */

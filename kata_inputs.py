@@ -249,3 +249,12 @@ def forward_inputs_torch(B: int, H: int, T: int, d: int, dv: int, seed: int, dev
     k = unit((B, H, T, d))
     v = torch.randn((B, H, T, dv), generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
     return q, k, v
+
+
+def draw_log_gamma(B: int, H: int, T: int, seed: int) -> np.ndarray:
+    """Per-token log gates for the gated read, float32 [B, H, T]:
+    log gamma = log sigmoid(u) with u ~ N(4, 1) i.i.d. (gates mostly 0.95 to
+    0.995, a memory of tens to hundreds of tokens), from PCG64([seed, 1])."""
+    g = np.random.Generator(np.random.PCG64([seed, 1]))
+    u = g.standard_normal((B, H, T)) + 4.0
+    return round_f32(-np.log1p(np.exp(-u)))

@@ -38,7 +38,7 @@ Capacity Wall with Symmetric Cones" (Ghriss & Chakraborty, arXiv 2607.17419):
       KATA-Lorentz psi(x) = (y, |y|_2 (1 + s^2)) with y = x_{1:d-1}, s = x_d
       (App. F.4; Sec. 2.3 names both cone families), read with the same
       normalised causal sum, score c_{t,s} = psi(q_t) . psi(k_s) unsquared.
-  gated_recurrence / forward_gated_quadratic
+  gated_recurrence / forward_gated_quadratic / forward_gated_rows
       GatedKATA (App. F.4): S_t = gamma_t S_{t-1} + psi(k_t) v_t^T,
       o_t = psi(q_t)^T S_t, no denominator; its unrolled form
       S_t = sum_s (prod_{r=s+1..t} gamma_r) psi(k_s) v_s^T (Sec. 5.2).
@@ -352,6 +352,21 @@ def forward_gated_quadratic(q: np.ndarray, k: np.ndarray, v: np.ndarray,
             decay = np.exp(np.where(cols <= rows, L[h, t0:t1][:, None] - L[h, :t1][None, :], -np.inf))
             out[h, t0:t1] = (c * decay) @ vf[h, :t1]
     return out.reshape(lead + (T, vf.shape[-1]))
+
+
+def forward_gated_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, log_gamma: np.ndarray, rows,
+                       g: int = 1) -> np.ndarray:
+    """forward_gated_quadratic for selected query rows of one head:
+    q, k: [T, d]; v: [T, dv]; log_gamma: [T]; returns [len(rows), dv]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    L = np.cumsum(np.asarray(log_gamma, dtype=np.float64))
+    out = np.empty((len(rows), v.shape[-1]))
+    for n, t in enumerate(rows):
+        c = block_scores(q[t][None, :], k[: t + 1], g)[0]
+        out[n] = (c * np.exp(L[t] - L[: t + 1])) @ v[: t + 1]
+    return out
 
 
 # ------------------------------------------------------------ recurrent decode

@@ -186,3 +186,35 @@ def test_linear_workspace_sizes():
     n = L.kata_forward_linear_workspace_bytes(1, 16, 131072, 64, 64, 64)
     assert n == 16 * 32 * 4 * 5 * 256 * 4
     assert L.kata_forward_linear_workspace_bytes(1, 16, 131072, 32, 64, 64) == 0  # unsupported
+
+
+def gated(q=P[0], k=P[1], v=P[2], lg=P[4], out=P[3], B=1, H=1, T=300, d=16, dv=64, chunk=128, dt=BF16,
+          ws=P[5], wsb=1 << 30):
+    return am.lib().kata_forward_gated(q, k, v, lg, out, B, H, T, d, dv, chunk, dt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), INVALID), (dict(lg=NULL), INVALID), (dict(out=NULL), INVALID), (dict(H=0), INVALID),
+    (dict(dt=5), INVALID), (dict(dt=F32), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dv=16), UNSUPPORTED),
+    (dict(chunk=32), UNSUPPORTED),
+    (dict(lg=ctypes.c_void_p(P[4].value + 4)), INVALID),   # misaligned
+    (dict(out=P[4]), INVALID),                              # out overlaps log_gamma
+    (dict(ws=NULL, wsb=0), WORKSPACE), (dict(wsb=64), WORKSPACE),
+    (dict(ws=P[3]), INVALID),                               # workspace overlaps out
+])
+def test_gated_error_paths(kw, status):
+    assert gated(**kw) == status
+
+
+def test_gated_workspace_sizes():
+    L = am.lib()
+    # T = 300, chunk 128: 3 chunks in 3 spans.  Span states (9 feature tiles x
+    # 4 value tiles x 256 floats + 9 x 16 floats of z each), then the gate sums
+    # (300 floats) and the chunk totals (3 floats), each 256-byte aligned
+    states = 3 * (9 * 4 * 256 + 9 * 16) * 4
+    gb_off = (states + 255) // 256 * 256
+    ctot_off = (gb_off + 300 * 4 + 255) // 256 * 256
+    assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 16, 64, 128) == ctot_off + 3 * 4
+    # 64 heads of one chunk: a single span, no states
+    assert L.kata_forward_gated_workspace_bytes(8, 8, 100, 16, 64, 128) == 25600 + 64 * 4
+    assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 32, 64, 128) == 0  # unsupported

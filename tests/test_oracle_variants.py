@@ -310,3 +310,14 @@ def test_gated_causal_and_linear_in_v():
     q3, k3, v3, lg3 = q.copy(), k.copy(), v1.copy(), lg.copy()
     q3[20:], k3[20:], v3[20:], lg3[20:] = 0.3, -0.2, 9.0, -0.01
     np.testing.assert_array_equal(orc.forward_gated_quadratic(q3, k3, v3, lg3)[:20], o1[:20])
+
+
+def test_gated_rows_match_the_full_form():
+    rng = np.random.Generator(np.random.PCG64(21))
+    T = 64
+    q, k, v = _unit(rng, (T, 8)), _unit(rng, (T, 8)), rng.standard_normal((T, 3))
+    lg = -rng.uniform(0, 0.2, T)
+    rows = [0, 1, 40, 63]
+    for g in (1, 2):
+        np.testing.assert_allclose(orc.forward_gated_rows(q, k, v, lg, rows, g),
+                                   orc.forward_gated_quadratic(q, k, v, lg, g)[rows], rtol=1e-12, atol=1e-14)
