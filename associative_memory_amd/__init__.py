@@ -42,6 +42,7 @@ EXPORTED = (
     "kata_forward_linear",
     "kata_forward_gated_workspace_bytes",
     "kata_forward_gated",
+    "kata_decode_step_gated",
 )
 
 
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_gated_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.kata_forward_gated.restype = i32
     L.kata_forward_gated.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, sz, vp]
+    L.kata_decode_step_gated.restype = i32
+    L.kata_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.kata_forward_plan.restype = i32
     L.kata_forward_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]
     _lib = L
@@ -359,4 +362,22 @@ def kata_forward_gated(q, k, v, log_gamma, chunk: int = 64, out=None, workspace=
     st = lib().kata_forward_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(out), B, H, T, d, dv,
                                   chunk, _dtype_code(q), wptr, wbytes, _stream(stream))
     _check(st, "kata_forward_gated")
+    return out
+
+
+def kata_decode_step_gated(S, q, k, v, log_gamma, out=None, stream=None):
+    """One GatedKATA step in place: S = exp(log_gamma) S + phi(k) v^T, then
+    out = phi(q)^T S.  S: [BH, D, dv] float32; q, k: [BH, d]; v: [BH, dv];
+    log_gamma: [BH] float32.  Returns out [BH, dv] (dtype of v)."""
+    torch = _torch()
+    for t, n in ((S, "S"), (q, "q"), (k, "k"), (v, "v"), (log_gamma, "log_gamma")):
+        _device_tensor(t, n)
+    BH, d = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((BH, dv), dtype=v.dtype, device=v.device)
+    _device_tensor(out, "out")
+    st = lib().kata_decode_step_gated(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(out),
+                                      1, BH, d, dv, _dtype_code(q), _stream(stream))
+    _check(st, "kata_decode_step_gated")
     return out

@@ -388,4 +388,31 @@ kata_status_t kata_decode_step(float* S, float* z, const void* q, const void* k,
                                       static_cast<hipStream_t>(stream)));
 }
 
+kata_status_t kata_decode_step_gated(float* S, const void* q, const void* k, const void* v,
+                                     const float* log_gamma, void* out, int B, int H, int d, int dv,
+                                     kata_dtype_t dtype, void* stream) {
+  if (S == nullptr || q == nullptr || k == nullptr || v == nullptr || log_gamma == nullptr ||
+      out == nullptr)
+    return KATA_ERR_INVALID_VALUE;
+  if (B <= 0 || H <= 0 || !dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(S) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(log_gamma) & 3u) != 0)
+    return KATA_ERR_INVALID_VALUE;
+  if (!head_dim_ok(d) || !value_dim_ok(dv)) return KATA_ERR_UNSUPPORTED;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (BH > (INT64_C(1) << 30)) return KATA_ERR_UNSUPPORTED;
+  const int64_t D = kata_feature_dim(d);
+  const size_t es = elem_size(dtype);
+  const size_t s_bytes = static_cast<size_t>(BH * D * dv) * 4;
+  const size_t qk_bytes = static_cast<size_t>(BH * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * dv) * es;
+  const size_t g_bytes = static_cast<size_t>(BH) * 4;
+  if (overlaps(out, v_bytes, S, s_bytes) || overlaps(out, v_bytes, q, qk_bytes) ||
+      overlaps(out, v_bytes, k, qk_bytes) || overlaps(out, v_bytes, v, v_bytes) ||
+      overlaps(out, v_bytes, log_gamma, g_bytes) || overlaps(S, s_bytes, log_gamma, g_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  return from_hip(kata::launch_decode_gated(S, q, k, v, log_gamma, out, BH, d, dv, dtype == KATA_BF16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

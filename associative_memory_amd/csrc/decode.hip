@@ -7,17 +7,21 @@
 // rows, loads all its rows first (so each lane has all its loads in flight),
 // adds phi(k)_r v, stores, and accumulates phi(q)_r S'_r.  Column sums across
 // the row groups and the denominator phi(q).z' are reduced through LDS.
+//
+// GATED: the GatedKATA step (App. F.4), S_t = gamma_t S_{t-1} + psi(k_t) v_t^T,
+// read o_t = psi(q_t)^T S_t with no z and no denominator; gamma_t =
+// exp(log_gamma) per head.
 #include "common.h"
 #include "kernels.h"
 
 namespace kata {
 namespace {
 
-template <int DK, int DV, bool BF16>
+template <int DK, int DV, bool BF16, bool GATED = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(
     float* __restrict__ S, float* __restrict__ z, const void* __restrict__ q,
     const void* __restrict__ k, const void* __restrict__ v, void* __restrict__ out,
-    float eps) {
+    float eps, const float* __restrict__ log_gamma = nullptr) {
   constexpr int D = feature_dim(DK);
   constexpr int TPR = DV / 4;            // threads per state row (float4 each)
   constexpr int RPP = kThreads / TPR;    // rows per pass
@@ -61,13 +65,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     const int r = r0 + n * RPP;
     if (r < D) s[n] = Sh[r * TPR + c4];
   }
-  float* zh = z + bh * D;
+  float* zh = GATED ? nullptr : z + bh * D;
   float zv[NZ];
+  if constexpr (!GATED) {
 #pragma unroll
-  for (int n = 0; n < NZ; ++n) {
-    const int f = tid + n * kThreads;
-    if (f < D) zv[n] = zh[f];
+    for (int n = 0; n < NZ; ++n) {
+      const int f = tid + n * kThreads;
+      if (f < D) zv[n] = zh[f];
+    }
   }
+  float gamma = 1.f;
+  if constexpr (GATED) gamma = __expf(log_gamma[bh]);
   __syncthreads();  // pq / pk ready
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -78,6 +86,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
       const float a = pk[r];
       const float b = pq[r];
       float4 t = s[n];
+      if constexpr (GATED) {
+        t.x *= gamma;
+        t.y *= gamma;
+        t.z *= gamma;
+        t.w *= gamma;
+      }
       t.x += a * vv.x;
       t.y += a * vv.y;
       t.z += a * vv.z;
@@ -90,18 +104,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
     }
   }
   float den = 0.f;
+  if constexpr (!GATED) {
 #pragma unroll
-  for (int n = 0; n < NZ; ++n) {
-    const int f = tid + n * kThreads;
-    if (f < D) {
-      const float t = zv[n] + pk[f];
-      zh[f] = t;
-      den += pq[f] * t;
+    for (int n = 0; n < NZ; ++n) {
+      const int f = tid + n * kThreads;
+      if (f < D) {
+        const float t = zv[n] + pk[f];
+        zh[f] = t;
+        den += pq[f] * t;
+      }
     }
   }
   red[r0][c4] = acc;
-  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
-  if ((tid & 63) == 0) dred[tid >> 6] = den;
+  if constexpr (!GATED) {
+    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o);
+    if ((tid & 63) == 0) dred[tid >> 6] = den;
+  }
   __syncthreads();
 
   if (tid < DV) {
@@ -112,18 +130,29 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
       const float4 x = red[r][cg];
       tot += (lane == 0) ? x.x : (lane == 1) ? x.y : (lane == 2) ? x.z : x.w;
     }
-    float dd = 0.f;
+    if constexpr (GATED) {
+      store_elem<BF16>(out, bh * DV + tid, tot);
+    } else {
+      float dd = 0.f;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) dd += dred[w];
-    store_elem<BF16>(out, bh * DV + tid, tot / (dd + eps));
+      for (int w = 0; w < kThreads / 64; ++w) dd += dred[w];
+      store_elem<BF16>(out, bh * DV + tid, tot / (dd + eps));
+    }
   }
 }
 
 template <int DK, int DV>
 hipError_t launch_dv(float* S, float* z, const void* q, const void* k, const void* v,
-                     void* out, int64_t BH, float eps, bool bf16, hipStream_t s) {
+                     void* out, int64_t BH, float eps, bool bf16, hipStream_t s,
+                     const float* log_gamma) {
   dim3 grid(static_cast<unsigned>(BH));
-  if (bf16) {
+  if (log_gamma != nullptr) {
+    if (bf16) {
+      decode_kernel<DK, DV, true, true><<<grid, kThreads, 0, s>>>(S, z, q, k, v, out, eps, log_gamma);
+    } else {
+      decode_kernel<DK, DV, false, true><<<grid, kThreads, 0, s>>>(S, z, q, k, v, out, eps, log_gamma);
+    }
+  } else if (bf16) {
     decode_kernel<DK, DV, true><<<grid, kThreads, 0, s>>>(S, z, q, k, v, out, eps);
   } else {
     decode_kernel<DK, DV, false><<<grid, kThreads, 0, s>>>(S, z, q, k, v, out, eps);
@@ -133,11 +162,12 @@ hipError_t launch_dv(float* S, float* z, const void* q, const void* k, const voi
 
 template <int DK>
 hipError_t launch_d(float* S, float* z, const void* q, const void* k, const void* v,
-                    void* out, int64_t BH, int dv, float eps, bool bf16, hipStream_t s) {
+                    void* out, int64_t BH, int dv, float eps, bool bf16, hipStream_t s,
+                    const float* log_gamma) {
   switch (dv) {
-    case 16: return launch_dv<DK, 16>(S, z, q, k, v, out, BH, eps, bf16, s);
-    case 32: return launch_dv<DK, 32>(S, z, q, k, v, out, BH, eps, bf16, s);
-    case 64: return launch_dv<DK, 64>(S, z, q, k, v, out, BH, eps, bf16, s);
+    case 16: return launch_dv<DK, 16>(S, z, q, k, v, out, BH, eps, bf16, s, log_gamma);
+    case 32: return launch_dv<DK, 32>(S, z, q, k, v, out, BH, eps, bf16, s, log_gamma);
+    case 64: return launch_dv<DK, 64>(S, z, q, k, v, out, BH, eps, bf16, s, log_gamma);
     default: return hipErrorInvalidValue;
   }
 }
@@ -148,8 +178,18 @@ hipError_t launch_decode(float* S, float* z, const void* q, const void* k,
                          const void* v, void* out, int64_t BH, int d, int dv,
                          float eps, bool bf16, hipStream_t stream) {
   switch (d) {
-    case 16: return launch_d<16>(S, z, q, k, v, out, BH, dv, eps, bf16, stream);
-    case 32: return launch_d<32>(S, z, q, k, v, out, BH, dv, eps, bf16, stream);
+    case 16: return launch_d<16>(S, z, q, k, v, out, BH, dv, eps, bf16, stream, nullptr);
+    case 32: return launch_d<32>(S, z, q, k, v, out, BH, dv, eps, bf16, stream, nullptr);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_decode_gated(float* S, const void* q, const void* k, const void* v,
+                               const float* log_gamma, void* out, int64_t BH, int d, int dv,
+                               bool bf16, hipStream_t stream) {
+  switch (d) {
+    case 16: return launch_d<16>(S, nullptr, q, k, v, out, BH, dv, 0.f, bf16, stream, log_gamma);
+    case 32: return launch_d<32>(S, nullptr, q, k, v, out, BH, dv, 0.f, bf16, stream, log_gamma);
     default: return hipErrorInvalidValue;
   }
 }

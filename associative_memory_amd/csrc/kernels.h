@@ -16,6 +16,10 @@ hipError_t launch_feature_map(const void* x, void* phi, int64_t rows, int d,
 hipError_t launch_decode(float* S, float* z, const void* q, const void* k,
                          const void* v, void* out, int64_t BH, int d, int dv,
                          float eps, bool bf16, hipStream_t stream);
+// One gated step (S = gamma S + phi(k) v^T, o = phi(q)^T S; no z).
+hipError_t launch_decode_gated(float* S, const void* q, const void* k, const void* v,
+                               const float* log_gamma, void* out, int64_t BH, int d, int dv,
+                               bool bf16, hipStream_t stream);
 
 // Sums over spans of tokens:
 //   S_out[(bh*n_spans+sp)*s_stride + f*dv + c] = sum_t w_f k_i k_j v_t[c]

@@ -258,6 +258,22 @@ kata_status_t kata_decode_step(float* S, float* z, const void* q,
                                kata_dtype_t dtype, void* stream);
 
 /*
+ * kata_decode_step_gated -- one token of the GatedKATA recurrence (the KATA
+ * page, App. F.4: S_t = gamma_t S_{t-1} + psi(k_t) v_t^T, read
+ * o_t = psi(q_t)^T S_t with no denominator), read after the update:
+ *   S = exp(log_gamma) S + phi(k) v^T;  out = phi(q)^T S.
+ *   S         : [B*H, D, dv] fp32, updated in place (layout as kata_prefill_state)
+ *   q, k      : [B*H, d] in dtype;  v, out : [B*H, dv] in dtype
+ *   log_gamma : [B*H] fp32, the step's log gate per head (4-byte aligned)
+ * fp32 arithmetic.  Supported: d in {16, 32}; dv in {16, 32, 64}.
+ * out must not overlap S, q, k, v or log_gamma.
+ */
+kata_status_t kata_decode_step_gated(float* S, const void* q, const void* k,
+                                     const void* v, const float* log_gamma,
+                                     void* out, int B, int H, int d, int dv,
+                                     kata_dtype_t dtype, void* stream);
+
+/*
  * kata_forward_plan -- describe the launch plan kata_forward_chunked uses for
  * these arguments as a one-line text (kernels, chunk span per prefix entry,
  * grid sizes) into buf (NUL-terminated, truncated to buf_len).  Returns the

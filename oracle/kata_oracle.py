@@ -44,6 +44,8 @@ Capacity Wall with Symmetric Cones" (Ghriss & Chakraborty, arXiv 2607.17419):
       S_t = sum_s (prod_{r=s+1..t} gamma_r) psi(k_s) v_s^T (Sec. 5.2).
       The per-token gate enters as log gamma_t (<= 0), the quantity the page's
       gate projection produces.
+  gated_state / decode_step_gated
+      the GatedKATA state after a history and one recurrent step of it.
 
 Readings where the page is silent (each also listed in the design notes):
   * eps is added once to the accumulated denominator, o = N / (D + eps); the
@@ -399,6 +401,26 @@ def decode_step(S: np.ndarray, z: np.ndarray, q: np.ndarray, k: np.ndarray,
     num = np.einsum("...f,...fc->...c", pq, S2)
     den = np.einsum("...f,...f->...", pq, z2)
     return S2, z2, num / (den + eps)[..., None]
+
+
+def gated_state(k: np.ndarray, v: np.ndarray, log_gamma: np.ndarray) -> np.ndarray:
+    """GatedKATA state after a history, the unrolled recurrence (Sec. 5.2):
+    S = sum_s (prod_{r=s+1..T} gamma_r) phi(k_s) v_s^T, public packing.
+    k: [T, d], v: [T, dv], log_gamma: [T]  ->  S [D, dv]."""
+    lg = np.asarray(log_gamma, dtype=np.float64)
+    after = np.cumsum(lg[::-1])[::-1] - lg          # sum of log gamma over r > s
+    pk = feature_map(k) * np.exp(after)[:, None]
+    return pk.T @ np.asarray(v, dtype=np.float64)
+
+
+def decode_step_gated(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                      log_gamma) -> Tuple[np.ndarray, np.ndarray]:
+    """One GatedKATA token (App. F.4), read after the update:
+    S' = gamma S + phi(k) v^T, o = phi(q)^T S'.  S [..., D, dv]; q, k [..., d];
+    v [..., dv]; log_gamma [...].  Returns (S', o)."""
+    gamma = np.exp(np.asarray(log_gamma, dtype=np.float64))
+    S2 = gamma[..., None, None] * S + feature_map(k)[..., :, None] * np.asarray(v, dtype=np.float64)[..., None, :]
+    return S2, np.einsum("...f,...fc->...c", feature_map(q), S2)
 
 
 # ------------------------------------------------------------ Proposition 1

@@ -218,3 +218,20 @@ def test_gated_workspace_sizes():
     # 64 heads of one chunk: a single span, no states
     assert L.kata_forward_gated_workspace_bytes(8, 8, 100, 16, 64, 128) == 25600 + 64 * 4
     assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 32, 64, 128) == 0  # unsupported
+
+
+def test_gated_decode_error_paths():
+    L = am.lib()
+
+    def step(S=P[0], q=P[1], k=P[2], v=P[3], lg=P[4], out=P[5], B=2, H=3, d=16, dv=64, dt=F32):
+        return L.kata_decode_step_gated(S, q, k, v, lg, out, B, H, d, dv, dt, None)
+
+    assert step(S=NULL) == INVALID
+    assert step(lg=NULL) == INVALID
+    assert step(B=0) == INVALID
+    assert step(dt=4) == INVALID
+    assert step(d=24) == UNSUPPORTED
+    assert step(dv=48) == UNSUPPORTED
+    assert step(lg=ctypes.c_void_p(P[4].value + 2)) == INVALID  # not 4-byte aligned
+    assert step(out=P[4]) == INVALID                            # out overlaps log_gamma
+    assert step(out=P[0]) == INVALID                            # out overlaps S

@@ -171,3 +171,34 @@ def test_decode_graph_replay_matches_eager():
         for s in range(n):
             assert torch.equal(outs[s], eager[s]), (rep, s)
         assert torch.equal(S, S_e) and torch.equal(z, z_e), rep
+
+
+@pytest.mark.parametrize("d,dv,dtype", [(16, 64, ki.F32), (16, 16, ki.F32), (32, 64, ki.F32),
+                                        (16, 64, ki.BF16)])
+def test_gated_decode_steps_match_oracle(d, dv, dtype):
+    # GatedKATA steps from a prefilled state (the additive prefill is a valid
+    # starting state).  No denominator: row bars scale with the decayed score
+    # mass A = phi(q)^T z_gated, tracked by running the oracle with v = 1.
+    say(f"gated decode d={d} dv={dv} dtype={dtype}")
+    heads, prefill, steps = 9, 200, 24
+    di, S, z, S_ref, z_ref = _decode_case(heads, prefill, steps, d, dv, seed=13)
+    rng = np.random.Generator(np.random.PCG64(14))
+    lg = (-np.log1p(np.exp(-(rng.standard_normal((steps, heads)) + 2.0)))).astype(np.float32)
+    vmax = max(np.abs(di.pv).max(), np.abs(di.sv).max())
+    M_ref = z_ref[..., None]  # the mass state: v = 1
+    tol = 1e-4 if dtype == ki.F32 else 2e-2
+    for s in range(steps):
+        qs, q64 = ki.as_storage(di.sq[s].astype(np.float64), dtype)
+        ks, k64 = ki.as_storage(di.sk[s].astype(np.float64), dtype)
+        vs, v64 = ki.as_storage(di.sv[s].astype(np.float64), dtype)
+        g = torch.from_numpy(lg[s]).cuda()
+        out = am.kata_decode_step_gated(S, to_dev(qs, dtype), to_dev(ks, dtype), to_dev(vs, dtype), g)
+        torch.cuda.synchronize()
+        S_ref, o_ref = orc.decode_step_gated(S_ref, q64, k64, v64, lg[s].astype(np.float64))
+        M_ref, mass = orc.decode_step_gated(M_ref, q64, k64, np.ones((heads, 1)), lg[s].astype(np.float64))
+        err = np.abs(to_host64(out) - o_ref).max(axis=-1)
+        bar = tol * vmax * np.maximum(1.0, mass[:, 0])
+        assert (err <= bar).all(), f"step {s}: worst err/bar {(err / bar).max()}"
+    # the state itself, after 24 decays and writes (fp32 throughout)
+    Sg = to_host64(S)
+    assert np.abs(Sg - S_ref).max() <= 1e-5 * (1 + np.abs(S_ref).max())

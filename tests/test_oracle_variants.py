@@ -321,3 +321,31 @@ def test_gated_rows_match_the_full_form():
     for g in (1, 2):
         np.testing.assert_allclose(orc.forward_gated_rows(q, k, v, lg, rows, g),
                                    orc.forward_gated_quadratic(q, k, v, lg, g)[rows], rtol=1e-12, atol=1e-14)
+
+
+def test_gated_decode_continues_the_forward():
+    # state of the first 40 tokens, then 25 gated steps == the gated read of all 65
+    rng = np.random.Generator(np.random.PCG64(22))
+    T, n, d, dv = 40, 25, 4, 3
+    q, k, v = _unit(rng, (T + n, d)), _unit(rng, (T + n, d)), rng.standard_normal((T + n, dv))
+    lg = -rng.uniform(0, 0.3, T + n)
+    want = orc.forward_gated_quadratic(q, k, v, lg)
+    S = orc.gated_state(k[:T], v[:T], lg[:T])
+    # the state reads out the history's last row: phi(q_T-1)^T S = o_T-1
+    np.testing.assert_allclose(orc.feature_map(q[T - 1]) @ S, want[T - 1], rtol=1e-12, atol=1e-13)
+    for t in range(T, T + n):
+        S, o = orc.decode_step_gated(S, q[t], k[t], v[t], lg[t])
+        np.testing.assert_allclose(o, want[t], rtol=1e-11, atol=1e-12)
+    # and matches the token-by-token recurrence's state
+    np.testing.assert_allclose(S, orc.gated_state(k, v, lg), rtol=1e-12, atol=1e-13)
+
+
+def test_gated_decode_without_decay_is_the_additive_step():
+    rng = np.random.Generator(np.random.PCG64(23))
+    d, dv = 5, 2
+    S0, z0 = orc.decode_state(_unit(rng, (30, d)), rng.standard_normal((30, dv)))
+    q, k, v = _unit(rng, d), _unit(rng, d), rng.standard_normal(dv)
+    S1, o = orc.decode_step_gated(S0, q, k, v, 0.0)
+    S2, z2, o2 = orc.decode_step(S0, z0, q, k, v, 0.0)
+    np.testing.assert_allclose(S1, S2, rtol=1e-14)
+    np.testing.assert_allclose(o, o2 * (orc.feature_map(q) @ z2), rtol=1e-12)
