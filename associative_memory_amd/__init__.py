@@ -43,6 +43,8 @@ EXPORTED = (
     "kata_forward_gated_workspace_bytes",
     "kata_forward_gated",
     "kata_decode_step_gated",
+    "kata_forward_chunked_blocks_workspace_bytes",
+    "kata_forward_chunked_blocks",
 )
 
 
@@ -96,6 +98,11 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_gated.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, sz, vp]
     L.kata_decode_step_gated.restype = i32
     L.kata_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.kata_forward_chunked_blocks_workspace_bytes.restype = sz
+    L.kata_forward_chunked_blocks_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32]
+    L.kata_forward_chunked_blocks.restype = i32
+    L.kata_forward_chunked_blocks.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, f32, i32,
+                                              i32, vp, sz, vp]
     L.kata_forward_plan.restype = i32
     L.kata_forward_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]
     _lib = L
@@ -380,4 +387,29 @@ def kata_decode_step_gated(S, q, k, v, log_gamma, out=None, stream=None):
     st = lib().kata_decode_step_gated(_ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(log_gamma), _ptr(out),
                                       1, BH, d, dv, _dtype_code(q), _stream(stream))
     _check(st, "kata_decode_step_gated")
+    return out
+
+
+def kata_forward_chunked_blocks(q, k, v, g: int, chunk: int = 64, eps: float = 1e-6, scan="auto",
+                                out=None, workspace=None, stream=None):
+    """The chunked read with the KATA-Mg score sum_a (q_a . k_a)^2 over g
+    blocks (g = 1: kata_forward_chunked).  q, k: [B, H, T, d]; v: [B, H, T, dv];
+    contiguous on the device.  Returns out [B, H, T, dv]."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _device_tensor(t, n)
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
+    _device_tensor(out, "out")
+    sc = _scan_code(scan)
+    need = int(lib().kata_forward_chunked_blocks_workspace_bytes(B, H, T, d, dv, g, chunk, sc))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wptr = _ptr(workspace) if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().kata_forward_chunked_blocks(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv, g, chunk,
+                                           float(eps), _dtype_code(q), sc, wptr, wbytes, _stream(stream))
+    _check(st, "kata_forward_chunked_blocks")
     return out

@@ -322,6 +322,52 @@ kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const 
                                     events, static_cast<hipStream_t>(stream)));
 }
 
+size_t kata_forward_chunked_blocks_workspace_bytes(int B, int H, int64_t T, int d, int dv, int g,
+                                                   int chunk, kata_scan_t scan) {
+  if (g == 1) return kata_forward_workspace_bytes(B, H, T, d, dv, chunk, scan);
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0 || g <= 0 || d % g != 0) return 0;
+  if (scan != KATA_SCAN_AUTO && scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return 0;
+  if (!kata::block_map_supported(true, d, dv, g, chunk)) return 0;
+  if (T > (INT64_C(1) << 40) / (static_cast<int64_t>(B) * H)) return 0;
+  return kata::plan_forward(B, H, T, d, dv, chunk, KATA_BF16, scan, g).ws_bytes;
+}
+
+kata_status_t kata_forward_chunked_blocks(const void* q, const void* k, const void* v, void* out,
+                                          int B, int H, int64_t T, int d, int dv, int g, int chunk,
+                                          float eps, kata_dtype_t dtype, kata_scan_t scan,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (g == 1)
+    return kata_forward_chunked(q, k, v, out, B, H, T, d, dv, chunk, eps, dtype, scan, workspace,
+                                workspace_bytes, stream);
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;
+  if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0 || chunk <= 0 || g <= 0 || d % g != 0)
+    return KATA_ERR_INVALID_VALUE;
+  if (scan != KATA_SCAN_AUTO && scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)
+    return KATA_ERR_INVALID_VALUE;
+  if (!dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!kata::block_map_supported(dtype == KATA_BF16, d, dv, g, chunk)) return KATA_ERR_UNSUPPORTED;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (T > (INT64_C(1) << 40) / BH) return KATA_ERR_UNSUPPORTED;
+  if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
+    return KATA_ERR_INVALID_VALUE;
+  const size_t es = elem_size(dtype);
+  const size_t qk_bytes = static_cast<size_t>(BH * T * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
+  if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
+      overlaps(out, v_bytes, v, v_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  const ForwardPlan p = kata::plan_forward(B, H, T, d, dv, chunk, dtype, scan, g);
+  if (p.ws_bytes > 0) {
+    if (workspace == nullptr || workspace_bytes < p.ws_bytes) return KATA_ERR_WORKSPACE;
+    if (overlaps(workspace, p.ws_bytes, out, v_bytes) || overlaps(workspace, p.ws_bytes, q, qk_bytes) ||
+        overlaps(workspace, p.ws_bytes, k, qk_bytes) || overlaps(workspace, p.ws_bytes, v, v_bytes))
+      return KATA_ERR_INVALID_VALUE;
+  }
+  return from_hip(kata::run_forward(p, q, k, v, out, eps, static_cast<float*>(workspace), nullptr,
+                                    static_cast<hipStream_t>(stream)));
+}
+
 kata_status_t kata_prefill_state(const void* k, const void* v, float* S, float* z, int B,
                                  int H, int64_t T, int d, int dv, kata_dtype_t dtype,
                                  void* stream) {

@@ -54,10 +54,18 @@ __device__ __forceinline__ int vrow(int vt, int r) { return vt == NDT - 1 ? DV +
 
 // ------------------------------------------------------------ feature schedule
 
+// DK = 64 is the KATA-M4 block map (Sec. 4.1): four blocks of 16 dimensions,
+// the 136 pairs of one block per lane group (group g holds block g, the
+// rotation by SH = 16 below), 544 feature positions; only pairs inside a
+// block carry features, and the score is sum_a (q_a . k_a)^2.
+template <int DK>
+constexpr bool kBlockMap = DK == 64;
+
 template <int DK>
 struct Schedule {
-  static constexpr int SH = DK / 4;                                     // index shift per lane group
-  static constexpr int NE = (DK * (DK + 1) / 2 - DK / 2) / 4 + DK / 4;  // orbit representatives
+  static constexpr int SH = DK / 4;  // index shift per lane group
+  // orbit representatives (block map: the pairs of one block)
+  static constexpr int NE = kBlockMap<DK> ? 16 * 17 / 2 : (DK * (DK + 1) / 2 - DK / 2) / 4 + DK / 4;
   static constexpr int NKS = (NE + 7) / 8;                              // 32-wide feature k-steps
   static constexpr int NPOS = 32 * NKS;                                 // feature positions
   int8_t a[8 * NKS];
@@ -69,7 +77,16 @@ template <int DK>
 constexpr Schedule<DK> make_schedule() {
   Schedule<DK> s{};
   constexpr int SH = Schedule<DK>::SH;
-  if constexpr (DK == 16) {
+  if constexpr (kBlockMap<DK>) {
+    int e = 0;
+    for (int i = 0; i < 16; ++i) {
+      for (int j = i; j < 16; ++j, ++e) {
+        s.a[e] = static_cast<int8_t>(i);
+        s.b[e] = static_cast<int8_t>(j);
+        s.pair2[e] = false;
+      }
+    }
+  } else if constexpr (DK == 16) {
     // entry 4 j + x is the pair (x, x + j): lane group g then holds the pairs
     // (4 g + x, 4 g + x + j), the rows 4 g + x of the key-feature tile j
     // built by lane rotation (state update, d = 16), so a run of 4 entries
@@ -112,6 +129,7 @@ constexpr Schedule<DK> kSched = make_schedule<DK>();
 
 __constant__ Schedule<16> kSchedDev16 = make_schedule<16>();
 __constant__ Schedule<32> kSchedDev32 = make_schedule<32>();
+__constant__ Schedule<64> kSchedDev64 = make_schedule<64>();
 
 template <int DK>
 constexpr bool schedule_ok() {
@@ -131,8 +149,25 @@ constexpr bool schedule_ok() {
   }
   return n == DK * (DK + 1) / 2;
 }
+
+// block map: every pair inside a block covered once, nothing across blocks
+template <int DK>
+constexpr bool block_schedule_ok() {
+  bool seen[DK][DK] = {};
+  int n = 0;
+  for (int e = 0; e < Schedule<DK>::NE; ++e) {
+    for (int g = 0; g < 4; ++g) {
+      const int x = kSched<DK>.a[e] + Schedule<DK>::SH * g, y = kSched<DK>.b[e] + Schedule<DK>::SH * g;
+      if (x > y || y >= DK || x / 16 != y / 16 || seen[x][y]) return false;
+      seen[x][y] = true;
+      ++n;
+    }
+  }
+  return n == 4 * 136;
+}
 static_assert(schedule_ok<16>(), "d = 16 feature schedule must cover every pair once");
 static_assert(schedule_ok<32>(), "d = 32 feature schedule must cover every pair once");
+static_assert(block_schedule_ok<64>(), "KATA-M4 schedule must cover every in-block pair once");
 
 // number of 16-position feature tiles holding at least one feature
 template <int DK>
@@ -146,13 +181,16 @@ constexpr int feature_tiles() {
 }
 static_assert(feature_tiles<16>() == mfma_feature_tiles(16), "feature tile count (d = 16)");
 static_assert(feature_tiles<32>() == mfma_feature_tiles(32), "feature tile count (d = 32)");
+static_assert(feature_tiles<64>() == mfma_feature_tiles(64), "feature tile count (KATA-M4)");
 
 template <int DK>
 __device__ __forceinline__ const Schedule<DK>& sched_dev() {
   if constexpr (DK == 16) {
     return kSchedDev16;
-  } else {
+  } else if constexpr (DK == 32) {
     return kSchedDev32;
+  } else {
+    return kSchedDev64;
   }
 }
 
@@ -277,6 +315,12 @@ template <>
 struct ScoreOpT<32> {
   using type = u32x4;
 };
+template <>
+struct ScoreOpT<64> {  // KATA-M4: one 16x16x16 operand per block
+  struct type {
+    uint2 p[4];
+  };
+};
 template <int DK>
 using ScoreOp = typename ScoreOpT<DK>::type;
 
@@ -352,7 +396,15 @@ struct alignas(16) SmemOut : Tiles<CF> {
 // score operand of row `row` from the fp32 Q tile / the bf16 K tile
 template <class CF>
 __device__ __forceinline__ ScoreOp<CF::DK> score_operand(const float* Qf, int row, int g) {
-  if constexpr (CF::DK == 16) {
+  if constexpr (kBlockMap<CF::DK>) {
+    ScoreOp<CF::DK> op;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 x = *reinterpret_cast<const float4*>(&Qf[row * CF::QF_LD + 16 * a + 4 * g]);
+      op.p[a] = uint2{pack2(x.x, x.y), pack2(x.z, x.w)};
+    }
+    return op;
+  } else if constexpr (CF::DK == 16) {
     const float4 x = *reinterpret_cast<const float4*>(&Qf[row * CF::QF_LD + 4 * g]);
     return uint2{pack2(x.x, x.y), pack2(x.z, x.w)};
   } else {
@@ -365,7 +417,12 @@ __device__ __forceinline__ ScoreOp<CF::DK> score_operand(const float* Qf, int ro
 
 template <class CF>
 __device__ __forceinline__ ScoreOp<CF::DK> score_operand_bf16(const uint16_t* Kb, int row, int g) {
-  if constexpr (CF::DK == 16) {
+  if constexpr (kBlockMap<CF::DK>) {
+    ScoreOp<CF::DK> op;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) op.p[a] = *reinterpret_cast<const uint2*>(&Kb[row * CF::KB_LD + 16 * a + 4 * g]);
+    return op;
+  } else if constexpr (CF::DK == 16) {
     return *reinterpret_cast<const uint2*>(&Kb[row * CF::KB_LD + 4 * g]);
   } else {
     return *reinterpret_cast<const u32x4*>(&Kb[row * CF::KB_LD + 8 * g]);
@@ -1167,7 +1224,22 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
         if (kt > L.qt[slot]) continue;  // fully masked tile: uniform per wave
-        f32x4 sc = score_mfma<DK>(kf[h], qf[slot]);  // [key 4g+j][query r]
+        f32x4 sc;  // [key 4g+j][query r]
+        if constexpr (kBlockMap<DK>) {
+          // sum over the blocks of the squared block scores, kept as its root
+          // so the squaring below is shared with the other maps
+          f32x4 sq = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 b = score_mfma<16>(kf[h].p[a], qf[slot].p[a]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sq[j] = __builtin_fmaf(b[j], b[j], sq[j]);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[j] = __builtin_sqrtf(sq[j]);
+        } else {
+          sc = score_mfma<DK>(kf[h], qf[slot]);
+        }
         if constexpr (G) {
           // p = sc^2 2^(beta_q - beta_k): fold the root of the weight into sc
           const float4 bk = src.gate4(16 * kt + 4 * g);
@@ -2062,6 +2134,7 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 16 && a.chunk == 128) return launch_span<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) return launch_span<32, 64>(a, stream);
   if (a.d == 32 && a.chunk == 128) return launch_span<32, 128>(a, stream);
+  if (a.d == 64 && a.chunk == 64) return launch_span<64, 64>(a, stream);
   return hipErrorInvalidValue;
 }
 
@@ -2142,6 +2215,7 @@ hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 16 && a.chunk == 128) return launch_readout<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) return launch_readout<32, 64>(a, stream);
   if (a.d == 32 && a.chunk == 128) return launch_readout<32, 128>(a, stream);
+  if (a.d == 64 && a.chunk == 64) return launch_readout<64, 64>(a, stream);
   return hipErrorInvalidValue;
 }
 

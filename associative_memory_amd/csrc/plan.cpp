@@ -19,7 +19,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 }  // namespace
 
 ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
-                         kata_dtype_t dtype, kata_scan_t scan) {
+                         kata_dtype_t dtype, kata_scan_t scan, int g) {
   ForwardPlan p;
   p.BH = static_cast<int64_t>(B) * H;
   p.T = T;
@@ -29,7 +29,7 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.D = d * (d + 1) / 2;
   p.bf16 = dtype == KATA_BF16;
   p.n_chunks = ceil_div(T, chunk);
-  const bool mfma = mfma_supported(p.bf16, d, dv, chunk);
+  const bool mfma = mfma_supported(p.bf16, d, dv, chunk) || (g > 1 && block_map_supported(p.bf16, d, dv, g, chunk));
   p.path = mfma ? Path::Mfma : Path::Valu;
   p.E = mfma ? mfma_state_floats(d) : static_cast<int64_t>(p.D) * dv + p.D;
 

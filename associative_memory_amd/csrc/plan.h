@@ -39,8 +39,10 @@ struct ForwardPlan {
   size_t ws_bytes = 0;
 };
 
+// g > 1: the KATA-Mg block map with g blocks (the matrix-core path supports
+// g = 4 at d = 64); g = 1: the full rank-one map
 ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
-                         kata_dtype_t dtype, kata_scan_t scan);
+                         kata_dtype_t dtype, kata_scan_t scan, int g = 1);
 
 void describe_plan(const ForwardPlan& p, char* buf, size_t len);
 

@@ -9,11 +9,13 @@ namespace kata {
 
 constexpr int kMfmaValueTiles = 5;  // 4 tiles of 16 value columns + the ones-column tile
 
-// waves per workgroup: the d = 32 state (33 feature tiles) is spread over 8
+// waves per workgroup: the d = 32 state (33 feature tiles) and the KATA-M4
+// state at d = 64 (34 tiles) are spread over 8
 __host__ __device__ constexpr int mfma_waves(int d) { return d == 16 ? 4 : 8; }
 
-// feature tiles of 16 positions holding the d(d+1)/2 features
-__host__ __device__ constexpr int mfma_feature_tiles(int d) { return d == 16 ? 9 : 33; }
+// feature tiles of 16 positions holding the features: d(d+1)/2 for the full
+// map at d = 16, 32; 4 x 136 for the KATA-M4 block map at d = 64
+__host__ __device__ constexpr int mfma_feature_tiles(int d) { return d == 16 ? 9 : (d == 32 ? 33 : 34); }
 
 // floats of one span state in the workspace: the fp32 accumulator tiles of
 // the 4 value tiles, then the denominator column z (16 floats per feature tile)
@@ -97,6 +99,11 @@ hipError_t launch_linear_readout(const LinArgs& a, hipStream_t stream);
 
 inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
   return bf16 && (d == 16 || d == 32) && dv == 64 && (chunk == 64 || chunk == 128);
+}
+
+// the chunked KATA-M4 read at d = 64 (blocks of 16): bf16, dv = 64, chunk 64
+inline bool block_map_supported(bool bf16, int d, int dv, int g, int chunk) {
+  return bf16 && d == 64 && g == 4 && dv == 64 && chunk == 64;
 }
 
 // span sums of spans 0 .. n_spans-2 of every head into ws

@@ -252,7 +252,10 @@ PAGE_TABLE8_QUAD_MS = {(1024, 1): 0.07, (4096, 1): 0.58, (16384, 1): 8.92,
 
 def bench_table8(args, hip, am, ki, torch):
     """The quadratic form with the KATA-Mg block maps (g = 1, 2, 4) on the
-    page's Table 8 shape, inputs drawn on the device."""
+    page's Table 8 shape, inputs drawn on the device; and the chunked O(T)
+    form of KATA-M4 (g = 4, chunk 64) on the same shape up to T = 131072.
+    Chunked useful FLOPs: 2 [(C+1)/2 (d + dv) + 2 D dv + 2 D] per token-head
+    with D = 4 x 136 block features."""
     res = {}
     for w in ki.TABLE8_QUAD:
         q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
@@ -261,6 +264,32 @@ def bench_table8(args, hip, am, ki, torch):
         r["page_h100_ms"] = PAGE_TABLE8_QUAD_MS.get((w.T, w.g))
         res[w.name] = r
         del q, k, v, out
+    stream = torch.cuda.current_stream().cuda_stream
+    C, D = 64, 4 * 136
+    for T in (1024, 4096, 16384, 131072):
+        w = ki.table8(T, 4, 70)
+        q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
+        out = torch.empty_like(v)
+        need = am.lib().kata_forward_chunked_blocks_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, 4, C, 0)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        for _ in range(args.warmup):
+            am.kata_forward_chunked_blocks(q, k, v, 4, chunk=C, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = hip.event(), hip.event()
+        hip.record(e0, stream)
+        for _ in range(args.steps):
+            am.kata_forward_chunked_blocks(q, k, v, 4, chunk=C, out=out, workspace=ws)
+        hip.record(e1, stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(e0, e1) / args.steps
+        hip.destroy(e0)
+        hip.destroy(e1)
+        flops = 2 * ((C + 1) / 2 * (w.d + w.dv) + 2 * D * w.dv + 2 * D) * w.B * w.H * w.T
+        res[w.name.replace("_bf16", "_chunked_bf16")] = {
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del q, k, v, out, ws
     return res
 
 

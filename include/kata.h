@@ -166,6 +166,29 @@ kata_status_t kata_forward_gated(const void* q, const void* k, const void* v,
                                  kata_dtype_t dtype, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * kata_forward_chunked_blocks -- the chunked read of kata_forward_chunked with
+ * the KATA-Mg block maps of the KATA page (Sec. 4.1): q and k split into g
+ * equal blocks of width m = d/g, psi_Mg(u) = (u_1 u_1^T, ..., u_g u_g^T), so
+ *   o_t = sum_{s<=t} c_{t,s} v_s / (sum_{s<=t} c_{t,s} + eps),
+ *   c_{t,s} = sum_a (q_{t,a} . k_{s,a})^2,
+ * in the same O(T) chunked-state form (Eqs. 17-20) with the g m(m+1)/2
+ * block features.  g = 1 is exactly kata_forward_chunked (and takes its
+ * supported set); the block map g = 4 is supported at d = 64 (KATA-M4, 544
+ * features), bf16, dv = 64, chunk 64.  Arguments, workspace, errors and
+ * determinism as kata_forward_chunked; workspace_bytes >=
+ * kata_forward_chunked_blocks_workspace_bytes(...).
+ */
+size_t kata_forward_chunked_blocks_workspace_bytes(int B, int H, int64_t T, int d,
+                                                   int dv, int g, int chunk,
+                                                   kata_scan_t scan);
+kata_status_t kata_forward_chunked_blocks(const void* q, const void* k, const void* v,
+                                          void* out, int B, int H, int64_t T, int d,
+                                          int dv, int g, int chunk, float eps,
+                                          kata_dtype_t dtype, kata_scan_t scan,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* stream);
+
 /* Linear (D = d) cone features of kata_forward_linear. */
 typedef enum {
   KATA_FEATURE_ORTHANT = 0, /* psi(x) = ReLU(x) + shift, every coordinate */

@@ -235,3 +235,33 @@ def test_gated_decode_error_paths():
     assert step(lg=ctypes.c_void_p(P[4].value + 2)) == INVALID  # not 4-byte aligned
     assert step(out=P[4]) == INVALID                            # out overlaps log_gamma
     assert step(out=P[0]) == INVALID                            # out overlaps S
+
+
+
+def blk(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=2, T=300, d=64, dv=64, g=4, chunk=64, eps=1e-6, dt=BF16,
+        scan=0, ws=P[5], wsb=1 << 30):
+    return am.lib().kata_forward_chunked_blocks(q, k, v, out, B, H, T, d, dv, g, chunk, eps, dt, scan, ws, wsb,
+                                                None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), INVALID), (dict(B=0), INVALID), (dict(g=0), INVALID), (dict(g=3), INVALID),
+    (dict(scan=9), INVALID), (dict(dt=3), INVALID), (dict(eps=-1.0), INVALID),
+    (dict(dt=F32), UNSUPPORTED), (dict(g=2), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
+    (dict(d=32, g=2), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
+    (dict(out=P[1]), INVALID), (dict(ws=NULL, wsb=0, T=1 << 16), WORKSPACE),
+    (dict(g=1, d=24), UNSUPPORTED),   # g = 1 takes kata_forward_chunked's checks
+])
+def test_chunked_blocks_error_paths(kw, status):
+    assert blk(**kw) == status
+
+
+def test_chunked_blocks_workspace():
+    L = am.lib()
+    # g = 1 is kata_forward_chunked's workspace
+    assert (L.kata_forward_chunked_blocks_workspace_bytes(1, 8, 131072, 16, 64, 1, 128, 0)
+            == L.kata_forward_workspace_bytes(1, 8, 131072, 16, 64, 128, 0))
+    # KATA-M4: 34 feature tiles x (4 x 256 + 16) floats per span state
+    n = L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, 4, 64, 0)
+    assert n > 0 and n % ((34 * 4 * 256 + 34 * 16) * 4) == 0
+    assert L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, 2, 64, 0) == 0
