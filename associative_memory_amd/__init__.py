@@ -342,11 +342,11 @@ def kata_forward_linear(q, k, v, feature: str = "orthant", shift: float = 1e-6, 
     return out
 
 
-def kata_forward_gated_workspace_bytes(B, H, T, d, dv, chunk=64) -> int:
+def kata_forward_gated_workspace_bytes(B, H, T, d, dv, chunk=128) -> int:
     return int(lib().kata_forward_gated_workspace_bytes(B, H, T, d, dv, chunk))
 
 
-def kata_forward_gated(q, k, v, log_gamma, chunk: int = 64, out=None, workspace=None, stream=None):
+def kata_forward_gated(q, k, v, log_gamma, chunk: int = 128, out=None, workspace=None, stream=None):
     """GatedKATA read o_t = phi(q_t)^T S_t with S_t = gamma_t S_{t-1} +
     phi(k_t) v_t^T (no denominator).  q, k: [B, H, T, d]; v: [B, H, T, dv];
     bf16; log_gamma: [B, H, T] float32; all contiguous on the device.

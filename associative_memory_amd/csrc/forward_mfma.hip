@@ -598,14 +598,15 @@ __device__ __forceinline__ float row_rotate(float x) {
 // k-step and takes the partner dimension from lane r + J of its row, so the
 // features of every tile come from one 32-byte read per lane and k-step.
 // Rows 8..15 of tile 8 repeat rows 0..7; the state copy drops them.
-template <int J>
+// N: value tiles updated (the gated read leaves out the ones-column tile)
+template <int J, int N = NDT>
 __device__ __forceinline__ void tile16_into(f32x4 (&dst)[NDT], const float (&kr)[8], const u32x4 (&bv)[NDT]) {
   float f[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) f[i] = kr[i] * row_rotate<J>(kr[i]);
   const u32x4 af = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) dst[dt] = mfma(af, bv[dt], dst[dt]);
+  for (int dt = 0; dt < N; ++dt) dst[dt] = mfma(af, bv[dt], dst[dt]);
 }
 
 template <class CF, int J>
@@ -804,17 +805,17 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
 // is unrolled over them, so the compiler's wait counts see that a chunk
 // arriving in one buffer does not alias reads of the other.
 // Gated read only: the chunk's running gate sums beta_t (log2 units, see
-// gate_prep_kernel), 1 KB so one DMA instruction fills it (entries past the
-// chunk read as 0).  The ungated tiles carry nothing (empty base).
-template <bool G>
+// gate_prep_kernel), filled by one DMA instruction of C/4 lanes (entries past
+// the sequence read as 0).  The ungated tiles carry nothing (empty base).
+template <int C, bool G>
 struct GateRows {};
-template <>
-struct GateRows<true> {
-  alignas(16) float gb[256];
+template <int C>
+struct GateRows<C, true> {
+  alignas(16) float gb[C];
 };
 
 template <int C, bool G = false>
-struct alignas(16) DmaTile16 : GateRows<G> {
+struct alignas(16) DmaTile16 : GateRows<C, G> {
   alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
   alignas(16) uint16_t k[C * 16];  // [token][dimension]
 };
@@ -832,11 +833,13 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
 
 // wave W's share of the chunk's DMA: V in 1 KB pieces of 8 rows, K in 1 KB
 // pieces of 32 rows; rows past the buffer resource's end arrive as zero
-// the gate sums of a chunk: one DMA by the last wave
+// the gate sums of a chunk of C tokens: one DMA by the last wave, lanes
+// [0, C/4) moving 16 bytes each
 template <bool G, int W, int NW, class B>
 __device__ __forceinline__ void dma_gate(B& b, const ChunkSrc& src, int lane) {
   if constexpr (G && W == NW - 1) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.g, KATA_LDS(&b.gb[0]), 16, 16 * lane, 0, 0, 0);
+    constexpr int NL = static_cast<int>(sizeof(b.gb)) / 16;
+    if (lane < NL) __builtin_amdgcn_raw_ptr_buffer_load_lds(src.g, KATA_LDS(&b.gb[0]), 16, 16 * lane, 0, 0, 0);
   }
 }
 
@@ -909,7 +912,7 @@ __device__ __forceinline__ void gate_decay(f32x4 (&acc)[NA][NB], float f) {
 #pragma unroll
   for (int m = 0; m < NA; ++m) {
 #pragma unroll
-    for (int dt = 0; dt < NB; ++dt) acc[m][dt] *= f;
+    for (int dt = 0; dt < NB - 1; ++dt) acc[m][dt] *= f;  // the ones-column tile is unused
   }
 }
 
@@ -949,9 +952,10 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
     if constexpr (G) gate_keys(kr, b.gb, beta_c, ks);
-    tile16_into<W>(acc[0], kr, bv);
-    tile16_into<W + 4>(acc[1], kr, bv);
-    if (ks % CF::NW == W) tile16_into<8>(acc8, kr, bv);  // compile-time per wave
+    constexpr int N = G ? NDT - 1 : NDT;
+    tile16_into<W, N>(acc[0], kr, bv);
+    tile16_into<W + 4, N>(acc[1], kr, bv);
+    if (ks % CF::NW == W) tile16_into<8, N>(acc8, kr, bv);  // compile-time per wave
   }
 }
 
@@ -1141,6 +1145,8 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
                                               const H& after_q = H{}) {
   constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
   constexpr int SB_LD = CF::SB_LD;
+  static_assert(!G || NDW == NDT, "the gated read uses whole output rows");
+  constexpr int NO = G ? NDW - 1 : NDW;  // value tiles read out (gated: no denominator)
   constexpr int SH = Schedule<DK>::SH;
   const int g = lane >> 4, r = lane & 15;
   const int qt_max = L.qt[NSLOT - 1] > L.qt[0] ? L.qt[NSLOT - 1] : L.qt[0];
@@ -1179,7 +1185,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
   for (int ks = 0; ks < CF::NKS; ++ks) {
     u32x4 bs[NDW];
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) {
+    for (int i = 0; i < NO; ++i) {
       bs[i] = *reinterpret_cast<const u32x4*>(&Sb[vrow(L.vt[i], r) * SB_LD + 32 * ks + 8 * g]);
     }
 #pragma unroll
@@ -1197,7 +1203,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
       }
       const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
 #pragma unroll
-      for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bs[i], qfeat, o[slot][i]);
+      for (int i = 0; i < NO; ++i) o[slot][i] = mfma(bs[i], qfeat, o[slot][i]);
     }
   }
   // intra-chunk term: squared causal scores.  The score product has K = d:
@@ -1213,7 +1219,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
     for (int h = 0; h < 2; ++h) kf[h] = src.score_k(16 * (2 * s + h) + r, g);
     u32x4 bv[NDW];
 #pragma unroll
-    for (int i = 0; i < NDW; ++i) bv[i] = src.v_op(L.vt[i], s, lane);
+    for (int i = 0; i < NO; ++i) bv[i] = src.v_op(L.vt[i], s, lane);
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
       if (2 * s > L.qt[slot]) continue;  // uniform per wave
@@ -1259,7 +1265,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
       const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
                         pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
 #pragma unroll
-      for (int i = 0; i < NDW; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
+      for (int i = 0; i < NO; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
     }
   }
   // normalise and store: lane r of group 0 holds the denominator of query r
@@ -1367,7 +1373,7 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
 // the other is read.  Query rows and score operands are plain row reads; V and
 // K operands come from transposing reads, as in the span sums.
 template <int C, bool G = false>
-struct alignas(16) DmaTileQ16 : GateRows<G> {
+struct alignas(16) DmaTileQ16 : GateRows<C, G> {
   alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
   alignas(16) uint16_t k[C * 16];  // [token][dimension]
   alignas(16) uint16_t q[C * 16];  // [token][dimension]
@@ -1439,9 +1445,10 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], co
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
     if constexpr (G) gate_keys(kr, b.gb, beta_c, ks);
-    tile16_into<W>(acc[0], kr, bv);
-    tile16_into<W + 4>(acc[1], kr, bv);
-    if constexpr (W == 0) tile16_into<8>(acc[2], kr, bv);
+    constexpr int N = G ? NDT - 1 : NDT;
+    tile16_into<W, N>(acc[0], kr, bv);
+    tile16_into<W + 4, N>(acc[1], kr, bv);
+    if constexpr (W == 0) tile16_into<8, N>(acc[2], kr, bv);
   }
 }
 

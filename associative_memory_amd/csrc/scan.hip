@@ -145,7 +145,20 @@ __global__ __launch_bounds__(kThreads) void scan_affine_kernel(float* __restrict
   if (e >= E) return;
   float* base = ws + bh * N * E + e;
   float run = 0.f;
-  for (int64_t n = 0; n < N; ++n) {
+  // loads batched eight at a time, as in the additive walk
+  constexpr int U = 8;
+  int64_t n = 0;
+  for (; n + U <= N; n += U) {
+    float a[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) a[u] = base[(n + u) * E];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      base[(n + u) * E] = run;
+      run = __builtin_fmaf(decay[n + u], run, a[u]);
+    }
+  }
+  for (; n < N; ++n) {
     const float a = base[n * E];
     base[n * E] = run;
     run = __builtin_fmaf(decay[n], run, a);
