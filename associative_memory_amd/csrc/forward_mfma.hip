@@ -30,27 +30,11 @@
 //    the readout, which is split across waves by query tile (and, for d = 32,
 //    by value tiles) and computed transposed, O^T = [S|z]^T phi_q^T + [V|1]^T P^T,
 //    so a lane holds 4 consecutive value columns of one query.
-#include <utility>
-
-#include "common.h"
 #include "kernels.h"
-#include "plan_mfma.h"
+#include "mfma_common.h"
 
 namespace kata {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int DV = 64;
-constexpr int NDT = kMfmaValueTiles;  // 4 value tiles + the ones-column tile
-// LDS rows of V^T and of the state copy: 64 value rows, then row 64 (ones
-// for V, z for the state) and row 65 (zeros).  Operand rows 65..79 of the
-// ones-column tile are all zero, so every lane past the first reads row 65.
-constexpr int VROWS = DV + 2;
-__device__ __forceinline__ int vrow(int vt, int r) { return vt == NDT - 1 ? DV + (r > 0) : 16 * vt + r; }
 
 // ------------------------------------------------------------ feature schedule
 
@@ -258,63 +242,6 @@ __device__ __forceinline__ int value_tile(int w, int idx) {
   }
 }
 
-// ------------------------------------------------------------ small helpers
-
-// Calls f(std::integral_constant<int, W>) for the wave index w (uniform per
-// wave): each wave runs a body specialised for its index, so the per-wave
-// work split (query tiles, feature tiles, lane rotations) is resolved at
-// compile time and the chunk body has no wave-dependent branches.
-template <int NW, class F>
-__device__ __forceinline__ void with_wave(int w, F&& f) {
-  static_assert(NW == 4 || NW == 8, "waves per workgroup");
-  switch (w) {
-    case 0: f(std::integral_constant<int, 0>{}); break;
-    case 1: f(std::integral_constant<int, 1>{}); break;
-    case 2: f(std::integral_constant<int, 2>{}); break;
-    case 3: f(std::integral_constant<int, 3>{}); break;
-    default:
-      if constexpr (NW == 8) {
-        switch (w) {
-          case 4: f(std::integral_constant<int, 4>{}); break;
-          case 5: f(std::integral_constant<int, 5>{}); break;
-          case 6: f(std::integral_constant<int, 6>{}); break;
-          default: f(std::integral_constant<int, 7>{}); break;
-        }
-      }
-      break;
-  }
-}
-
-// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt unconstrained
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-// Score products Sc^T[key][query] = K Q^T with K = d.  At d = 16 the
-// 16x16x16 form takes 4 bf16 per lane (k = 4g + i); at d = 32 the 16x16x32
-// form takes 8 (k = 8g + i).
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-template <int DK>
-struct ScoreOpT;
-template <>
-struct ScoreOpT<16> {
-  using type = uint2;
-};
-template <>
-struct ScoreOpT<32> {
-  using type = u32x4;
-};
 template <>
 struct ScoreOpT<64> {  // KATA-M4: one 16x16x16 operand per block
   struct type {
@@ -324,44 +251,12 @@ struct ScoreOpT<64> {  // KATA-M4: one 16x16x16 operand per block
 template <int DK>
 using ScoreOp = typename ScoreOpT<DK>::type;
 
-template <int DK>
-__device__ __forceinline__ f32x4 score_mfma(const ScoreOp<DK>& a, const ScoreOp<DK>& b) {
-  if constexpr (DK == 16) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                     __builtin_bit_cast(s16x4, b),
-                                                     f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-  } else {
-    return mfma(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
-  }
-}
-
 // position of the first of 4 consecutive tokens (group tg) inside a chunk:
 // within each 32-token block, token groups 0..3 sit at 8a, groups 4..7 at
 // 8(a-4)+4, matching the key order of a pair of 16x16 accumulators.
 __device__ __forceinline__ int group_pos(int tg) {
   const int a = tg & 7;
   return (tg >> 3) * 32 + ((a < 4) ? 8 * a : 8 * (a - 4) + 4);
-}
-
-// Buffer resource over `rows` rows of `row_bytes` starting at row `row0` of
-// `base`.  Buffer reads past the last row return 0 and writes past it are
-// dropped by the hardware range check, which is how the ragged last chunk of
-// a sequence is read and written.  The resource is uniform (scalar registers).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int64_t row0, int64_t rows,
-                                                           int row_bytes) {
-  char* p = const_cast<char*>(static_cast<const char*>(base)) + row0 * row_bytes;
-  const int n = rows > 0 ? static_cast<int>(rows) * row_bytes : 0;
-  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0), n, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  return make_uint4(x[0], x[1], x[2], x[3]);
-}
-
-__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, uint2 x) {
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{x.x, x.y}, r, off, 0, 0);
 }
 
 // ------------------------------------------------------------ LDS tiles
@@ -382,8 +277,6 @@ struct alignas(16) Tiles : Smem<CF> {
   alignas(16) uint16_t Kb[CF::C * CF::KB_LD];  // [token][d] bf16 (score operand)
   alignas(16) float Qf[CF::C * CF::QF_LD];     // [token][d] fp32
 };
-
-constexpr int OB_LD = DV + 8;  // bf16 row stride of a wave's output staging tile
 
 template <class CF>
 struct alignas(16) SmemOut : Tiles<CF> {
@@ -434,19 +327,6 @@ __device__ __forceinline__ ScoreOp<CF::DK> score_operand_bf16(const uint16_t* Kb
 // Global -> registers -> LDS for one chunk.  V: groups of 4 tokens x 8
 // columns (16 B per token), written transposed; K and Q: one token row per
 // thread.  Tokens at or past T read as zero (buffer range check).
-struct ChunkSrc {
-  __amdgpu_buffer_rsrc_t q, k, v;
-  __amdgpu_buffer_rsrc_t g;  // per-token gate sums (gated read only)
-};
-
-template <int DK, int C>
-__device__ __forceinline__ ChunkSrc chunk_src(const void* q, const void* k, const void* v, int64_t tok0,
-                                              int64_t c0, int64_t T, const float* gb = nullptr) {
-  const int64_t n = (T - c0 < C) ? T - c0 : C;
-  return ChunkSrc{rows_rsrc(q, tok0 + c0, n, 2 * DK), rows_rsrc(k, tok0 + c0, n, 2 * DK),
-                  rows_rsrc(v, tok0 + c0, n, 2 * DV), rows_rsrc(gb, tok0 + c0, n, 4)};
-}
-
 template <class CF, bool WITH_Q>
 struct Stage {
   static constexpr int C = CF::C, DK = CF::DK;
@@ -820,17 +700,6 @@ struct alignas(16) DmaTile16 : GateRows<C, G> {
   alignas(16) uint16_t k[C * 16];  // [token][dimension]
 };
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-#define KATA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-
-__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
-
-__device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
-  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(uint2, x);
-}
-
 // wave W's share of the chunk's DMA: V in 1 KB pieces of 8 rows, K in 1 KB
 // pieces of 32 rows; rows past the buffer resource's end arrive as zero
 // the gate sums of a chunk of C tokens: one DMA by the last wave, lanes
@@ -859,48 +728,6 @@ __device__ __forceinline__ void dma_chunk16(DmaTile16<C, G>& b, const ChunkSrc& 
   dma_gate<G, W, NW>(b, src, lane);
 }
 
-// Per-lane element offsets of the transposing reads.  Lane (g, s) addresses
-// row 4g + s/4 (+ 32 ks + 16 h), columns 4(s % 4)..+3 of the 16-column block;
-// within a 32-row k-step the V swizzle (row >> 1) & 7 reduces to
-// (2g + s/8) & 7, so the offsets are lane constants and k-step / half are
-// immediate offsets.
-struct TrOffsets {
-  int v[NDT - 1];  // V, per value tile
-  int k;           // K
-};
-
-__device__ __forceinline__ TrOffsets tr_offsets(int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int row = 4 * g + (s >> 2);
-  const int z = (2 * g + (s >> 3)) & 7;
-  TrOffsets o;
-#pragma unroll
-  for (int dt = 0; dt < NDT - 1; ++dt) {
-    const int chunk = (2 * dt + ((s & 3) >> 1)) ^ z;
-    o.v[dt] = row * DV + 8 * chunk + 4 * (s & 1);
-  }
-  o.k = row * 16 + 4 * (s & 3);
-  return o;
-}
-
-// operand of k-step ks: lane (g, r) gets column r of the block of tokens
-// 32 ks + 4g + m and 32 ks + 16 + 4g + m (m = 0..3), the key order of a pair
-// of 16x16 score accumulators
-template <int LD>
-__device__ __forceinline__ u32x4 tr_operand(const uint16_t* t, int off, int ks) {
-  u32x4 out;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint2 x = tr_read(&t[off + (32 * ks + 16 * h) * LD]);
-    out[2 * h] = x.x;
-    out[2 * h + 1] = x.y;
-  }
-  return out;
-}
-
-// Span-sum update: wave W reduces feature tiles W and W + 4 over every k-step
-// and the last tile (8) over the k-steps ks % 4 == W into acc8, so the waves
-// carry equal work; the partial acc8 of the waves are added once per span.
 // Gated read (GatedKATA, S_t = gamma_t S_{t-1} + phi(k_t) v_t^T): over a
 // chunk with running gate sums beta_t (log2 units) and total beta_C,
 //   S <- 2^beta_C S + sum_s 2^(beta_C - beta_s) phi(k_s) v_s^T.
@@ -957,17 +784,6 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
     tile16_into<W + 4, N>(acc[1], kr, bv);
     if (ks % CF::NW == W) tile16_into<8, N>(acc8, kr, bv);  // compile-time per wave
   }
-}
-
-// s_waitcnt immediate with vmcnt = n (gfx9 encoding), expcnt and lgkmcnt free
-constexpr int wait_vmcnt(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
-
-// Workgroup barrier that leaves vector-memory loads in flight: LDS reads and
-// writes of this wave complete first (lgkmcnt), global loads and LDS DMA do
-// not.  The memory clobber keeps the compiler from moving memory operations
-// across it.
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // DMA instructions one wave issues per chunk
@@ -1125,10 +941,6 @@ struct TileSrc {
     const int g = lane >> 4, r = lane & 15;
     return *reinterpret_cast<const u32x4*>(&tl.Vt[vrow(vt, r) * CF::LDT + 32 * s + 8 * g]);
   }
-};
-
-struct NoHook {
-  __device__ __forceinline__ void operator()() const {}
 };
 
 // `after_q` runs once the query rows are in registers (the DMA readout issues
@@ -1532,583 +1344,6 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
   });
 }
 
-// ------------------------------------------------------------ quadratic forward
-//
-// The O(T^2) form of the read, Eq. 2 of the KATA page evaluated directly (its
-// flash-style "quadratic" operating point, Sec. 4): per block of 128 queries,
-// the key blocks up to the diagonal stream through LDS (DMA, two buffers);
-// each gives the squared scores on the matrix cores, masked only on the
-// diagonal block, and adds P [V | 1] to fp32 accumulators that stay in
-// registers.  No state, no workspace.  Wave W owns query tiles W and 7 - W.
-//
-// Scores follow the KATA-Mg block family of Sec. 4.1: the d dimensions split
-// into g = DK / M blocks of width M and the score is sum_a (q_a . k_a)^2
-// (g = 1: the full map's (q . k)^2).  A score operand is a set of pieces:
-// at M = 16 one 16x16x16 product per block (4 dimensions per lane), otherwise
-// 16x16x32 products over 32-dimension pieces, chained within a block.
-constexpr int QB = 128;
-
-template <int DK, int M>
-struct QkOp {
-  static constexpr bool K16 = (M == 16);
-  static constexpr int NP = K16 ? DK / 16 : DK / 32;  // pieces per operand
-  static constexpr int PPB = K16 ? 1 : M / 32;         // pieces per block
-  using Piece = typename ScoreOpT<K16 ? 16 : 32>::type;
-  Piece p[NP];
-  // first dimension of piece i held by lane group g
-  static constexpr __device__ int col(int i, int g) { return K16 ? 16 * i + 4 * g : 32 * i + 8 * g; }
-};
-
-// sum over blocks of the squared score tile [key 4g + j][query r]
-template <int DK, int M>
-__device__ __forceinline__ void block_sq_scores(const QkOp<DK, M>& k, const QkOp<DK, M>& q, float (&p)[4]) {
-  using Op = QkOp<DK, M>;
-#pragma unroll
-  for (int b = 0; b < Op::NP / Op::PPB; ++b) {
-    f32x4 sc;
-    if constexpr (Op::K16) {
-      sc = score_mfma<16>(k.p[b], q.p[b]);
-    } else {
-      sc = mfma(k.p[b * Op::PPB], q.p[b * Op::PPB], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int j = 1; j < Op::PPB; ++j) sc = mfma(k.p[b * Op::PPB + j], q.p[b * Op::PPB + j], sc);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[j] = b == 0 ? sc[j] * sc[j] : __builtin_fmaf(sc[j], sc[j], p[j]);
-  }
-}
-
-// K rows in LDS hold their 16-byte pieces XOR-swizzled by the row, so that
-// the 16 rows one operand read touches fall in distinct banks:
-// piece c of row r sits at c ^ ksw(r).
-template <int DK>
-__device__ __forceinline__ int ksw(int r) {
-  constexpr int SH = DK == 16 ? 3 : (DK == 32 ? 2 : 1);  // log2(128 / DK)
-  return (r >> SH) & (DK / 8 - 1);
-}
-
-template <int DK>
-struct alignas(16) QuadTile {
-  alignas(16) uint16_t v[QB * DV];  // [key][value column], swizzled
-  alignas(16) uint16_t k[QB * DK];  // [key][dimension], swizzled
-};
-
-template <int DK, int W>
-__device__ __forceinline__ void dma_quad(QuadTile<DK>& b, const ChunkSrc& src, int lane) {
-#pragma unroll
-  for (int j = W; j < QB / 8; j += 4) {
-    const int t = 8 * j + (lane >> 3);
-    const int cg = (lane & 7) ^ vswz(t);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, KATA_LDS(&b.v[8 * j * DV]), 16, t * (2 * DV) + 16 * cg, 0, 0, 0);
-  }
-  constexpr int PPR = 2 * DK / 16;  // 16-byte pieces per K row
-  constexpr int RPI = 64 / PPR;     // K rows per 1 KB transfer
-#pragma unroll
-  for (int j = W; j < QB / RPI; j += 4) {
-    const int t = RPI * j + lane / PPR;
-    const int c = (lane % PPR) ^ ksw<DK>(t);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[RPI * j * DK]), 16, t * (2 * DK) + 16 * c,
-                                             0, 0, 0);
-  }
-}
-
-template <int DK, int M>
-__device__ __forceinline__ QkOp<DK, M> quad_key_op(const QuadTile<DK>& b, int row, int g) {
-  using Op = QkOp<DK, M>;
-  Op op;
-#pragma unroll
-  for (int i = 0; i < Op::NP; ++i) {
-    const int col = Op::col(i, g);
-    const uint16_t* at = &b.k[row * DK + 8 * ((col >> 3) ^ ksw<DK>(row)) + (col & 7)];
-    op.p[i] = *reinterpret_cast<const typename Op::Piece*>(at);
-  }
-  return op;
-}
-
-// one key block against the wave's two query tiles; DIAG: the block holding
-// the queries themselves (causal mask, fully masked tiles skipped)
-// `after_k` runs once the block's key operands are in registers (the next
-// block's transfer is issued there: any earlier, the compiler's wait counts
-// make these reads wait for it)
-template <int DK, int M, int W, bool DIAG, class H>
-__device__ __forceinline__ void quad_block(f32x4 (&o)[2][NDT], const QuadTile<DK>& b,
-                                           const QkOp<DK, M> (&qf)[2], const bool (&keep)[4],
-                                           const TrOffsets& to, const u32x4& bones, int lane,
-                                           const H& after_k) {
-  constexpr int qt[2] = {W, 7 - W};
-  constexpr int qt_max = qt[0] > qt[1] ? qt[0] : qt[1];
-  constexpr int NS = DIAG ? qt_max / 2 + 1 : QB / 32;  // 32-key steps read
-  const int g = lane >> 4, r = lane & 15;
-  QkOp<DK, M> kall[NS][2];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) kall[s][h] = quad_key_op<DK, M>(b, 16 * (2 * s + h) + r, g);
-  }
-  after_k();
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 bv[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], s);
-    bv[NDT - 1] = bones;
-#pragma unroll
-    for (int slot = 0; slot < 2; ++slot) {
-      if (DIAG && 2 * s > qt[slot]) continue;
-      float p[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kt = 2 * s + h;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
-        if (DIAG && kt > qt[slot]) continue;
-        block_sq_scores<DK, M>(kall[s][h], qf[slot], p[h]);
-        if (DIAG && kt == qt[slot]) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p[h][j] = keep[j] ? p[h][j] : 0.f;
-        }
-      }
-      const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
-                        pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
-    }
-  }
-}
-
-template <int DK, int M>
-__global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
-  using Op = QkOp<DK, M>;
-  __shared__ QuadTile<DK> x0;
-  __shared__ QuadTile<DK> x1;
-  __shared__ alignas(16) uint16_t ones[128];
-  __shared__ alignas(16) uint16_t Ob[4][16 * OB_LD];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t nqb = (a.T + QB - 1) / QB;
-  const int64_t bh = blockIdx.x / nqb;
-  const int64_t qb = nqb - 1 - (blockIdx.x - bh * nqb);  // the longest rows of blocks first
-  const int64_t tok0 = bh * a.T;
-  const int64_t q0 = qb * QB;
-  const int64_t kend = (a.T < q0 + QB) ? a.T : q0 + QB;  // keys [0, kend) are read
-  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
-
-  with_wave<4>(w, [&](auto wc) {
-    constexpr int W = decltype(wc)::value;
-    constexpr int qt[2] = {W, 7 - W};
-    const int g = lane >> 4, r = lane & 15;
-    bool keep[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) keep[j] = 4 * g + j <= r;
-    const TrOffsets to = tr_offsets(lane);
-    // the wave's query score operands, straight from HBM (rows past T read 0)
-    const __amdgpu_buffer_rsrc_t qsrc = rows_rsrc(a.q, tok0 + q0, a.T - q0 < QB ? a.T - q0 : QB, 2 * DK);
-    Op qf[2];
-#pragma unroll
-    for (int slot = 0; slot < 2; ++slot) {
-#pragma unroll
-      for (int i = 0; i < Op::NP; ++i) {
-        const int off = (16 * qt[slot] + r) * (2 * DK) + 2 * Op::col(i, g);
-        if constexpr (Op::K16) {
-          const auto x = __builtin_amdgcn_raw_buffer_load_b64(qsrc, off, 0, 0);
-          qf[slot].p[i] = uint2{x[0], x[1]};
-        } else {
-          qf[slot].p[i] = __builtin_amdgcn_raw_buffer_load_b128(qsrc, off, 0, 0);
-        }
-      }
-    }
-    f32x4 o[2][NDT];
-#pragma unroll
-    for (int slot = 0; slot < 2; ++slot) {
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) o[slot][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    auto src = [&](int64_t kb) { return chunk_src<DK, QB>(nullptr, a.k, a.v, tok0, kb * QB, kend); };
-    dma_quad<DK, W>(x0, src(0), lane);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[(r > 0 ? 64 : 0) + 8 * g]);
-    auto prefetch = [&](QuadTile<DK>& nxt, int64_t kb) {
-      return [&src, lane, kb, p = &nxt]() {
-        __builtin_amdgcn_sched_barrier(0);
-        dma_quad<DK, W>(*p, src(kb), lane);
-        __builtin_amdgcn_sched_barrier(0);
-      };
-    };
-    for (int64_t kb = 0; kb < qb; kb += 2) {
-      quad_block<DK, M, W, false>(o, x0, qf, keep, to, bones, lane, prefetch(x1, kb + 1));
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      barrier_lds();
-      if (kb + 1 < qb) {
-        quad_block<DK, M, W, false>(o, x1, qf, keep, to, bones, lane, prefetch(x0, kb + 2));
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        barrier_lds();
-      }
-    }
-    // the diagonal block: in x0 when qb is even, in x1 when odd
-    if (qb & 1) {
-      quad_block<DK, M, W, true>(o, x1, qf, keep, to, bones, lane, NoHook{});
-    } else {
-      quad_block<DK, M, W, true>(o, x0, qf, keep, to, bones, lane, NoHook{});
-    }
-    // normalise; stage each 16 x 64 tile and store it as 1 KB contiguous rows
-    const __amdgpu_buffer_rsrc_t dst = rows_rsrc(a.out, tok0 + q0, a.T - q0 < QB ? a.T - q0 : QB, 2 * DV);
-    uint16_t* ob = Ob[W];
-#pragma unroll
-    for (int slot = 0; slot < 2; ++slot) {
-      const float den = __shfl(o[slot][NDT - 1][0], r);
-      const float inv = __builtin_amdgcn_rcpf(den + a.eps);
-#pragma unroll
-      for (int i = 0; i < NDT - 1; ++i) {
-        uint2 x;
-        x.x = pack2(o[slot][i][0] * inv, o[slot][i][1] * inv);
-        x.y = pack2(o[slot][i][2] * inv, o[slot][i][3] * inv);
-        *reinterpret_cast<uint2*>(&ob[r * OB_LD + 16 * i + 4 * g]) = x;
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 8 * h + (lane >> 3);
-        const uint4 x = *reinterpret_cast<const uint4*>(&ob[row * OB_LD + 8 * (lane & 7)]);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, dst,
-                                               (16 * qt[slot] + row) * (2 * DV) + 16 * (lane & 7), 0, 0);
-      }
-    }
-  });
-}
-
-// ------------------------------------------------------------ linear cone features
-//
-// The chunked read with a linear feature psi (D = d = 64), the KATA-Orthant
-// and KATA-Lorentz maps of the page (App. F.4), through the same three stages
-// as the PSD map (Sec. 4.1 Eqs. 17-20 with the unsquared score
-// psi(q) . psi(k)).  Per chunk of 64 tokens the raw K and Q rows pass through
-// registers, where psi is applied in fp32 (orthant: ReLU(x) + shift per
-// coordinate; Lorentz: (y, |y| (1 + s^2)), |y| summed over the 4 lanes that
-// hold a row), and land in LDS as bf16 rows in the V layout (16-byte pieces
-// swizzled by (row >> 1) & 7); V arrives by DMA into two buffers.  The fp32
-// state [S | z] (64 features x 65) is one feature tile per wave, 5 value
-// tiles of accumulators; psi(K)^T and [V | 1] operands of its update both come
-// from transposing LDS reads.  Wave W reads out query tile W:
-// O^T = [S|z]^T psi(Q)^T + [V|1]^T P^T, P = (psi(K) psi(Q)^T)^T masked.
-constexpr int LCH = 64;       // chunk (tokens)
-constexpr int LSB = DV + 8;   // bf16 row stride of the state copy [value row][feature]
-
-struct alignas(16) LinRows {
-  alignas(16) uint16_t r[LCH * 64];  // [token][64], 16-byte pieces swizzled by vswz
-};
-
-// One quarter row (16 dimensions) of K and of Q per thread: row tid / 4,
-// dimensions 16 (tid % 4) .. +15.  Rows past the sequence read as zero and
-// are written as zero features.
-template <int FEAT, bool WITH_Q>
-struct LinStage {
-  u32x4 k[2];
-  u32x4 q[2];
-
-  __device__ __forceinline__ void load(const ChunkSrc& src, int tid) {
-    const int off = (tid >> 2) * 128 + 32 * (tid & 3);
-    k[0] = __builtin_amdgcn_raw_buffer_load_b128(src.k, off, 0, 0);
-    k[1] = __builtin_amdgcn_raw_buffer_load_b128(src.k, off + 16, 0, 0);
-    if constexpr (WITH_Q) {
-      q[0] = __builtin_amdgcn_raw_buffer_load_b128(src.q, off, 0, 0);
-      q[1] = __builtin_amdgcn_raw_buffer_load_b128(src.q, off + 16, 0, 0);
-    }
-  }
-
-  // psi of one quarter row, written to its swizzled place
-  static __device__ __forceinline__ void put(uint16_t* rows, const u32x4 (&x)[2], int tid, bool valid,
-                                             float shift) {
-    const int row = tid >> 2, qq = tid & 3;
-    float f[16];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[8 * h + 2 * i] = lo_bf16(x[h][i]);
-        f[8 * h + 2 * i + 1] = hi_bf16(x[h][i]);
-      }
-    }
-    if constexpr (FEAT == kLinFeatOrthant) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) f[i] = __builtin_fmaxf(f[i], 0.f) + shift;
-    } else {
-      // |y|^2 over dimensions 0..62: the last quarter leaves out its last entry (s)
-      float ss = 0.f;
-#pragma unroll
-      for (int i = 0; i < 15; ++i) ss = __builtin_fmaf(f[i], f[i], ss);
-      if (qq != 3) ss = __builtin_fmaf(f[15], f[15], ss);
-      ss += __shfl_xor(ss, 1);
-      ss += __shfl_xor(ss, 2);
-      if (qq == 3) f[15] = __builtin_sqrtf(ss) * __builtin_fmaf(f[15], f[15], 1.f);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = (2 * qq + h) ^ vswz(row);
-      u32x4 y;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[i] = valid ? pack2(f[8 * h + 2 * i], f[8 * h + 2 * i + 1]) : 0u;
-      *reinterpret_cast<u32x4*>(&rows[row * 64 + 8 * c]) = y;
-    }
-  }
-
-  __device__ __forceinline__ void store(LinRows& kr, LinRows* qr, int tid, int64_t valid_rows,
-                                        float shift) const {
-    const bool valid = (tid >> 2) < valid_rows;
-    put(kr.r, k, tid, valid, shift);
-    if constexpr (WITH_Q) put(qr->r, q, tid, valid, shift);
-  }
-};
-
-// 16-byte row operand: row t, dimensions 32 kf + 8 g .. +7
-__device__ __forceinline__ u32x4 lin_row_op(const uint16_t* rows, int t, int kf, int g) {
-  return *reinterpret_cast<const u32x4*>(&rows[t * 64 + 8 * ((4 * kf + g) ^ vswz(t))]);
-}
-
-// wave W's share of a chunk's V transfer (8 pieces of 8 rows, 2 per wave)
-template <int W>
-__device__ __forceinline__ void dma_lin_v(LinRows& b, const ChunkSrc& src, int lane) {
-#pragma unroll
-  for (int j = W; j < LCH / 8; j += 4) {
-    const int t = 8 * j + (lane >> 3);
-    const int cg = (lane & 7) ^ vswz(t);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, KATA_LDS(&b.r[8 * j * DV]), 16, t * (2 * DV) + 16 * cg, 0, 0, 0);
-  }
-}
-
-// acc[i] += psi(K)^T [V | 1] for feature tile W over the chunk
-template <int W>
-__device__ __forceinline__ void lin_state_update(f32x4 (&acc)[NDT], const LinRows& kr, const LinRows& vb,
-                                                 const TrOffsets& to, const u32x4& bones) {
-#pragma unroll
-  for (int s = 0; s < LCH / 32; ++s) {
-    const u32x4 ak = tr_operand<64>(kr.r, to.v[W], s);
-#pragma unroll
-    for (int i = 0; i < NDT; ++i) {
-      const u32x4 bv = i < NDT - 1 ? tr_operand<DV>(vb.r, to.v[i], s) : bones;
-      acc[i] = mfma(ak, bv, acc[i]);
-    }
-  }
-}
-
-// workspace layout of a span state: [feature tile][value tile][lane] f32x4
-__device__ __forceinline__ int lin_state_off(int W, int i, int lane) { return ((W * NDT + i) * 64 + lane) * 4; }
-
-template <int FEAT>
-__global__ __launch_bounds__(256, 2) void lin_span_kernel(LinArgs a) {
-  __shared__ LinRows kr;
-  __shared__ LinRows v0;
-  __shared__ LinRows v1;
-  __shared__ alignas(16) uint16_t ones[128];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t nsp = a.n_spans - 1;  // the last span's sum is not needed
-  const int64_t bh = blockIdx.x / nsp;
-  const int64_t sp = blockIdx.x - bh * nsp;
-  const int64_t tok0 = bh * a.T;
-  const int64_t first = sp * a.G * LCH;
-  const int64_t end = (a.T < first + a.G * LCH) ? a.T : first + a.G * LCH;
-  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
-
-  with_wave<4>(w, [&](auto wc) {
-    constexpr int W = decltype(wc)::value;
-    const int g = lane >> 4, r = lane & 15;
-    const TrOffsets to = tr_offsets(lane);
-    f32x4 acc[NDT];
-#pragma unroll
-    for (int i = 0; i < NDT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto src = [&](int64_t c0) { return chunk_src<64, LCH>(nullptr, a.k, a.v, tok0, c0, end); };
-    LinStage<FEAT, false> st;
-    st.load(src(first), tid);
-    dma_lin_v<W>(v0, src(first), lane);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    st.store(kr, nullptr, tid, end - first, a.shift);
-    __syncthreads();
-    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[(r > 0 ? 64 : 0) + 8 * g]);
-    // chunk loop, unrolled over the two V buffers
-    for (int64_t c0 = first; c0 < end; c0 += 2 * LCH) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t c = c0 + u * LCH;
-        if (c >= end) break;
-        LinRows& cur = u == 0 ? v0 : v1;
-        LinRows& nxt = u == 0 ? v1 : v0;
-        const bool more = c + LCH < end;
-        if (more) {
-          st.load(src(c + LCH), tid);
-          dma_lin_v<W>(nxt, src(c + LCH), lane);
-        }
-        lin_state_update<W>(acc, kr, cur, to, bones);
-        barrier_lds();
-        if (more) {
-          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-          st.store(kr, nullptr, tid, end - (c + LCH), a.shift);
-        }
-        barrier_lds();
-      }
-    }
-    float* dst = a.ws + (bh * a.n_spans + sp) * kLinStateFloats;
-#pragma unroll
-    for (int i = 0; i < NDT; ++i) *reinterpret_cast<f32x4*>(&dst[lin_state_off(W, i, lane)]) = acc[i];
-  });
-}
-
-// the bf16 state copy [value row][feature] for the readout: rows 0..63 are
-// S^T, row 64 is z, row 65 stays zero
-template <int W>
-__device__ __forceinline__ void lin_write_sb(uint16_t* sb, const f32x4 (&acc)[NDT], int lane) {
-  const int g = lane >> 4, r = lane & 15;
-#pragma unroll
-  for (int i = 0; i < NDT - 1; ++i) {
-    uint2 x;
-    x.x = pack2(acc[i][0], acc[i][1]);
-    x.y = pack2(acc[i][2], acc[i][3]);
-    *reinterpret_cast<uint2*>(&sb[(16 * i + r) * LSB + 16 * W + 4 * g]) = x;
-  }
-  if (r == 0) {
-    uint2 x;
-    x.x = pack2(acc[NDT - 1][0], acc[NDT - 1][1]);
-    x.y = pack2(acc[NDT - 1][2], acc[NDT - 1][3]);
-    *reinterpret_cast<uint2*>(&sb[DV * LSB + 16 * W + 4 * g]) = x;
-  }
-}
-
-template <int FEAT>
-__global__ __launch_bounds__(256, 2) void lin_readout_kernel(LinArgs a) {
-  __shared__ LinRows kr;
-  __shared__ LinRows qr;
-  __shared__ LinRows v0;
-  __shared__ LinRows v1;
-  __shared__ alignas(16) uint16_t sb[(DV + 2) * LSB];
-  __shared__ alignas(16) uint16_t ones[128];
-  __shared__ alignas(16) uint16_t Ob[4][16 * OB_LD];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x / a.n_spans;
-  const int64_t sp = blockIdx.x - bh * a.n_spans;
-  const int64_t tok0 = bh * a.T;
-  const int64_t first = sp * a.G * LCH;
-  const int64_t end = (a.T < first + a.G * LCH) ? a.T : first + a.G * LCH;
-  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
-  if (tid < LSB / 8) *reinterpret_cast<uint4*>(&sb[(DV + 1) * LSB + 8 * tid]) = make_uint4(0, 0, 0, 0);
-
-  with_wave<4>(w, [&](auto wc) {
-    constexpr int W = decltype(wc)::value;
-    const int g = lane >> 4, r = lane & 15;
-    bool keep[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) keep[j] = 4 * g + j <= r;
-    const TrOffsets to = tr_offsets(lane);
-    f32x4 acc[NDT];
-    if (a.n_spans > 1) {
-      const float* P = a.ws + (bh * a.n_spans + sp) * kLinStateFloats;
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) acc[i] = *reinterpret_cast<const f32x4*>(&P[lin_state_off(W, i, lane)]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    auto src = [&](int64_t c0) { return chunk_src<64, LCH>(a.q, a.k, a.v, tok0, c0, end); };
-    LinStage<FEAT, true> st;
-    st.load(src(first), tid);
-    dma_lin_v<W>(v0, src(first), lane);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    lin_write_sb<W>(sb, acc, lane);
-    st.store(kr, &qr, tid, end - first, a.shift);
-    __syncthreads();
-    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[(r > 0 ? 64 : 0) + 8 * g]);
-    uint16_t* ob = Ob[W];
-    for (int64_t c0 = first; c0 < end; c0 += 2 * LCH) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t c = c0 + u * LCH;
-        if (c >= end) break;
-        LinRows& cur = u == 0 ? v0 : v1;
-        LinRows& nxt = u == 0 ? v1 : v0;
-        const bool more = c + LCH < end;
-        // the query tile's operands, then the next chunk's loads
-        u32x4 qop[2];
-#pragma unroll
-        for (int kf = 0; kf < 2; ++kf) qop[kf] = lin_row_op(qr.r, 16 * W + r, kf, g);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) {
-          st.load(src(c + LCH), tid);
-          dma_lin_v<W>(nxt, src(c + LCH), lane);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // inter-chunk term: [S|z]^T psi(Q)^T
-        f32x4 o[NDT];
-#pragma unroll
-        for (int i = 0; i < NDT; ++i) {
-          o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kf = 0; kf < 2; ++kf) {
-            const u32x4 as = *reinterpret_cast<const u32x4*>(&sb[vrow(i, r) * LSB + 32 * kf + 8 * g]);
-            o[i] = mfma(as, qop[kf], o[i]);
-          }
-        }
-        // intra-chunk term over the key steps up to the diagonal, and the
-        // state update over the whole chunk
-#pragma unroll
-        for (int s = 0; s < LCH / 32; ++s) {
-          u32x4 bv[NDT];
-#pragma unroll
-          for (int i = 0; i < NDT - 1; ++i) bv[i] = tr_operand<DV>(cur.r, to.v[i], s);
-          bv[NDT - 1] = bones;
-          if (2 * s <= W) {
-            float p[2][4];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int kt = 2 * s + h;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
-              if (kt > W) continue;
-              f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int kf = 0; kf < 2; ++kf) sc = mfma(lin_row_op(kr.r, 16 * kt + r, kf, g), qop[kf], sc);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) p[h][j] = (kt < W || keep[j]) ? sc[j] : 0.f;
-            }
-            const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
-                              pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
-#pragma unroll
-            for (int i = 0; i < NDT; ++i) o[i] = mfma(bv[i], pf, o[i]);
-          }
-          const u32x4 ak = tr_operand<64>(kr.r, to.v[W], s);
-#pragma unroll
-          for (int i = 0; i < NDT; ++i) acc[i] = mfma(ak, bv[i], acc[i]);
-        }
-        // normalise, stage the 16 x 64 tile, store it as 1 KB of rows
-        {
-          const __amdgpu_buffer_rsrc_t dst = rows_rsrc(a.out, tok0 + c, end - c < LCH ? end - c : LCH, 2 * DV);
-          const float den = __shfl(o[NDT - 1][0], r);
-          const float inv = __builtin_amdgcn_rcpf(den + a.eps);
-#pragma unroll
-          for (int i = 0; i < NDT - 1; ++i) {
-            uint2 x;
-            x.x = pack2(o[i][0] * inv, o[i][1] * inv);
-            x.y = pack2(o[i][2] * inv, o[i][3] * inv);
-            *reinterpret_cast<uint2*>(&ob[r * OB_LD + 16 * i + 4 * g]) = x;
-          }
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int row = 8 * h + (lane >> 3);
-            const uint4 x = *reinterpret_cast<const uint4*>(&ob[row * OB_LD + 8 * (lane & 7)]);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, dst,
-                                                   (16 * W + row) * (2 * DV) + 16 * (lane & 7), 0, 0);
-          }
-        }
-        barrier_lds();
-        if (more) {
-          lin_write_sb<W>(sb, acc, lane);
-          __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-          st.store(kr, &qr, tid, end - (c + LCH), a.shift);
-        }
-        barrier_lds();
-      }
-    }
-  });
-}
-
 template <int DK, int C>
 hipError_t launch_span(const MfmaArgs& a, hipStream_t stream) {
   using CF = Cfg<DK, C>;
@@ -2143,53 +1378,6 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 32 && a.chunk == 128) return launch_span<32, 128>(a, stream);
   if (a.d == 64 && a.chunk == 64) return launch_span<64, 64>(a, stream);
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_forward_quadratic_mfma(const QuadArgs& a, hipStream_t stream) {
-  const int64_t nqb = (a.T + QB - 1) / QB;
-  dim3 grid(static_cast<unsigned>(a.BH * nqb));
-  const int m = a.g > 0 ? a.d / a.g : 0;
-  if (a.d == 16 && m == 16) {
-    quad_kernel<16, 16><<<grid, 256, 0, stream>>>(a);
-  } else if (a.d == 32 && m == 32) {
-    quad_kernel<32, 32><<<grid, 256, 0, stream>>>(a);
-  } else if (a.d == 32 && m == 16) {
-    quad_kernel<32, 16><<<grid, 256, 0, stream>>>(a);
-  } else if (a.d == 64 && m == 64) {
-    quad_kernel<64, 64><<<grid, 256, 0, stream>>>(a);
-  } else if (a.d == 64 && m == 32) {
-    quad_kernel<64, 32><<<grid, 256, 0, stream>>>(a);
-  } else if (a.d == 64 && m == 16) {
-    quad_kernel<64, 16><<<grid, 256, 0, stream>>>(a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_linear_span_state(const LinArgs& a, hipStream_t stream) {
-  if (a.n_spans < 2) return hipSuccess;
-  dim3 grid(static_cast<unsigned>(a.BH * (a.n_spans - 1)));
-  if (a.feature == kLinFeatOrthant) {
-    lin_span_kernel<kLinFeatOrthant><<<grid, 256, 0, stream>>>(a);
-  } else if (a.feature == kLinFeatLorentz) {
-    lin_span_kernel<kLinFeatLorentz><<<grid, 256, 0, stream>>>(a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_linear_readout(const LinArgs& a, hipStream_t stream) {
-  dim3 grid(static_cast<unsigned>(a.BH * a.n_spans));
-  if (a.feature == kLinFeatOrthant) {
-    lin_readout_kernel<kLinFeatOrthant><<<grid, 256, 0, stream>>>(a);
-  } else if (a.feature == kLinFeatLorentz) {
-    lin_readout_kernel<kLinFeatLorentz><<<grid, 256, 0, stream>>>(a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 hipError_t launch_span_state_gated(const MfmaArgs& a, hipStream_t stream) {

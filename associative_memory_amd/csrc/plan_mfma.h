@@ -1,5 +1,7 @@
 // Interface of the matrix-core chunked forward (bf16, dv = 64, head dim 16 or
-// 32, chunk 64 or 128).  See forward_mfma.hip for the kernel design.
+// 32, chunk 64 or 128), the quadratic form, the linear cone features and the
+// gated read.  The kernels are in forward_mfma.hip, forward_quadratic.hip and
+// forward_linear.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>
