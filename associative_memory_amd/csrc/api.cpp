@@ -324,7 +324,7 @@ kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const 
 
 size_t kata_forward_chunked_blocks_workspace_bytes(int B, int H, int64_t T, int d, int dv, int g,
                                                    int chunk, kata_scan_t scan) {
-  if (g == 1) return kata_forward_workspace_bytes(B, H, T, d, dv, chunk, scan);
+  if (g == 1 && d != 64) return kata_forward_workspace_bytes(B, H, T, d, dv, chunk, scan);
   if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0 || g <= 0 || d % g != 0) return 0;
   if (scan != KATA_SCAN_AUTO && scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE) return 0;
   if (!kata::block_map_supported(true, d, dv, g, chunk)) return 0;
@@ -336,7 +336,7 @@ kata_status_t kata_forward_chunked_blocks(const void* q, const void* k, const vo
                                           int B, int H, int64_t T, int d, int dv, int g, int chunk,
                                           float eps, kata_dtype_t dtype, kata_scan_t scan,
                                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (g == 1)
+  if (g == 1 && d != 64)
     return kata_forward_chunked(q, k, v, out, B, H, T, d, dv, chunk, eps, dtype, scan, workspace,
                                 workspace_bytes, stream);
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;

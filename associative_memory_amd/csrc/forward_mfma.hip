@@ -38,18 +38,115 @@ namespace {
 
 // ------------------------------------------------------------ feature schedule
 
-// DK = 64 is the KATA-M4 block map (Sec. 4.1): four blocks of 16 dimensions,
-// the 136 pairs of one block per lane group (group g holds block g, the
-// rotation by SH = 16 below), 544 feature positions; only pairs inside a
-// block carry features, and the score is sum_a (q_a . k_a)^2.
+// Feature maps of the chunked read are keyed by an id FM (the schedule,
+// configuration and kernels below take it where a head width would be):
+//   16, 32   the full rank-one map at d = 16, 32;
+//   64       KATA-M4 at d = 64 (Sec. 4.1): four blocks of 16 dimensions, the
+//            136 pairs of one block per lane group (group g holds block g,
+//            the rotation by SH = 16 below), 544 feature positions; only pairs
+//            inside a block carry features, the score is sum_a (q_a . k_a)^2;
+//   100 + s  slice s (0..3) of the full map at d = 64 (KATA-M1): the orbits of
+//            its 2,080 pairs under the rotation, 136 per slice;
+//   200 + s  slice s (0..1) of KATA-M2 at d = 64 (two blocks of 32).  Q and K
+//            are staged with dimension quarters 1 and 2 swapped, so the blocks
+//            sit on staged quarters {0, 2} and {1, 3} and the rotation by 16
+//            per lane group maps each block onto the other.
+// A sliced map keeps each slice's state in its own workgroups; the slices run
+// one after another and add their partial reads (fp32) before normalising.
+constexpr int fm_dk(int fm) { return fm < 64 ? fm : 64; }
+constexpr int fm_family(int fm) { return fm < 100 ? fm : (fm / 100) * 100; }
+constexpr int fm_slice(int fm) { return fm < 100 ? 0 : fm % 100; }
+constexpr int fm_slices(int fm) { return fm_family(fm) == 100 ? 4 : (fm_family(fm) == 200 ? 2 : 1); }
+
 template <int DK>
 constexpr bool kBlockMap = DK == 64;
 
+// staged position of dimension x (KATA-M2 swaps quarters 1 and 2)
+template <int FM>
+constexpr int staged_dim(int x) {
+  if constexpr (fm_family(FM) == 200) {
+    const int q = x >> 4;
+    return ((q == 1 ? 2 : (q == 2 ? 1 : q)) << 4) | (x & 15);
+  } else {
+    return x;
+  }
+}
+
+// orbit representatives of the pairs (i <= j, staged frame) of the d = 64
+// sliced maps under the shift by 16 per lane group, size-4 orbits first:
+// all pairs (KATA-M1) or the pairs inside a block (KATA-M2: blocks are the
+// staged quarters of equal parity)
+template <int FAM>
+struct Orbits64 {
+  int n4 = 0, n = 0;
+  int8_t a[1056] = {};
+  int8_t b[1056] = {};
+  bool pair2[1056] = {};
+};
+
+template <int FAM>
+constexpr Orbits64<FAM> make_orbits64() {
+  Orbits64<FAM> o;
+  bool used[64][64] = {};
+  int n4 = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int i = 0; i < 64; ++i) {
+      for (int j = i; j < 64; ++j) {
+        if (FAM == 200 && ((i >> 4) & 1) != ((j >> 4) & 1)) continue;
+        if (used[i][j]) continue;
+        int size = 0;
+        bool mark[4][2] = {};
+        for (int g = 0; g < 4; ++g) {
+          int x = (i + 16 * g) % 64, y = (j + 16 * g) % 64;
+          if (x > y) { const int t = x; x = y; y = t; }
+          bool dup = false;
+          for (int h = 0; h < g; ++h) {
+            int u = (i + 16 * h) % 64, w = (j + 16 * h) % 64;
+            if (u > w) { const int t = u; u = w; w = t; }
+            if (u == x && w == y) dup = true;
+          }
+          if (!dup) ++size;
+        }
+        if ((pass == 0) != (size == 4)) continue;
+        for (int g = 0; g < 4; ++g) {
+          int x = (i + 16 * g) % 64, y = (j + 16 * g) % 64;
+          if (x > y) { const int t = x; x = y; y = t; }
+          used[x][y] = true;
+        }
+        o.a[o.n] = static_cast<int8_t>(i);
+        o.b[o.n] = static_cast<int8_t>(j);
+        o.pair2[o.n] = size == 2;
+        ++o.n;
+        if (size == 4) ++n4;
+        (void)mark;
+      }
+    }
+  }
+  o.n4 = n4;
+  return o;
+}
+
+template <int FAM>
+constexpr Orbits64<FAM> kOrbits64 = make_orbits64<FAM>();
+
+template <int FM>
+constexpr int slice_entries() {
+  if constexpr (FM >= 100) {
+    constexpr int total = kOrbits64<fm_family(FM)>.n;
+    constexpr int first = 136 * fm_slice(FM);
+    return total - first < 136 ? total - first : 136;
+  } else {
+    return 0;
+  }
+}
+
 template <int DK>
 struct Schedule {
-  static constexpr int SH = DK / 4;  // index shift per lane group
-  // orbit representatives (block map: the pairs of one block)
-  static constexpr int NE = kBlockMap<DK> ? 16 * 17 / 2 : (DK * (DK + 1) / 2 - DK / 2) / 4 + DK / 4;
+  static constexpr int SH = fm_dk(DK) / 4;  // index shift per lane group
+  // orbit representatives (block map: the pairs of one block; slices: the
+  // slice's share of the orbit list)
+  static constexpr int NE = DK >= 100 ? slice_entries<DK>()
+                            : kBlockMap<DK> ? 16 * 17 / 2 : (DK * (DK + 1) / 2 - DK / 2) / 4 + DK / 4;
   static constexpr int NKS = (NE + 7) / 8;                              // 32-wide feature k-steps
   static constexpr int NPOS = 32 * NKS;                                 // feature positions
   int8_t a[8 * NKS];
@@ -61,7 +158,14 @@ template <int DK>
 constexpr Schedule<DK> make_schedule() {
   Schedule<DK> s{};
   constexpr int SH = Schedule<DK>::SH;
-  if constexpr (kBlockMap<DK>) {
+  if constexpr (DK >= 100) {
+    constexpr auto& o = kOrbits64<fm_family(DK)>;
+    for (int e = 0; e < Schedule<DK>::NE; ++e) {
+      s.a[e] = o.a[136 * fm_slice(DK) + e];
+      s.b[e] = o.b[136 * fm_slice(DK) + e];
+      s.pair2[e] = o.pair2[136 * fm_slice(DK) + e];
+    }
+  } else if constexpr (kBlockMap<DK>) {
     int e = 0;
     for (int i = 0; i < 16; ++i) {
       for (int j = i; j < 16; ++j, ++e) {
@@ -114,6 +218,12 @@ constexpr Schedule<DK> kSched = make_schedule<DK>();
 __constant__ Schedule<16> kSchedDev16 = make_schedule<16>();
 __constant__ Schedule<32> kSchedDev32 = make_schedule<32>();
 __constant__ Schedule<64> kSchedDev64 = make_schedule<64>();
+__constant__ Schedule<100> kSchedDev100 = make_schedule<100>();
+__constant__ Schedule<101> kSchedDev101 = make_schedule<101>();
+__constant__ Schedule<102> kSchedDev102 = make_schedule<102>();
+__constant__ Schedule<103> kSchedDev103 = make_schedule<103>();
+__constant__ Schedule<200> kSchedDev200 = make_schedule<200>();
+__constant__ Schedule<201> kSchedDev201 = make_schedule<201>();
 
 template <int DK>
 constexpr bool schedule_ok() {
@@ -153,6 +263,28 @@ static_assert(schedule_ok<16>(), "d = 16 feature schedule must cover every pair 
 static_assert(schedule_ok<32>(), "d = 32 feature schedule must cover every pair once");
 static_assert(block_schedule_ok<64>(), "KATA-M4 schedule must cover every in-block pair once");
 
+// sliced maps: the slices together cover every allowed pair once
+template <int FAM>
+constexpr bool sliced_ok() {
+  constexpr auto& o = kOrbits64<FAM>;
+  bool seen[64][64] = {};
+  int n = 0;
+  for (int e = 0; e < o.n; ++e) {
+    for (int g = 0; g < (o.pair2[e] ? 2 : 4); ++g) {
+      int x = (o.a[e] + 16 * g) % 64, y = (o.b[e] + 16 * g) % 64;
+      if (x > y) { const int t = x; x = y; y = t; }
+      if (seen[x][y]) return false;
+      if (FAM == 200 && ((x >> 4) & 1) != ((y >> 4) & 1)) return false;
+      seen[x][y] = true;
+      ++n;
+    }
+  }
+  if (FAM == 100) return n == 2080 && o.n == 528 && o.n4 == 512 && o.n <= 136 * 4;
+  return n == 1056 && o.n == 272 && o.n4 == 256 && o.n <= 136 * 2;
+}
+static_assert(sliced_ok<100>(), "KATA-M1 slices must cover every pair once");
+static_assert(sliced_ok<200>(), "KATA-M2 slices must cover every in-block pair once");
+
 // number of 16-position feature tiles holding at least one feature
 template <int DK>
 constexpr int feature_tiles() {
@@ -173,8 +305,20 @@ __device__ __forceinline__ const Schedule<DK>& sched_dev() {
     return kSchedDev16;
   } else if constexpr (DK == 32) {
     return kSchedDev32;
-  } else {
+  } else if constexpr (DK == 64) {
     return kSchedDev64;
+  } else if constexpr (DK == 100) {
+    return kSchedDev100;
+  } else if constexpr (DK == 101) {
+    return kSchedDev101;
+  } else if constexpr (DK == 102) {
+    return kSchedDev102;
+  } else if constexpr (DK == 103) {
+    return kSchedDev103;
+  } else if constexpr (DK == 200) {
+    return kSchedDev200;
+  } else {
+    return kSchedDev201;
   }
 }
 
@@ -185,21 +329,23 @@ __device__ __forceinline__ void pair_at(int p, int& a, int& b) {
   const int ks = p >> 5, o = p & 31, g = o >> 3, i = o & 7;
   const int e = 8 * ks + i;
   if (e >= Schedule<DK>::NE || (s.pair2[e] && g >= 2)) { a = -1; b = -1; return; }
-  a = (s.a[e] + Schedule<DK>::SH * g) % DK;
-  b = (s.b[e] + Schedule<DK>::SH * g) % DK;
+  a = (s.a[e] + Schedule<DK>::SH * g) % fm_dk(DK);
+  b = (s.b[e] + Schedule<DK>::SH * g) % fm_dk(DK);
 }
 
 // ------------------------------------------------------------ configuration
 
-template <int DK_, int C_>
+template <int FM_, int C_>
 struct Cfg {
-  static constexpr int DK = DK_;
+  static constexpr int FM = FM_;           // feature map id
+  static constexpr int DK = fm_dk(FM_);    // head width
+  static constexpr int NSL = fm_slices(FM_), SLICE = fm_slice(FM_);
   static constexpr int C = C_;
-  static constexpr int NW = mfma_waves(DK_);  // waves per workgroup
+  static constexpr int NW = mfma_waves(DK);  // waves per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr int NKS = Schedule<DK>::NKS;
-  static constexpr int NPOS = Schedule<DK>::NPOS;
-  static constexpr int NFT = mfma_feature_tiles(DK_);
+  static constexpr int NKS = Schedule<FM>::NKS;
+  static constexpr int NPOS = Schedule<FM>::NPOS;
+  static constexpr int NFT = FM_ < 100 ? mfma_feature_tiles(DK) : feature_tiles<FM_>();
   static constexpr int MFT = (NFT + NW - 1) / NW;   // feature tiles per wave (max)
   static constexpr int SB_LD = NPOS + 8;            // bf16 row stride of the state copy
   static constexpr int QF_LD = DK + 4;              // fp32 row stride of Q
@@ -248,8 +394,14 @@ struct ScoreOpT<64> {  // KATA-M4: one 16x16x16 operand per block
     uint2 p[4];
   };
 };
-template <int DK>
-using ScoreOp = typename ScoreOpT<DK>::type;
+template <>
+struct ScoreOpT<100> {  // d = 64 sliced maps: two 16x16x32 operands
+  struct type {
+    u32x4 p[2];
+  };
+};
+template <int FM>
+using ScoreOp = typename ScoreOpT<(FM >= 100 ? 100 : FM)>::type;
 
 // position of the first of 4 consecutive tokens (group tg) inside a chunk:
 // within each 32-token block, token groups 0..3 sit at 8a, groups 4..7 at
@@ -287,10 +439,32 @@ struct alignas(16) SmemOut : Tiles<CF> {
 };
 
 // score operand of row `row` from the fp32 Q tile / the bf16 K tile
+// first staged dimension of piece j of lane group g: the full map at d = 64
+// takes 32-dimension pieces; KATA-M2 takes block j's 8 dimensions of group g
+// (staged quarters j and j + 2)
+template <int FM>
+__device__ __forceinline__ int piece_dim(int j, int g) {
+  if constexpr (fm_family(FM) == 200) {
+    return 16 * (j + 2 * (g >> 1)) + 8 * (g & 1);
+  } else {
+    return 32 * j + 8 * g;
+  }
+}
+
 template <class CF>
-__device__ __forceinline__ ScoreOp<CF::DK> score_operand(const float* Qf, int row, int g) {
-  if constexpr (kBlockMap<CF::DK>) {
-    ScoreOp<CF::DK> op;
+__device__ __forceinline__ ScoreOp<CF::FM> score_operand(const float* Qf, int row, int g) {
+  if constexpr (CF::FM >= 100) {
+    ScoreOp<CF::FM> op;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float* q = &Qf[row * CF::QF_LD + piece_dim<CF::FM>(j, g)];
+      const float4 x0 = *reinterpret_cast<const float4*>(q);
+      const float4 x1 = *reinterpret_cast<const float4*>(q + 4);
+      op.p[j] = u32x4{pack2(x0.x, x0.y), pack2(x0.z, x0.w), pack2(x1.x, x1.y), pack2(x1.z, x1.w)};
+    }
+    return op;
+  } else if constexpr (kBlockMap<CF::FM>) {
+    ScoreOp<CF::FM> op;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const float4 x = *reinterpret_cast<const float4*>(&Qf[row * CF::QF_LD + 16 * a + 4 * g]);
@@ -309,9 +483,14 @@ __device__ __forceinline__ ScoreOp<CF::DK> score_operand(const float* Qf, int ro
 }
 
 template <class CF>
-__device__ __forceinline__ ScoreOp<CF::DK> score_operand_bf16(const uint16_t* Kb, int row, int g) {
-  if constexpr (kBlockMap<CF::DK>) {
-    ScoreOp<CF::DK> op;
+__device__ __forceinline__ ScoreOp<CF::FM> score_operand_bf16(const uint16_t* Kb, int row, int g) {
+  if constexpr (CF::FM >= 100) {
+    ScoreOp<CF::FM> op;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) op.p[j] = *reinterpret_cast<const u32x4*>(&Kb[row * CF::KB_LD + piece_dim<CF::FM>(j, g)]);
+    return op;
+  } else if constexpr (kBlockMap<CF::FM>) {
+    ScoreOp<CF::FM> op;
 #pragma unroll
     for (int a = 0; a < 4; ++a) op.p[a] = *reinterpret_cast<const uint2*>(&Kb[row * CF::KB_LD + 16 * a + 4 * g]);
     return op;
@@ -403,11 +582,13 @@ struct Stage {
       const int pos = group_pos(t >> 2) + (t & 3);
 #pragma unroll
       for (int x = 0; x < DK; ++x) {
-        sm.Kt[x * LDK + pos] = kSqrt2 * ((x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]));
+        sm.Kt[staged_dim<CF::FM>(x) * LDK + pos] = kSqrt2 * ((x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]));
       }
       if constexpr (WITH_Q) {
 #pragma unroll
-        for (int u = 0; u < RW; ++u) *reinterpret_cast<uint4*>(&sm.Kb[t * CF::KB_LD + 8 * u]) = kq[u];
+        for (int u = 0; u < RW; ++u) {
+          *reinterpret_cast<uint4*>(&sm.Kb[t * CF::KB_LD + staged_dim<CF::FM>(8 * u)]) = kq[u];
+        }
       }
     } else if (WITH_Q && tid < 2 * C) {
       if constexpr (WITH_Q) {
@@ -419,7 +600,7 @@ struct Stage {
           f.y = hi_bf16(w[2 * c]);
           f.z = lo_bf16(w[2 * c + 1]);
           f.w = hi_bf16(w[2 * c + 1]);
-          *reinterpret_cast<float4*>(&sm.Qf[t * CF::QF_LD + 4 * c]) = f;
+          *reinterpret_cast<float4*>(&sm.Qf[t * CF::QF_LD + staged_dim<CF::FM>(4 * c)]) = f;
         }
       }
     }
@@ -454,7 +635,7 @@ __device__ __forceinline__ KeyPairs<CF> key_pairs(int w, int r) {
   for (int m = 0; m < CF::MFT; ++m) {
     const int ft = w + CF::NW * m;
     int a = -1, b = -1;
-    if (ft < CF::NFT) pair_at<CF::DK>(16 * ft + r, a, b);
+    if (ft < CF::NFT) pair_at<CF::FM>(16 * ft + r, a, b);
     // an empty position reads the zero row of K^T: its features are 0
     kp.a[m] = a < 0 ? CF::DK : a;
     kp.b[m] = b < 0 ? CF::DK : b;
@@ -931,16 +1112,24 @@ struct TileSrc {
   __device__ __forceinline__ float4 qrow4(int row, int c4) const {
     return *reinterpret_cast<const float4*>(&tl.Qf[row * CF::QF_LD + 4 * c4]);
   }
-  __device__ __forceinline__ ScoreOp<CF::DK> score_q(int row, int g) const {
+  __device__ __forceinline__ ScoreOp<CF::FM> score_q(int row, int g) const {
     return score_operand<CF>(tl.Qf, row, g);
   }
-  __device__ __forceinline__ ScoreOp<CF::DK> score_k(int row, int g) const {
+  __device__ __forceinline__ ScoreOp<CF::FM> score_k(int row, int g) const {
     return score_operand_bf16<CF>(tl.Kb, row, g);
   }
   __device__ __forceinline__ u32x4 v_op(int vt, int s, int lane) const {
     const int g = lane >> 4, r = lane & 15;
     return *reinterpret_cast<const u32x4*>(&tl.Vt[vrow(vt, r) * CF::LDT + 32 * s + 8 * g]);
   }
+};
+
+// fp32 partial reads of a sliced feature map: rows of PART_LD floats (64
+// value columns, the denominator, padding) for the chunk's tokens
+constexpr int PART_LD = 68;
+struct NoPart {};
+struct PartRows {
+  __amdgpu_buffer_rsrc_t r;
 };
 
 // `after_q` runs once the query rows are in registers (the DMA readout issues
@@ -950,16 +1139,20 @@ struct TileSrc {
 // (log2 units).  The inter term of query t is 2^beta_t phi(q_t) S, so the
 // query row is scaled by 2^(beta_t / 2); the intra score of key s is weighted
 // by 2^(beta_t - beta_s); there is no denominator.
-template <class CF, class S, class H = NoHook, bool G = false>
+//
+// Sliced maps (CF::NSL > 1): the first slice also carries the intra-chunk
+// term; each slice adds its read to the fp32 partial rows `part` (the first
+// writes them), and the last normalises and stores the output.
+template <class CF, class S, class H = NoHook, bool G = false, class P = NoPart>
 __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __restrict__ Sb,
                                               const ReadoutLane<CF>& L, int lane, float eps,
                                               __amdgpu_buffer_rsrc_t dst, uint16_t* __restrict__ ob_tile,
-                                              const H& after_q = H{}) {
-  constexpr int C = CF::C, DK = CF::DK, NSLOT = CF::NSLOT, NDW = CF::NDW;
+                                              const H& after_q = H{}, const P& part = P{}) {
+  constexpr int C = CF::C, DK = CF::DK, FM = CF::FM, NSLOT = CF::NSLOT, NDW = CF::NDW;
   constexpr int SB_LD = CF::SB_LD;
   static_assert(!G || NDW == NDT, "the gated read uses whole output rows");
   constexpr int NO = G ? NDW - 1 : NDW;  // value tiles read out (gated: no denominator)
-  constexpr int SH = Schedule<DK>::SH;
+  constexpr int SH = Schedule<FM>::SH;
   const int g = lane >> 4, r = lane & 15;
   const int qt_max = L.qt[NSLOT - 1] > L.qt[0] ? L.qt[NSLOT - 1] : L.qt[0];
 
@@ -1006,10 +1199,10 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int e = 8 * ks + i;
-        if (e >= Schedule<DK>::NE) {
+        if (e >= Schedule<FM>::NE) {
           f[i] = 0.f;
         } else {
-          const int pa = kSched<DK>.a[e], pb = kSched<DK>.b[e];
+          const int pa = kSched<FM>.a[e], pb = kSched<FM>.b[e];
           f[i] = (pa == pb) ? (0.5f * qr[slot][pa]) * qr[slot][pa] : qr[slot][pa] * qr[slot][pb];
         }
       }
@@ -1020,13 +1213,14 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
   }
   // intra-chunk term: squared causal scores.  The score product has K = d:
   // one 16x16x16 product at d = 16, one 16x16x32 product at d = 32.
-  ScoreOp<DK> qf[NSLOT];
+  if constexpr (CF::SLICE == 0) {
+  ScoreOp<FM> qf[NSLOT];
 #pragma unroll
   for (int slot = 0; slot < NSLOT; ++slot) qf[slot] = src.score_q(16 * L.qt[slot] + r, g);
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
     if (2 * s > qt_max) break;
-    ScoreOp<DK> kf[2];
+    ScoreOp<FM> kf[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) kf[h] = src.score_k(16 * (2 * s + h) + r, g);
     u32x4 bv[NDW];
@@ -1043,7 +1237,17 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
         for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
         if (kt > L.qt[slot]) continue;  // fully masked tile: uniform per wave
         f32x4 sc;  // [key 4g+j][query r]
-        if constexpr (kBlockMap<DK>) {
+        if constexpr (fm_family(FM) == 100) {
+          // full map at d = 64: two chained 16x16x32 products
+          sc = mfma(kf[h].p[0], qf[slot].p[0], f32x4{0.f, 0.f, 0.f, 0.f});
+          sc = mfma(kf[h].p[1], qf[slot].p[1], sc);
+        } else if constexpr (fm_family(FM) == 200) {
+          // KATA-M2: one product per block, squares summed, kept as the root
+          const f32x4 b0 = mfma(kf[h].p[0], qf[slot].p[0], f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 b1 = mfma(kf[h].p[1], qf[slot].p[1], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sc[j] = __builtin_sqrtf(__builtin_fmaf(b0[j], b0[j], b1[j] * b1[j]));
+        } else if constexpr (kBlockMap<FM>) {
           // sum over the blocks of the squared block scores, kept as its root
           // so the squaring below is shared with the other maps
           f32x4 sq = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1078,6 +1282,41 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
                         pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
 #pragma unroll
       for (int i = 0; i < NO; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
+    }
+  }
+  }  // intra-chunk term
+  if constexpr (CF::NSL > 1) {
+    // partial reads: value columns 16 vt + 4g + j and (ones-column tile,
+    // lanes of group 0) the denominator of query r.  With two waves sharing a
+    // query tile, the one holding value tile 0 owns the denominator.
+    static_assert(NDW < NDT && NSLOT == 1, "sliced maps use the 8-wave chunk-64 split");
+    const bool own_den = L.vt[0] == 0 && g == 0;
+    const int row = 16 * L.qt[0] + r;
+    if constexpr (CF::SLICE > 0) {
+#pragma unroll
+      for (int i = 0; i < NDW; ++i) {
+        if (L.vt[i] == NDT - 1) {
+          const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part.r, (row * PART_LD + DV) * 4, 0, 0));
+          if (own_den || CF::SLICE == CF::NSL - 1) o[0][i][0] += g == 0 ? x : 0.f;
+        } else {
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(part.r, (row * PART_LD + 16 * L.vt[i] + 4 * g) * 4, 0, 0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[0][i][j] += __uint_as_float(x[j]);
+        }
+      }
+    }
+    if constexpr (CF::SLICE < CF::NSL - 1) {
+#pragma unroll
+      for (int i = 0; i < NDW; ++i) {
+        if (L.vt[i] == NDT - 1) {
+          if (own_den) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[0][i][0]), part.r, (row * PART_LD + DV) * 4, 0, 0);
+        } else {
+          const u32x4 x = {__float_as_uint(o[0][i][0]), __float_as_uint(o[0][i][1]), __float_as_uint(o[0][i][2]),
+                           __float_as_uint(o[0][i][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(x, part.r, (row * PART_LD + 16 * L.vt[i] + 4 * g) * 4, 0, 0);
+        }
+      }
+      return;
     }
   }
   // normalise and store: lane r of group 0 holds the denominator of query r
@@ -1166,8 +1405,14 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
       // the next chunk's loads go out first, to overlap this chunk's compute
       if (c0 + C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + C, a.T), tid);
       const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
-      readout_chunk<CF>(TileSrc<CF>{sm}, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV),
-                        sm.Ob[CF::NDW == NDT ? W : 0]);
+      if constexpr (CF::NSL > 1) {
+        readout_chunk<CF, TileSrc<CF>, NoHook, false, PartRows>(
+            TileSrc<CF>{sm}, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV), sm.Ob[0], NoHook{},
+            PartRows{rows_rsrc(a.part, tok0 + c0, n, PART_LD * 4)});
+      } else {
+        readout_chunk<CF>(TileSrc<CF>{sm}, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV),
+                          sm.Ob[CF::NDW == NDT ? W : 0]);
+      }
       if (c0 + C >= end) break;
       // carry the state across the chunk
       state_update<CF>(acc, sm, W, lane, kp);
@@ -1372,6 +1617,17 @@ hipError_t launch_readout(const MfmaArgs& a, hipStream_t stream) {
 
 hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.n_spans < 2) return hipSuccess;
+  if (a.fm >= 100 && a.chunk == 64) {
+    switch (a.fm) {
+      case 100: return launch_span<100, 64>(a, stream);
+      case 101: return launch_span<101, 64>(a, stream);
+      case 102: return launch_span<102, 64>(a, stream);
+      case 103: return launch_span<103, 64>(a, stream);
+      case 200: return launch_span<200, 64>(a, stream);
+      case 201: return launch_span<201, 64>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (a.d == 16 && a.chunk == 64) return launch_span<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_span<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) return launch_span<32, 64>(a, stream);
@@ -1406,6 +1662,17 @@ hipError_t launch_readout_gated(const MfmaArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream) {
+  if (a.fm >= 100 && a.chunk == 64) {
+    switch (a.fm) {
+      case 100: return launch_readout<100, 64>(a, stream);
+      case 101: return launch_readout<101, 64>(a, stream);
+      case 102: return launch_readout<102, 64>(a, stream);
+      case 103: return launch_readout<103, 64>(a, stream);
+      case 200: return launch_readout<200, 64>(a, stream);
+      case 201: return launch_readout<201, 64>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (a.d == 16 && a.chunk == 64) return launch_readout<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_readout<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) return launch_readout<32, 64>(a, stream);

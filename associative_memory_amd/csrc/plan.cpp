@@ -29,7 +29,12 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.D = d * (d + 1) / 2;
   p.bf16 = dtype == KATA_BF16;
   p.n_chunks = ceil_div(T, chunk);
-  const bool mfma = mfma_supported(p.bf16, d, dv, chunk) || (g > 1 && block_map_supported(p.bf16, d, dv, g, chunk));
+  const bool blocks = d == 64 && block_map_supported(p.bf16, d, dv, g, chunk);
+  const bool mfma = mfma_supported(p.bf16, d, dv, chunk) || blocks;
+  if (blocks && g != 4) {
+    p.nsl = g == 1 ? 4 : 2;
+    p.fm_base = g == 1 ? 100 : 200;
+  }
   p.path = mfma ? Path::Mfma : Path::Valu;
   p.E = mfma ? mfma_state_floats(d) : static_cast<int64_t>(p.D) * dv + p.D;
 
@@ -52,8 +57,12 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.scan = scan;
   p.wg_output = p.BH * p.n_spans * tiles;
   if (p.n_spans > 1) {
-    p.wg_state = p.BH * (mfma ? p.n_spans - 1 : p.n_spans) * tiles;
-    p.ws_bytes = static_cast<size_t>(p.BH * p.n_spans * p.E) * sizeof(float);
+    p.wg_state = p.BH * (mfma ? p.n_spans - 1 : p.n_spans) * tiles * p.nsl;
+    p.ws_bytes = static_cast<size_t>(p.nsl * p.BH * p.n_spans * p.E) * sizeof(float);
+  }
+  if (p.nsl > 1) {
+    p.part_off = (p.ws_bytes + 255) & ~static_cast<size_t>(255);
+    p.ws_bytes = p.part_off + static_cast<size_t>(p.BH * T * kPartFloats) * sizeof(float);
   }
   return p;
 }
@@ -90,6 +99,41 @@ hipError_t run_forward(const ForwardPlan& p, const void* q, const void* k, const
     if (e != hipSuccess) return e;   \
   } while (0)
   KATA_TRY(mark(ev, true, 0, stream));
+  if (p.path == Path::Mfma && p.nsl > 1) {
+    // sliced feature map: span sums per slice, one prefix over every slice's
+    // heads, then the slices' readouts in order (each adds to the fp32 partial
+    // reads; the last normalises)
+    MfmaArgs m{};
+    m.q = q;
+    m.k = k;
+    m.v = v;
+    m.out = out;
+    m.BH = p.BH;
+    m.T = p.T;
+    m.d = p.d;
+    m.chunk = p.chunk;
+    m.G = p.G;
+    m.n_spans = p.n_spans;
+    m.eps = eps;
+    m.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + p.part_off);
+    const int64_t slice_floats = p.BH * p.n_spans * p.E;
+    if (p.n_spans > 1) {
+      for (int s = 0; s < p.nsl; ++s) {
+        m.fm = p.fm_base + s;
+        m.ws = ws + s * slice_floats;
+        KATA_TRY(launch_span_state_mfma(m, stream));
+      }
+      KATA_TRY((p.scan == KATA_SCAN_ASSOCIATIVE)
+                   ? launch_scan_associative(ws, p.nsl * p.BH, p.n_spans, p.E, stream)
+                   : launch_scan_sequential(ws, p.nsl * p.BH, p.n_spans, p.E, stream));
+    }
+    for (int s = 0; s < p.nsl; ++s) {
+      m.fm = p.fm_base + s;
+      m.ws = p.n_spans > 1 ? ws + s * slice_floats : nullptr;
+      KATA_TRY(launch_readout_mfma(m, stream));
+    }
+    return hipSuccess;
+  }
   if (p.path == Path::Mfma) {
     MfmaArgs m{};
     m.q = q;

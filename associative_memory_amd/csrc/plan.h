@@ -37,6 +37,11 @@ struct ForwardPlan {
   int64_t wg_state = 0;  // workgroups of the span-state kernel (0 if not run)
   int64_t wg_output = 0; // workgroups of the readout kernel
   size_t ws_bytes = 0;
+  // sliced feature maps (KATA-M1 / KATA-M2 at d = 64): slices, id of slice 0,
+  // and the byte offset of the fp32 partial reads in the workspace
+  int nsl = 1;
+  int fm_base = 0;
+  size_t part_off = 0;
 };
 
 // g > 1: the KATA-Mg block map with g blocks (the matrix-core path supports

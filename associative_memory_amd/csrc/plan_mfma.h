@@ -40,6 +40,8 @@ struct MfmaArgs {
   int64_t n_spans;  // spans per head
   float eps;
   const float* gb = nullptr;  // gated read: running gate sums per token, log2 units
+  float* part = nullptr;      // sliced maps: fp32 partial reads [BH*T][68]
+  int fm = 0;                 // sliced maps: 100 + slice (KATA-M1), 200 + slice (KATA-M2)
 };
 
 struct QuadArgs {
@@ -103,10 +105,13 @@ inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
   return bf16 && (d == 16 || d == 32) && dv == 64 && (chunk == 64 || chunk == 128);
 }
 
-// the chunked KATA-M4 read at d = 64 (blocks of 16): bf16, dv = 64, chunk 64
+// the chunked reads at d = 64: KATA-M4 (g = 4, blocks of 16), KATA-M2 (g = 2,
+// two slices of the feature axis) and the full map KATA-M1 (g = 1, four
+// slices); bf16, dv = 64, chunk 64
 inline bool block_map_supported(bool bf16, int d, int dv, int g, int chunk) {
-  return bf16 && d == 64 && g == 4 && dv == 64 && chunk == 64;
+  return bf16 && d == 64 && (g == 1 || g == 2 || g == 4) && dv == 64 && chunk == 64;
 }
+constexpr int kPartFloats = 68;  // fp32 partial read per token: 64 values, denominator, padding
 
 // span sums of spans 0 .. n_spans-2 of every head into ws
 hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream);

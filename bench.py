@@ -248,14 +248,17 @@ def bench_quadratic(args, hip, am, torch, w, q, k, v, out):
 # context for the same shapes here, not a target on this hardware
 PAGE_TABLE8_QUAD_MS = {(1024, 1): 0.07, (4096, 1): 0.58, (16384, 1): 8.92,
                        (1024, 2): 0.07, (4096, 2): 0.72, (16384, 2): 10.62}
+# the page's linear-state (O(T)) KATA-M1 / KATA-M2 kernels on the same shape
+PAGE_TABLE8_LINEAR_MS = {(1024, 1): 2.68, (4096, 1): 10.34, (16384, 1): 41.14, (131072, 1): 327.9,
+                         (1024, 2): 0.68, (4096, 2): 2.70, (16384, 2): 10.68, (131072, 2): 85.66}
 
 
 def bench_table8(args, hip, am, ki, torch):
     """The quadratic form with the KATA-Mg block maps (g = 1, 2, 4) on the
     page's Table 8 shape, inputs drawn on the device; and the chunked O(T)
-    form of KATA-M4 (g = 4, chunk 64) on the same shape up to T = 131072.
-    Chunked useful FLOPs: 2 [(C+1)/2 (d + dv) + 2 D dv + 2 D] per token-head
-    with D = 4 x 136 block features."""
+    form of KATA-M4, KATA-M2 and KATA-M1 (g = 4, 2, 1; chunk 64) on the same
+    shape up to T = 131072.  Chunked useful FLOPs: 2 [(C+1)/2 (d + dv) +
+    2 D dv + 2 D] per token-head with D = 544, 1056, 2080 features."""
     res = {}
     for w in ki.TABLE8_QUAD:
         q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
@@ -265,20 +268,21 @@ def bench_table8(args, hip, am, ki, torch):
         res[w.name] = r
         del q, k, v, out
     stream = torch.cuda.current_stream().cuda_stream
-    C, D = 64, 4 * 136
-    for T in (1024, 4096, 16384, 131072):
-        w = ki.table8(T, 4, 70)
+    C = 64
+    for T, g in ((T, g) for T in (1024, 4096, 16384, 131072) for g in (4, 2, 1)):
+        D = {4: 4 * 136, 2: 2 * 528, 1: 2080}[g]
+        w = ki.table8(T, g, 70)
         q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
         out = torch.empty_like(v)
-        need = am.lib().kata_forward_chunked_blocks_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, 4, C, 0)
+        need = am.lib().kata_forward_chunked_blocks_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, g, C, 0)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         for _ in range(args.warmup):
-            am.kata_forward_chunked_blocks(q, k, v, 4, chunk=C, out=out, workspace=ws)
+            am.kata_forward_chunked_blocks(q, k, v, g, chunk=C, out=out, workspace=ws)
         torch.cuda.synchronize()
         e0, e1 = hip.event(), hip.event()
         hip.record(e0, stream)
         for _ in range(args.steps):
-            am.kata_forward_chunked_blocks(q, k, v, 4, chunk=C, out=out, workspace=ws)
+            am.kata_forward_chunked_blocks(q, k, v, g, chunk=C, out=out, workspace=ws)
         hip.record(e1, stream)
         torch.cuda.synchronize()
         ms = hip.ms(e0, e1) / args.steps
@@ -288,7 +292,8 @@ def bench_table8(args, hip, am, ki, torch):
         res[w.name.replace("_bf16", "_chunked_bf16")] = {
             "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "page_h100_ms": PAGE_TABLE8_LINEAR_MS.get((T, g))}
         del q, k, v, out, ws
     return res
 

@@ -247,8 +247,8 @@ def blk(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=2, T=300, d=64, dv=64, g=4, chu
 @pytest.mark.parametrize("kw,status", [
     (dict(q=NULL), INVALID), (dict(B=0), INVALID), (dict(g=0), INVALID), (dict(g=3), INVALID),
     (dict(scan=9), INVALID), (dict(dt=3), INVALID), (dict(eps=-1.0), INVALID),
-    (dict(dt=F32), UNSUPPORTED), (dict(g=2), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
-    (dict(d=32, g=2), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
+    (dict(dt=F32), UNSUPPORTED), (dict(g=8), UNSUPPORTED), (dict(chunk=128), UNSUPPORTED),
+    (dict(d=32, g=2), UNSUPPORTED), (dict(dv=32), UNSUPPORTED), (dict(g=2, chunk=128), UNSUPPORTED),
     (dict(out=P[1]), INVALID), (dict(ws=NULL, wsb=0, T=1 << 16), WORKSPACE),
     (dict(g=1, d=24), UNSUPPORTED),   # g = 1 takes kata_forward_chunked's checks
 ])
@@ -262,6 +262,13 @@ def test_chunked_blocks_workspace():
     assert (L.kata_forward_chunked_blocks_workspace_bytes(1, 8, 131072, 16, 64, 1, 128, 0)
             == L.kata_forward_workspace_bytes(1, 8, 131072, 16, 64, 128, 0))
     # KATA-M4: 34 feature tiles x (4 x 256 + 16) floats per span state
-    n = L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, 4, 64, 0)
-    assert n > 0 and n % ((34 * 4 * 256 + 34 * 16) * 4) == 0
-    assert L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, 2, 64, 0) == 0
+    E = (34 * 4 * 256 + 34 * 16) * 4
+    n4 = L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, 4, 64, 0)
+    assert n4 > 0 and n4 % E == 0
+    # KATA-M2 / M1: 2 / 4 slices of span states, then fp32 partial reads
+    # (68 floats per token-head), 256-byte aligned
+    part = 8 * 16 * 16384 * 68 * 4
+    for g, nsl in ((2, 2), (1, 4)):
+        n = L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, g, 64, 0)
+        assert n == (nsl * n4 + 255) // 256 * 256 + part
+    assert L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, 8, 64, 0) == 0

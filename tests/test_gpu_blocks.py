@@ -1,8 +1,10 @@
-"""GPU parity of the chunked read with the KATA-M4 block map (d = 64, four
-blocks of 16) against the fp64 oracle, through the C ABI: full outputs on
-ragged and multi-span shapes, sampled rows at the page's Table 8 shape
-(B = 8, H = 16, d_head = 64) and at T = 65536, agreement with the quadratic
-form of the same map, both prefix variants, and determinism."""
+"""GPU parity of the chunked read at d = 64 with the KATA-Mg maps against the
+fp64 oracle, through the C ABI: KATA-M4 (four blocks of 16), KATA-M2 (two
+blocks of 32, two slices of the feature axis) and the full map KATA-M1 (four
+slices).  Full outputs on ragged and multi-span shapes, sampled rows at the
+page's Table 8 shape (B = 8, H = 16, d_head = 64) and at T = 65536,
+agreement with the quadratic form of the same map, both prefix variants, and
+determinism."""
 import numpy as np
 import pytest
 import torch
@@ -14,12 +16,12 @@ from gpu_util import check, say, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
-G = 4
+GS = [4, 2, 1]
 
 
-def run(inp, eps=1e-6, scan="auto"):
+def run(inp, g, eps=1e-6, scan="auto"):
     q, k, v = (to_dev(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
-    out = am.kata_forward_chunked_blocks(q, k, v, G, eps=eps, scan=scan)
+    out = am.kata_forward_chunked_blocks(q, k, v, g, eps=eps, scan=scan)
     torch.cuda.synchronize()
     return to_host64(out)
 
@@ -32,59 +34,64 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("g", GS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}T{}".format(*c))
-def test_ragged_and_multispan(case):
+def test_ragged_and_multispan(case, g):
     B, H, T = case
-    say(f"chunked M4 {case}")
-    inp = ki.forward_inputs(B, H, T, 64, 64, ki.BF16, seed=T + 11)
-    got = run(inp)
-    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6, g=G)
-    check(got, ref, ki.BF16, np.abs(inp.v64).max(), f"chunked M4 {case}")
+    say(f"chunked M{g} {case}")
+    inp = ki.forward_inputs(B, H, T, 64, 64, ki.BF16, seed=T + 11 + g)
+    got = run(inp, g)
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6, g=g)
+    check(got, ref, ki.BF16, np.abs(inp.v64).max(), f"chunked M{g} {case}")
 
 
+@pytest.mark.parametrize("g", GS)
 @pytest.mark.parametrize("scan", ["sequential", "associative"])
-def test_table8_shape_sampled_rows(scan):
-    w = ki.table8(4096, G, 45)
+def test_table8_shape_sampled_rows(scan, g):
+    w = ki.table8(4096, g, 45)
     say(f"chunked {w.name} sampled rows, {scan} prefix")
     inp = ki.workload_inputs(w)
-    got = run(inp, w.eps, scan)
+    got = run(inp, g, w.eps, scan)
     rng = np.random.Generator(np.random.PCG64(46))
     refs, gots = [], []
     for b in range(w.B):
         for h in rng.choice(w.H, 3, replace=False):
             rows = sorted({0, 63, 64, w.T - 1} | {int(x) for x in rng.integers(0, w.T, 6)})
-            refs.append(orc.forward_rows(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], rows, w.eps, g=G))
+            refs.append(orc.forward_rows(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], rows, w.eps, g=g))
             gots.append(got[b, h, rows])
     check(np.concatenate(gots), np.concatenate(refs), w.dtype, np.abs(inp.v64).max(), w.name + " rows")
 
 
-def test_long_sequence_sampled_rows():
+@pytest.mark.parametrize("g", GS)
+def test_long_sequence_sampled_rows(g):
     B, H, T = 1, 4, 65536
-    say(f"chunked M4 B{B} H{H} T{T} sampled rows")
+    say(f"chunked M{g} B{B} H{H} T{T} sampled rows")
     inp = ki.forward_inputs(B, H, T, 64, 64, ki.BF16, seed=47)
-    got = run(inp)
+    got = run(inp, g)
     rng = np.random.Generator(np.random.PCG64(48))
     refs, gots = [], []
     for h in range(H):
         rows = sorted({0, 64, 4095, T - 1} | {int(x) for x in rng.integers(0, T, 8)})
-        refs.append(orc.forward_rows(inp.q64[0, h], inp.k64[0, h], inp.v64[0, h], rows, 1e-6, g=G))
+        refs.append(orc.forward_rows(inp.q64[0, h], inp.k64[0, h], inp.v64[0, h], rows, 1e-6, g=g))
         gots.append(got[0, h, rows])
-    check(np.concatenate(gots), np.concatenate(refs), ki.BF16, np.abs(inp.v64).max(), "chunked M4 long rows")
+    check(np.concatenate(gots), np.concatenate(refs), ki.BF16, np.abs(inp.v64).max(), f"chunked M{g} long rows")
 
 
-def test_matches_quadratic_form():
+@pytest.mark.parametrize("g", GS)
+def test_matches_quadratic_form(g):
     inp = ki.forward_inputs(2, 3, 3000, 64, 64, ki.BF16, seed=49)
     q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
-    a = to_host64(am.kata_forward_chunked_blocks(q, k, v, G))
-    b = to_host64(am.kata_forward_quadratic(q, k, v, g=G))
+    a = to_host64(am.kata_forward_chunked_blocks(q, k, v, g))
+    b = to_host64(am.kata_forward_quadratic(q, k, v, g=g))
     torch.cuda.synchronize()
     assert np.abs(a - b).max() <= 2e-2 * np.abs(inp.v64).max()
 
 
-def test_deterministic():
+@pytest.mark.parametrize("g", GS)
+def test_deterministic(g):
     inp = ki.forward_inputs(1, 2, 9000, 64, 64, ki.BF16, seed=50)
     q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
-    x = am.kata_forward_chunked_blocks(q, k, v, G)
-    y = am.kata_forward_chunked_blocks(q, k, v, G)
+    x = am.kata_forward_chunked_blocks(q, k, v, g)
+    y = am.kata_forward_chunked_blocks(q, k, v, g)
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int16), y.view(torch.int16))
