@@ -525,6 +525,10 @@ def main():
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
         return
 
+    def progress(what):
+        print(f"bench: {what}", file=sys.stderr, flush=True)
+
+    progress("forward T=131072")
     w, inp, fwd = bench_forward(args, hip, am, ki, torch)
     main_r = fwd["auto"]
     D = w.d * (w.d + 1) // 2
@@ -573,17 +577,23 @@ def main():
                           for s in ("sequential", "associative")},
     }
     if not args.no_other:
+        progress("other forward workloads")
         rec["other_workloads"] = bench_other_workloads(args, hip, am, ki, torch)
     if not args.no_table8:
+        progress("quadratic and chunked block maps, d = 64")
         rec["quadratic_block_maps_d64"] = bench_table8(args, hip, am, ki, torch)
     if not args.no_linear:
+        progress("linear features")
         rec["linear_features_d64"] = bench_linear(args, hip, am, ki, torch)
     if not args.no_gated:
+        progress("gated read")
         rec["gated"] = bench_gated(args, hip, am, ki, torch)
     if not args.no_decode:
+        progress("decode")
         rec["decode"] = bench_decode(args, hip, am, ki, torch, ki.DECODE)
         rec["decode_beyond_cache"] = bench_decode(args, hip, am, ki, torch, ki.DECODE_512)
     if not args.no_cpu_baseline:
+        progress("CPU oracle baseline")
         rec["cpu_baseline"] = cpu_baseline(w, inp)
     else:
         rec["cpu_baseline"] = None
