@@ -73,12 +73,18 @@ constexpr int staged_dim(int x) {
 }
 
 // orbit representatives of the pairs (i <= j, staged frame) of the d = 64
-// sliced maps under the shift by 16 per lane group, size-4 orbits first:
-// all pairs (KATA-M1) or the pairs inside a block (KATA-M2: blocks are the
-// staged quarters of equal parity)
+// sliced maps under the shift by 16 per lane group, and the slices' bounds.
+// KATA-M1 groups them by the quarter distance of the pair, which the shift
+// keeps: slice 0 the pairs inside quarter 0 (136), slices 1 and 2 the pairs
+// between quarters 0 and 1 (i < 8, i >= 8: 128 each), slice 3 the pairs
+// between quarters 0 and 2 (136, the 16 pairs (x, x + 32) with orbits of
+// size 2), so a lane needs at most 32 of its query's dimensions per slice.
+// KATA-M2 (blocks are the staged quarters of equal parity) takes its 272 orbits
+// size-4 first, in two slices of 136.
 template <int FAM>
 struct Orbits64 {
   int n4 = 0, n = 0;
+  int start[5] = {};  // slice s holds entries [start[s], start[s + 1])
   int8_t a[1056] = {};
   int8_t b[1056] = {};
   bool pair2[1056] = {};
@@ -87,6 +93,28 @@ struct Orbits64 {
 template <int FAM>
 constexpr Orbits64<FAM> make_orbits64() {
   Orbits64<FAM> o;
+  if constexpr (FAM == 100) {
+    auto add = [&o](int i, int j, bool two) {
+      o.a[o.n] = static_cast<int8_t>(i);
+      o.b[o.n] = static_cast<int8_t>(j);
+      o.pair2[o.n] = two;
+      ++o.n;
+      if (!two) ++o.n4;
+    };
+    for (int i = 0; i < 16; ++i)
+      for (int j = i; j < 16; ++j) add(i, j, false);
+    o.start[1] = o.n;
+    for (int i = 0; i < 8; ++i)
+      for (int j = 16; j < 32; ++j) add(i, j, false);
+    o.start[2] = o.n;
+    for (int i = 8; i < 16; ++i)
+      for (int j = 16; j < 32; ++j) add(i, j, false);
+    o.start[3] = o.n;
+    for (int u = 0; u < 16; ++u)
+      for (int x = 0; x <= u; ++x) add(x, u + 32, x == u);
+    o.start[4] = o.n;
+    return o;
+  }
   bool used[64][64] = {};
   int n4 = 0;
   for (int pass = 0; pass < 2; ++pass) {
@@ -123,6 +151,8 @@ constexpr Orbits64<FAM> make_orbits64() {
     }
   }
   o.n4 = n4;
+  o.start[1] = 136;
+  o.start[2] = o.n;
   return o;
 }
 
@@ -132,9 +162,8 @@ constexpr Orbits64<FAM> kOrbits64 = make_orbits64<FAM>();
 template <int FM>
 constexpr int slice_entries() {
   if constexpr (FM >= 100) {
-    constexpr int total = kOrbits64<fm_family(FM)>.n;
-    constexpr int first = 136 * fm_slice(FM);
-    return total - first < 136 ? total - first : 136;
+    constexpr auto& o = kOrbits64<fm_family(FM)>;
+    return o.start[fm_slice(FM) + 1] - o.start[fm_slice(FM)];
   } else {
     return 0;
   }
@@ -160,10 +189,11 @@ constexpr Schedule<DK> make_schedule() {
   constexpr int SH = Schedule<DK>::SH;
   if constexpr (DK >= 100) {
     constexpr auto& o = kOrbits64<fm_family(DK)>;
+    constexpr int first = o.start[fm_slice(DK)];
     for (int e = 0; e < Schedule<DK>::NE; ++e) {
-      s.a[e] = o.a[136 * fm_slice(DK) + e];
-      s.b[e] = o.b[136 * fm_slice(DK) + e];
-      s.pair2[e] = o.pair2[136 * fm_slice(DK) + e];
+      s.a[e] = o.a[first + e];
+      s.b[e] = o.b[first + e];
+      s.pair2[e] = o.pair2[first + e];
     }
   } else if constexpr (kBlockMap<DK>) {
     int e = 0;
@@ -279,8 +309,11 @@ constexpr bool sliced_ok() {
       ++n;
     }
   }
-  if (FAM == 100) return n == 2080 && o.n == 528 && o.n4 == 512 && o.n <= 136 * 4;
-  return n == 1056 && o.n == 272 && o.n4 == 256 && o.n <= 136 * 2;
+  for (int sl = 0; sl < (FAM == 100 ? 4 : 2); ++sl) {
+    if (o.start[sl + 1] - o.start[sl] > 136) return false;  // one 34-tile state per slice
+  }
+  if (FAM == 100) return n == 2080 && o.n == 528 && o.n4 == 512 && o.start[4] == 528;
+  return n == 1056 && o.n == 272 && o.n4 == 256 && o.start[2] == 272;
 }
 static_assert(sliced_ok<100>(), "KATA-M1 slices must cover every pair once");
 static_assert(sliced_ok<200>(), "KATA-M2 slices must cover every in-block pair once");
@@ -1293,8 +1326,11 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
     const bool own_den = L.vt[0] == 0 && g == 0;
     const int row = 16 * L.qt[0] + r;
     if constexpr (CF::SLICE > 0) {
+      // one value tile at a time: the accumulators of the whole state are
+      // live here, so the partial rows are not all loaded up front
 #pragma unroll
       for (int i = 0; i < NDW; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
         if (L.vt[i] == NDT - 1) {
           const float x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(part.r, (row * PART_LD + DV) * 4, 0, 0));
           if (own_den || CF::SLICE == CF::NSL - 1) o[0][i][0] += g == 0 ? x : 0.f;
@@ -1304,6 +1340,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
           for (int j = 0; j < 4; ++j) o[0][i][j] += __uint_as_float(x[j]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (CF::SLICE < CF::NSL - 1) {
 #pragma unroll
