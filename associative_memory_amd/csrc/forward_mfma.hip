@@ -123,7 +123,6 @@ constexpr Orbits64<FAM> make_orbits64() {
         if (FAM == 200 && ((i >> 4) & 1) != ((j >> 4) & 1)) continue;
         if (used[i][j]) continue;
         int size = 0;
-        bool mark[4][2] = {};
         for (int g = 0; g < 4; ++g) {
           int x = (i + 16 * g) % 64, y = (j + 16 * g) % 64;
           if (x > y) { const int t = x; x = y; y = t; }
@@ -146,7 +145,6 @@ constexpr Orbits64<FAM> make_orbits64() {
         o.pair2[o.n] = size == 2;
         ++o.n;
         if (size == 4) ++n4;
-        (void)mark;
       }
     }
   }
