@@ -1008,6 +1008,41 @@ constexpr int dma_count16() {
   return n;
 }
 
+// Span layout of the d = 16 kernels.  Uniform (GL = 0): span sp covers
+// chunks [sp G, (sp + 1) G).  Paired (GL > 0): spans come in pairs of 2G
+// chunks, the even span of a pair GL chunks and the odd one 2G - GL, and the
+// readout grid's first half takes the even spans.  With two readout
+// workgroups per CU, the first half is placed first on the CUs; its waves
+// are older and win the issue arbitration, so the longer spans go to them
+// and both workgroups of a CU finish at about the same time.
+__device__ inline int64_t span_first_chunk(const MfmaArgs& a, int64_t sp) {
+  return a.GL == 0 ? sp * a.G : (sp >> 1) * 2 * a.G + ((sp & 1) ? a.GL : 0);
+}
+
+struct SpanOf {
+  int64_t bh, sp;
+};
+
+__device__ inline SpanOf readout_span(const MfmaArgs& a) {
+  const int64_t b = blockIdx.x;
+  if (a.GL == 0) return {b / a.n_spans, b % a.n_spans};
+  const int64_t per = a.n_spans / 2, half = a.BH * per;
+  const int64_t odd = b >= half ? 1 : 0;
+  const int64_t r = b - odd * half;
+  return {r / per, 2 * (r % per) + odd};
+}
+
+// Span of a span-sum workgroup: spans 0 .. n_spans - 2 of every head (the
+// last span's sum is never read); paired spans put the even ones first.
+__device__ inline SpanOf sum_span(const MfmaArgs& a) {
+  const int64_t b = blockIdx.x;
+  if (a.GL == 0) return {b / (a.n_spans - 1), b % (a.n_spans - 1)};
+  const int64_t per_even = a.n_spans / 2, per_odd = per_even - 1, half = a.BH * per_even;
+  if (b < half) return {b / per_even, 2 * (b % per_even)};
+  const int64_t r = b - half;
+  return {r / per_odd, 2 * (r % per_odd) + 1};
+}
+
 // Three LDS buffers: chunk i is reduced while chunks i+1 and i+2 are in
 // flight.  Before each chunk a wave waits for its own share of that chunk
 // (vmcnt: the later chunk's transfers may stay outstanding) and the barrier
@@ -1023,9 +1058,8 @@ __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
   __shared__ alignas(16) uint16_t ones[128];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t nsp_work = a.n_spans - 1;  // the last span's sum is never read
-  const int64_t bh = blockIdx.x / nsp_work;
-  const int64_t sp = blockIdx.x - bh * nsp_work;
+  const SpanOf span = sum_span(a);
+  const int64_t bh = span.bh, sp = span.sp;
   const int64_t tok0 = bh * a.T;
   if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
   __syncthreads();  // the ones rows
@@ -1041,8 +1075,8 @@ __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
     const TrOffsets to = tr_offsets(lane);
     // the ones-column tile: row 0 of `ones` is all ones, row 1 all zeros
     const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[((lane & 15) > 0 ? 64 : 0) + 8 * (lane >> 4)]);
-    const int64_t first = sp * a.G * C;
-    int64_t end = first + a.G * C;
+    const int64_t first = span_first_chunk(a, sp) * C;
+    int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
     auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, end, a.gb); };
     dma_chunk16<C, W, CF::NW, G>(b0, src(first), lane);
@@ -1556,8 +1590,8 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
   __shared__ alignas(16) uint16_t Ob[CF::NW][16 * OB_LD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x / a.n_spans;
-  const int64_t sp = blockIdx.x - bh * a.n_spans;
+  const SpanOf span = readout_span(a);
+  const int64_t bh = span.bh, sp = span.sp;
   const int64_t tok0 = bh * a.T;
 
   // feature positions no tile writes hold no feature: zero once
@@ -1576,8 +1610,8 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
     load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
                    W, lane);
     write_sb<CF>(Sb, acc, W, lane);
-    const int64_t first = sp * a.G * C;
-    int64_t end = first + a.G * C;
+    const int64_t first = span_first_chunk(a, sp) * C;
+    int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
     auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb); };
     dma_chunkq16<C, W, CF::NW, G>(x0, src(first), lane);

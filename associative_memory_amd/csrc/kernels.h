@@ -62,6 +62,11 @@ hipError_t launch_gate_prep(const float* log_gamma, float* gb, float* ctot, int6
 // P_0 = 0, P_{j+1} = 2^(sum of span j's chunk totals) P_j + ws[j].
 hipError_t launch_scan_affine(float* ws, const float* ctot, int64_t BH, int64_t n_spans,
                               int64_t E, int64_t G, int64_t n_chunks, hipStream_t stream);
+// The same affine prefix by reduce-then-scan (segments of the span axis,
+// log-depth combine of the segment maps).
+hipError_t launch_scan_affine_associative(float* ws, const float* ctot, int64_t BH,
+                                          int64_t n_spans, int64_t E, int64_t G,
+                                          int64_t n_chunks, hipStream_t stream);
 
 // Chunked readout with carried state, VALU fp32 arithmetic.  Each workgroup
 // takes one span of `G` chunks of one head (and a slice of dv columns),

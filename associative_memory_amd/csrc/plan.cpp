@@ -9,10 +9,15 @@ namespace kata {
 namespace {
 
 constexpr int64_t kValuDvTile = 16;
-constexpr int64_t kMaxSpans = 8192;     // the associative scan keeps a head's spans in LDS
+constexpr int64_t kMaxSpans = 8192;     // the gated affine prefix keeps span decays in LDS
 constexpr int64_t kTargetWorkgroups = 2048;
 // resident readout workgroups per CU: two of 4 waves at d = 16, one of 8 at d = 32
 constexpr int64_t mfma_target_workgroups(int d) { return d == 16 ? 512 : 256; }
+// paired spans at d = 16: the even span of a pair takes G + G / kPairSkewDiv
+// chunks and runs in the readout workgroup placed first on its CU, which
+// issues ahead of the second (measured at 8 heads x 64 spans of 16 chunks:
+// readout 84 -> 81 us, span sums 38 -> 37 us)
+constexpr int64_t kPairSkewDiv = 8;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -46,13 +51,15 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.G = ceil_div(p.n_chunks, spans);
   if (ceil_div(p.n_chunks, p.G) > kMaxSpans) p.G = ceil_div(p.n_chunks, kMaxSpans);
   p.n_spans = ceil_div(p.n_chunks, p.G);
+  if (mfma && d == 16 && p.n_spans % 2 == 0 && p.n_chunks == p.n_spans * p.G &&
+      p.G >= kPairSkewDiv && p.n_spans * p.BH == mfma_target_workgroups(d))
+    p.GL = p.G + p.G / kPairSkewDiv;
 
   if (scan == KATA_SCAN_AUTO) {
-    // measured on MI355X: with the span counts this planner produces (<= 8192
-    // per head, typically 16..64) the sequential pass is the faster prefix
-    // (e.g. 11 us vs 47 us at 8 heads x 64 spans of 46 KB states); the
-    // log-depth scan only pays off for very long span axes
-    scan = p.n_spans >= 1024 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;
+    // measured on MI355X at 9,360-float span states (prefix stage, us,
+    // sequential / associative): 8 heads x 64 spans 11.2 / 11.7, 4 x 128
+    // 12.7 / 12.4, 1 x 512 29.8 / 19.6; d = 32, 32 x 8 spans 14.4 / 15.1
+    scan = p.n_spans >= 128 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;
   }
   p.scan = scan;
   p.wg_output = p.BH * p.n_spans * tiles;
@@ -70,10 +77,12 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
 void describe_plan(const ForwardPlan& p, char* buf, size_t len) {
   std::snprintf(buf, len,
                 "path=%s scan=%s D=%d chunk=%d n_chunks=%lld chunks_per_span=%lld "
-                "n_spans=%lld wg_state=%lld wg_output=%lld workspace_bytes=%zu",
+                "paired_even_span=%lld n_spans=%lld wg_state=%lld wg_output=%lld "
+                "workspace_bytes=%zu",
                 p.path == Path::Mfma ? "mfma" : "valu",
                 p.scan == KATA_SCAN_ASSOCIATIVE ? "associative" : "sequential", p.D, p.chunk,
                 static_cast<long long>(p.n_chunks), static_cast<long long>(p.G),
+                static_cast<long long>(p.GL),
                 static_cast<long long>(p.n_spans), static_cast<long long>(p.wg_state),
                 static_cast<long long>(p.wg_output), p.ws_bytes);
 }
@@ -146,6 +155,7 @@ hipError_t run_forward(const ForwardPlan& p, const void* q, const void* k, const
     m.d = p.d;
     m.chunk = p.chunk;
     m.G = p.G;
+    m.GL = p.GL;
     m.n_spans = p.n_spans;
     m.eps = eps;
     if (p.n_spans > 1) KATA_TRY(launch_span_state_mfma(m, stream));

@@ -32,6 +32,7 @@ struct ForwardPlan {
   Path path = Path::Valu;
   int64_t n_chunks = 0;  // ceil(T / chunk)
   int64_t G = 1;         // chunks per span
+  int64_t GL = 0;        // paired spans: chunks of each even span (0: all spans G chunks)
   int64_t n_spans = 1;   // spans per head
   int64_t E = 0;         // floats per state pair: D*dv + D
   int64_t wg_state = 0;  // workgroups of the span-state kernel (0 if not run)

@@ -38,6 +38,9 @@ struct MfmaArgs {
   int chunk;
   int64_t G;        // chunks per span
   int64_t n_spans;  // spans per head
+  // paired spans (d = 16 kernels): with GL > 0 the spans come in pairs of 2G
+  // chunks, the even span of a pair GL chunks and the odd one 2G - GL
+  int64_t GL = 0;
   float eps;
   const float* gb = nullptr;  // gated read: running gate sums per token, log2 units
   float* part = nullptr;      // sliced maps: fp32 partial reads [BH*T][68]

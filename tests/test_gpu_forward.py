@@ -67,6 +67,37 @@ def test_sampled_parity_long_workloads(w, scan):
     check(np.concatenate(gots), np.concatenate(refs), w.dtype, vmax, f"{w.name} sampled rows")
 
 
+def _plan_fields(plan):
+    return {k: v for k, v in (f.split("=", 1) for f in plan.split())}
+
+
+@pytest.mark.parametrize("scan", SCANS)
+@pytest.mark.parametrize("shape", [(4, 8, 16384, 64), (4, 8, 32768, 128)], ids=lambda s: "B{}H{}T{}C{}".format(*s))
+def test_paired_spans_boundaries(shape, scan):
+    # plans with paired spans (even spans G + G/8 chunks, odd spans the rest
+    # of 2G): the first and last rows of every span of sampled heads, plus
+    # random rows of every head
+    B, H, T, chunk = shape
+    plan = am.kata_forward_plan(B, H, T, 16, 64, chunk, am.KATA_BF16, scan)
+    say(f"forward paired spans {shape} scan={scan} plan: {plan}")
+    f = _plan_fields(plan)
+    G, GL, n_spans = int(f["chunks_per_span"]), int(f["paired_even_span"]), int(f["n_spans"])
+    assert GL > G, "the plan does not pair spans"
+    starts = [((j // 2) * 2 * G + (GL if j % 2 else 0)) * chunk for j in range(n_spans + 1)]
+    assert starts[-1] == T
+    inp = ki.forward_inputs(B, H, T, 16, 64, ki.BF16, seed=T + chunk)
+    got = run(inp, chunk, 1e-6, scan)
+    g = np.random.Generator(np.random.PCG64(T + 1))
+    edges = sorted({r for s in starts[1:-1] for r in (s - 1, s)} | {0, T - 1})
+    refs, gots = [], []
+    for b in range(B):
+        for h in range(H):
+            rows = sorted(set(int(x) for x in g.integers(0, T, 6)) | (set(edges) if (b + h) % 3 == 0 else set()))
+            refs.append(orc.forward_rows(inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], rows, 1e-6))
+            gots.append(got[b, h, rows])
+    check(np.concatenate(gots), np.concatenate(refs), ki.BF16, np.abs(inp.v64).max(), f"paired spans {shape}")
+
+
 RAGGED = [
     # (B, H, T, d, dv, chunk, dtype)
     (1, 1, 1, 16, 16, 32, ki.F32),
