@@ -79,7 +79,7 @@ kata_status_t check_linear_shape(int B, int H, int64_t T, int d, int dv, int chu
 // then the running gate sums [BH*T], then the chunk totals [BH][n_chunks].
 struct GatedLayout {
   ForwardPlan p;
-  size_t gb_off = 0, ctot_off = 0, bytes = 0;
+  size_t gb_off = 0, gk_off = 0, ctot_off = 0, bytes = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -88,7 +88,8 @@ GatedLayout plan_gated(int B, int H, int64_t T, int d, int dv, int chunk) {
   GatedLayout l;
   l.p = kata::plan_forward(B, H, T, d, dv, chunk, KATA_BF16, KATA_SCAN_SEQUENTIAL);
   l.gb_off = align256(l.p.ws_bytes);
-  l.ctot_off = align256(l.gb_off + static_cast<size_t>(l.p.BH * T) * sizeof(float));
+  l.gk_off = align256(l.gb_off + static_cast<size_t>(l.p.BH * T) * sizeof(float));
+  l.ctot_off = align256(l.gk_off + static_cast<size_t>(l.p.BH * T) * sizeof(float));
   l.bytes = l.ctot_off + static_cast<size_t>(l.p.BH * l.p.n_chunks) * sizeof(float);
   return l;
 }
@@ -266,6 +267,7 @@ kata_status_t kata_forward_gated(const void* q, const void* k, const void* v, co
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* wsb = static_cast<char*>(workspace);
   float* gb = reinterpret_cast<float*>(wsb + l.gb_off);
+  float* gk = reinterpret_cast<float*>(wsb + l.gk_off);
   float* ctot = reinterpret_cast<float*>(wsb + l.ctot_off);
   kata::MfmaArgs m{};
   m.q = q;
@@ -281,7 +283,8 @@ kata_status_t kata_forward_gated(const void* q, const void* k, const void* v, co
   m.n_spans = p.n_spans;
   m.eps = 0.f;
   m.gb = gb;
-  hipError_t e = kata::launch_gate_prep(log_gamma, gb, ctot, BH, T, chunk, s);
+  m.gk = gk;
+  hipError_t e = kata::launch_gate_prep(log_gamma, gb, gk, ctot, BH, T, chunk, s);
   if (e == hipSuccess && p.n_spans > 1) {
     e = kata::launch_span_state_gated(m, s);
     if (e == hipSuccess) e = kata::launch_scan_affine(m.ws, ctot, BH, p.n_spans, p.E, p.G, p.n_chunks, s);

@@ -897,30 +897,44 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
 // is unrolled over them, so the compiler's wait counts see that a chunk
 // arriving in one buffer does not alias reads of the other.
 // Gated read only: the chunk's running gate sums beta_t (log2 units, see
-// gate_prep_kernel), filled by one DMA instruction of C/4 lanes (entries past
-// the sequence read as 0).  The ungated tiles carry nothing (empty base).
-template <int C, bool G>
+// gate_prep_kernel) and, in the span-sum tiles, the key factors
+// 2^((beta_C - beta_t) / 2), each filled by one DMA instruction of C/4 lanes
+// (entries past the sequence read as 0).  The ungated tiles carry nothing
+// (empty base).  The readout tiles leave the key factors out (at C = 128
+// their 2 x 512 bytes would exceed the LDS of two workgroups per CU) and
+// compute them from beta.
+template <int C, bool G, bool KF = G>
 struct GateRows {};
 template <int C>
-struct GateRows<C, true> {
+struct GateRows<C, true, false> {
   alignas(16) float gb[C];
+};
+template <int C>
+struct GateRows<C, true, true> {
+  alignas(16) float gb[C];
+  alignas(16) float gk[C];
 };
 
 template <int C, bool G = false>
 struct alignas(16) DmaTile16 : GateRows<C, G> {
+  static constexpr bool kKeyFactors = G;
   alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
   alignas(16) uint16_t k[C * 16];  // [token][dimension]
 };
 
 // wave W's share of the chunk's DMA: V in 1 KB pieces of 8 rows, K in 1 KB
 // pieces of 32 rows; rows past the buffer resource's end arrive as zero
-// the gate sums of a chunk of C tokens: one DMA by the last wave, lanes
-// [0, C/4) moving 16 bytes each
+// the gate sums and (span sums) key factors of a chunk of C tokens: one DMA
+// each, by the last two waves, lanes [0, C/4) moving 16 bytes each
 template <bool G, int W, int NW, class B>
 __device__ __forceinline__ void dma_gate(B& b, const ChunkSrc& src, int lane) {
   if constexpr (G && W == NW - 1) {
     constexpr int NL = static_cast<int>(sizeof(b.gb)) / 16;
     if (lane < NL) __builtin_amdgcn_raw_ptr_buffer_load_lds(src.g, KATA_LDS(&b.gb[0]), 16, 16 * lane, 0, 0, 0);
+  }
+  if constexpr (G && W == NW - 2 && B::kKeyFactors) {
+    constexpr int NL = static_cast<int>(sizeof(b.gk)) / 16;
+    if (lane < NL) __builtin_amdgcn_raw_ptr_buffer_load_lds(src.gk, KATA_LDS(&b.gk[0]), 16, 16 * lane, 0, 0, 0);
   }
 }
 
@@ -943,9 +957,10 @@ __device__ __forceinline__ void dma_chunk16(DmaTile16<C, G>& b, const ChunkSrc& 
 // Gated read (GatedKATA, S_t = gamma_t S_{t-1} + phi(k_t) v_t^T): over a
 // chunk with running gate sums beta_t (log2 units) and total beta_C,
 //   S <- 2^beta_C S + sum_s 2^(beta_C - beta_s) phi(k_s) v_s^T.
-// phi is quadratic in k, so token s's key row is scaled by
-// 2^((beta_C - beta_s) / 2); the lane's 8 tokens are those of its transposed
-// K operand (32 ks + 4g + m and 32 ks + 16 + 4g + m).
+// phi is quadratic in k, so token s's key row is scaled by its key factor
+// 2^((beta_C - beta_s) / 2) (computed once per token by gate_prep_kernel);
+// the lane's 8 tokens are those of its transposed K operand (32 ks + 4g + m
+// and 32 ks + 16 + 4g + m).
 template <int NA, int NB>
 __device__ __forceinline__ void gate_decay(f32x4 (&acc)[NA][NB], float f) {
 #pragma unroll
@@ -955,6 +970,16 @@ __device__ __forceinline__ void gate_decay(f32x4 (&acc)[NA][NB], float f) {
   }
 }
 
+__device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gk, int ks) {
+  const int g = __lane_id() >> 4;
+  const float4 f0 = *reinterpret_cast<const float4*>(&gk[32 * ks + 4 * g]);
+  const float4 f1 = *reinterpret_cast<const float4*>(&gk[32 * ks + 16 + 4 * g]);
+  const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kr[i] *= f[i];
+}
+
+// the same factors computed from the gate sums (readout tiles)
 __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gb, float beta_c, int ks) {
   const int g = __lane_id() >> 4;
   const float4 b0 = *reinterpret_cast<const float4*>(&gb[32 * ks + 4 * g]);
@@ -969,10 +994,9 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
                                                    const DmaTile16<CF::C, G>& b, const u32x4& bones,
                                                    const TrOffsets& to) {
   static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
-  float beta_c = 0.f;
   if constexpr (G) {
-    beta_c = b.gb[CF::C - 1];
-    const float f = __builtin_amdgcn_exp2f(beta_c);
+    // the chunk's decay 2^beta_C (beta at its last token)
+    const float f = __builtin_amdgcn_exp2f(b.gb[CF::C - 1]);
     gate_decay(acc, f);
     f32x4(&a8)[1][NDT] = *reinterpret_cast<f32x4(*)[1][NDT]>(&acc8);
     gate_decay(a8, f);
@@ -990,7 +1014,7 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
       kr[2 * i] = kSqrt2 * lo_bf16(kb[i]);
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
-    if constexpr (G) gate_keys(kr, b.gb, beta_c, ks);
+    if constexpr (G) gate_keys(kr, b.gk, ks);
     constexpr int N = G ? NDT - 1 : NDT;
     tile16_into<W, N>(acc[0], kr, bv);
     tile16_into<W + 4, N>(acc[1], kr, bv);
@@ -1004,7 +1028,7 @@ constexpr int dma_count16() {
   int n = 0;
   for (int j = W; j < C / 8; j += NW) ++n;
   for (int j = W; j < C / 32; j += NW) ++n;
-  if (G && W == NW - 1) ++n;
+  if (G && (W == NW - 1 || W == NW - 2)) ++n;  // gate sums, key factors
   return n;
 }
 
@@ -1078,7 +1102,7 @@ __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
     const int64_t first = span_first_chunk(a, sp) * C;
     int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
-    auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, end, a.gb); };
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, end, a.gb, a.gk); };
     dma_chunk16<C, W, CF::NW, G>(b0, src(first), lane);
     dma_chunk16<C, W, CF::NW, G>(b1, src(first + C), lane);
     for (int64_t c0 = first; c0 < end; c0 += 3 * C) {
@@ -1499,7 +1523,8 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
 // the other is read.  Query rows and score operands are plain row reads; V and
 // K operands come from transposing reads, as in the span sums.
 template <int C, bool G = false>
-struct alignas(16) DmaTileQ16 : GateRows<C, G> {
+struct alignas(16) DmaTileQ16 : GateRows<C, G, false> {
+  static constexpr bool kKeyFactors = false;
   alignas(16) uint16_t v[C * DV];  // [token][value column], swizzled
   alignas(16) uint16_t k[C * 16];  // [token][dimension]
   alignas(16) uint16_t q[C * 16];  // [token][dimension]
@@ -1585,7 +1610,8 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
   static_assert(CF::NDW == NDT, "whole output rows per wave");
   __shared__ DmaTileQ16<C, G> x0;
   __shared__ DmaTileQ16<C, G> x1;
-  __shared__ alignas(16) uint16_t ones[128];
+  // the ones-column tile (the gated read has none: no denominator)
+  __shared__ alignas(16) uint16_t ones[G ? 8 : 128];
   __shared__ alignas(16) uint16_t Sb[VROWS * SB_LD];
   __shared__ alignas(16) uint16_t Ob[CF::NW][16 * OB_LD];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1599,7 +1625,7 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
     const int c = e % CF::NPOS;
     if (sb_col_unused<CF>(c)) Sb[(e / CF::NPOS) * SB_LD + c] = 0;
   }
-  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
+  if (!G && tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
   with_wave<CF::NW>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
     // output stores a wave issues per chunk: two 1 KB stores per query tile
@@ -1613,14 +1639,15 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
     const int64_t first = span_first_chunk(a, sp) * C;
     int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
-    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb); };
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb, a.gk); };
     dma_chunkq16<C, W, CF::NW, G>(x0, src(first), lane);
     // the state loads and the first chunk; an unconditional vmcnt(0) also
     // retires the state loads for the compiler's wait-count analysis
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     // the ones-column tile: row 0 of `ones` is all ones, row 1 all zeros
-    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[((lane & 15) > 0 ? 64 : 0) + 8 * (lane >> 4)]);
+    u32x4 bones = {0u, 0u, 0u, 0u};
+    if constexpr (!G) bones = *reinterpret_cast<const u32x4*>(&ones[((lane & 15) > 0 ? 64 : 0) + 8 * (lane >> 4)]);
 
     // one chunk: prefetch the next into the other buffer, read out, and
     // (unless it is the span's last) carry the state and refresh Sb

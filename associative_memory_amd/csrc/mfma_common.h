@@ -124,15 +124,18 @@ constexpr int OB_LD = DV + 8;  // bf16 row stride of a wave's output staging til
 // gated read).  Rows at or past the end read as zero.
 struct ChunkSrc {
   __amdgpu_buffer_rsrc_t q, k, v;
-  __amdgpu_buffer_rsrc_t g;  // per-token gate sums (gated read only)
+  __amdgpu_buffer_rsrc_t g;   // per-token gate sums (gated read only)
+  __amdgpu_buffer_rsrc_t gk;  // per-token key factors (gated read only)
 };
 
 template <int DK, int C>
 __device__ __forceinline__ ChunkSrc chunk_src(const void* q, const void* k, const void* v, int64_t tok0,
-                                              int64_t c0, int64_t T, const float* gb = nullptr) {
+                                              int64_t c0, int64_t T, const float* gb = nullptr,
+                                              const float* gk = nullptr) {
   const int64_t n = (T - c0 < C) ? T - c0 : C;
   return ChunkSrc{rows_rsrc(q, tok0 + c0, n, 2 * DK), rows_rsrc(k, tok0 + c0, n, 2 * DK),
-                  rows_rsrc(v, tok0 + c0, n, 2 * DV), rows_rsrc(gb, tok0 + c0, n, 4)};
+                  rows_rsrc(v, tok0 + c0, n, 2 * DV), rows_rsrc(gb, tok0 + c0, n, 4),
+                  rows_rsrc(gk, tok0 + c0, n, 4)};
 }
 
 // ------------------------------------------------------------ LDS DMA and transposing reads

@@ -187,12 +187,15 @@ hipError_t launch_blocked(float* ws, const float* ctot, int64_t BH, int64_t N, i
 //
 // gate_prep_kernel: one wave per chunk of C tokens writes the running gate
 // sums beta_t = log2(e) sum_{c0 <= r <= t} log gamma_r (inclusive, from the
-// chunk start c0) and the chunk total; a lane holds C/64 consecutive tokens.
+// chunk start c0), the key factors 2^((beta_C - beta_t) / 2) that scale key
+// row t in the chunk's state update (beta_C = beta at the chunk's last
+// token), and the chunk total; a lane holds C/64 consecutive tokens.
 constexpr float kLog2e = 1.44269504088896340736f;
 
 template <int C>
 __global__ __launch_bounds__(kThreads) void gate_prep_kernel(const float* __restrict__ lg,
                                                              float* __restrict__ gb,
+                                                             float* __restrict__ gk,
                                                              float* __restrict__ ctot, int64_t BH,
                                                              int64_t T, int64_t n_chunks) {
   constexpr int PER = C / 64;
@@ -216,9 +219,13 @@ __global__ __launch_bounds__(kThreads) void gate_prep_kernel(const float* __rest
     if (lane >= off) incl += y;
   }
   const float excl = incl - run;
+  const float beta_c = __shfl(excl + x[PER - 1], 63);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    if (t0 + i < T) gb[bh * T + t0 + i] = excl + x[i];
+    if (t0 + i < T) {
+      gb[bh * T + t0 + i] = excl + x[i];
+      gk[bh * T + t0 + i] = __builtin_amdgcn_exp2f(0.5f * (beta_c - (excl + x[i])));
+    }
   }
   if (lane == 63) ctot[bh * n_chunks + c] = incl;
 }
@@ -264,15 +271,15 @@ __global__ __launch_bounds__(kThreads) void scan_affine_kernel(float* __restrict
 
 }  // namespace
 
-hipError_t launch_gate_prep(const float* log_gamma, float* gb, float* ctot, int64_t BH, int64_t T,
-                            int chunk, hipStream_t stream) {
+hipError_t launch_gate_prep(const float* log_gamma, float* gb, float* gk, float* ctot, int64_t BH,
+                            int64_t T, int chunk, hipStream_t stream) {
   const int64_t n_chunks = (T + chunk - 1) / chunk;
   const int64_t waves = BH * n_chunks;
   dim3 grid(static_cast<unsigned>((waves + kThreads / 64 - 1) / (kThreads / 64)));
   if (chunk == 64) {
-    gate_prep_kernel<64><<<grid, kThreads, 0, stream>>>(log_gamma, gb, ctot, BH, T, n_chunks);
+    gate_prep_kernel<64><<<grid, kThreads, 0, stream>>>(log_gamma, gb, gk, ctot, BH, T, n_chunks);
   } else if (chunk == 128) {
-    gate_prep_kernel<128><<<grid, kThreads, 0, stream>>>(log_gamma, gb, ctot, BH, T, n_chunks);
+    gate_prep_kernel<128><<<grid, kThreads, 0, stream>>>(log_gamma, gb, gk, ctot, BH, T, n_chunks);
   } else {
     return hipErrorInvalidValue;
   }

@@ -210,13 +210,15 @@ def test_gated_workspace_sizes():
     L = am.lib()
     # T = 300, chunk 128: 3 chunks in 3 spans.  Span states (9 feature tiles x
     # 4 value tiles x 256 floats + 9 x 16 floats of z each), then the gate sums
-    # (300 floats) and the chunk totals (3 floats), each 256-byte aligned
+    # and the key factors (300 floats each) and the chunk totals (3 floats),
+    # each 256-byte aligned
     states = 3 * (9 * 4 * 256 + 9 * 16) * 4
     gb_off = (states + 255) // 256 * 256
-    ctot_off = (gb_off + 300 * 4 + 255) // 256 * 256
+    gk_off = (gb_off + 300 * 4 + 255) // 256 * 256
+    ctot_off = (gk_off + 300 * 4 + 255) // 256 * 256
     assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 16, 64, 128) == ctot_off + 3 * 4
     # 64 heads of one chunk: a single span, no states
-    assert L.kata_forward_gated_workspace_bytes(8, 8, 100, 16, 64, 128) == 25600 + 64 * 4
+    assert L.kata_forward_gated_workspace_bytes(8, 8, 100, 16, 64, 128) == 2 * 25600 + 64 * 4
     assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 32, 64, 128) == 0  # unsupported
 
 
