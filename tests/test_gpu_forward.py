@@ -98,6 +98,32 @@ def test_paired_spans_boundaries(shape, scan):
     check(np.concatenate(gots), np.concatenate(refs), ki.BF16, np.abs(inp.v64).max(), f"paired spans {shape}")
 
 
+@pytest.mark.parametrize("T", [1 << 22, (1 << 22) + 333], ids=["T4194304", "T4194637"])
+def test_sequences_far_beyond_the_benchmark(T):
+    # two heads of 4M tokens (32x the benchmarked length): 64-bit offsets, a
+    # 256-span plan (paired spans when the chunks divide evenly, a ragged last
+    # span otherwise) and the associative prefix the library picks there.
+    # Inputs are drawn on the device (the host draw would take minutes);
+    # each head is copied back for the oracle rows.
+    B, H, d, dv, chunk = 1, 2, 16, 64, 128
+    plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, "auto")
+    say(f"forward B{B} H{H} T{T} plan: {plan}")
+    assert "scan=associative" in plan
+    q, k, v = ki.forward_inputs_torch(B, H, T, d, dv, seed=T % 1000, device="cuda")
+    out = am.kata_forward_chunked(q, k, v, chunk, eps=1e-6)
+    torch.cuda.synchronize()
+    g = np.random.Generator(np.random.PCG64(T))
+    vmax = float(v.float().abs().max())
+    refs, gots = [], []
+    for h in range(H):
+        rows = sorted({0, chunk - 1, chunk, T // 2, T - 1} | {int(x) for x in g.integers(0, T, 8)})
+        qh, kh, vh = (to_host64(x[0, h]) for x in (q, k, v))
+        refs.append(orc.forward_rows(qh, kh, vh, rows, 1e-6))
+        gots.append(to_host64(out[0, h, rows]))
+        del qh, kh, vh
+    check(np.concatenate(gots), np.concatenate(refs), ki.BF16, vmax, f"T{T} rows")
+
+
 RAGGED = [
     # (B, H, T, d, dv, chunk, dtype)
     (1, 1, 1, 16, 16, 32, ki.F32),
