@@ -45,6 +45,7 @@ EXPORTED = (
     "kata_decode_step_gated",
     "kata_forward_chunked_blocks_workspace_bytes",
     "kata_forward_chunked_blocks",
+    "kata_probe_mfma_bf16",
 )
 
 
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
                                               i32, vp, sz, vp]
     L.kata_forward_plan.restype = i32
     L.kata_forward_plan.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, ctypes.c_char_p, sz]
+    L.kata_probe_mfma_bf16.restype = i64
+    L.kata_probe_mfma_bf16.argtypes = [vp, i32, i32, vp]
     _lib = L
     return L
 
@@ -184,6 +187,18 @@ def kata_feature_map(x, phi_dtype=None, out=None, stream=None):
 
 def kata_forward_workspace_bytes(B, H, T, d, dv, chunk, scan="auto") -> int:
     return int(lib().kata_forward_workspace_bytes(B, H, T, d, dv, chunk, _scan_code(scan)))
+
+
+def kata_probe_mfma_bf16(sink, workgroups: int, iters: int, stream=None) -> int:
+    """Measurement aid: launch the matrix-core rate probe (see include/kata.h)
+    on `stream`; sink is a float32 device tensor of >= workgroups * 256
+    elements.  Returns the launch's FLOP count."""
+    if sink.dtype != _torch().float32 or sink.numel() < workgroups * 256 or not sink.is_cuda:
+        raise ValueError("sink: float32 device tensor of >= workgroups * 256 elements")
+    flops = int(lib().kata_probe_mfma_bf16(sink.data_ptr(), workgroups, iters, _stream(stream)))
+    if flops < 0:
+        raise RuntimeError("kata_probe_mfma_bf16: invalid arguments or launch error")
+    return flops
 
 
 def kata_forward_plan(B, H, T, d, dv, chunk, dtype_code=KATA_BF16, scan="auto") -> str:

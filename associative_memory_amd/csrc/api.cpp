@@ -464,4 +464,12 @@ kata_status_t kata_decode_step_gated(float* S, const void* q, const void* k, con
                                             static_cast<hipStream_t>(stream)));
 }
 
+int64_t kata_probe_mfma_bf16(float* sink, int workgroups, int iters, void* stream) {
+  if (sink == nullptr || !aligned16(sink) || workgroups <= 0 || iters <= 0) return -1;
+  if (workgroups > (1 << 20) || iters > (1 << 24)) return -1;
+  if (kata::launch_probe_mfma(sink, workgroups, iters, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return -1;
+  return kata::probe_mfma_flops(workgroups, iters);
+}
+
 }  // extern "C"

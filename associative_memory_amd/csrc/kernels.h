@@ -91,4 +91,10 @@ struct OutputArgs {
 };
 hipError_t launch_output_valu(const OutputArgs& a, hipStream_t stream);
 
+// Measurement aid: a loop of independent bf16 16x16x32 matrix-core products,
+// `workgroups` workgroups of 4 waves, `iters` rounds of 8 products per wave;
+// each thread writes one sum to sink[workgroups * 256].
+hipError_t launch_probe_mfma(float* sink, int workgroups, int iters, hipStream_t stream);
+int64_t probe_mfma_flops(int workgroups, int iters);
+
 }  // namespace kata

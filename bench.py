@@ -113,6 +113,49 @@ def traffic_for(kernel_key: str):
     return e.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ measured peaks
+
+def measure_peaks(hip, am, torch):
+    """The datasheet peaks re-measured on this device: the dense bf16
+    matrix-core rate from the library's probe (independent 16x16x32 product
+    chains, 8 waves per SIMD) and the HBM bandwidth of a 1 GiB
+    device-to-device copy (bytes read + written), each the best of 5 timed
+    launches after 2 warm-ups."""
+    stream = torch.cuda.current_stream().cuda_stream
+    wgs, iters = 2048, 5000  # 8 waves per SIMD
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+
+    def best(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            fn()
+            hip.record(e1, stream)
+            ts.append(hip.ms(e0, e1) * 1e-3)
+            hip.destroy(e0)
+            hip.destroy(e1)
+        return min(ts)
+
+    flops = am.kata_probe_mfma_bf16(sink, wgs, iters)
+    t_mfma = best(lambda: am.kata_probe_mfma_bf16(sink, wgs, iters))
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    del src, dst, sink
+    return {"mfma_bf16_tflops": round(flops / t_mfma / 1e12, 1),
+            "mfma_bf16_datasheet_tflops": BF16_PEAK_TFLOPS,
+            "hbm_copy_gbs": round(2 * n / t_copy / 1e9, 1),
+            "hbm_datasheet_gbs": HBM_PEAK_GBS,
+            "method": "matrix cores: kata_probe_mfma_bf16, 2048 workgroups x 4 waves x 8 independent "
+                      "16x16x32 bf16 chains x 5000 rounds; HBM: 1 GiB device-to-device copy, read + "
+                      "write bytes; best of 5 after 2 warm-ups"}
+
+
 # ------------------------------------------------------------------ forward
 
 def bench_forward(args, hip, am, ki, torch):
@@ -576,6 +619,12 @@ def main():
                               "plan": fwd[s]["plan"]}
                           for s in ("sequential", "associative")},
     }
+    progress("measured peaks")
+    peaks = measure_peaks(hip, am, torch)
+    peaks["readout_frac_of_copy_bw"] = round(achieved / peaks["hbm_copy_gbs"], 4)
+    peaks["step_useful_frac_of_measured_mfma"] = round(
+        flop_per_tok * BHT / (main_r["ms_per_step"] * 1e-3) / 1e12 / peaks["mfma_bf16_tflops"], 5)
+    rec["measured_peaks"] = peaks
     if not args.no_other:
         progress("other forward workloads")
         rec["other_workloads"] = bench_other_workloads(args, hip, am, ki, torch)

@@ -306,6 +306,21 @@ kata_status_t kata_forward_plan(int B, int H, int64_t T, int d, int dv,
                                 int chunk, kata_dtype_t dtype,
                                 kata_scan_t scan, char* buf, size_t buf_len);
 
+/*
+ * kata_probe_mfma_bf16 -- measurement aid, not part of the method: the
+ * device's dense bf16 matrix-core rate, for reporting measured peaks beside
+ * the datasheet ones.  Launches `workgroups` workgroups of 4 waves on
+ * `stream`; each wave runs `iters` rounds of 8 independent 16x16x32 bf16
+ * products with fp32 accumulation on constant operands, and every thread
+ * writes one fp32 sum to sink (device, caller-owned, >= workgroups * 256
+ * floats, 16-byte aligned; its values carry no meaning).  Returns the FLOP
+ * count of the launch (workgroups * 4 * iters * 8 * 16384), to be divided by
+ * the launch's duration between events on `stream`, or -1 for a null or
+ * misaligned sink, workgroups outside [1, 2^20], iters outside [1, 2^24], or
+ * a launch error.
+ */
+int64_t kata_probe_mfma_bf16(float* sink, int workgroups, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -274,3 +274,14 @@ def test_chunked_blocks_workspace():
         n = L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, g, 64, 0)
         assert n == (nsl * n4 + 255) // 256 * 256 + part
     assert L.kata_forward_chunked_blocks_workspace_bytes(8, 16, 16384, 64, 64, 8, 64, 0) == 0
+
+
+def test_probe_rejects_bad_arguments():
+    # every rejection happens before any launch
+    L = am.lib()
+    assert L.kata_probe_mfma_bf16(None, 8, 100, None) == -1
+    assert L.kata_probe_mfma_bf16(8, 8, 100, None) == -1          # misaligned sink
+    assert L.kata_probe_mfma_bf16(256, 0, 100, None) == -1        # no workgroups
+    assert L.kata_probe_mfma_bf16(256, 8, 0, None) == -1          # no rounds
+    assert L.kata_probe_mfma_bf16(256, (1 << 20) + 1, 1, None) == -1
+    assert L.kata_probe_mfma_bf16(256, 1, (1 << 24) + 1, None) == -1
