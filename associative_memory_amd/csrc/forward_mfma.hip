@@ -1325,46 +1325,48 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 #pragma unroll
         for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
         if (kt > L.qt[slot]) continue;  // fully masked tile: uniform per wave
-        f32x4 sc;  // [key 4g+j][query r]
-        if constexpr (fm_family(FM) == 100) {
-          // full map at d = 64: two chained 16x16x32 products
-          sc = mfma(kf[h].p[0], qf[slot].p[0], f32x4{0.f, 0.f, 0.f, 0.f});
-          sc = mfma(kf[h].p[1], qf[slot].p[1], sc);
-        } else if constexpr (fm_family(FM) == 200) {
-          // KATA-M2: one product per block, squares summed, kept as the root
+        f32x4 s2;  // squared score, [key 4g+j][query r]
+        if constexpr (fm_family(FM) == 200) {
+          // KATA-M2: one product per block, squares summed
           const f32x4 b0 = mfma(kf[h].p[0], qf[slot].p[0], f32x4{0.f, 0.f, 0.f, 0.f});
           const f32x4 b1 = mfma(kf[h].p[1], qf[slot].p[1], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sc[j] = __builtin_sqrtf(__builtin_fmaf(b0[j], b0[j], b1[j] * b1[j]));
+          for (int j = 0; j < 4; ++j) s2[j] = __builtin_fmaf(b0[j], b0[j], b1[j] * b1[j]);
         } else if constexpr (kBlockMap<FM>) {
-          // sum over the blocks of the squared block scores, kept as its root
-          // so the squaring below is shared with the other maps
-          f32x4 sq = f32x4{0.f, 0.f, 0.f, 0.f};
+          // sum over the blocks of the squared block scores
+          s2 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
             const f32x4 b = score_mfma<16>(kf[h].p[a], qf[slot].p[a]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sq[j] = __builtin_fmaf(b[j], b[j], sq[j]);
+            for (int j = 0; j < 4; ++j) s2[j] = __builtin_fmaf(b[j], b[j], s2[j]);
+          }
+        } else {
+          f32x4 sc;
+          if constexpr (fm_family(FM) == 100) {
+            // full map at d = 64: two chained 16x16x32 products
+            sc = mfma(kf[h].p[0], qf[slot].p[0], f32x4{0.f, 0.f, 0.f, 0.f});
+            sc = mfma(kf[h].p[1], qf[slot].p[1], sc);
+          } else {
+            sc = score_mfma<DK>(kf[h], qf[slot]);
+          }
+          if constexpr (G) {
+            // p = sc^2 2^(beta_q - beta_k): fold the root of the weight into sc
+            const float4 bk = src.gate4(16 * kt + 4 * g);
+            sc[0] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.x));
+            sc[1] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.y));
+            sc[2] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.z));
+            sc[3] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.w));
           }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) sc[j] = __builtin_sqrtf(sq[j]);
-        } else {
-          sc = score_mfma<DK>(kf[h], qf[slot]);
-        }
-        if constexpr (G) {
-          // p = sc^2 2^(beta_q - beta_k): fold the root of the weight into sc
-          const float4 bk = src.gate4(16 * kt + 4 * g);
-          sc[0] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.x));
-          sc[1] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.y));
-          sc[2] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.z));
-          sc[3] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.w));
+          for (int j = 0; j < 4; ++j) s2[j] = sc[j] * sc[j];
         }
         if (kt < L.qt[slot]) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[h][j] = sc[j] * sc[j];
+          for (int j = 0; j < 4; ++j) p[h][j] = s2[j];
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) p[h][j] = L.keep[j] ? sc[j] * sc[j] : 0.f;
+          for (int j = 0; j < 4; ++j) p[h][j] = L.keep[j] ? s2[j] : 0.f;
         }
       }
       const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
