@@ -979,14 +979,27 @@ __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gk, int k
   for (int i = 0; i < 8; ++i) kr[i] *= f[i];
 }
 
-// the same factors computed from the gate sums (readout tiles)
+// the same factors computed from the gate sums (readout tiles).  All 16
+// lanes of a row use the same 8 tokens, so lane r of the row computes the
+// factor of slot r % 8 only and a swizzle within the row (bit mode: keep
+// lane bit 4, set the low bits to the slot) hands every slot to every lane.
+template <int I>
+__device__ __forceinline__ float row_slot(float f) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(f), 0x10 | (I << 5)));
+}
+
 __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gb, float beta_c, int ks) {
-  const int g = __lane_id() >> 4;
-  const float4 b0 = *reinterpret_cast<const float4*>(&gb[32 * ks + 4 * g]);
-  const float4 b1 = *reinterpret_cast<const float4*>(&gb[32 * ks + 16 + 4 * g]);
-  const float bs[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) kr[i] *= __builtin_amdgcn_exp2f(0.5f * (beta_c - bs[i]));
+  const int lane = __lane_id(), g = lane >> 4, r = lane & 15;
+  const int t = 32 * ks + 4 * g + (r & 3) + 16 * ((r >> 2) & 1);
+  const float f = __builtin_amdgcn_exp2f(0.5f * (beta_c - gb[t]));
+  kr[0] *= row_slot<0>(f);
+  kr[1] *= row_slot<1>(f);
+  kr[2] *= row_slot<2>(f);
+  kr[3] *= row_slot<3>(f);
+  kr[4] *= row_slot<4>(f);
+  kr[5] *= row_slot<5>(f);
+  kr[6] *= row_slot<6>(f);
+  kr[7] *= row_slot<7>(f);
 }
 
 template <class CF, int W, bool G = false>
