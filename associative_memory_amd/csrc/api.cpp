@@ -76,7 +76,8 @@ kata_status_t check_linear_shape(int B, int H, int64_t T, int d, int dv, int chu
 }
 
 // Workspace of the gated read: span states (when there are several spans),
-// then the running gate sums [BH*T], then the chunk totals [BH][n_chunks].
+// then the running gate sums [BH*T], the key factors [BH*T] and the chunk
+// totals [BH][n_chunks], each 256-byte aligned.
 struct GatedLayout {
   ForwardPlan p;
   size_t gb_off = 0, gk_off = 0, ctot_off = 0, bytes = 0;
@@ -287,7 +288,13 @@ kata_status_t kata_forward_gated(const void* q, const void* k, const void* v, co
   hipError_t e = kata::launch_gate_prep(log_gamma, gb, gk, ctot, BH, T, chunk, s);
   if (e == hipSuccess && p.n_spans > 1) {
     e = kata::launch_span_state_gated(m, s);
-    if (e == hipSuccess) e = kata::launch_scan_affine(m.ws, ctot, BH, p.n_spans, p.E, p.G, p.n_chunks, s);
+    // the affine prefix: sequential below 128 spans per head, reduce-then-scan
+    // from there (the additive prefix's measured crossover)
+    if (e == hipSuccess) {
+      e = p.n_spans >= 128
+              ? kata::launch_scan_affine_associative(m.ws, ctot, BH, p.n_spans, p.E, p.G, p.n_chunks, s)
+              : kata::launch_scan_affine(m.ws, ctot, BH, p.n_spans, p.E, p.G, p.n_chunks, s);
+    }
   }
   if (e == hipSuccess) e = kata::launch_readout_gated(m, s);
   return from_hip(e);
