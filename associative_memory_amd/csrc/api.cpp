@@ -226,7 +226,11 @@ kata_status_t kata_forward_linear(const void* q, const void* k, const void* v, v
                   shift, p.G, p.n_spans, eps};
   if (p.n_spans > 1) {
     hipError_t e = kata::launch_linear_span_state(a, s);
-    if (e == hipSuccess) e = kata::launch_scan_sequential(a.ws, BH, p.n_spans, kata::kLinStateFloats, s);
+    // sequential below 128 spans per head, reduce-then-scan from there
+    if (e == hipSuccess) {
+      e = p.n_spans >= 128 ? kata::launch_scan_associative(a.ws, BH, p.n_spans, kata::kLinStateFloats, s)
+                           : kata::launch_scan_sequential(a.ws, BH, p.n_spans, kata::kLinStateFloats, s);
+    }
     if (e != hipSuccess) return KATA_ERR_DEVICE;
   }
   return from_hip(kata::launch_linear_readout(a, s));
