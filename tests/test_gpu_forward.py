@@ -216,3 +216,29 @@ def test_constant_values_reproduced():
     check(got, ref, ki.BF16, np.abs(v64).max(), "constant v")
     # beyond the first few tokens the read equals v to bf16 rounding
     assert np.abs(got[0, 0, 64:] - v64[0, 0, 64:]).max() <= 2 ** -7 * 2
+
+
+@pytest.mark.parametrize("scan", SCANS)
+def test_profiled_entry_matches_plain(scan):
+    # the benchmark's entry point: same output bits as kata_forward_chunked,
+    # and every stage event recorded in order on the library's stream
+    import bench
+
+    hip = bench.Hip()
+    w = ki.MEDIUM
+    inp = ki.workload_inputs(w)
+    q, k, v = (to_dev(a, inp.dtype) for a in (inp.q, inp.k, inp.v))
+    plain = am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan)
+    ev = am.StageEvents()
+    hs = [hip.event() for _ in range(6)]
+    for i in range(3):
+        ev.stage_begin[i] = hs[2 * i]
+        ev.stage_end[i] = hs[2 * i + 1]
+    prof = am.kata_forward_chunked_profiled(q, k, v, w.chunk, ev, eps=w.eps, scan=scan)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), prof.view(torch.int16))
+    for i in range(3):
+        assert hip.ms(hs[2 * i], hs[2 * i + 1]) >= 0.0
+    assert hip.ms(hs[1], hs[2]) >= 0.0 and hip.ms(hs[3], hs[4]) >= 0.0  # stages in order
+    for h in hs:
+        hip.destroy(h)
