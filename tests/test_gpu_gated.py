@@ -103,6 +103,22 @@ def test_long_sequence_sampled_rows():
                 np.abs(inp.v64).max(), "gated long rows")
 
 
+def test_many_spans_sampled_rows():
+    # one head of 40000 tokens at chunk 64: 313 spans, so the affine prefix
+    # is the reduce-then-scan form with two passes over each segment
+    B, H, T, C = 1, 1, 40000, 64
+    say(f"gated B{B} H{H} T{T} C{C} sampled rows")
+    inp = ki.forward_inputs(B, H, T, 16, 64, ki.BF16, seed=95)
+    lg = ki.draw_log_gamma(B, H, T, seed=95)
+    got = run(inp, lg, C)
+    rng = np.random.Generator(np.random.PCG64(96))
+    rows = sorted({0, 63, 64, 127, 128, T // 2, T - 1} | {int(x) for x in rng.integers(0, T, 16)})
+    q, k, v, g = inp.q64[0, 0], inp.k64[0, 0], inp.v64[0, 0], lg[0, 0].astype(np.float64)
+    ref = orc.forward_gated_rows(q, k, v, g, rows)
+    mass = orc.forward_gated_rows(q, k, np.ones((T, 1)), g, rows)[:, 0]
+    check_gated(got[0, 0, rows], ref, mass, np.abs(inp.v64).max(), "gated many spans")
+
+
 def test_deterministic():
     inp = ki.forward_inputs(1, 4, 7000, 16, 64, ki.BF16, seed=94)
     lg = torch.from_numpy(ki.draw_log_gamma(1, 4, 7000, seed=94)).cuda()
