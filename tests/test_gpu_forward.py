@@ -124,6 +124,21 @@ def test_sequences_far_beyond_the_benchmark(T):
     check(np.concatenate(gots), np.concatenate(refs), ki.BF16, vmax, f"T{T} rows")
 
 
+def test_many_spans_sampled_rows():
+    # one head of 70001 tokens at chunk 64: 365 spans of 3 chunks, so the
+    # associative prefix reduces segments of 23 spans in two passes
+    B, H, T, d, dv, chunk = 1, 1, 70001, 16, 64, 64
+    plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, "auto")
+    say(f"forward B{B} H{H} T{T} plan: {plan}")
+    assert "scan=associative" in plan and "n_spans=365" in plan
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.BF16, seed=97)
+    got = run(inp, chunk, 1e-6)
+    rng = np.random.Generator(np.random.PCG64(98))
+    rows = sorted({0, 191, 192, T // 2, T - 1} | {int(x) for x in rng.integers(0, T, 16)})
+    ref = orc.forward_rows(inp.q64[0, 0], inp.k64[0, 0], inp.v64[0, 0], rows, 1e-6)
+    check(got[0, 0, rows], ref, ki.BF16, np.abs(inp.v64).max(), "many spans")
+
+
 RAGGED = [
     # (B, H, T, d, dv, chunk, dtype)
     (1, 1, 1, 16, 16, 32, ki.F32),
