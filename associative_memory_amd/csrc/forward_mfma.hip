@@ -366,13 +366,13 @@ __device__ __forceinline__ void pair_at(int p, int& a, int& b) {
 
 // ------------------------------------------------------------ configuration
 
-template <int FM_, int C_>
+template <int FM_, int C_, int NW_ = mfma_waves(fm_dk(FM_))>
 struct Cfg {
   static constexpr int FM = FM_;           // feature map id
   static constexpr int DK = fm_dk(FM_);    // head width
   static constexpr int NSL = fm_slices(FM_), SLICE = fm_slice(FM_);
   static constexpr int C = C_;
-  static constexpr int NW = mfma_waves(DK);  // waves per workgroup
+  static constexpr int NW = NW_;           // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int NKS = Schedule<FM>::NKS;
   static constexpr int NPOS = Schedule<FM>::NPOS;
@@ -389,6 +389,9 @@ struct Cfg {
   static constexpr int NSLOT = (NW == 4 && C == 128) ? 2 : 1;  // query tiles per wave
   static constexpr int NDW = (NW == 8 && C == 64) ? 3 : NDT;   // value tiles per wave
   static constexpr int ZOFF = NFT * (NDT - 1) * 256;  // z column offset in a span state
+  // whole output rows leave through a per-wave LDS tile as 16-byte stores;
+  // otherwise 8-byte stores from the accumulators
+  static constexpr bool STAGE_OUT = NDW == NDT;
   static_assert(NT >= 2 * C, "one thread per K row and per Q row");
   static_assert((NW == 4 || NW == 8) && (C == 64 || C == 128), "tiling");
 };
@@ -466,7 +469,7 @@ struct alignas(16) SmemOut : Tiles<CF> {
   alignas(16) uint16_t Sb[VROWS * CF::SB_LD];  // [value row][feature position] bf16 state
   // per-wave 16 x 64 output tile, staged so the chunk's rows leave as
   // contiguous 16-byte stores (used when a wave owns whole output rows)
-  alignas(16) uint16_t Ob[CF::NDW == NDT ? CF::NW : 1][16 * OB_LD];
+  alignas(16) uint16_t Ob[CF::STAGE_OUT ? CF::NW : 1][16 * OB_LD];
 };
 
 // score operand of row `row` from the fp32 Q tile / the bf16 K tile
@@ -1437,7 +1440,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
       const float den = __shfl(o[slot][NDW - 1][0], r);
       inv = __builtin_amdgcn_rcpf(den + eps);
     }
-    if constexpr (NDW == NDT) {
+    if constexpr (CF::STAGE_OUT) {
       // whole rows: stage the 16 x 64 tile in the wave's LDS tile, then
       // write it back as 1 KB contiguous stores (16 bytes per lane)
 #pragma unroll
@@ -1591,7 +1594,7 @@ struct DmaSrc16 {
 template <class CF, int W, bool G = false>
 __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], const DmaTileQ16<CF::C, G>& b,
                                                   const u32x4& bones, const TrOffsets& to) {
-  static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
+  static_assert((CF::NW == 4 || CF::NW == 8) && CF::NFT == 9, "d = 16 tiling");
   float beta_c = 0.f;
   if constexpr (G) {
     beta_c = b.gb[CF::C - 1];
@@ -1611,15 +1614,19 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], co
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
     if constexpr (G) gate_keys(kr, b.gb, beta_c, ks);
-    constexpr int N = G ? NDT - 1 : NDT;
+    constexpr int N = G ? NDT - 1 : NDT, NW = CF::NW;
+    // wave W owns feature tiles W, W + NW, ... (below 9)
     tile16_into<W, N>(acc[0], kr, bv);
-    tile16_into<W + 4, N>(acc[1], kr, bv);
-    if constexpr (W == 0) tile16_into<8, N>(acc[2], kr, bv);
+    if constexpr (W + NW < 9) tile16_into<W + NW, N>(acc[1], kr, bv);
+    if constexpr (W + 2 * NW < 9) tile16_into<W + 2 * NW, N>(acc[2], kr, bv);
   }
 }
 
-template <int C, bool G = false>
-__global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
+// The kernel body, a device function taking the arguments by reference (this
+// form compiles to slightly fewer registers and branches than the body in the
+// kernel itself, and measured 2% faster at T = 131072).
+template <int C, bool G>
+__device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   using CF = Cfg<16, C>;
   constexpr int DK = 16, SB_LD = CF::SB_LD;
   static_assert(CF::NDW == NDT, "whole output rows per wave");
@@ -1628,7 +1635,7 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
   // the ones-column tile (the gated read has none: no denominator)
   __shared__ alignas(16) uint16_t ones[G ? 8 : 128];
   __shared__ alignas(16) uint16_t Sb[VROWS * SB_LD];
-  __shared__ alignas(16) uint16_t Ob[CF::NW][16 * OB_LD];
+  __shared__ alignas(16) uint16_t Ob[CF::STAGE_OUT ? CF::NW : 1][16 * OB_LD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const SpanOf span = readout_span(a);
@@ -1643,8 +1650,9 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
   if (!G && tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
   with_wave<CF::NW>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    // output stores a wave issues per chunk: two 1 KB stores per query tile
-    constexpr int NSTORE = 2 * CF::NSLOT;
+    // output stores a wave issues per chunk: two 1 KB stores per query tile,
+    // or one 8-byte store per value tile without the LDS staging
+    constexpr int NSTORE = (CF::STAGE_OUT ? 2 : NDT - 1) * CF::NSLOT;
     const ReadoutLane<CF> L = readout_lane<CF>(W, lane);
     const TrOffsets to = tr_offsets(lane);
     f32x4 acc[CF::MFT][NDT];
@@ -1677,7 +1685,8 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       };
       readout_chunk<CF, DmaSrc16<C, G>, decltype(prefetch), G>(
-          DmaSrc16<C, G>{cur, to, bones}, Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c, n, 2 * DV), Ob[W],
+          DmaSrc16<C, G>{cur, to, bones}, Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c, n, 2 * DV),
+          Ob[CF::STAGE_OUT ? W : 0],
           prefetch);
       const bool more = c + C < end;
       if (more) state_update_ro16<CF, W, G>(acc, cur, bones, to);
@@ -1698,6 +1707,11 @@ __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
   });
+}
+
+template <int C, bool G = false>
+__global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
+  readout_dma16_body<C, G>(a);
 }
 
 template <int DK, int C>
