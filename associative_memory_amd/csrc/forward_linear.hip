@@ -123,7 +123,7 @@ __device__ __forceinline__ void lin_state_update(f32x4 (&acc)[NDT], const LinRow
 __device__ __forceinline__ int lin_state_off(int W, int i, int lane) { return ((W * NDT + i) * 64 + lane) * 4; }
 
 template <int FEAT>
-__global__ __launch_bounds__(256, 2) void lin_span_kernel(LinArgs a) {
+__device__ __forceinline__ void lin_span_body(const LinArgs& a) {
   __shared__ LinRows kr;
   __shared__ LinRows v0;
   __shared__ LinRows v1;
@@ -181,6 +181,11 @@ __global__ __launch_bounds__(256, 2) void lin_span_kernel(LinArgs a) {
   });
 }
 
+template <int FEAT>
+__global__ __launch_bounds__(256, 2) void lin_span_kernel(LinArgs a) {
+  lin_span_body<FEAT>(a);
+}
+
 // the bf16 state copy [value row][feature] for the readout: rows 0..63 are
 // S^T, row 64 is z, row 65 stays zero
 template <int W>
@@ -202,7 +207,7 @@ __device__ __forceinline__ void lin_write_sb(uint16_t* sb, const f32x4 (&acc)[ND
 }
 
 template <int FEAT>
-__global__ __launch_bounds__(256, 2) void lin_readout_kernel(LinArgs a) {
+__device__ __forceinline__ void lin_readout_body(const LinArgs& a) {
   __shared__ LinRows kr;
   __shared__ LinRows qr;
   __shared__ LinRows v0;
@@ -336,6 +341,11 @@ __global__ __launch_bounds__(256, 2) void lin_readout_kernel(LinArgs a) {
       }
     }
   });
+}
+
+template <int FEAT>
+__global__ __launch_bounds__(256, 2) void lin_readout_kernel(LinArgs a) {
+  lin_readout_body<FEAT>(a);
 }
 
 }  // namespace

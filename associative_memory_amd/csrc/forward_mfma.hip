@@ -849,7 +849,7 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
 // ------------------------------------------------------------ span sums
 
 template <class CF>
-__global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
+__device__ __forceinline__ void span_state_mfma_body(const MfmaArgs& a) {
   constexpr int C = CF::C, DK = CF::DK;
   // two LDS tile buffers: chunk i is staged into buffer i % 2 while the
   // other buffer may still be read for chunk i - 1, so one barrier per chunk
@@ -885,6 +885,11 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
     }
     store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
   });
+}
+
+template <class CF>
+__global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
+  span_state_mfma_body<CF>(a);
 }
 
 // ------------------------------------------------------------ span sums, d = 16, LDS DMA
@@ -1088,8 +1093,8 @@ __device__ inline SpanOf sum_span(const MfmaArgs& a) {
 // (vmcnt: the later chunk's transfers may stay outstanding) and the barrier
 // then publishes every wave's share.  Chunks at or past the span's end read
 // as zero; their reduction is skipped.
-template <int C, bool G = false>
-__global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
+template <int C, bool G>
+__device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
   using CF = Cfg<16, C>;
   constexpr int DK = 16;
   __shared__ DmaTile16<C, G> b0;
@@ -1177,6 +1182,11 @@ __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
     }
     store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
   });
+}
+
+template <int C, bool G = false>
+__global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
+  span_state_dma16_body<C, G>(a);
 }
 
 // ------------------------------------------------------------ readout
@@ -1472,7 +1482,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 
 // every wave reads out and carries its share of the state
 template <class CF>
-__global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
+__device__ __forceinline__ void readout_mfma_body(const MfmaArgs& a) {
   constexpr int C = CF::C, DK = CF::DK, SB_LD = CF::SB_LD;
   __shared__ SmemOut<CF> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1533,6 +1543,11 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
       __syncthreads();
     }
   });
+}
+
+template <class CF>
+__global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
+  readout_mfma_body<CF>(a);
 }
 
 // ------------------------------------------------------------ readout, d = 16, LDS DMA

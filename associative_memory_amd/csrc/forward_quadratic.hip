@@ -150,7 +150,7 @@ __device__ __forceinline__ void quad_block(f32x4 (&o)[2][NDT], const QuadTile<DK
 }
 
 template <int DK, int M>
-__global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
+__device__ __forceinline__ void quad_body(const QuadArgs& a) {
   using Op = QkOp<DK, M>;
   __shared__ QuadTile<DK> x0;
   __shared__ QuadTile<DK> x1;
@@ -247,6 +247,11 @@ __global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
       }
     }
   });
+}
+
+template <int DK, int M>
+__global__ __launch_bounds__(256, 2) void quad_kernel(QuadArgs a) {
+  quad_body<DK, M>(a);
 }
 
 }  // namespace
