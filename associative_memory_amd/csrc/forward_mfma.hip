@@ -18,9 +18,14 @@
 //    key feature carries weight 2; query features carry 1 off the diagonal
 //    and 1/2 on it, so phi_q . phi_k = (q.k)^2 and only the few diagonal
 //    query features pay an extra multiply.
-//  * Denominators ride through the MFMAs: V gets a column of ones (value tile
-//    4, built in registers), so P.1 and phi_q.z come out of the same products
-//    as the numerators, and z is column 64 of the fp32 state.
+//  * Denominators.  In the register-staged kernels (d = 32, the block maps)
+//    they ride through the MFMAs: V gets a column of ones (value tile 4), so
+//    P.1 and phi_q.z come out of the same products as the numerators.  At
+//    d = 16 (DMA kernels) a ones column would cost 9 products per 32 keys for
+//    16 useful values; there z is carried as the key Gram matrix
+//    Z = sum_s k_s k_s^T (one product per 32 keys), phi_q.z = q^T Z q, and
+//    P.1 is summed on the vector ALU.  Either way the span state stores z as
+//    a feature vector after the value tiles.
 //  * Tokens inside each 32-token k-step are stored in the order in which a
 //    pair of 16x16 score accumulators hands keys to the next product (the two
 //    16-key halves interleaved in groups of 4), so squared scores feed P.V
@@ -783,7 +788,8 @@ __device__ __forceinline__ void load_state(f32x4 (&acc)[CF::MFT][NDT], const flo
   }
 }
 
-template <class CF>
+// (WITH_Z false: the z column is written elsewhere)
+template <class CF, bool WITH_Z = true>
 __device__ __forceinline__ void store_state(const f32x4 (&acc)[CF::MFT][NDT], float* __restrict__ P,
                                             int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
@@ -796,7 +802,7 @@ __device__ __forceinline__ void store_state(const f32x4 (&acc)[CF::MFT][NDT], fl
       *reinterpret_cast<float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4) =
           make_float4(acc[m][dt][0], acc[m][dt][1], acc[m][dt][2], acc[m][dt][3]);
     }
-    if (r == 0) {
+    if (WITH_Z && r == 0) {
       *reinterpret_cast<float4*>(P + CF::ZOFF + ft * 16 + 4 * g) =
           make_float4(acc[m][NDT - 1][0], acc[m][NDT - 1][1], acc[m][NDT - 1][2],
                       acc[m][NDT - 1][3]);
@@ -824,7 +830,8 @@ __host__ __device__ constexpr bool sb_col_unused(int c) {
 }
 
 // bf16 copy of the owned state tiles into Sb[value row][feature position]
-template <class CF>
+// (ND: value tiles copied; the d = 16 DMA readout keeps no z column in Sb)
+template <class CF, int ND = NDT>
 __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 (&acc)[CF::MFT][NDT],
                                          int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
@@ -835,7 +842,7 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
     // d = 16, tile 8: rows 8..15 repeat rows 0..7 and are stored as zero
     const bool dup = CF::DK == 16 && ft == 8 && g >= 2;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
+    for (int dt = 0; dt < ND; ++dt) {
       // ones-column tile: column 0 is z (row 64), the rest are zero (row 65)
       if (dt == NDT - 1 && r > 1) continue;
       uint2 o;
@@ -1010,10 +1017,12 @@ __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gb, float
   kr[7] *= row_slot<7>(f);
 }
 
+// The value tiles only.  z is carried as the key Gram matrix Z = K^T K (the
+// transposing key read is both operands) by the wave that takes tile 8 on
+// the k-step, in the place of tile 8's ones-column tile (acc8[NDT - 1]).
 template <class CF, int W, bool G = false>
 __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f32x4 (&acc8)[NDT],
-                                                   const DmaTile16<CF::C, G>& b, const u32x4& bones,
-                                                   const TrOffsets& to) {
+                                                   const DmaTile16<CF::C, G>& b, const TrOffsets& to) {
   static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
   if constexpr (G) {
     // the chunk's decay 2^beta_C (beta at its last token)
@@ -1027,7 +1036,6 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
     u32x4 bv[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], ks);
-    bv[NDT - 1] = bones;
     const u32x4 kb = tr_operand<16>(b.k, to.k, ks);
     float kr[8];
 #pragma unroll
@@ -1036,10 +1044,13 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
     if constexpr (G) gate_keys(kr, b.gk, ks);
-    constexpr int N = G ? NDT - 1 : NDT;
+    constexpr int N = NDT - 1;
     tile16_into<W, N>(acc[0], kr, bv);
     tile16_into<W + 4, N>(acc[1], kr, bv);
-    if (ks % CF::NW == W) tile16_into<8, N>(acc8, kr, bv);  // compile-time per wave
+    if (ks % CF::NW == W) {  // compile-time per wave
+      tile16_into<8, N>(acc8, kr, bv);
+      if constexpr (!G) acc8[NDT - 1] = mfma(kb, kb, acc8[NDT - 1]);
+    }
   }
 }
 
@@ -1088,6 +1099,20 @@ __device__ inline SpanOf sum_span(const MfmaArgs& a) {
   return {r / per_odd, 2 * (r % per_odd) + 1};
 }
 
+// The z column of a span state from the key Gram matrix Z (lane (g, r)
+// holding Z[4g + i][r]): tile J's row R gets 2 Z[R][R + J mod 16] for
+// J = 0 .. 8, the value of the key features' sum (they are built from
+// sqrt(2) k).  Each (J, R) is written by the one lane holding that entry.
+template <class CF>
+__device__ __forceinline__ void store_gram16(const f32x4& z, float* __restrict__ P, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i, j = (r - row) & 15;
+    if (j <= 8) P[CF::ZOFF + 16 * j + row] = 2.f * z[i];
+  }
+}
+
 // Three LDS buffers: chunk i is reduced while chunks i+1 and i+2 are in
 // flight.  Before each chunk a wave waits for its own share of that chunk
 // (vmcnt: the later chunk's transfers may stay outstanding) and the barrier
@@ -1100,14 +1125,11 @@ __device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
   __shared__ DmaTile16<C, G> b0;
   __shared__ DmaTile16<C, G> b1;
   __shared__ DmaTile16<C, G> b2;
-  __shared__ alignas(16) uint16_t ones[128];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const SpanOf span = sum_span(a);
   const int64_t bh = span.bh, sp = span.sp;
   const int64_t tok0 = bh * a.T;
-  if (tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
-  __syncthreads();  // the ones rows
 
   with_wave<CF::NW>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
@@ -1118,8 +1140,6 @@ __device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) acc8[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     const TrOffsets to = tr_offsets(lane);
-    // the ones-column tile: row 0 of `ones` is all ones, row 1 all zeros
-    const u32x4 bones = *reinterpret_cast<const u32x4*>(&ones[((lane & 15) > 0 ? 64 : 0) + 8 * (lane >> 4)]);
     const int64_t first = span_first_chunk(a, sp) * C;
     int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
@@ -1131,20 +1151,21 @@ __device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
       barrier_lds();
       dma_chunk16<C, W, CF::NW, G>(b2, src(c0 + 2 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      state_update_dma16<CF, W, G>(acc, acc8, b0, bones, to);
+      state_update_dma16<CF, W, G>(acc, acc8, b0, to);
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
       dma_chunk16<C, W, CF::NW, G>(b0, src(c0 + 3 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (c0 + C < end) state_update_dma16<CF, W, G>(acc, acc8, b1, bones, to);
+      if (c0 + C < end) state_update_dma16<CF, W, G>(acc, acc8, b1, to);
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
       dma_chunk16<C, W, CF::NW, G>(b1, src(c0 + 4 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (c0 + 2 * C < end) state_update_dma16<CF, W, G>(acc, acc8, b2, bones, to);
+      if (c0 + 2 * C < end) state_update_dma16<CF, W, G>(acc, acc8, b2, to);
     }
     // drain the transfers still in flight, then add the waves' parts of tile 8
-    // through LDS (4 x 64 lanes x 5 x 16 bytes = 20 KB over the tile buffers)
+    // and of Z through LDS (4 x 64 lanes x 5 x 16 bytes = 20 KB over the tile
+    // buffers)
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     __syncthreads();
     constexpr int RED_BYTES = NDT * 16 * 64;  // one wave's part
@@ -1180,7 +1201,13 @@ __device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) acc[2][dt] = acc8[dt];
     }
-    store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
+    float* P = a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK);
+    if constexpr (G) {
+      store_state<CF>(acc, P, W, lane);  // z column: zeros (no denominator)
+    } else {
+      store_state<CF, false>(acc, P, W, lane);
+      if constexpr (W == 0) store_gram16<CF>(acc8[NDT - 1], P, lane);
+    }
   });
 }
 
@@ -1223,6 +1250,7 @@ __device__ __forceinline__ ReadoutLane<CF> readout_lane(int w, int lane) {
 // query / key row, and the V operand of a value tile and 32-key block.
 template <class CF>
 struct TileSrc {
+  static constexpr bool kGramDen = false;  // denominators from the ones-column tile
   const Tiles<CF>& tl;
   __device__ __forceinline__ float4 qrow4(int row, int c4) const {
     return *reinterpret_cast<const float4*>(&tl.Qf[row * CF::QF_LD + 4 * c4]);
@@ -1266,7 +1294,10 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
   constexpr int C = CF::C, DK = CF::DK, FM = CF::FM, NSLOT = CF::NSLOT, NDW = CF::NDW;
   constexpr int SB_LD = CF::SB_LD;
   static_assert(!G || NDW == NDT, "the gated read uses whole output rows");
-  constexpr int NO = G ? NDW - 1 : NDW;  // value tiles read out (gated: no denominator)
+  // denominators from the key Gram matrix (see below) instead of the ones-column tile
+  constexpr bool ZD = S::kGramDen;
+  static_assert(!ZD || (DK == 16 && NDW == NDT && !G && CF::NSL == 1), "Gram denominators: d = 16, whole rows");
+  constexpr int NO = (G || ZD) ? NDW - 1 : NDW;  // value tiles read out
   constexpr int SH = Schedule<FM>::SH;
   const int g = lane >> 4, r = lane & 15;
   const int qt_max = L.qt[NSLOT - 1] > L.qt[0] ? L.qt[NSLOT - 1] : L.qt[0];
@@ -1328,10 +1359,32 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
   }
   // intra-chunk term: squared causal scores.  The score product has K = d:
   // one 16x16x16 product at d = 16, one 16x16x32 product at d = 32.
+  //
+  // Gram denominators (ZD): the prefix part of query q's denominator is
+  // phi(q) . z = q^T Z q with Z = sum_s k_s k_s^T, the 16 x 16 Gram matrix of
+  // the keys before the chunk (bf16 copy from `src`).  One 16x16x16 product
+  // E = Z Q^T gives lane (g, r) the entries 4g + i of Z q_r, which it dots with
+  // dimensions 4g + i of q_r; the chunk part is the sum of the query's weights
+  // (the bf16 values the numerator uses).  The four lane groups' shares are
+  // summed at the end.
+  float den[NSLOT];
+#pragma unroll
+  for (int slot = 0; slot < NSLOT; ++slot) den[slot] = 0.f;
   if constexpr (CF::SLICE == 0) {
   ScoreOp<FM> qf[NSLOT];
 #pragma unroll
   for (int slot = 0; slot < NSLOT; ++slot) qf[slot] = src.score_q(16 * L.qt[slot] + r, g);
+  if constexpr (ZD) {
+    const uint2 zop = src.gram_op(r, g);
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) {
+      const f32x4 e = score_mfma<16>(zop, qf[slot]);
+      float d = lo_bf16(qf[slot].x) * e[0];
+      d = __builtin_fmaf(hi_bf16(qf[slot].x), e[1], d);
+      d = __builtin_fmaf(lo_bf16(qf[slot].y), e[2], d);
+      den[slot] = __builtin_fmaf(hi_bf16(qf[slot].y), e[3], d);
+    }
+  }
 #pragma unroll
   for (int s = 0; s < C / 32; ++s) {
     if (2 * s > qt_max) break;
@@ -1399,6 +1452,17 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
                         pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
 #pragma unroll
       for (int i = 0; i < NO; ++i) o[slot][i] = mfma(bv[i], pf, o[slot][i]);
+      if constexpr (ZD) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) den[slot] = dot2_bf16(pf[i], kOnesBf16x2, den[slot]);
+      }
+    }
+  }
+  if constexpr (ZD) {
+#pragma unroll
+    for (int slot = 0; slot < NSLOT; ++slot) {
+      den[slot] += __shfl_xor(den[slot], 16);
+      den[slot] += __shfl_xor(den[slot], 32);
     }
   }
   }  // intra-chunk term
@@ -1446,9 +1510,11 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 #pragma unroll
   for (int slot = 0; slot < NSLOT; ++slot) {
     float inv = 1.f;  // the gated read has no denominator
-    if constexpr (!G) {
-      const float den = __shfl(o[slot][NDW - 1][0], r);
-      inv = __builtin_amdgcn_rcpf(den + eps);
+    if constexpr (ZD) {
+      inv = __builtin_amdgcn_rcpf(den[slot] + eps);
+    } else if constexpr (!G) {
+      const float dn = __shfl(o[slot][NDW - 1][0], r);
+      inv = __builtin_amdgcn_rcpf(dn + eps);
     }
     if constexpr (CF::STAGE_OUT) {
       // whole rows: stage the 16 x 64 tile in the wave's LDS tile, then
@@ -1582,9 +1648,10 @@ __device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C, G>& b, const ChunkSrc
 
 template <int C, bool G = false>
 struct DmaSrc16 {
+  static constexpr bool kGramDen = !G;
   const DmaTileQ16<C, G>& b;
   const TrOffsets& to;
-  const u32x4& bones;
+  const uint16_t* gram;  // bf16 Z, 16 x 16 row-major (ungated read)
   __device__ __forceinline__ float4 qrow4(int row, int c4) const {
     const uint2 x = *reinterpret_cast<const uint2*>(&b.q[row * 16 + 4 * c4]);
     return make_float4(lo_bf16(x.x), hi_bf16(x.x), lo_bf16(x.y), hi_bf16(x.y));
@@ -1596,7 +1663,11 @@ struct DmaSrc16 {
     return *reinterpret_cast<const uint2*>(&b.k[row * 16 + 4 * g]);
   }
   __device__ __forceinline__ u32x4 v_op(int vt, int s, int lane) const {
-    return vt == NDT - 1 ? bones : tr_operand<DV>(b.v, to.v[vt], s);
+    return tr_operand<DV>(b.v, to.v[vt], s);
+  }
+  // Z[r][4g .. 4g + 3], the A operand of E = Z Q^T
+  __device__ __forceinline__ uint2 gram_op(int r, int g) const {
+    return *reinterpret_cast<const uint2*>(&gram[r * 16 + 4 * g]);
   }
   __device__ __forceinline__ float gate(int row) const { return b.gb[row]; }
   __device__ __forceinline__ float4 gate4(int row) const {
@@ -1605,10 +1676,12 @@ struct DmaSrc16 {
 };
 
 // state carry of the readout: wave W owns feature tiles W, W + 4 (and 8 for
-// wave 0), the whole state being needed for the next chunk's state copy
+// wave 0), the whole state being needed for the next chunk's state copy.
+// The value tiles only: the ungated read carries z as the Gram matrix
+// Z += K^T K (wave 0; the transposing key read is both operands).
 template <class CF, int W, bool G = false>
-__device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], const DmaTileQ16<CF::C, G>& b,
-                                                  const u32x4& bones, const TrOffsets& to) {
+__device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], f32x4& gram,
+                                                  const DmaTileQ16<CF::C, G>& b, const TrOffsets& to) {
   static_assert((CF::NW == 4 || CF::NW == 8) && CF::NFT == 9, "d = 16 tiling");
   float beta_c = 0.f;
   if constexpr (G) {
@@ -1620,8 +1693,8 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], co
     u32x4 bv[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], ks);
-    bv[NDT - 1] = bones;
     const u32x4 kb = tr_operand<16>(b.k, to.k, ks);
+    if constexpr (!G && W == 0) gram = mfma(kb, kb, gram);
     float kr[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1629,7 +1702,7 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], co
       kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
     }
     if constexpr (G) gate_keys(kr, b.gb, beta_c, ks);
-    constexpr int N = G ? NDT - 1 : NDT, NW = CF::NW;
+    constexpr int N = NDT - 1, NW = CF::NW;
     // wave W owns feature tiles W, W + NW, ... (below 9)
     tile16_into<W, N>(acc[0], kr, bv);
     if constexpr (W + NW < 9) tile16_into<W + NW, N>(acc[1], kr, bv);
@@ -1637,9 +1710,36 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], co
   }
 }
 
+// d = 16: the key Gram matrix Z = sum_s k_s k_s^T of a span state (zero for
+// none).  The state's z column holds, on tile J's row R, 2 Z[R][R + J mod 16]
+// (key features are built from sqrt(2) k); Z is symmetric, so each entry sits
+// on a tile J <= 8.  Lane (g, r) gets Z[4g + i][r], the accumulator layout.
+template <class CF>
+__device__ __forceinline__ f32x4 load_gram16(const float* __restrict__ P, int lane) {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  if (P == nullptr) return z;
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i, j = (r - row) & 15;
+    z[i] = 0.5f * P[CF::ZOFF + (j <= 8 ? 16 * j + row : 16 * (16 - j) + r)];
+  }
+  return z;
+}
+
+// bf16 copy of Z, row-major: lane (g, r) holds Z[4g + i][r] = Z[r][4g + i]
+__device__ __forceinline__ void write_gram16(uint16_t* __restrict__ zb, const f32x4& z, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  *reinterpret_cast<uint2*>(&zb[16 * r + 4 * g]) = make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3]));
+}
+
 // The kernel body, a device function taking the arguments by reference (this
 // form compiles to slightly fewer registers and branches than the body in the
 // kernel itself, and measured 2% faster at T = 131072).
+//
+// Denominators (ungated read): no ones-column tile.  Wave 0 carries the key
+// Gram matrix Z (one 16x16x32 product per 32 keys, against 9 for a ones
+// column over the feature tiles) and publishes its bf16 copy with Sb.
 template <int C, bool G>
 __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   using CF = Cfg<16, C>;
@@ -1647,8 +1747,8 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   static_assert(CF::NDW == NDT, "whole output rows per wave");
   __shared__ DmaTileQ16<C, G> x0;
   __shared__ DmaTileQ16<C, G> x1;
-  // the ones-column tile (the gated read has none: no denominator)
-  __shared__ alignas(16) uint16_t ones[G ? 8 : 128];
+  // bf16 Z (the gated read has no denominator)
+  __shared__ alignas(16) uint16_t Zb[G ? 4 : 256];
   __shared__ alignas(16) uint16_t Sb[VROWS * SB_LD];
   __shared__ alignas(16) uint16_t Ob[CF::STAGE_OUT ? CF::NW : 1][16 * OB_LD];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1662,7 +1762,6 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     const int c = e % CF::NPOS;
     if (sb_col_unused<CF>(c)) Sb[(e / CF::NPOS) * SB_LD + c] = 0;
   }
-  if (!G && tid < 128) ones[tid] = tid < 64 ? static_cast<uint16_t>(0x3f80u) : static_cast<uint16_t>(0);
   with_wave<CF::NW>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
     // output stores a wave issues per chunk: two 1 KB stores per query tile,
@@ -1671,9 +1770,14 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     const ReadoutLane<CF> L = readout_lane<CF>(W, lane);
     const TrOffsets to = tr_offsets(lane);
     f32x4 acc[CF::MFT][NDT];
-    load_state<CF>(acc, a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr,
-                   W, lane);
-    write_sb<CF>(Sb, acc, W, lane);
+    const float* prefix = a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
+    load_state<CF>(acc, prefix, W, lane);
+    write_sb<CF, NDT - 1>(Sb, acc, W, lane);
+    f32x4 gram = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!G && W == 0) {
+      gram = load_gram16<CF>(prefix, lane);
+      write_gram16(Zb, gram, lane);
+    }
     const int64_t first = span_first_chunk(a, sp) * C;
     int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
@@ -1683,9 +1787,6 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     // retires the state loads for the compiler's wait-count analysis
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    // the ones-column tile: row 0 of `ones` is all ones, row 1 all zeros
-    u32x4 bones = {0u, 0u, 0u, 0u};
-    if constexpr (!G) bones = *reinterpret_cast<const u32x4*>(&ones[((lane & 15) > 0 ? 64 : 0) + 8 * (lane >> 4)]);
 
     // one chunk: prefetch the next into the other buffer, read out, and
     // (unless it is the span's last) carry the state and refresh Sb
@@ -1700,11 +1801,11 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
         __builtin_amdgcn_sched_barrier(0);
       };
       readout_chunk<CF, DmaSrc16<C, G>, decltype(prefetch), G>(
-          DmaSrc16<C, G>{cur, to, bones}, Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c, n, 2 * DV),
+          DmaSrc16<C, G>{cur, to, Zb}, Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c, n, 2 * DV),
           Ob[CF::STAGE_OUT ? W : 0],
           prefetch);
       const bool more = c + C < end;
-      if (more) state_update_ro16<CF, W, G>(acc, cur, bones, to);
+      if (more) state_update_ro16<CF, W, G>(acc, gram, cur, to);
       // this wave's share of the next chunk has landed (the output stores
       // issued after it may still be in flight).  Unconditional, so that on
       // every path the compiler's wait counts see the transfer retired.
@@ -1712,7 +1813,8 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
       if (more) {
         // every wave is done reading `cur` and Sb, and the next chunk is visible
         barrier_lds();
-        write_sb<CF>(Sb, acc, W, lane);
+        write_sb<CF, NDT - 1>(Sb, acc, W, lane);
+        if constexpr (!G && W == 0) write_gram16(Zb, gram, lane);
         barrier_lds();
       }
     };

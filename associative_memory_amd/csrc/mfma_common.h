@@ -71,6 +71,12 @@ __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float lo_bf16(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// lo(a) lo(b) + hi(a) hi(b) + c for bf16 pairs, fp32 accumulation
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+constexpr uint32_t kOnesBf16x2 = 0x3f803f80u;  // (1, 1) in bf16
+
 // Score products Sc^T[key][query] = K Q^T with K = d.  At d = 16 the
 // 16x16x16 form takes 4 bf16 per lane (k = 4g + i); at d = 32 the 16x16x32
 // form takes 8 (k = 8g + i).
