@@ -257,3 +257,28 @@ def test_profiled_entry_matches_plain(scan):
     assert hip.ms(hs[1], hs[2]) >= 0.0 and hip.ms(hs[3], hs[4]) >= 0.0  # stages in order
     for h in hs:
         hip.destroy(h)
+
+
+@pytest.mark.parametrize("chunk", (64, 128))
+def test_denominator_edges(chunk):
+    # Zero keys over whole spans leave the carried key Gram matrix exactly 0,
+    # so those rows read 0 / (0 + eps) = 0; a zero gap in the middle keeps it
+    # constant across spans; zero query rows read 0; keys and queries scaled
+    # by 4 raise q^T Z q by 256; a large eps weighs in on every row.
+    B, H, T, d, dv = 1, 2, 20000, 16, 64
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.BF16, seed=91)
+    q, k = inp.q64.copy(), inp.k64.copy()
+    k[0, 0, :9000] = 0.0
+    k[0, 1, 5000:15000] = 0.0
+    q[:, :, ::97] = 0.0
+    for scale, eps in ((1.0, 1e-6), (4.0, 1e-6), (1.0, 10.0)):
+        qs, q64 = ki.as_storage(q * scale, ki.BF16)
+        ks, k64 = ki.as_storage(k * scale, ki.BF16)
+        alt = ki.ForwardInputs(qs, ks, inp.v, q64, k64, inp.v64, ki.BF16)
+        what = f"chunk={chunk} scale={scale} eps={eps}"
+        say(f"forward denominator edges {what}")
+        got = run(alt, chunk, eps)
+        ref = orc.forward_quadratic(q64, k64, inp.v64, eps)
+        check(got, ref, ki.BF16, np.abs(inp.v64).max(), what)
+        assert np.all(got[0, 0, :9000] == 0.0), "rows with no nonzero key before them"
+        assert np.all(got[:, :, ::97] == 0.0), "zero query rows"
