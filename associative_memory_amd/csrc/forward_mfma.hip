@@ -698,7 +698,7 @@ __device__ __forceinline__ float row_rotate(float x) {
 // k-step and takes the partner dimension from lane r + J of its row, so the
 // features of every tile come from one 32-byte read per lane and k-step.
 // Rows 8..15 of tile 8 repeat rows 0..7; the state copy drops them.
-// N: value tiles updated (the gated read leaves out the ones-column tile)
+// N: value tiles updated (the d = 16 DMA kernels leave out the ones-column tile)
 template <int J, int N = NDT>
 __device__ __forceinline__ void tile16_into(f32x4 (&dst)[NDT], const float (&kr)[8], const u32x4 (&bv)[NDT]) {
   float f[8];
@@ -1504,9 +1504,10 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
       return;
     }
   }
-  // normalise and store: lane r of group 0 holds the denominator of query r
-  // (the last readout value tile of every wave is the ones-column tile);
-  // rows past T fall outside `dst` and are dropped
+  // normalise and store: with the ones-column tile (the last readout value
+  // tile of every wave) lane r of group 0 holds the denominator of query r;
+  // with Gram denominators every lane holds its query's.  Rows past T fall
+  // outside `dst` and are dropped
 #pragma unroll
   for (int slot = 0; slot < NSLOT; ++slot) {
     float inv = 1.f;  // the gated read has no denominator
