@@ -4,8 +4,9 @@
 //
 // One workgroup per head.  The head's state S[D][dv] (fp32, dv contiguous) is
 // streamed once: every thread owns a float4 column group and a strided set of
-// rows, loads all its rows first (so each lane has all its loads in flight),
-// adds phi(k)_r v, stores, and accumulates phi(q)_r S'_r.  Column sums across
+// rows, loads all its rows first (so each lane has all its loads in flight,
+// issued before the feature products), adds phi(k)_r v, stores, and
+// accumulates phi(q)_r S'_r.  Column sums across
 // the row groups and the denominator phi(q).z' are reduced through LDS.
 //
 // GATED: the GatedKATA step (App. F.4), S_t = gamma_t S_{t-1} + psi(k_t) v_t^T,
@@ -37,19 +38,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
   const int64_t bh = blockIdx.x;
   const int tid = threadIdx.x;
-  if (tid < DK) {
-    xq[tid] = load_elem<BF16>(q, bh * DK + tid);
-    xk[tid] = load_elem<BF16>(k, bh * DK + tid);
-  }
-  __syncthreads();
-  for (int f = tid; f < D; f += kThreads) {
-    int i, j;
-    pair_of(f, DK, i, j);
-    const float w = (i == j) ? 1.0f : kSqrt2;
-    pq[f] = w * xq[i] * xq[j];
-    pk[f] = w * xk[i] * xk[j];
-  }
 
+  // q and k go out first, then the state, z and v loads: loads retire in
+  // order, so q and k reach LDS without waiting for the state, and the state's
+  // latency overlaps the barrier and the feature products.
+  float qx = 0.f, kx = 0.f;
+  if (tid < DK) {
+    qx = load_elem<BF16>(q, bh * DK + tid);
+    kx = load_elem<BF16>(k, bh * DK + tid);
+  }
   const int r0 = tid / TPR;
   const int c4 = tid - r0 * TPR;
   float4 vv;
@@ -76,6 +73,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   }
   float gamma = 1.f;
   if constexpr (GATED) gamma = __expf(log_gamma[bh]);
+
+  if (tid < DK) {
+    xq[tid] = qx;
+    xk[tid] = kx;
+  }
+  __syncthreads();
+  for (int f = tid; f < D; f += kThreads) {
+    int i, j;
+    pair_of(f, DK, i, j);
+    const float w = (i == j) ? 1.0f : kSqrt2;
+    pq[f] = w * xq[i] * xq[j];
+    pk[f] = w * xk[i] * xk[j];
+  }
   __syncthreads();  // pq / pk ready
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -123,13 +133,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   __syncthreads();
 
   if (tid < DV) {
+    // column tid of the row groups' partial sums (red[r] holds DV floats)
+    const float* redf = reinterpret_cast<const float*>(&red[0][0]);
     float tot = 0.f;
-    const int cg = tid >> 2;
-    const int lane = tid & 3;
-    for (int r = 0; r < RPP; ++r) {
-      const float4 x = red[r][cg];
-      tot += (lane == 0) ? x.x : (lane == 1) ? x.y : (lane == 2) ? x.z : x.w;
-    }
+#pragma unroll
+    for (int r = 0; r < RPP; ++r) tot += redf[r * DV + tid];
     if constexpr (GATED) {
       store_elem<BF16>(out, bh * DV + tid, tot);
     } else {
