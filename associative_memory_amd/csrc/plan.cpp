@@ -18,6 +18,14 @@ constexpr int64_t mfma_target_workgroups(int d) { return d == 16 ? 512 : 256; }
 // issues ahead of the second (measured at 8 heads x 64 spans of 16 chunks:
 // readout 84 -> 81 us, span sums 38 -> 37 us)
 constexpr int64_t kPairSkewDiv = 8;
+// d = 16 matrix-core path: spans of at least this many tokens, as long as
+// the readout keeps one workgroup per CU.  Below it a span's 37 KB state
+// (written, scanned, read back) costs more than the extra workgroups give
+// (B=4 H=8 T=2048, chunk 64 / 128: 16 spans per head 30.4 / 31.4 us, 8 spans
+// 28.7 / 28.5 us, 4 spans 34.7 / 31.0 us); from T = 8192 on the workgroup
+// target already gives spans of 256 tokens or more.
+constexpr int64_t kMinSpanTokens16 = 256;
+constexpr int64_t kMinReadoutWorkgroups16 = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -47,6 +55,10 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   // enough spans to give the readout about the target number of workgroups
   int64_t spans = ceil_div(mfma ? mfma_target_workgroups(d) : kTargetWorkgroups, p.BH * tiles);
   if (spans > p.n_chunks) spans = p.n_chunks;
+  if (mfma && d == 16 && spans > T / kMinSpanTokens16 && T >= kMinSpanTokens16) {
+    const int64_t cap = T / kMinSpanTokens16;
+    if (ceil_div(p.n_chunks, ceil_div(p.n_chunks, cap)) * p.BH >= kMinReadoutWorkgroups16) spans = cap;
+  }
   if (spans < 1) spans = 1;
   p.G = ceil_div(p.n_chunks, spans);
   if (ceil_div(p.n_chunks, p.G) > kMaxSpans) p.G = ceil_div(p.n_chunks, kMaxSpans);
