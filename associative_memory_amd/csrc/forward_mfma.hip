@@ -830,8 +830,10 @@ __host__ __device__ constexpr bool sb_col_unused(int c) {
 }
 
 // bf16 copy of the owned state tiles into Sb[value row][feature position]
-// (ND: value tiles copied; the d = 16 DMA readout keeps no z column in Sb)
-template <class CF, int ND = NDT>
+// (ND: value tiles copied; the d = 16 DMA readout keeps no z column in Sb.
+// HALF_DIAG: feature tile 0, the diagonal pairs at d = 16, is stored halved,
+// so the query's diagonal features need no factor 1/2.)
+template <class CF, int ND = NDT, bool HALF_DIAG = false>
 __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 (&acc)[CF::MFT][NDT],
                                          int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
@@ -846,8 +848,9 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
       // ones-column tile: column 0 is z (row 64), the rest are zero (row 65)
       if (dt == NDT - 1 && r > 1) continue;
       uint2 o;
-      o.x = dup ? 0u : pack2(acc[m][dt][0], acc[m][dt][1]);
-      o.y = dup ? 0u : pack2(acc[m][dt][2], acc[m][dt][3]);
+      const float h = HALF_DIAG && ft == 0 ? 0.5f : 1.f;
+      o.x = dup ? 0u : pack2(h * acc[m][dt][0], h * acc[m][dt][1]);
+      o.y = dup ? 0u : pack2(h * acc[m][dt][2], h * acc[m][dt][3]);
       *reinterpret_cast<uint2*>(&Sb[vrow(dt, r) * CF::SB_LD + sb_col<CF>(ft, g)]) = o;
     }
   }
@@ -1251,6 +1254,7 @@ __device__ __forceinline__ ReadoutLane<CF> readout_lane(int w, int lane) {
 template <class CF>
 struct TileSrc {
   static constexpr bool kGramDen = false;  // denominators from the ones-column tile
+  static constexpr bool kHalfDiag = false;  // Sb holds the diagonal features at full weight
   const Tiles<CF>& tl;
   __device__ __forceinline__ float4 qrow4(int row, int c4) const {
     return *reinterpret_cast<const float4*>(&tl.Qf[row * CF::QF_LD + 4 * c4]);
@@ -1349,7 +1353,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
           f[i] = 0.f;
         } else {
           const int pa = kSched<FM>.a[e], pb = kSched<FM>.b[e];
-          f[i] = (pa == pb) ? (0.5f * qr[slot][pa]) * qr[slot][pa] : qr[slot][pa] * qr[slot][pb];
+          f[i] = (pa == pb && !S::kHalfDiag) ? (0.5f * qr[slot][pa]) * qr[slot][pa] : qr[slot][pa] * qr[slot][pb];
         }
       }
       const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
@@ -1461,8 +1465,13 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
   if constexpr (ZD) {
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
-      den[slot] += __shfl_xor(den[slot], 16);
-      den[slot] += __shfl_xor(den[slot], 32);
+      // the four 16-lane rows: swap odd and even rows, then the two halves;
+      // each swap returns both registers, whose sum is the pairwise sum
+      const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(den[slot]), __float_as_uint(den[slot]),
+                                                        false, false);
+      const float d2 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d2), __float_as_uint(d2), false, false);
+      den[slot] = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
     }
   }
   }  // intra-chunk term
@@ -1650,6 +1659,7 @@ __device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C, G>& b, const ChunkSrc
 template <int C, bool G = false>
 struct DmaSrc16 {
   static constexpr bool kGramDen = !G;
+  static constexpr bool kHalfDiag = !G;  // Sb's diagonal tile is stored halved
   const DmaTileQ16<C, G>& b;
   const TrOffsets& to;
   const uint16_t* gram;  // bf16 Z, 16 x 16 row-major (ungated read)
@@ -1773,7 +1783,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     f32x4 acc[CF::MFT][NDT];
     const float* prefix = a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
     load_state<CF>(acc, prefix, W, lane);
-    write_sb<CF, NDT - 1>(Sb, acc, W, lane);
+    write_sb<CF, NDT - 1, DmaSrc16<C, G>::kHalfDiag>(Sb, acc, W, lane);
     f32x4 gram = {0.f, 0.f, 0.f, 0.f};
     if constexpr (!G && W == 0) {
       gram = load_gram16<CF>(prefix, lane);
@@ -1814,7 +1824,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
       if (more) {
         // every wave is done reading `cur` and Sb, and the next chunk is visible
         barrier_lds();
-        write_sb<CF, NDT - 1>(Sb, acc, W, lane);
+        write_sb<CF, NDT - 1, DmaSrc16<C, G>::kHalfDiag>(Sb, acc, W, lane);
         if constexpr (!G && W == 0) write_gram16(Zb, gram, lane);
         barrier_lds();
       }
