@@ -1023,6 +1023,10 @@ __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gb, float
 // The value tiles only.  z is carried as the key Gram matrix Z = K^T K (the
 // transposing key read is both operands) by the wave that takes tile 8 on
 // the k-step, in the place of tile 8's ones-column tile (acc8[NDT - 1]).
+// The key features are built from k, not sqrt(2) k: every feature, and so
+// the stored value tiles, come out exactly half the state's (scaling by 2 is
+// exact in bf16 and fp32), which saves a multiply per key value; the readout
+// doubles what it loads.
 template <class CF, int W, bool G = false>
 __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f32x4 (&acc8)[NDT],
                                                    const DmaTile16<CF::C, G>& b, const TrOffsets& to) {
@@ -1043,8 +1047,8 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
     float kr[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      kr[2 * i] = kSqrt2 * lo_bf16(kb[i]);
-      kr[2 * i + 1] = kSqrt2 * hi_bf16(kb[i]);
+      kr[2 * i] = lo_bf16(kb[i]);
+      kr[2 * i + 1] = hi_bf16(kb[i]);
     }
     if constexpr (G) gate_keys(kr, b.gk, ks);
     constexpr int N = NDT - 1;
@@ -1783,6 +1787,12 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     f32x4 acc[CF::MFT][NDT];
     const float* prefix = a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
     load_state<CF>(acc, prefix, W, lane);
+    // the d = 16 span sums store the value tiles halved
+#pragma unroll
+    for (int m = 0; m < CF::MFT; ++m) {
+#pragma unroll
+      for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] *= 2.f;
+    }
     write_sb<CF, NDT - 1, DmaSrc16<C, G>::kHalfDiag>(Sb, acc, W, lane);
     f32x4 gram = {0.f, 0.f, 0.f, 0.f};
     if constexpr (!G && W == 0) {
