@@ -76,7 +76,7 @@ kata_status_t check_linear_shape(int B, int H, int64_t T, int d, int dv, int chu
 }
 
 // Workspace of the gated read: span states (when there are several spans),
-// then the running gate sums [BH*T], the key factors [BH*T] and the chunk
+// then half the running gate sums [BH*T], the key factors [BH*T] and the chunk
 // totals [BH][n_chunks], each 256-byte aligned.
 struct GatedLayout {
   ForwardPlan p;

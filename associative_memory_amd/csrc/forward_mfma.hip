@@ -914,8 +914,8 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
 // consecutive rows.  The two buffers are distinct LDS variables and the loop
 // is unrolled over them, so the compiler's wait counts see that a chunk
 // arriving in one buffer does not alias reads of the other.
-// Gated read only: the chunk's running gate sums beta_t (log2 units, see
-// gate_prep_kernel) and, in the span-sum tiles, the key factors
+// Gated read only: half the chunk's running gate sums, beta_t / 2 (log2
+// units, see gate_prep_kernel) and, in the span-sum tiles, the key factors
 // 2^((beta_C - beta_t) / 2), each filled by one DMA instruction of C/4 lanes
 // (entries past the sequence read as 0).  The ungated tiles carry nothing
 // (empty base).  The readout tiles leave the key factors out (at C = 128
@@ -1009,7 +1009,7 @@ __device__ __forceinline__ float row_slot(float f) {
 __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gb, float beta_c, int ks) {
   const int lane = __lane_id(), g = lane >> 4, r = lane & 15;
   const int t = 32 * ks + 4 * g + (r & 3) + 16 * ((r >> 2) & 1);
-  const float f = __builtin_amdgcn_exp2f(0.5f * (beta_c - gb[t]));
+  const float f = __builtin_amdgcn_exp2f(beta_c - gb[t]);  // both halved
   kr[0] *= row_slot<0>(f);
   kr[1] *= row_slot<1>(f);
   kr[2] *= row_slot<2>(f);
@@ -1033,7 +1033,7 @@ __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f
   static_assert(CF::NW == 4 && CF::NFT == 9, "d = 16 tiling");
   if constexpr (G) {
     // the chunk's decay 2^beta_C (beta at its last token)
-    const float f = __builtin_amdgcn_exp2f(b.gb[CF::C - 1]);
+    const float f = __builtin_amdgcn_exp2f(2.f * b.gb[CF::C - 1]);  // gb holds beta / 2
     gate_decay(acc, f);
     f32x4(&a8)[1][NDT] = *reinterpret_cast<f32x4(*)[1][NDT]>(&acc8);
     gate_decay(a8, f);
@@ -1286,8 +1286,8 @@ struct PartRows {
 // `after_q` runs once the query rows are in registers (the DMA readout issues
 // the next chunk's transfer there)
 //
-// G (gated read): the source also gives the chunk's running gate sums beta_t
-// (log2 units).  The inter term of query t is 2^beta_t phi(q_t) S, so the
+// G (gated read): the source also gives half the chunk's running gate sums,
+// beta_t / 2 (log2 units).  The inter term of query t is 2^beta_t phi(q_t) S, so the
 // query row is scaled by 2^(beta_t / 2); the intra score of key s is weighted
 // by 2^(beta_t - beta_s); there is no denominator.
 //
@@ -1331,7 +1331,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 #pragma unroll
     for (int slot = 0; slot < NSLOT; ++slot) {
       bq[slot] = src.gate(16 * L.qt[slot] + r);
-      const float f = __builtin_amdgcn_exp2f(0.5f * bq[slot]);
+      const float f = __builtin_amdgcn_exp2f(bq[slot]);  // the source holds beta / 2
 #pragma unroll
       for (int c = 0; c < DK; ++c) qr[slot][c] *= f;
     }
@@ -1438,12 +1438,13 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
             sc = score_mfma<DK>(kf[h], qf[slot]);
           }
           if constexpr (G) {
-            // p = sc^2 2^(beta_q - beta_k): fold the root of the weight into sc
+            // p = sc^2 2^(beta_q - beta_k): fold the root of the weight,
+            // 2^(beta_q / 2 - beta_k / 2), into sc
             const float4 bk = src.gate4(16 * kt + 4 * g);
-            sc[0] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.x));
-            sc[1] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.y));
-            sc[2] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.z));
-            sc[3] *= __builtin_amdgcn_exp2f(0.5f * (bq[slot] - bk.w));
+            sc[0] *= __builtin_amdgcn_exp2f(bq[slot] - bk.x);
+            sc[1] *= __builtin_amdgcn_exp2f(bq[slot] - bk.y);
+            sc[2] *= __builtin_amdgcn_exp2f(bq[slot] - bk.z);
+            sc[3] *= __builtin_amdgcn_exp2f(bq[slot] - bk.w);
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) s2[j] = sc[j] * sc[j];
@@ -1700,8 +1701,8 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], f3
   static_assert((CF::NW == 4 || CF::NW == 8) && CF::NFT == 9, "d = 16 tiling");
   float beta_c = 0.f;
   if constexpr (G) {
-    beta_c = b.gb[CF::C - 1];
-    gate_decay(acc, __builtin_amdgcn_exp2f(beta_c));
+    beta_c = b.gb[CF::C - 1];  // beta_C / 2
+    gate_decay(acc, __builtin_amdgcn_exp2f(2.f * beta_c));
   }
 #pragma unroll
   for (int ks = 0; ks < CF::C / 32; ++ks) {

@@ -53,8 +53,8 @@ hipError_t launch_scan_sequential(float* ws, int64_t BH, int64_t n_spans,
 hipError_t launch_scan_associative(float* ws, int64_t BH, int64_t n_spans,
                                    int64_t E, hipStream_t stream);
 
-// Gated read: running gate sums per chunk, beta_t = log2(e) * sum of
-// log_gamma from the chunk start to t (gb[BH*T]), key factors
+// Gated read: half the running gate sums per chunk, beta_t / 2 with
+// beta_t = log2(e) * sum of log_gamma from the chunk start to t (gb[BH*T]), key factors
 // 2^((beta_C - beta_t) / 2) with beta_C the chunk's last beta (gk[BH*T]), and
 // chunk totals (ctot[BH][ceil(T/chunk)]); chunk 64 or 128.
 hipError_t launch_gate_prep(const float* log_gamma, float* gb, float* gk, float* ctot, int64_t BH,

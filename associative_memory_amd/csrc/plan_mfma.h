@@ -42,7 +42,7 @@ struct MfmaArgs {
   // chunks, the even span of a pair GL chunks and the odd one 2G - GL
   int64_t GL = 0;
   float eps;
-  const float* gb = nullptr;  // gated read: running gate sums per token, log2 units
+  const float* gb = nullptr;  // gated read: half the running gate sums per token, log2 units
   const float* gk = nullptr;  // gated read: key factors 2^((beta_C - beta_t) / 2) per token
   float* part = nullptr;      // sliced maps: fp32 partial reads [BH*T][68]
   int fm = 0;                 // sliced maps: 100 + slice (KATA-M1), 200 + slice (KATA-M2)

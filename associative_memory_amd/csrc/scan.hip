@@ -185,12 +185,14 @@ hipError_t launch_blocked(float* ws, const float* ctot, int64_t BH, int64_t N, i
 // phi(k_t) v_t^T makes the prefix over spans affine, P_0 = 0,
 // P_{j+1} = a_j P_j + A_j with a_j the product of the gates over span j.
 //
-// gate_prep_kernel: one wave per chunk of C tokens writes the running gate
-// sums beta_t = log2(e) sum_{c0 <= r <= t} log gamma_r (inclusive, from the
-// chunk start c0), the key factors 2^((beta_C - beta_t) / 2) that scale key
-// row t in the chunk's state update (beta_C = beta at the chunk's last
-// token), and the chunk total; a lane holds C/64 consecutive tokens.
-constexpr float kLog2e = 1.44269504088896340736f;
+// gate_prep_kernel: one wave per chunk of C tokens writes half the running
+// gate sums, beta_t / 2 with beta_t = log2(e) sum_{c0 <= r <= t} log gamma_r
+// (inclusive, from the chunk start c0; the readout's factors are all square
+// roots 2^((beta_t - beta_s) / 2), so the halves save a multiply each), the
+// key factors 2^((beta_C - beta_t) / 2) that scale key row t in the chunk's
+// state update (beta_C = beta at the chunk's last token), and the chunk total
+// beta_C; a lane holds C/64 consecutive tokens.
+constexpr float kHalfLog2e = 0.72134752044448170368f;
 
 template <int C>
 __global__ __launch_bounds__(kThreads) void gate_prep_kernel(const float* __restrict__ lg,
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void gate_prep_kernel(const float* __rest
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int64_t t = t0 + i;
-    run += (t < T) ? lg[bh * T + t] * kLog2e : 0.f;
+    run += (t < T) ? lg[bh * T + t] * kHalfLog2e : 0.f;
     x[i] = run;
   }
   float incl = run;  // inclusive prefix of the lane totals over the wave
@@ -219,15 +221,15 @@ __global__ __launch_bounds__(kThreads) void gate_prep_kernel(const float* __rest
     if (lane >= off) incl += y;
   }
   const float excl = incl - run;
-  const float beta_c = __shfl(excl + x[PER - 1], 63);
+  const float beta_c = __shfl(excl + x[PER - 1], 63);  // beta_C / 2
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     if (t0 + i < T) {
       gb[bh * T + t0 + i] = excl + x[i];
-      gk[bh * T + t0 + i] = __builtin_amdgcn_exp2f(0.5f * (beta_c - (excl + x[i])));
+      gk[bh * T + t0 + i] = __builtin_amdgcn_exp2f(beta_c - (excl + x[i]));
     }
   }
-  if (lane == 63) ctot[bh * n_chunks + c] = incl;
+  if (lane == 63) ctot[bh * n_chunks + c] = 2.f * incl;
 }
 
 // Sequential affine prefix in place over ws[BH][N][E]: one thread per (head,
