@@ -1024,9 +1024,9 @@ __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gb, float
 // transposing key read is both operands) by the wave that takes tile 8 on
 // the k-step, in the place of tile 8's ones-column tile (acc8[NDT - 1]).
 // The key features are built from k, not sqrt(2) k: every feature, and so
-// the stored value tiles, come out exactly half the state's (scaling by 2 is
-// exact in bf16 and fp32), which saves a multiply per key value; the readout
-// doubles what it loads.
+// the stored value tiles, come out exactly kSpanValueScale = 1/2 of the
+// state's (scaling by 2 is exact in bf16 and fp32), which saves a multiply
+// per key value; the readout rescales what it loads.
 template <class CF, int W, bool G = false>
 __device__ __forceinline__ void state_update_dma16(f32x4 (&acc)[CF::MFT][NDT], f32x4 (&acc8)[NDT],
                                                    const DmaTile16<CF::C, G>& b, const TrOffsets& to) {
@@ -1106,10 +1106,19 @@ __device__ inline SpanOf sum_span(const MfmaArgs& a) {
   return {r / per_odd, 2 * (r % per_odd) + 1};
 }
 
+// Span-state layout at d = 16 (workspace, one state per span): the value
+// tiles hold kSpanValueScale times the state's value rows (the span sums
+// build key features from k, not sqrt(2) k), and the z column holds the
+// state's z at full scale.  The prefix sums both linearly, so the scales
+// carry through it; the readout divides the value tiles by kSpanValueScale
+// on load.
+constexpr float kSpanValueScale = 0.5f;
+
 // The z column of a span state from the key Gram matrix Z (lane (g, r)
-// holding Z[4g + i][r]): tile J's row R gets 2 Z[R][R + J mod 16] for
-// J = 0 .. 8, the value of the key features' sum (they are built from
-// sqrt(2) k).  Each (J, R) is written by the one lane holding that entry.
+// holding Z[4g + i][r]): tile J's row R gets z of the state's key features
+// (weight 2 on every pair, sqrt(2) k times sqrt(2) k), 2 Z[R][R + J mod 16]
+// for J = 0 .. 8, whatever scale the value tiles are stored at.  Each
+// (J, R) is written by the one lane holding that entry.
 template <class CF>
 __device__ __forceinline__ void store_gram16(const f32x4& z, float* __restrict__ P, int lane) {
   const int g = lane >> 4, r = lane & 15;
@@ -1728,8 +1737,9 @@ __device__ __forceinline__ void state_update_ro16(f32x4 (&acc)[CF::MFT][NDT], f3
 
 // d = 16: the key Gram matrix Z = sum_s k_s k_s^T of a span state (zero for
 // none).  The state's z column holds, on tile J's row R, 2 Z[R][R + J mod 16]
-// (key features are built from sqrt(2) k); Z is symmetric, so each entry sits
-// on a tile J <= 8.  Lane (g, r) gets Z[4g + i][r], the accumulator layout.
+// (the state's key features carry weight 2 on every pair; see store_gram16);
+// Z is symmetric, so each entry sits on a tile J <= 8.  Lane (g, r) gets
+// Z[4g + i][r], the accumulator layout.
 template <class CF>
 __device__ __forceinline__ f32x4 load_gram16(const float* __restrict__ P, int lane) {
   f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -1788,11 +1798,11 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     f32x4 acc[CF::MFT][NDT];
     const float* prefix = a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
     load_state<CF>(acc, prefix, W, lane);
-    // the d = 16 span sums store the value tiles halved
+    // the d = 16 span sums store the value tiles at kSpanValueScale
 #pragma unroll
     for (int m = 0; m < CF::MFT; ++m) {
 #pragma unroll
-      for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] *= 2.f;
+      for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] *= 1.f / kSpanValueScale;
     }
     write_sb<CF, NDT - 1, DmaSrc16<C, G>::kHalfDiag>(Sb, acc, W, lane);
     f32x4 gram = {0.f, 0.f, 0.f, 0.f};

@@ -100,9 +100,10 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     Finite inputs only (the generators never produce NaN/Inf).
     """
     f = round_f32(x)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    u = (u + 0x7FFF + lsb) >> 16
+    u = f.view(np.uint32)
+    # finite values stay below 0xFF800000, so the sum cannot wrap in 32 bits
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    u = (u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)
     return u.astype(np.uint16)
 
 

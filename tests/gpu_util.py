@@ -51,3 +51,44 @@ def check(got: np.ndarray, ref: np.ndarray, dtype: str, vmax: float, what: str =
     assert mx <= ABS_TOL[dtype] * vmax, f"{what}: max abs err {mx} > {ABS_TOL[dtype]} * {vmax}"
     assert rms_rel <= RMS_TOL[dtype], f"{what}: rms rel err {rms_rel} > {RMS_TOL[dtype]}"
     return mx, rms_rel
+
+
+# ------------------------------------------------------------------ guard bands
+#
+# An output (or state) tensor placed inside a larger buffer whose margins hold
+# a fill pattern: any write past either end of the tensor changes the pattern.
+GUARD = 4096  # elements on each side
+
+
+def _fill_bits(dtype):
+    # bf16 0x7FA5 and fp32 0x7FA5A5A5 are quiet NaNs no kernel writes
+    return 0x7FA5 if dtype == torch.bfloat16 else 0x7FA5A5A5
+
+
+def guarded(shape, dtype):
+    """(buffer, view): `view` of `shape` inside `buffer` with GUARD canary
+    elements on both sides."""
+    n = int(np.prod(shape))
+    if dtype == torch.bfloat16:
+        buf = torch.full((n + 2 * GUARD,), _fill_bits(dtype), dtype=torch.int16, device=DEV)
+        view = buf[GUARD:GUARD + n].view(torch.bfloat16).view(shape)
+    else:
+        buf = torch.full((n + 2 * GUARD,), _fill_bits(dtype), dtype=torch.int32, device=DEV)
+        view = buf[GUARD:GUARD + n].view(torch.float32).view(shape)
+    return buf, view
+
+
+def assert_guards(buf, what=""):
+    fill = int(buf[0].item())
+    head, tail = buf[:GUARD], buf[-GUARD:]
+    assert torch.all(head == fill) and torch.all(tail == fill), f"{what}: write outside the tensor"
+
+
+def guarded_workspace(need):
+    """(buffer, workspace view of `need` bytes, guard bytes after it)."""
+    buf = torch.full((need + GUARD,), 0x5A, dtype=torch.uint8, device=DEV)
+    return buf, buf[:max(need, 1)]
+
+
+def assert_workspace_guard(buf, need, what=""):
+    assert torch.all(buf[need:] == 0x5A), f"{what}: write past the workspace"

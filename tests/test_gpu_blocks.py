@@ -2,7 +2,8 @@
 fp64 oracle, through the C ABI: KATA-M4 (four blocks of 16), KATA-M2 (two
 blocks of 32, two slices of the feature axis) and the full map KATA-M1 (four
 slices).  Full outputs on ragged and multi-span shapes, sampled rows at the
-page's Table 8 shape (B = 8, H = 16, d_head = 64) and at T = 65536,
+page's Table 8 shape (B = 8, H = 16, d_head = 64) up to the T = 131072 the
+benchmark times, at T = 65536,
 agreement with the quadratic form of the same map, both prefix variants, and
 determinism."""
 import numpy as np
@@ -12,7 +13,8 @@ import torch
 import associative_memory_amd as am
 import kata_inputs as ki
 from oracle import kata_oracle as orc
-from gpu_util import check, say, to_dev, to_host64
+from gpu_util import (assert_guards, assert_workspace_guard, check, guarded, guarded_workspace, say,
+                      to_dev, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -95,3 +97,43 @@ def test_deterministic(g):
     y = am.kata_forward_chunked_blocks(q, k, v, g)
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("g", GS)
+def test_timed_shape_sampled_rows(g):
+    # B = 8, H = 16, T = 131072: the shape and launch plan the benchmark
+    # times, inputs drawn on the device as there; sampled rows of 6 heads
+    w = ki.table8(131072, g, 70)
+    say(f"chunked {w.name} (timed shape) sampled rows")
+    q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
+    out = am.kata_forward_chunked_blocks(q, k, v, g, chunk=64, eps=w.eps)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(71))
+    vmax = float(v.float().abs().max())
+    refs, gots = [], []
+    for n in range(6):
+        b, h = int(rng.integers(0, w.B)), int(rng.integers(0, w.H))
+        rows = sorted({0, 64, w.T // 2, w.T - 1} | {int(x) for x in rng.integers(0, w.T, 4)})
+        qh, kh, vh = (to_host64(x[b, h]) for x in (q, k, v))
+        refs.append(orc.forward_rows(qh, kh, vh, rows, w.eps, g=g))
+        gots.append(to_host64(out[b, h, rows]))
+    check(np.concatenate(gots), np.concatenate(refs), ki.BF16, vmax, f"{w.name} rows")
+
+
+@pytest.mark.parametrize("g", GS)
+@pytest.mark.parametrize("case", [(1, 2, 1000), (2, 1, 20000)], ids=lambda c: "B{}H{}T{}".format(*c))
+def test_guard_bands(case, g):
+    B, H, T = case
+    say(f"chunked M{g} guard bands {case}")
+    inp = ki.forward_inputs(B, H, T, 64, 64, ki.BF16, seed=T + 3 * g)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    buf, out = guarded((B, H, T, 64), torch.bfloat16)
+    need = int(am.lib().kata_forward_chunked_blocks_workspace_bytes(B, H, T, 64, 64, g, 64, 0))
+    wbuf, ws = guarded_workspace(need)
+    am.kata_forward_chunked_blocks(q, k, v, g, out=out, workspace=ws if need else None)
+    torch.cuda.synchronize()
+    assert_guards(buf, f"M{g} out")
+    assert_workspace_guard(wbuf, need, f"M{g} workspace")
+    if T <= 1000:
+        ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6, g=g)
+        check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"guarded M{g}")

@@ -7,7 +7,7 @@ import torch
 import associative_memory_amd as am
 import kata_inputs as ki
 from oracle import kata_oracle as orc
-from gpu_util import check, say, to_dev, to_host64
+from gpu_util import assert_guards, check, guarded, say, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -115,27 +115,65 @@ def test_checkpoint_resume_bitwise():
     assert torch.equal(S, S3) and torch.equal(z, z3)
 
 
-def test_decode_full_size_sampled_heads():
+def test_decode_full_size_all_steps():
+    # the 4096-head workload at its configured length: all 1024 steps on the
+    # device (every head), every step's output and the final state of eight
+    # heads spread over the range against the recurrence in fp64
     w = ki.DECODE
     say(f"decode full size {w.name}: drawing inputs on the device")
-    steps = 8
+    steps = w.steps
     pk, pv, sq, sk, sv = ki.decode_inputs_torch(w.seed, w.heads, w.prefill, steps, w.d, w.dv, "cuda")
     S, z = am.kata_prefill_state(pk[:, None], pv[:, None])
-    outs = [am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps) for s in range(steps)]
+    heads = torch.tensor([0, 1, 17, 1000, 2047, 3333, 4094, 4095], device="cuda")
+    outs = torch.empty((steps, len(heads), w.dv), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.heads, w.dv), dtype=torch.float32, device="cuda")
+    for s in range(steps):
+        am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps, out=out)
+        outs[s] = out.index_select(0, heads)
     torch.cuda.synchronize()
-    heads = [0, 1, 17, 1000, 2047, 3333, 4094, 4095]
+    say(f"  {steps} steps done; oracle on {len(heads)} heads")
     vmax = max(float(pv.abs().max()), float(sv.abs().max()))
-    got = np.stack([to_host64(o[heads]) for o in outs])
-    hk = pk[heads].double().cpu().numpy()
-    hv = pv[heads].double().cpu().numpy()
-    S_ref, z_ref = orc.decode_state(hk, hv)
+    hs = heads.cpu().tolist()
+    S_ref, z_ref = orc.decode_state(pk[hs].double().cpu().numpy(), pv[hs].double().cpu().numpy())
+    q64, k64, v64 = (x[:, hs].double().cpu().numpy() for x in (sq, sk, sv))
     refs = []
     for s in range(steps):
-        S_ref, z_ref, o = orc.decode_step(S_ref, z_ref, sq[s, heads].double().cpu().numpy(),
-                                          sk[s, heads].double().cpu().numpy(),
-                                          sv[s, heads].double().cpu().numpy(), w.eps)
+        S_ref, z_ref, o = orc.decode_step(S_ref, z_ref, q64[s], k64[s], v64[s], w.eps)
         refs.append(o)
-    check(got, np.stack(refs), ki.F32, vmax, "decode full size, sampled heads")
+    check(to_host64(outs), np.stack(refs), ki.F32, vmax, f"decode {steps} steps, sampled heads")
+    # fp32 sums of prefill + steps terms, each at most 2 max|v| (S) or 2 (z)
+    n = w.prefill + steps
+    Sg, zg = to_host64(S[heads]), to_host64(z[heads])
+    assert np.abs(Sg - S_ref).max() <= n * 4 * 2.0 ** -24 * 2 * (1 + vmax)
+    assert np.abs(zg - z_ref).max() <= n * 4 * 2.0 ** -24 * 2
+
+
+@pytest.mark.parametrize("d,dv", [(16, 64), (32, 16)])
+def test_decode_guard_bands(d, dv):
+    # S, z and out inside larger buffers: prefill, additive and gated steps
+    # write nothing outside them
+    heads, prefill, steps = 37, 100, 5
+    say(f"decode guard bands d={d} dv={dv}")
+    di = ki.decode_inputs(17, heads, prefill, steps, d, dv)
+    D = d * (d + 1) // 2
+    sbuf, S = guarded((heads, D, dv), torch.float32)
+    zbuf, z = guarded((heads, D), torch.float32)
+    obuf, out = guarded((heads, dv), torch.float32)
+    am.kata_prefill_state(to_dev(di.pk[:, None], ki.F32), to_dev(di.pv[:, None], ki.F32), S=S, z=z)
+    S_ref, z_ref = orc.decode_state(di.pk.astype(np.float64), di.pv.astype(np.float64))
+    vmax = max(np.abs(di.pv).max(), np.abs(di.sv).max())
+    for s in range(steps):
+        am.kata_decode_step(S, z, to_dev(di.sq[s], ki.F32), to_dev(di.sk[s], ki.F32),
+                            to_dev(di.sv[s], ki.F32), out=out)
+        S_ref, z_ref, o = orc.decode_step(S_ref, z_ref, di.sq[s], di.sk[s], di.sv[s], 1e-6)
+        torch.cuda.synchronize()
+        check(to_host64(out), o, ki.F32, vmax, f"guarded decode step {s}")
+    lg = torch.full((heads,), -0.1, dtype=torch.float32, device="cuda")
+    am.kata_decode_step_gated(S, to_dev(di.sq[0], ki.F32), to_dev(di.sk[0], ki.F32),
+                              to_dev(di.sv[0], ki.F32), lg, out=out)
+    torch.cuda.synchronize()
+    for buf, what in ((sbuf, "S"), (zbuf, "z"), (obuf, "out")):
+        assert_guards(buf, f"decode {what}")
 
 
 def test_decode_graph_replay_matches_eager():

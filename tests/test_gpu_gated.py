@@ -16,7 +16,8 @@ import torch
 import associative_memory_amd as am
 import kata_inputs as ki
 from oracle import kata_oracle as orc
-from gpu_util import RMS_TOL, say, to_dev, to_host64
+from gpu_util import (RMS_TOL, assert_guards, assert_workspace_guard, guarded, guarded_workspace, say,
+                      to_dev, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -127,3 +128,24 @@ def test_deterministic():
     y = am.kata_forward_gated(q, k, v, lg)
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("case", [(1, 2, 1000), (2, 1, 20000)], ids=lambda c: "B{}H{}T{}".format(*c))
+def test_guard_bands(case, C):
+    B, H, T = case
+    say(f"gated guard bands {case} C{C}")
+    inp = ki.forward_inputs(B, H, T, 16, 64, ki.BF16, seed=T + C + 1)
+    lg = ki.draw_log_gamma(B, H, T, seed=T + C + 1)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    buf, out = guarded((B, H, T, 64), torch.bfloat16)
+    need = am.kata_forward_gated_workspace_bytes(B, H, T, 16, 64, C)
+    wbuf, ws = guarded_workspace(need)
+    am.kata_forward_gated(q, k, v, torch.from_numpy(lg).cuda(), chunk=C, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert_guards(buf, "gated out")
+    assert_workspace_guard(wbuf, need, "gated workspace")
+    if T <= 1000:
+        ref = orc.forward_gated_quadratic(inp.q64, inp.k64, inp.v64, lg.astype(np.float64))
+        mass = orc.forward_gated_quadratic(inp.q64, inp.k64, np.ones((B, H, T, 1)), lg.astype(np.float64))[..., 0]
+        check_gated(to_host64(out), ref, mass, np.abs(inp.v64).max(), "guarded gated")

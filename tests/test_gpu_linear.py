@@ -11,7 +11,8 @@ import torch
 import associative_memory_amd as am
 import kata_inputs as ki
 from oracle import kata_oracle as orc
-from gpu_util import check, say, to_dev, to_host64
+from gpu_util import (assert_guards, assert_workspace_guard, check, guarded, guarded_workspace, say,
+                      to_dev, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -87,3 +88,22 @@ def test_deterministic(feature):
     y = am.kata_forward_linear(q, k, v, feature=feature)
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("feature", FEATURES)
+@pytest.mark.parametrize("case", [(1, 2, 1000), (2, 1, 20000)], ids=lambda c: "B{}H{}T{}".format(*c))
+def test_guard_bands(case, feature):
+    B, H, T = case
+    say(f"linear {feature} guard bands {case}")
+    inp = ki.forward_inputs(B, H, T, 64, 64, ki.BF16, seed=T + 9)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    buf, out = guarded((B, H, T, 64), torch.bfloat16)
+    need = am.kata_forward_linear_workspace_bytes(B, H, T, 64, 64, 64)
+    wbuf, ws = guarded_workspace(need)
+    am.kata_forward_linear(q, k, v, feature=feature, out=out, workspace=ws if need else None)
+    torch.cuda.synchronize()
+    assert_guards(buf, f"linear {feature} out")
+    assert_workspace_guard(wbuf, need, f"linear {feature} workspace")
+    if T <= 1000:
+        ref = orc.forward_linear_quadratic(inp.q64, inp.k64, inp.v64, feature, 1e-6)
+        check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"guarded linear {feature}")

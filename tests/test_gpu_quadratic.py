@@ -10,7 +10,7 @@ import torch
 import associative_memory_amd as am
 import kata_inputs as ki
 from oracle import kata_oracle as orc
-from gpu_util import check, say, to_dev, to_host64
+from gpu_util import assert_guards, check, guarded, say, to_dev, to_host64
 
 pytestmark = pytest.mark.gpu
 
@@ -115,3 +115,17 @@ def test_deterministic():
     y = am.kata_forward_quadratic(q, k, v)
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("d,g", [(16, 1), (32, 1), (64, 1), (64, 2), (64, 4)])
+def test_guard_bands(d, g):
+    B, H, T = 2, 3, 333
+    say(f"quadratic guard bands d={d} g={g}")
+    inp = ki.forward_inputs(B, H, T, d, 64, ki.BF16, seed=d + g)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    buf, out = guarded((B, H, T, 64), torch.bfloat16)
+    am.kata_forward_quadratic(q, k, v, g=g, out=out)
+    torch.cuda.synchronize()
+    assert_guards(buf, f"quadratic d={d} g={g}")
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6, g=g)
+    check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"guarded quadratic d={d} g={g}")
