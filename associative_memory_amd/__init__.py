@@ -33,6 +33,7 @@ EXPORTED = (
     "kata_feature_map",
     "kata_forward_workspace_bytes",
     "kata_forward_chunked",
+    "kata_forward_chunked_noalloc",
     "kata_prefill_state",
     "kata_decode_step",
     "kata_forward_plan",
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_chunked.restype = i32
     L.kata_forward_chunked.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, i32, i32,
                                        vp, sz, vp]
+    L.kata_forward_chunked_noalloc.restype = i32
+    L.kata_forward_chunked_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, f32, i32, i32,
+                                               vp]
     L.kata_prefill_state.restype = i32
     L.kata_prefill_state.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, vp]
     L.kata_decode_step.restype = i32
@@ -232,6 +236,29 @@ def kata_forward_chunked(q, k, v, chunk: int, eps: float = 1e-6, scan="auto", ou
     st = lib().kata_forward_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv, chunk,
                                     float(eps), _dtype_code(q), sc, wptr, wbytes, _stream(stream))
     _check(st, "kata_forward_chunked")
+    return out
+
+
+KATA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def kata_forward_chunked_noalloc(q, k, v, chunk: int, eps: float = 1e-6, scan="auto", out=None,
+                                 stream=None):
+    """kata_forward_chunked with the library's static device scratch as its
+    workspace: allocates nothing when `out` is given.  Shapes whose workspace
+    exceeds KATA_NOALLOC_SCRATCH_BYTES raise (KATA_ERR_WORKSPACE); calls that
+    overlap in time on one device race on the shared scratch."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _device_tensor(t, n)
+    B, H, T, d = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=v.dtype, device=v.device)
+    _device_tensor(out, "out")
+    st = lib().kata_forward_chunked_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv, chunk,
+                                            float(eps), _dtype_code(q), _scan_code(scan), _stream(stream))
+    _check(st, "kata_forward_chunked_noalloc")
     return out
 
 

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 #include "plan.h"
@@ -45,6 +46,25 @@ kata_status_t check_forward_shape(int B, int H, int64_t T, int d, int dv, int ch
   // every element index must fit comfortably in int64 and every grid in 2^31
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (T > (INT64_C(1) << 40) / BH) return KATA_ERR_UNSUPPORTED;
+  return KATA_OK;
+}
+
+// Every check of kata_forward_chunked except those of the workspace.
+kata_status_t check_forward_args(const void* q, const void* k, const void* v, const void* out, int B,
+                                 int H, int64_t T, int d, int dv, int chunk, float eps,
+                                 kata_dtype_t dtype, kata_scan_t scan) {
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;
+  const kata_status_t st = check_forward_shape(B, H, T, d, dv, chunk, dtype, scan);
+  if (st != KATA_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return KATA_ERR_INVALID_VALUE;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  const size_t es = elem_size(dtype);
+  const size_t qk_bytes = static_cast<size_t>(BH * T * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
+  if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
+      overlaps(out, v_bytes, v, v_bytes))
+    return KATA_ERR_INVALID_VALUE;
   return KATA_OK;
 }
 
@@ -102,6 +122,37 @@ kata_status_t check_gated_shape(int B, int H, int64_t T, int d, int dv, int chun
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (T > (INT64_C(1) << 40) / BH) return KATA_ERR_UNSUPPORTED;
   return KATA_OK;
+}
+
+// ------------------------------------------------------------ static scratch
+//
+// The workspace of kata_forward_chunked_noalloc: one array per device, part of
+// the library's code object (each device the library runs on holds it until
+// the process ends).  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept in scratch_dev.
+static __device__ __align__(256) unsigned char scratch[KATA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+
+// device address of the current device's scratch array
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -310,19 +361,13 @@ kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const 
                                             kata_scan_t scan, void* workspace,
                                             size_t workspace_bytes,
                                             const kata_stage_events_t* events, void* stream) {
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;
-  const kata_status_t st = check_forward_shape(B, H, T, d, dv, chunk, dtype, scan);
+  const kata_status_t st = check_forward_args(q, k, v, out, B, H, T, d, dv, chunk, eps, dtype, scan);
   if (st != KATA_OK) return st;
-  if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
-    return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(workspace)) return KATA_ERR_INVALID_VALUE;
   const int64_t BH = static_cast<int64_t>(B) * H;
   const size_t es = elem_size(dtype);
   const size_t qk_bytes = static_cast<size_t>(BH * T * d) * es;
   const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
-  if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
-      overlaps(out, v_bytes, v, v_bytes))
-    return KATA_ERR_INVALID_VALUE;
   const ForwardPlan p = kata::plan_forward(B, H, T, d, dv, chunk, dtype, scan);
   if (p.ws_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < p.ws_bytes) return KATA_ERR_WORKSPACE;
@@ -334,6 +379,20 @@ kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const 
   }
   return from_hip(kata::run_forward(p, q, k, v, out, eps, static_cast<float*>(workspace),
                                     events, static_cast<hipStream_t>(stream)));
+}
+
+kata_status_t kata_forward_chunked_noalloc(const void* q, const void* k, const void* v, void* out,
+                                           int B, int H, int64_t T, int d, int dv, int chunk,
+                                           float eps, kata_dtype_t dtype, kata_scan_t scan,
+                                           void* stream) {
+  const kata_status_t st = check_forward_args(q, k, v, out, B, H, T, d, dv, chunk, eps, dtype, scan);
+  if (st != KATA_OK) return st;
+  const ForwardPlan p = kata::plan_forward(B, H, T, d, dv, chunk, dtype, scan);
+  if (p.ws_bytes > KATA_NOALLOC_SCRATCH_BYTES) return KATA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0 && scratch_address(&ws) != hipSuccess) return KATA_ERR_DEVICE;
+  return from_hip(kata::run_forward(p, q, k, v, out, eps, static_cast<float*>(ws), nullptr,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 size_t kata_forward_chunked_blocks_workspace_bytes(int B, int H, int64_t T, int d, int dv, int g,

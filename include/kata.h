@@ -10,7 +10,8 @@
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers (hipMalloc'd or equivalent) owned
  *    by the caller.  The library never allocates, frees or keeps device
- *    memory, and keeps no mutable global state; calls are reentrant.
+ *    memory, and keeps no mutable global state; calls are reentrant.  The one
+ *    exception is kata_forward_chunked_noalloc's static scratch array (below).
  *  - Tensors are dense, row-major, with the layouts stated per call.  Every
  *    pointer must be 16-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
@@ -105,6 +106,34 @@ kata_status_t kata_forward_chunked(const void* q, const void* k, const void* v,
                                    kata_dtype_t dtype, kata_scan_t scan,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * kata_forward_chunked_noalloc -- kata_forward_chunked for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same computation, kernels,
+ * arguments, validation, status codes and output bits as kata_forward_chunked
+ * with the same scan mode, but no workspace argument.  Its workspace is a
+ * static device array of KATA_NOALLOC_SCRATCH_BYTES inside the library (each
+ * device the library runs on holds its own copy until the process ends); the
+ * call allocates nothing and calls no allocating routine.
+ *   - A shape whose workspace (kata_forward_workspace_bytes) exceeds
+ *     KATA_NOALLOC_SCRATCH_BYTES returns KATA_ERR_WORKSPACE before anything
+ *     is enqueued (the T = 131072, 8-head, d = 16 forward needs 19.2 MB).
+ *   - Every call on a device shares that device's array and leaves its last
+ *     contents there (nothing in it needs to start at zero).  Calls that
+ *     overlap in time on one device -- concurrent streams, or host threads
+ *     without ordering between their streams -- race on it and must not be
+ *     issued; calls ordered on one stream are safe.
+ *   - The first call on each device looks up the array's device address
+ *     (hipGetSymbolAddress) with that device current; a failure there
+ *     returns KATA_ERR_DEVICE.
+ */
+#define KATA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kata_status_t kata_forward_chunked_noalloc(const void* q, const void* k, const void* v,
+                                           void* out, int B, int H, int64_t T, int d,
+                                           int dv, int chunk, float eps,
+                                           kata_dtype_t dtype, kata_scan_t scan,
+                                           void* stream);
 
 /*
  * kata_forward_quadratic -- the causal read of kata_forward_chunked,

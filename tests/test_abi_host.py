@@ -105,6 +105,36 @@ def test_forward_error_paths(kw, status):
     assert fwd(**kw) == status
 
 
+def fwd_noalloc(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=64, d=16, dv=16, C=32, eps=1e-6,
+                dt=BF16, scan=0, stream=None):
+    return am.lib().kata_forward_chunked_noalloc(q, k, v, out, B, H, T, d, dv, C, eps, dt, scan, stream)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), INVALID), (dict(out=NULL), INVALID), (dict(B=0), INVALID), (dict(T=0), INVALID),
+    (dict(d=24), UNSUPPORTED), (dict(dv=48), UNSUPPORTED), (dict(C=16), UNSUPPORTED),
+    (dict(eps=float("nan")), INVALID), (dict(dt=7), INVALID), (dict(scan=5), INVALID),
+    (dict(q=ctypes.c_void_p(P[0].value + 4)), INVALID),
+    (dict(out=P[0]), INVALID), (dict(out=ctypes.c_void_p(P[2].value + 16)), INVALID),
+    # the fp32 forward of 8 heads of T = 131072 at d = 32 needs 67 MiB
+    (dict(B=1, H=8, T=131072, d=32, dv=64, C=64, dt=F32), WORKSPACE),
+])
+def test_forward_noalloc_error_paths(kw, status):
+    assert fwd_noalloc(**kw) == status
+
+
+def test_forward_noalloc_scratch_limit():
+    L = am.lib()
+    assert am.KATA_NOALLOC_SCRATCH_BYTES == 64 << 20
+    # the benchmarked bf16 forwards fit the scratch; the rejected fp32 shape above does not
+    for (B, H, T, d, C) in [(4, 8, 2048, 16, 64), (2, 16, 8192, 32, 64), (1, 8, 131072, 16, 128)]:
+        for scan in (0, 1, 2):
+            plan = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, d, 64, C, BF16, scan).split())
+            assert 0 < int(plan["workspace_bytes"]) <= am.KATA_NOALLOC_SCRATCH_BYTES
+    plan = dict(kv.split("=") for kv in am.kata_forward_plan(1, 8, 131072, 32, 64, 64, F32, 0).split())
+    assert int(plan["workspace_bytes"]) > am.KATA_NOALLOC_SCRATCH_BYTES
+
+
 def test_decode_error_paths():
     L = am.lib()
     dec = lambda S=P[0], z=P[1], q=P[2], k=P[3], v=P[4], out=P[5], B=1, H=1, d=16, dv=64, eps=1e-6, dt=F32: \
