@@ -14,8 +14,9 @@ kernel alone, and the loop captured in one HIP graph.  The same decode over
 under "decode_beyond_cache".  "attainable" gives the whole step against the
 larger of its HBM time (minimal bytes) and its MFMA time (useful FLOPs).
 
-The fp64 oracle's timing on the host (a bounded sample, extrapolated to the
-whole workload) is reported as cpu_baseline: a baseline, not the target.
+The fp64 oracle's timing on the host is reported as cpu_baseline: its chunked
+form over the whole T = 131072 workload, with the plain definition on one head
+and per-workload timings beside it.  A baseline, not the target.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -26,8 +27,11 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -42,6 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="interleaved timed regions of K steps per prefix variant (median reported)")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -159,6 +165,13 @@ def measure_peaks(hip, am, torch):
 # ------------------------------------------------------------------ forward
 
 def bench_forward(args, hip, am, ki, torch):
+    """The T = 131072 forward with each prefix variant (sequential,
+    associative, auto).  The variants are timed interleaved: `repeats`
+    rounds, each running every variant once (the order rotating from round to
+    round) as a region of exactly K forwards between events on the library's
+    stream; a variant's figure is the median over its regions.  Per-stage
+    kernel durations come from a separate pass of K profiled forwards per
+    variant (median per stage)."""
     w = ki.LONG
     inp = ki.workload_inputs(w)
 
@@ -168,23 +181,33 @@ def bench_forward(args, hip, am, ki, torch):
     q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
     out = torch.empty((w.B, w.H, w.T, w.dv), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    results = {}
-    for scan in ("sequential", "associative", "auto"):
+    scans = ("sequential", "associative", "auto")
+    ws = {}
+    for scan in scans:
         ws_bytes = am.kata_forward_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, w.chunk, scan)
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        ws[scan] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
         for _ in range(args.warmup):
-            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan, out=out, workspace=ws)
-        torch.cuda.synchronize()
-        # timed region: K whole forwards, bracketed by events on the library's stream
-        e0, e1 = hip.event(), hip.event()
-        t_wall = time.perf_counter()
-        hip.record(e0, stream)
-        for _ in range(args.steps):
-            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan, out=out, workspace=ws)
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
-        ms_step = hip.ms(e0, e1) / args.steps
+            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan, out=out, workspace=ws[scan])
+    torch.cuda.synchronize()
+    samples = {scan: [] for scan in scans}
+    walls = {scan: [] for scan in scans}
+    for r in range(args.repeats):
+        for i in range(len(scans)):
+            scan = scans[(r + i) % len(scans)]
+            e0, e1 = hip.event(), hip.event()
+            torch.cuda.synchronize()
+            t_wall = time.perf_counter()
+            hip.record(e0, stream)
+            for _ in range(args.steps):
+                am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan, out=out, workspace=ws[scan])
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            walls[scan].append(1e3 * (time.perf_counter() - t_wall) / args.steps)
+            samples[scan].append(hip.ms(e0, e1) / args.steps)
+            hip.destroy(e0)
+            hip.destroy(e1)
+    results = {}
+    for scan in scans:
         # per-stage kernel durations, same launches, one event set per step
         sets = []
         for _ in range(args.steps):
@@ -194,25 +217,26 @@ def bench_forward(args, hip, am, ki, torch):
                 ev.stage_begin[i] = hs[2 * i]
                 ev.stage_end[i] = hs[2 * i + 1]
             am.kata_forward_chunked_profiled(q, k, v, w.chunk, ev, eps=w.eps, scan=scan, out=out,
-                                             workspace=ws)
+                                             workspace=ws[scan])
             sets.append(hs)
         torch.cuda.synchronize()
-        stage_ms = [0.0, 0.0, 0.0]
+        per_stage = [[], [], []]
         for hs in sets:
             for i in range(3):
-                stage_ms[i] += hip.ms(hs[2 * i], hs[2 * i + 1]) / args.steps
+                per_stage[i].append(hip.ms(hs[2 * i], hs[2 * i + 1]))
             for h in hs:
                 hip.destroy(h)
+        stage_ms = [statistics.median(x) for x in per_stage]
+        ms_step = statistics.median(samples[scan])
         results[scan] = {
             "ms_per_step": ms_step,
-            "wall_ms_per_step": 1e3 * t_wall / args.steps,
+            "ms_per_step_samples": [round(x, 5) for x in samples[scan]],
+            "wall_ms_per_step": statistics.median(walls[scan]),
             "tokens_per_s": w.B * w.T / (ms_step * 1e-3),
             "stage_ms": {"span_states": stage_ms[0], "prefix": stage_ms[1], "readout": stage_ms[2]},
             "plan": am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk, am.KATA_BF16, scan),
         }
-        hip.destroy(e0)
-        hip.destroy(e1)
-        del ws
+    del ws
     return w, inp, results
 
 
@@ -522,23 +546,55 @@ def bench_decode(args, hip, am, ki, torch, w):
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(w, inp):
+def cpu_baseline(w, inp, ki):
+    """The fp64 oracle timed on this host's cores: a baseline, not a target.
+
+    value: the whole T = 131072 workload (all heads, every token) through the
+    oracle's chunked form (Eqs. 17-20, the O(T) algorithm the device runs).
+    Beside it: the plain O(T^2) definition on one head of that workload,
+    scaled to all heads; the definition over the whole of each smaller
+    forward workload; and the decode recurrence for 64 of the 4096 heads over
+    the prefill and all steps, scaled to every head."""
     from threadpoolctl import threadpool_info
 
     from oracle import kata_oracle as orc
 
-    # one whole head (T tokens, about 20 s of fp64 work on the host), scaled
-    # to every head of the workload
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    affinity = len(os.sched_getaffinity(0))
+    t = time.perf_counter()
+    orc.forward_chunked(inp.q64, inp.k64, inp.v64, w.chunk, w.eps)
+    dt_chunked = time.perf_counter() - t
     t = time.perf_counter()
     orc.forward_quadratic(inp.q64[0, 0], inp.k64[0, 0], inp.v64[0, 0], w.eps)
-    dt = time.perf_counter() - t
-    full = dt * (w.B * w.H)
-    cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": round(w.B * w.T / full, 1), "unit": "tokens/s", "cores": cores,
+    dt_quad = time.perf_counter() - t
+    per_config = {w.name: {
+        "chunked_s": round(dt_chunked, 2), "chunked_tokens_per_s": round(w.B * w.T / dt_chunked, 1),
+        "quadratic_s_extrapolated": round(dt_quad * w.B * w.H, 1),
+        "quadratic_tokens_per_s": round(w.B * w.T / (dt_quad * w.B * w.H), 1),
+        "quadratic_sample": f"head (0,0), all {w.T} tokens ({dt_quad:.1f} s), times {w.B * w.H} heads"}}
+    for cw in (ki.TINY, ki.MEDIUM, ki.WIDE):
+        ci = ki.workload_inputs(cw)
+        t = time.perf_counter()
+        orc.forward_quadratic(ci.q64, ci.k64, ci.v64, cw.eps)
+        dt = time.perf_counter() - t
+        per_config[cw.name] = {"quadratic_s": round(dt, 3), "quadratic_tokens_per_s": round(cw.B * cw.T / dt, 1)}
+    dw = ki.DECODE
+    nh = 64
+    di = ki.decode_inputs(dw.seed, nh, dw.prefill, dw.steps, dw.d, dw.dv)
+    t = time.perf_counter()
+    S, z = orc.decode_state(di.pk.astype(np.float64), di.pv.astype(np.float64))
+    for s_ in range(dw.steps):
+        S, z, _ = orc.decode_step(S, z, di.sq[s_], di.sk[s_], di.sv[s_], dw.eps)
+    dt = (time.perf_counter() - t) * dw.heads / nh
+    per_config[dw.name] = {"s_extrapolated": round(dt, 1), "tokens_per_s": round(dw.seqs * dw.steps / dt, 1),
+                           "sample": f"{nh} of {dw.heads} heads (prefill and {dw.steps} steps), scaled"}
+    return {"value": round(w.B * w.T / dt_chunked, 1), "unit": "tokens/s", "cores": min(blas, affinity),
             "kind": "oracle",
-            "sample": f"fp64 quadratic oracle on head (0,0), all {w.T} tokens ({dt:.1f} s), "
-                      f"times {w.B * w.H} heads",
-            "sample_seconds": round(dt, 2)}
+            "sample": f"fp64 chunked oracle (Eqs. 17-20) over the whole workload: {w.B * w.H} heads x "
+                      f"{w.T} tokens in {dt_chunked:.1f} s; no extrapolation",
+            "sample_seconds": round(dt_chunked, 2),
+            "blas_threads": blas, "host_cpus": os.cpu_count(), "affinity_cpus": affinity,
+            "per_config": per_config}
 
 
 # ------------------------------------------------------------------ main
@@ -613,8 +669,11 @@ def main():
             "frac": round(max(bytes_per_tok * BHT / (HBM_PEAK_GBS * 1e9),
                               flop_per_tok * BHT / (BF16_PEAK_TFLOPS * 1e12))
                           / (main_r["ms_per_step"] * 1e-3), 4)},
+        "timing": f"median over {args.repeats} regions of exactly {args.steps} forwards each, the three "
+                  "prefix variants interleaved (rotating order), HIP events on the library's stream",
         "scan_variants": {s: {"tokens_per_s": round(fwd[s]["tokens_per_s"], 1),
                               "ms_per_step": round(fwd[s]["ms_per_step"], 4),
+                              "ms_per_step_samples": fwd[s]["ms_per_step_samples"],
                               "stage_ms": {kk: round(vv, 4) for kk, vv in fwd[s]["stage_ms"].items()},
                               "plan": fwd[s]["plan"]}
                           for s in ("sequential", "associative")},
@@ -643,7 +702,7 @@ def main():
         rec["decode_beyond_cache"] = bench_decode(args, hip, am, ki, torch, ki.DECODE_512)
     if not args.no_cpu_baseline:
         progress("CPU oracle baseline")
-        rec["cpu_baseline"] = cpu_baseline(w, inp)
+        rec["cpu_baseline"] = cpu_baseline(w, inp, ki)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec))
