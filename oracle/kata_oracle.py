@@ -38,6 +38,10 @@ Capacity Wall with Symmetric Cones" (Ghriss & Chakraborty, arXiv 2607.17419):
       KATA-Lorentz psi(x) = (y, |y|_2 (1 + s^2)) with y = x_{1:d-1}, s = x_d
       (App. F.4; Sec. 2.3 names both cone families), read with the same
       normalised causal sum, score c_{t,s} = psi(q_t) . psi(k_s) unsquared.
+  forward_identity_quadratic / forward_identity_rows / forward_identity_chunked
+      the identity feature psi(x) = x with a d x dv state, the first-order
+      workload of the associative-scan tables (Sec. 4.2, Tables 10-11):
+      o_t = sum_{s<=t} (q_t . k_s) v_s, read without a denominator.
   gated_recurrence / forward_gated_quadratic / forward_gated_rows
       GatedKATA (App. F.4): S_t = gamma_t S_{t-1} + psi(k_t) v_t^T,
       o_t = psi(q_t)^T S_t, no denominator; its unrolled form
@@ -58,6 +62,9 @@ Readings where the page is silent (each also listed in the design notes):
     map (the page's orthant recurrence divides without one; its orthant shift
     keeps that denominator positive, the Lorentz map only makes it >= 0).
   * the gated read has no denominator and no eps, as the page writes it.
+  * the identity feature's scores q.k are signed, so its sum can vanish or
+    change sign; it is read without a denominator (the d x dv state of the
+    page's first-order tables carries no normaliser).
 """
 from __future__ import annotations
 
@@ -306,6 +313,76 @@ def forward_linear_chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: i
                            feature: str, eps: float, shift: float = 1e-6) -> np.ndarray:
     """Eqs. 17-20 with a linear feature (state D x dv with D = d)."""
     return _chunked(q, k, v, chunk, eps, linear_feature(feature, shift))
+
+
+# ------------------------------------------------------------ identity feature
+
+def forward_identity_quadratic(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                               block: int = 256) -> np.ndarray:
+    """The first-order read with the identity feature psi(x) = x and a d x dv
+    state, the workload of the page's associative-scan tables (Sec. 4.2,
+    Tables 10-11): o_t = sum_{s<=t} (q_t . k_s) v_s.  Its scores are signed,
+    so it is read without a denominator (a normalised read could divide by
+    zero or flip sign).  q, k: [..., T, d]; v: [..., T, dv] -> [..., T, dv]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lead = q.shape[:-2]
+    T = q.shape[-2]
+    qf = q.reshape((-1, T, q.shape[-1]))
+    kf = k.reshape((-1, T, k.shape[-1]))
+    vf = v.reshape((-1, T, v.shape[-1]))
+    out = np.empty((qf.shape[0], T, vf.shape[-1]))
+    for h in range(qf.shape[0]):
+        for t0 in range(0, T, block):
+            t1 = min(T, t0 + block)
+            c = qf[h, t0:t1] @ kf[h, :t1].T
+            rows = np.arange(t0, t1)[:, None]
+            cols = np.arange(t1)[None, :]
+            out[h, t0:t1] = np.where(cols <= rows, c, 0.0) @ vf[h, :t1]
+    return out.reshape(lead + (T, vf.shape[-1]))
+
+
+def forward_identity_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows) -> np.ndarray:
+    """forward_identity_quadratic for selected query rows of one head:
+    q, k: [T, d]; v: [T, dv]; returns [len(rows), dv]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty((len(rows), v.shape[-1]))
+    for n, t in enumerate(rows):
+        out[n] = (k[: t + 1] @ q[t]) @ v[: t + 1]
+    return out
+
+
+def forward_identity_chunked(q: np.ndarray, k: np.ndarray, v: np.ndarray, chunk: int) -> np.ndarray:
+    """Eqs. 17-20 with psi(x) = x and no normalisation, per head: S = 0
+    (d x dv); for each chunk c, O_c = Q_c S + ((Q_c K_c^T) * M) V_c, then
+    S += K_c^T V_c.  The final chunk is zero-padded, padded rows dropped."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lead = q.shape[:-2]
+    T, d = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    nc = -(-T // chunk)
+    Tp = nc * chunk
+    qf = np.zeros((int(np.prod(lead, dtype=np.int64)), Tp, d))
+    kf = np.zeros_like(qf)
+    vf = np.zeros((qf.shape[0], Tp, dv))
+    qf[:, :T] = q.reshape((-1, T, d))
+    kf[:, :T] = k.reshape((-1, T, d))
+    vf[:, :T] = v.reshape((-1, T, dv))
+    M = np.tril(np.ones((chunk, chunk)))
+    out = np.empty((qf.shape[0], Tp, dv))
+    for h in range(qf.shape[0]):
+        S = np.zeros((d, dv))
+        for c in range(nc):
+            sl = slice(c * chunk, (c + 1) * chunk)
+            Qc, Kc, Vc = qf[h, sl], kf[h, sl], vf[h, sl]
+            out[h, sl] = Qc @ S + ((Qc @ Kc.T) * M) @ Vc
+            S = S + Kc.T @ Vc
+    return out[:, :T].reshape(lead + (T, dv))
 
 
 # ------------------------------------------------------------ gated recurrence

@@ -251,6 +251,89 @@ def test_orthant_invariant_under_coordinate_permutation():
                                atol=1e-13)
 
 
+# ------------------------------------------------------------------ identity feature
+
+def test_identity_worked_example():
+    ex = GOLDEN["identity_example"]
+    q, k, v = _f64(ex["q"]), _f64(ex["k"]), _f64(ex["v"])
+    want = _f64(ex["out"])
+    np.testing.assert_allclose(orc.forward_identity_quadratic(q, k, v), want, atol=1e-15)
+    np.testing.assert_allclose(orc.forward_identity_rows(q, k, v, [0, 1, 2]), want, atol=1e-15)
+    for C in (1, 2, 3):
+        np.testing.assert_allclose(orc.forward_identity_chunked(q, k, v, C), want, atol=1e-15)
+
+
+def test_identity_brute_force_in_rationals():
+    # o_t = sum_{s<=t} (q_t . k_s) v_s evaluated in exact rationals
+    rng = np.random.Generator(np.random.PCG64(31))
+    T, d, dv = 6, 3, 2
+    qi, ki_, vi = (rng.integers(-4, 5, (T, n)) for n in (d, d, dv))
+    den = 3
+    want = []
+    for t in range(T):
+        acc = [Fraction(0)] * dv
+        for s in range(t + 1):
+            c = sum(Fraction(int(qi[t, a]), den) * Fraction(int(ki_[s, a]), den) for a in range(d))
+            acc = [acc[j] + c * int(vi[s, j]) for j in range(dv)]
+        want.append([float(x) for x in acc])
+    got = orc.forward_identity_quadratic(qi / den, ki_ / den, vi.astype(np.float64))
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-14, atol=1e-14)
+
+
+@pytest.mark.parametrize("T", [1, 5, 97, 300])
+def test_identity_chunked_equals_quadratic(T):
+    rng = np.random.Generator(np.random.PCG64(T + 3))
+    q, k, v = rng.standard_normal((2, T, 8)), rng.standard_normal((2, T, 8)), rng.standard_normal((2, T, 3))
+    want = orc.forward_identity_quadratic(q, k, v)
+    for C in (1, 3, 32, 128, T):
+        np.testing.assert_allclose(orc.forward_identity_chunked(q, k, v, C), want, rtol=1e-11, atol=1e-11)
+
+
+def test_identity_recurrence_token_by_token():
+    # Sec. 2 with psi(x) = x: S_t = S_{t-1} + k_t v_t^T, o_t = q_t^T S_t
+    rng = np.random.Generator(np.random.PCG64(32))
+    T, d, dv = 40, 5, 4
+    q, k, v = rng.standard_normal((T, d)), rng.standard_normal((T, d)), rng.standard_normal((T, dv))
+    S = np.zeros((d, dv))
+    want = np.empty((T, dv))
+    for t in range(T):
+        S = S + np.outer(k[t], v[t])
+        want[t] = q[t] @ S
+    np.testing.assert_allclose(orc.forward_identity_quadratic(q, k, v), want, rtol=1e-12, atol=1e-12)
+
+
+def test_identity_is_the_orthant_numerator_on_nonnegative_inputs():
+    # with q, k >= 0 and no shift the orthant map is the identity, so the
+    # identity read equals the orthant read (eps = 0) times its denominator
+    # (the identity read of v = 1)
+    rng = np.random.Generator(np.random.PCG64(33))
+    T = 50
+    q, k, v = np.abs(rng.standard_normal((T, 6))), np.abs(rng.standard_normal((T, 6))), rng.standard_normal((T, 3))
+    den = orc.forward_identity_quadratic(q, k, np.ones((T, 1)))
+    np.testing.assert_allclose(orc.forward_identity_quadratic(q, k, v),
+                               orc.forward_linear_quadratic(q, k, v, "orthant", 0.0, shift=0.0) * den,
+                               rtol=1e-12)
+
+
+def test_identity_basis_keys_causal_and_linear():
+    T = d = 6
+    k = np.eye(d)
+    rng = np.random.Generator(np.random.PCG64(34))
+    v = rng.standard_normal((T, 3))
+    for j in range(d):
+        q = np.tile(np.eye(d)[j], (T, 1))
+        o = orc.forward_identity_quadratic(q, k, v)
+        for t in range(T):
+            np.testing.assert_allclose(o[t], v[j] if j <= t else 0.0, atol=0)
+    q, kk = rng.standard_normal((T, 4)), rng.standard_normal((T, 4))
+    a = orc.forward_identity_quadratic(q, kk, v)
+    b = orc.forward_identity_quadratic(q, kk, 2.0 * v - 1.0)
+    np.testing.assert_allclose(b, 2.0 * a - orc.forward_identity_quadratic(q, kk, np.ones_like(v)), atol=1e-12)
+    v2 = v.copy()
+    v2[4:] = 100.0
+    np.testing.assert_array_equal(orc.forward_identity_quadratic(q, kk, v2)[:4], a[:4])
+
+
 # ------------------------------------------------------------------ gated recurrence
 
 def _three_token():
