@@ -96,7 +96,7 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_linear_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.kata_forward_linear.restype = i32
     L.kata_forward_linear.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, f32, f32, i32,
-                                      vp, sz, vp]
+                                      i32, vp, sz, vp]
     L.kata_forward_gated_workspace_bytes.restype = sz
     L.kata_forward_gated_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.kata_forward_gated.restype = i32
@@ -348,7 +348,9 @@ def kata_decode_step(S, z, q, k, v, eps: float = 1e-6, out=None, B: Optional[int
 
 KATA_FEATURE_ORTHANT = 0
 KATA_FEATURE_LORENTZ = 1
-_FEATURES = {"orthant": KATA_FEATURE_ORTHANT, "lorentz": KATA_FEATURE_LORENTZ}
+KATA_FEATURE_IDENTITY = 2
+_FEATURES = {"orthant": KATA_FEATURE_ORTHANT, "lorentz": KATA_FEATURE_LORENTZ,
+             "identity": KATA_FEATURE_IDENTITY}
 
 
 def kata_forward_linear_workspace_bytes(B, H, T, d, dv, chunk=64) -> int:
@@ -356,12 +358,13 @@ def kata_forward_linear_workspace_bytes(B, H, T, d, dv, chunk=64) -> int:
 
 
 def kata_forward_linear(q, k, v, feature: str = "orthant", shift: float = 1e-6, eps: float = 1e-6,
-                        chunk: int = 64, out=None, workspace=None, stream=None):
-    """Causal normalised read with a linear cone feature,
-    o_t = sum_{s<=t} (psi(q_t).psi(k_s)) v_s / (sum + eps), psi the orthant
-    (ReLU(x) + shift) or Lorentz ((y, |y|(1 + s^2))) map.  q, k: [B, H, T, d];
-    v: [B, H, T, dv]; bf16, contiguous, on the device.  Returns out
-    [B, H, T, dv] bf16."""
+                        chunk: int = 64, scan="auto", out=None, workspace=None, stream=None):
+    """Causal read with a linear feature: the orthant (ReLU(x) + shift) or
+    Lorentz ((y, |y|(1 + s^2))) map read normalised,
+    o_t = sum_{s<=t} (psi(q_t).psi(k_s)) v_s / (sum + eps), or the identity
+    map read without a denominator, o_t = sum_{s<=t} (q_t.k_s) v_s.
+    q, k: [B, H, T, d]; v: [B, H, T, dv]; bf16, contiguous, on the device.
+    Returns out [B, H, T, dv] bf16."""
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _device_tensor(t, n)
@@ -378,8 +381,8 @@ def kata_forward_linear(q, k, v, feature: str = "orthant", shift: float = 1e-6, 
     wptr = _ptr(workspace) if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().kata_forward_linear(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, d, dv, chunk,
-                                   _FEATURES[feature], float(shift), float(eps), _dtype_code(q), wptr,
-                                   wbytes, _stream(stream))
+                                   _FEATURES[feature], float(shift), float(eps), _dtype_code(q),
+                                   _scan_code(scan), wptr, wbytes, _stream(stream))
     _check(st, "kata_forward_linear")
     return out
 

@@ -74,9 +74,11 @@ struct LinPlan {
   size_t ws_bytes;
 };
 
-LinPlan plan_linear(int64_t BH, int64_t T) {
+// The workspace is sized for the largest span state (the normalised maps'
+// [S | z]); the identity map uses the first 4096 floats of each.
+LinPlan plan_linear(int64_t BH, int64_t T, int chunk) {
   LinPlan p;
-  p.n_chunks = (T + kata::kLinChunk - 1) / kata::kLinChunk;
+  p.n_chunks = (T + chunk - 1) / chunk;
   const int64_t spans = (512 + BH - 1) / BH;
   p.G = (p.n_chunks + spans - 1) / spans;
   p.n_spans = (p.n_chunks + p.G - 1) / p.G;
@@ -88,7 +90,8 @@ kata_status_t check_linear_shape(int B, int H, int64_t T, int d, int dv, int chu
                                  kata_feature_t feature, kata_dtype_t dtype) {
   if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || dv <= 0 || chunk <= 0) return KATA_ERR_INVALID_VALUE;
   if (!dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
-  if (feature != KATA_FEATURE_ORTHANT && feature != KATA_FEATURE_LORENTZ) return KATA_ERR_INVALID_VALUE;
+  if (feature != KATA_FEATURE_ORTHANT && feature != KATA_FEATURE_LORENTZ && feature != KATA_FEATURE_IDENTITY)
+    return KATA_ERR_INVALID_VALUE;
   if (!kata::linear_supported(dtype == KATA_BF16, d, dv, chunk)) return KATA_ERR_UNSUPPORTED;
   const int64_t BH = static_cast<int64_t>(B) * H;
   if (T > (INT64_C(1) << 40) / BH) return KATA_ERR_UNSUPPORTED;
@@ -242,17 +245,19 @@ kata_status_t kata_forward_quadratic(const void* q, const void* k, const void* v
 
 size_t kata_forward_linear_workspace_bytes(int B, int H, int64_t T, int d, int dv, int chunk) {
   if (check_linear_shape(B, H, T, d, dv, chunk, KATA_FEATURE_ORTHANT, KATA_BF16) != KATA_OK) return 0;
-  return plan_linear(static_cast<int64_t>(B) * H, T).ws_bytes;
+  return plan_linear(static_cast<int64_t>(B) * H, T, chunk).ws_bytes;
 }
 
 kata_status_t kata_forward_linear(const void* q, const void* k, const void* v, void* out, int B,
                                   int H, int64_t T, int d, int dv, int chunk,
                                   kata_feature_t feature, float shift, float eps,
-                                  kata_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  kata_dtype_t dtype, kata_scan_t scan, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return KATA_ERR_INVALID_VALUE;
   const kata_status_t st = check_linear_shape(B, H, T, d, dv, chunk, feature, dtype);
   if (st != KATA_OK) return st;
+  if (scan != KATA_SCAN_AUTO && scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE)
+    return KATA_ERR_INVALID_VALUE;
   if (!std::isfinite(eps) || eps < 0.f) return KATA_ERR_INVALID_VALUE;
   if (!std::isfinite(shift) || shift < 0.f) return KATA_ERR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace))
@@ -264,7 +269,7 @@ kata_status_t kata_forward_linear(const void* q, const void* k, const void* v, v
   if (overlaps(out, v_bytes, q, qk_bytes) || overlaps(out, v_bytes, k, qk_bytes) ||
       overlaps(out, v_bytes, v, v_bytes))
     return KATA_ERR_INVALID_VALUE;
-  const LinPlan p = plan_linear(BH, T);
+  const LinPlan p = plan_linear(BH, T, chunk);
   if (p.ws_bytes > 0) {
     if (workspace == nullptr || workspace_bytes < p.ws_bytes) return KATA_ERR_WORKSPACE;
     if (overlaps(workspace, p.ws_bytes, out, v_bytes) || overlaps(workspace, p.ws_bytes, q, qk_bytes) ||
@@ -274,13 +279,15 @@ kata_status_t kata_forward_linear(const void* q, const void* k, const void* v, v
   if (BH * p.n_spans > INT64_C(0x7fffffff)) return KATA_ERR_UNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   kata::LinArgs a{q, k, v, out, static_cast<float*>(workspace), BH, T, static_cast<int>(feature),
-                  shift, p.G, p.n_spans, eps};
+                  shift, p.G, p.n_spans, eps, chunk};
   if (p.n_spans > 1) {
     hipError_t e = kata::launch_linear_span_state(a, s);
-    // sequential below 128 spans per head, reduce-then-scan from there
+    // AUTO: sequential below 128 spans per head, reduce-then-scan from there
+    const bool assoc = scan == KATA_SCAN_ASSOCIATIVE || (scan == KATA_SCAN_AUTO && p.n_spans >= 128);
+    const int64_t E = kata::linear_state_floats(feature);
     if (e == hipSuccess) {
-      e = p.n_spans >= 128 ? kata::launch_scan_associative(a.ws, BH, p.n_spans, kata::kLinStateFloats, s)
-                           : kata::launch_scan_sequential(a.ws, BH, p.n_spans, kata::kLinStateFloats, s);
+      e = assoc ? kata::launch_scan_associative(a.ws, BH, p.n_spans, E, s)
+                : kata::launch_scan_sequential(a.ws, BH, p.n_spans, E, s);
     }
     if (e != hipSuccess) return KATA_ERR_DEVICE;
   }

@@ -71,22 +71,25 @@ inline bool quadratic_supported(bool bf16, int d, int dv, int g) {
 // the O(T^2) form: one workgroup per (head, 128-query block)
 hipError_t launch_forward_quadratic_mfma(const QuadArgs& a, hipStream_t stream);
 
-// ------------------------------------------------------------ linear cone features
-// (D = d = 64, chunk 64): orthant psi(x) = ReLU(x) + shift, Lorentz
-// psi(x) = (y, |y| (1 + s^2))
+// ------------------------------------------------------------ linear features
+// (D = d = 64, chunk 32, 64 or 128): orthant psi(x) = ReLU(x) + shift,
+// Lorentz psi(x) = (y, |y| (1 + s^2)) (normalised reads), identity psi(x) = x
+// (first-order read, no denominator)
 constexpr int kLinFeatOrthant = 0;
 constexpr int kLinFeatLorentz = 1;
-constexpr int kLinChunk = 64;
+constexpr int kLinFeatIdentity = 2;
 // floats of one span state: 4 feature tiles x 5 value tiles of accumulator
-// tiles (the ones-column tile holds z in its first column)
+// tiles (the ones-column tile holds z in its first column); the identity map
+// keeps 4 value tiles (4096 floats)
 constexpr int64_t kLinStateFloats = int64_t(4) * kMfmaValueTiles * 256;
+int64_t linear_state_floats(int feature);
 
 struct LinArgs {
   const void* q;
   const void* k;
   const void* v;
   void* out;
-  float* ws;  // [BH][n_spans][kLinStateFloats]
+  float* ws;  // [BH][n_spans][linear_state_floats(feature)]
   int64_t BH;
   int64_t T;
   int feature;
@@ -94,10 +97,11 @@ struct LinArgs {
   int64_t G;        // chunks per span
   int64_t n_spans;  // spans per head
   float eps;
+  int chunk = 64;   // chunk length: 32, 64 or 128
 };
 
 inline bool linear_supported(bool bf16, int d, int dv, int chunk) {
-  return bf16 && d == 64 && dv == 64 && chunk == kLinChunk;
+  return bf16 && d == 64 && dv == 64 && (chunk == 32 || chunk == 64 || chunk == 128);
 }
 
 // span sums psi(K)^T [V | 1] of spans 0 .. n_spans-2 of every head into ws

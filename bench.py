@@ -365,56 +365,77 @@ def bench_table8(args, hip, am, ki, torch):
     return res
 
 
-# throughput of linear-feature kernels on one H100, Mtok/s, from the KATA page:
-# Table 11 (B = 1, H = 16, d_head = 64, bf16, psi(x) = x, chunk 128: its
-# tree-scan kernel) and the orthant/Lorentz table of Sec. 4.2 (B = 4, H = 12,
-# dv = 64, chunk 32, tree scan): context for the same shapes, not targets
-PAGE_LINEAR_MTOKS = {(1, 16, 131072, "orthant"): 69.4, (1, 16, 131072, "lorentz"): 69.4,
-                     (4, 12, 1024, "orthant"): 25.6, (4, 12, 1024, "lorentz"): 25.6,
-                     (4, 12, 2048, "orthant"): 30.3, (4, 12, 2048, "lorentz"): 30.3,
-                     (4, 12, 4096, "orthant"): 33.5}
+# throughput of the page's first-order kernels on one H100, Mtok/s (context
+# for the same shapes, not targets on this hardware):
+# Table 11 -- B = 1, H = 16, d_head = 64, bf16, the identity feature
+# psi(x) = x, chunk 128: its sequential linear-chunk kernel and its tree-scan
+# kernel, by T;
+PAGE_TABLE11_MTOKS = {2048: (6.7, 19.4), 4096: (13.6, 39.9), 8192: (23.4, 44.5), 16384: (24.1, 47.6),
+                      32768: (24.9, 49.4), 65536: (25.5, 67.5), 131072: (25.8, 69.4)}
+# App. E.1 -- B = 4, H = 12, dv = 64, chunk 32, orthant / Lorentz features:
+# its linear (sequential) and tree (associative) kernels, by (T, feature)
+PAGE_E1_MTOKS = {(1024, "orthant"): (24.1, 25.6), (1024, "lorentz"): (24.1, 25.6),
+                 (2048, "orthant"): (27.3, 30.3), (2048, "lorentz"): (27.3, 30.3),
+                 (4096, "orthant"): (29.8, 33.5)}
+
+
+def _time_linear(args, hip, am, torch, q, k, v, out, ws, feature, chunk, scan):
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(args.warmup):
+        am.kata_forward_linear(q, k, v, feature=feature, chunk=chunk, scan=scan, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, stream)
+    for _ in range(args.steps):
+        am.kata_forward_linear(q, k, v, feature=feature, chunk=chunk, scan=scan, out=out, workspace=ws)
+    hip.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = hip.ms(e0, e1) / args.steps
+    hip.destroy(e0)
+    hip.destroy(e1)
+    return ms
 
 
 def bench_linear(args, hip, am, ki, torch):
-    """The linear-feature chunked forward (orthant, Lorentz; D = d = 64) on
-    the page's Table 11 shape and its Sec. 4.2 table shapes, inputs drawn on
-    the device.  Algorithmic bytes: q, k, v read and out written once,
-    2 (2d + dv) + 2 dv = 512 B per token-head; useful FLOPs
-    2 [(C+1)/2 (d + dv) + 2 d dv + 2 d] per token-head."""
+    """The linear-feature chunked forward (D = d = 64), both prefixes side by
+    side: the identity map on the page's Table 11 slice (B = 1, H = 16,
+    chunk 128, T = 2048 .. 131072) and the orthant / Lorentz maps on its
+    App. E.1 shape (B = 4, H = 12, chunk 32, T = 1024 .. 4096) and at the
+    Table 11 shape, inputs drawn on the device.  Algorithmic bytes: q, k, v
+    read and out written once, 2 (2d + dv) + 2 dv = 512 B per token-head;
+    useful FLOPs 2 [(C+1)/2 (d + dv) + 2 d dv (+ 2 d for the denominator)]
+    per token-head."""
     res = {}
-    shapes = [(1, 16, 131072), (4, 12, 1024), (4, 12, 2048), (4, 12, 4096)]
     d = dv = 64
-    C = 64
-    stream = torch.cuda.current_stream().cuda_stream
-    for (B, H, T) in shapes:
+    runs = [(1, 16, T, "identity", 128) for T in sorted(PAGE_TABLE11_MTOKS)]
+    runs += [(4, 12, T, f, 32) for T in (1024, 2048, 4096) for f in ("orthant", "lorentz")]
+    runs += [(1, 16, 131072, f, 128) for f in ("orthant", "lorentz")]
+    for (B, H, T, feature, C) in runs:
         q, k, v = ki.forward_inputs_torch(B, H, T, d, dv, 80 + T % 97, "cuda")
         out = torch.empty_like(v)
         need = am.kata_forward_linear_workspace_bytes(B, H, T, d, dv, C)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-        for feature in ("orthant", "lorentz"):
-            for _ in range(args.warmup):
-                am.kata_forward_linear(q, k, v, feature=feature, out=out, workspace=ws)
-            torch.cuda.synchronize()
-            e0, e1 = hip.event(), hip.event()
-            hip.record(e0, stream)
-            for _ in range(args.steps):
-                am.kata_forward_linear(q, k, v, feature=feature, out=out, workspace=ws)
-            hip.record(e1, stream)
-            torch.cuda.synchronize()
-            ms = hip.ms(e0, e1) / args.steps
-            hip.destroy(e0)
-            hip.destroy(e1)
-            BHT = B * H * T
-            bytes_ = (2 * (2 * d + dv) + 2 * dv) * BHT
-            flops = 2 * ((C + 1) / 2 * (d + dv) + 2 * d * dv + 2 * d) * BHT
-            res[f"B{B}_H{H}_T{T}_d64_dv64_{feature}_bf16"] = {
-                "ms_per_step": round(ms, 4),
-                "tokens_per_s": round(B * T / (ms * 1e-3), 1),
-                "hbm_gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
-                "hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-                "page_h100_mtoks": PAGE_LINEAR_MTOKS.get((B, H, T, feature)),
-            }
+        BHT = B * H * T
+        bytes_ = (2 * (2 * d + dv) + 2 * dv) * BHT
+        den = 0 if feature == "identity" else 2 * d
+        flops = 2 * ((C + 1) / 2 * (d + dv) + 2 * d * dv + den) * BHT
+        r = {}
+        for scan in ("sequential", "associative"):
+            ms = _time_linear(args, hip, am, torch, q, k, v, out, ws, feature, C, scan)
+            r[scan] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                       "hbm_frac": round(bytes_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2)}
+        r["assoc_over_seq"] = round(r["sequential"]["ms_per_step"] / r["associative"]["ms_per_step"], 3)
+        if feature == "identity":
+            page = PAGE_TABLE11_MTOKS.get(T)
+            r["page_h100_mtoks"] = {"linear_chunk": page[0], "tree_scan": page[1],
+                                    "source": "Table 11 (same shape, identity feature, chunk 128)"}
+        elif C == 32:
+            page = PAGE_E1_MTOKS.get((T, feature))
+            if page:
+                r["page_h100_mtoks"] = {"linear": page[0], "tree": page[1],
+                                        "source": "App. E.1 table (same shape, same feature, chunk 32)"}
+        res[f"B{B}_H{H}_T{T}_d64_dv64_{feature}_C{C}_bf16"] = r
         del q, k, v, out, ws
     return res
 

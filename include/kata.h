@@ -218,43 +218,50 @@ kata_status_t kata_forward_chunked_blocks(const void* q, const void* k, const vo
                                           void* workspace, size_t workspace_bytes,
                                           void* stream);
 
-/* Linear (D = d) cone features of kata_forward_linear. */
+/* Linear (D = d) features of kata_forward_linear. */
 typedef enum {
-  KATA_FEATURE_ORTHANT = 0, /* psi(x) = ReLU(x) + shift, every coordinate */
-  KATA_FEATURE_LORENTZ = 1  /* psi(x) = (y, |y|_2 (1 + s^2)), y = x_{1..d-1}, s = x_d */
+  KATA_FEATURE_ORTHANT = 0,  /* psi(x) = ReLU(x) + shift, every coordinate */
+  KATA_FEATURE_LORENTZ = 1,  /* psi(x) = (y, |y|_2 (1 + s^2)), y = x_{1..d-1}, s = x_d */
+  KATA_FEATURE_IDENTITY = 2  /* psi(x) = x; read without a denominator (see below) */
 } kata_feature_t;
 
 /*
- * kata_forward_linear -- the causal normalised read with a linear cone
- * feature instead of the rank-one lift:
- *   o_t = sum_{s<=t} c_{t,s} v_s / (sum_{s<=t} c_{t,s} + eps),
- *   c_{t,s} = psi(q_t) . psi(k_s),
- * with the KATA-Orthant or KATA-Lorentz map of the KATA page (App. F.4; both
- * cone families of Sec. 2.3), whose scores are never negative.  Computed in
- * the chunked form of Sec. 4.1 Eqs. 17-20 with D = d: per-span states
- * psi(K)^T [V | 1], a sequential exclusive prefix over spans (Sec. 4.2), and
- * per chunk psi(Q) [S | z] plus the causally masked psi(Q) psi(K)^T block
- * times [V | 1], normalised.
+ * kata_forward_linear -- the causal read with a linear (D = d) feature psi
+ * instead of the rank-one lift, c_{t,s} = psi(q_t) . psi(k_s):
+ *   cone maps (KATA-Orthant, KATA-Lorentz of the KATA page, App. F.4; the
+ *   two cone families of Sec. 2.3), whose scores are never negative, read
+ *   normalised:  o_t = sum_{s<=t} c_{t,s} v_s / (sum_{s<=t} c_{t,s} + eps);
+ *   the identity map psi(x) = x, the first-order workload of the page's
+ *   associative-scan tables (Sec. 4.2, Tables 10-11, a d x dv state), has
+ *   signed scores and is read without a denominator:
+ *                o_t = sum_{s<=t} (q_t . k_s) v_s   (shift and eps unused).
+ * Computed in the chunked form of Sec. 4.1 Eqs. 17-20 with D = d: per-span
+ * states psi(K)^T [V | 1], an exclusive prefix over spans (Sec. 4.2),
+ * sequential or log-depth associative (`scan`; AUTO takes the associative
+ * one from 128 spans per head), and per chunk psi(Q) [S | z] plus the
+ * causally masked psi(Q) psi(K)^T block times [V | 1].
  *   q, k : [B, H, T, d] bf16;  v, out : [B, H, T, dv] bf16
- *   chunk: chunk length (64); a final partial chunk is zero-padded
- *   shift: the orthant map's shift, finite, >= 0 (ignored for Lorentz)
+ *   chunk: chunk length, 32, 64 or 128; a final partial chunk is zero-padded
+ *   shift: the orthant map's shift, finite, >= 0 (ignored by the others)
  *   eps  : finite, >= 0; added once to the accumulated denominator
  * Arithmetic: psi computed in fp32 from the bf16 inputs and rounded to bf16;
  * fp32 scores, states and accumulation; scores and the readout's state copy
  * rounded to bf16 before they multiply; fp32 normalisation; bf16 output.
- * Supported: KATA_BF16, d = 64, dv = 64, chunk = 64, T >= 1 (other shapes and
- * KATA_F32 return KATA_ERR_UNSUPPORTED).  workspace_bytes >=
- * kata_forward_linear_workspace_bytes(...) (workspace may be NULL when that
- * is 0).  Pointers 16-byte aligned; out and the workspace must not overlap
- * each other or the inputs.  Deterministic for fixed arguments and device.
+ * Supported: KATA_BF16, d = 64, dv = 64, chunk in {32, 64, 128}, T >= 1
+ * (other shapes and KATA_F32 return KATA_ERR_UNSUPPORTED).  workspace_bytes
+ * >= kata_forward_linear_workspace_bytes(...) (workspace may be NULL when
+ * that is 0).  Pointers 16-byte aligned; out and the workspace must not
+ * overlap each other or the inputs.  Deterministic for fixed arguments, scan
+ * mode and device.
  */
 size_t kata_forward_linear_workspace_bytes(int B, int H, int64_t T, int d, int dv,
                                            int chunk);
 kata_status_t kata_forward_linear(const void* q, const void* k, const void* v,
                                   void* out, int B, int H, int64_t T, int d, int dv,
                                   int chunk, kata_feature_t feature, float shift,
-                                  float eps, kata_dtype_t dtype, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  float eps, kata_dtype_t dtype, kata_scan_t scan,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * Optional profiling hook: hipEvent_t handles (as void*) recorded on `stream`

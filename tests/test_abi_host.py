@@ -189,16 +189,17 @@ def test_quadratic_error_paths(kw, status):
 
 
 def lin(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=300, d=64, dv=64, chunk=64, feat=0, shift=1e-6,
-        eps=1e-6, dt=BF16, ws=None, wsb=0):
-    return am.lib().kata_forward_linear(q, k, v, out, B, H, T, d, dv, chunk, feat, shift, eps, dt, ws,
+        eps=1e-6, dt=BF16, scan=0, ws=None, wsb=0):
+    return am.lib().kata_forward_linear(q, k, v, out, B, H, T, d, dv, chunk, feat, shift, eps, dt, scan, ws,
                                         wsb, None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=NULL), INVALID), (dict(v=NULL), INVALID), (dict(B=0), INVALID), (dict(T=-1), INVALID),
-    (dict(feat=2), INVALID), (dict(feat=-1), INVALID), (dict(dt=7), INVALID),
+    (dict(feat=3), INVALID), (dict(feat=-1), INVALID), (dict(dt=7), INVALID), (dict(scan=3), INVALID),
     (dict(dt=F32), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dv=32), UNSUPPORTED),
-    (dict(chunk=128), UNSUPPORTED),
+    (dict(chunk=16), UNSUPPORTED), (dict(chunk=256), UNSUPPORTED), (dict(chunk=96), UNSUPPORTED),
+    (dict(feat=2, chunk=48), UNSUPPORTED),
     (dict(shift=-1.0), INVALID), (dict(shift=float("inf")), INVALID), (dict(eps=float("nan")), INVALID),
     (dict(out=ctypes.c_void_p(P[3].value + 8)), INVALID),  # misaligned
     (dict(out=P[0]), INVALID),                              # out aliases q
@@ -216,6 +217,11 @@ def test_linear_workspace_sizes():
     n = L.kata_forward_linear_workspace_bytes(1, 16, 131072, 64, 64, 64)
     assert n == 16 * 32 * 4 * 5 * 256 * 4
     assert L.kata_forward_linear_workspace_bytes(1, 16, 131072, 32, 64, 64) == 0  # unsupported
+    # chunk 128: 1024 chunks per head in 32 spans of 32; chunk 32: 4096 in 32 spans of 128
+    assert L.kata_forward_linear_workspace_bytes(1, 16, 131072, 64, 64, 128) == n
+    assert L.kata_forward_linear_workspace_bytes(1, 16, 131072, 64, 64, 32) == n
+    # B = 4, H = 12, T = 1024, chunk 32: 32 chunks in 11 spans of 3
+    assert L.kata_forward_linear_workspace_bytes(4, 12, 1024, 64, 64, 32) == 48 * 11 * 4 * 5 * 256 * 4
 
 
 def gated(q=P[0], k=P[1], v=P[2], lg=P[4], out=P[3], B=1, H=1, T=300, d=16, dv=64, chunk=128, dt=BF16,
