@@ -44,6 +44,7 @@ EXPORTED = (
     "kata_forward_gated_workspace_bytes",
     "kata_forward_gated",
     "kata_decode_step_gated",
+    "kata_prefill_state_gated",
     "kata_forward_chunked_blocks_workspace_bytes",
     "kata_forward_chunked_blocks",
     "kata_probe_mfma_bf16",
@@ -101,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.kata_forward_gated_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
     L.kata_forward_gated.restype = i32
     L.kata_forward_gated.argtypes = [vp, vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, i32, vp, sz, vp]
+    L.kata_prefill_state_gated.restype = i32
+    L.kata_prefill_state_gated.argtypes = [vp, vp, vp, vp, i32, i32, i64, i32, i32, i32, vp]
     L.kata_decode_step_gated.restype = i32
     L.kata_decode_step_gated.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.kata_forward_chunked_blocks_workspace_bytes.restype = sz
@@ -415,6 +418,28 @@ def kata_forward_gated(q, k, v, log_gamma, chunk: int = 128, out=None, workspace
                                   chunk, _dtype_code(q), wptr, wbytes, _stream(stream))
     _check(st, "kata_forward_gated")
     return out
+
+
+def kata_prefill_state_gated(k, v, log_gamma, S=None, stream=None):
+    """GatedKATA state of a history (S_t = gamma_t S_{t-1} + phi(k_t) v_t^T):
+    k [B, H, T, d], v [B, H, T, dv], log_gamma [B, H, T] float32, all on the
+    device.  Returns S [B*H, D, dv] float32, the layout kata_decode_step_gated
+    continues from."""
+    torch = _torch()
+    for t, n in ((k, "k"), (v, "v"), (log_gamma, "log_gamma")):
+        _device_tensor(t, n)
+    B, H, T, d = k.shape
+    dv = v.shape[-1]
+    if tuple(log_gamma.shape) != (B, H, T) or log_gamma.dtype != torch.float32:
+        raise ValueError("log_gamma must be a float32 tensor of shape [B, H, T]")
+    D = kata_feature_dim(d)
+    if S is None:
+        S = torch.empty((B * H, D, dv), dtype=torch.float32, device=k.device)
+    _device_tensor(S, "S")
+    st = lib().kata_prefill_state_gated(_ptr(k), _ptr(v), _ptr(log_gamma), _ptr(S), B, H, T, d, dv,
+                                        _dtype_code(k), _stream(stream))
+    _check(st, "kata_prefill_state_gated")
+    return S
 
 
 def kata_decode_step_gated(S, q, k, v, log_gamma, out=None, stream=None):

@@ -486,6 +486,45 @@ kata_status_t kata_prefill_state(const void* k, const void* v, float* S, float* 
   return from_hip(kata::launch_state_valu(a, static_cast<hipStream_t>(stream)));
 }
 
+kata_status_t kata_prefill_state_gated(const void* k, const void* v, const float* log_gamma, float* S,
+                                       int B, int H, int64_t T, int d, int dv, kata_dtype_t dtype,
+                                       void* stream) {
+  if (k == nullptr || v == nullptr || log_gamma == nullptr || S == nullptr) return KATA_ERR_INVALID_VALUE;
+  if (B <= 0 || H <= 0 || T <= 0 || !dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(S) || (reinterpret_cast<uintptr_t>(log_gamma) & 3u) != 0)
+    return KATA_ERR_INVALID_VALUE;
+  if (!head_dim_ok(d) || !value_dim_ok(dv)) return KATA_ERR_UNSUPPORTED;
+  const int64_t BH = static_cast<int64_t>(B) * H;
+  if (T > (INT64_C(1) << 40) / BH || BH > (INT64_C(1) << 26)) return KATA_ERR_UNSUPPORTED;
+  const int64_t D = kata_feature_dim(d);
+  const size_t es = elem_size(dtype);
+  const size_t s_bytes = static_cast<size_t>(BH * D * dv) * 4;
+  const size_t k_bytes = static_cast<size_t>(BH * T * d) * es;
+  const size_t v_bytes = static_cast<size_t>(BH * T * dv) * es;
+  const size_t g_bytes = static_cast<size_t>(BH * T) * 4;
+  if (overlaps(S, s_bytes, k, k_bytes) || overlaps(S, s_bytes, v, v_bytes) ||
+      overlaps(S, s_bytes, log_gamma, g_bytes))
+    return KATA_ERR_INVALID_VALUE;
+  kata::StateArgs a{};
+  a.k = k;
+  a.v = v;
+  a.S_out = S;
+  a.z_out = nullptr;
+  a.BH = BH;
+  a.T = T;
+  a.d = d;
+  a.dv = dv;
+  a.span = T;
+  a.n_spans = 1;
+  a.s_stride = D * dv;
+  a.z_stride = 0;
+  a.bf16 = dtype == KATA_BF16;
+  a.sym = true;
+  a.skip_last = false;
+  a.log_gamma = log_gamma;
+  return from_hip(kata::launch_state_valu(a, static_cast<hipStream_t>(stream)));
+}
+
 kata_status_t kata_decode_step(float* S, float* z, const void* q, const void* k,
                                const void* v, void* out, int B, int H, int d, int dv,
                                float eps, kata_dtype_t dtype, void* stream) {

@@ -545,13 +545,18 @@ __device__ __forceinline__ ScoreOp<CF::FM> score_operand_bf16(const uint16_t* Kb
 // Global -> registers -> LDS for one chunk.  V: groups of 4 tokens x 8
 // columns (16 B per token), written transposed; K and Q: one token row per
 // thread.  Tokens at or past T read as zero (buffer range check).
-template <class CF, bool WITH_Q>
+// Gated read (G): a K row thread also loads its token's key factor
+// 2^((beta_C - beta_t) / 2) and scales the row's fp32 copy (the state
+// update's operand) by it; a Q row thread loads its token's beta_t / 2 into
+// the chunk's gate row `gb`.  The bf16 K rows of the scores stay unscaled.
+template <class CF, bool WITH_Q, bool G = false>
 struct Stage {
   static constexpr int C = CF::C, DK = CF::DK;
   static constexpr int NVG = (C / 4) * (DV / 8);
   static constexpr int RW = DK / 8;  // 16-byte words per K/Q row
   uint4 v[4];
   uint4 kq[RW];  // one K row or, with Q, one Q row (threads [C, 2C))
+  float gate;    // gated read: the key factor (K rows) or beta / 2 (Q rows)
 
   // K row staged by thread tid, or -1: threads [0, C) with Q; without Q the
   // last C threads, away from wave 0, which reduces the extra feature tile
@@ -575,18 +580,20 @@ struct Stage {
         const int t = is_q ? tid - C : tid;
 #pragma unroll
         for (int u = 0; u < RW; ++u) kq[u] = buf_load16(is_q ? src.q : src.k, t * (2 * DK) + 16 * u);
+        if constexpr (G) gate = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(is_q ? src.g : src.gk, 4 * t, 0, 0));
       }
     } else {
       const int t = krow(tid);
       if (t >= 0) {
 #pragma unroll
         for (int u = 0; u < RW; ++u) kq[u] = buf_load16(src.k, t * (2 * DK) + 16 * u);
+        if constexpr (G) gate = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(src.gk, 4 * t, 0, 0));
       }
     }
   }
 
   template <class S>
-  __device__ __forceinline__ void store(S& sm, int tid) const {
+  __device__ __forceinline__ void store(S& sm, int tid, float* gb = nullptr) const {
     constexpr int LDT = CF::LDT, LDK = CF::LDK;
     if (tid < NVG) {
       const int tg = tid % (C / 4), cg = tid / (C / 4);
@@ -619,9 +626,10 @@ struct Stage {
       // with Q, a bf16 row copy (scores)
       const int t = krow(tid);
       const int pos = group_pos(t >> 2) + (t & 3);
+      const float ks = G ? kSqrt2 * gate : kSqrt2;
 #pragma unroll
       for (int x = 0; x < DK; ++x) {
-        sm.Kt[staged_dim<CF::FM>(x) * LDK + pos] = kSqrt2 * ((x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]));
+        sm.Kt[staged_dim<CF::FM>(x) * LDK + pos] = ks * ((x & 1) ? hi_bf16(w[x >> 1]) : lo_bf16(w[x >> 1]));
       }
       if constexpr (WITH_Q) {
 #pragma unroll
@@ -632,6 +640,7 @@ struct Stage {
     } else if (WITH_Q && tid < 2 * C) {
       if constexpr (WITH_Q) {
         const int t = tid - C;
+        if constexpr (G) gb[t] = gate;
 #pragma unroll
         for (int c = 0; c < DK / 4; ++c) {
           float4 f;
@@ -723,7 +732,8 @@ __device__ __forceinline__ void state_tiles16(f32x4 (&acc)[CF::MFT][NDT], const 
   (state_tile16<CF, J>(acc, kr, bv, w), ...);
 }
 
-template <class CF, class S>
+// (N: value tiles updated; the gated read leaves out the ones-column tile)
+template <class CF, class S, int N = NDT>
 __device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S& sm, int w, int lane,
                                              const KeyPairs<CF>& kp) {
   constexpr int LDT = CF::LDT, LDK = CF::LDK;
@@ -757,7 +767,7 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S
         af.z = pack2(a1.x * b1.x, a1.y * b1.y);
         af.w = pack2(a1.z * b1.z, a1.w * b1.w);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = mfma(af, bv[dt], acc[m][dt]);
+        for (int dt = 0; dt < N; ++dt) acc[m][dt] = mfma(af, bv[dt], acc[m][dt]);
       }
     }
   }
@@ -856,9 +866,23 @@ __device__ __forceinline__ void write_sb(uint16_t* __restrict__ Sb, const f32x4 
   }
 }
 
+// state decay of the gated read (the ones-column tile is unused there)
+template <int NA, int NB>
+__device__ __forceinline__ void gate_decay(f32x4 (&acc)[NA][NB], float f) {
+#pragma unroll
+  for (int m = 0; m < NA; ++m) {
+#pragma unroll
+    for (int dt = 0; dt < NB - 1; ++dt) acc[m][dt] *= f;  // the ones-column tile is unused
+  }
+}
+
 // ------------------------------------------------------------ span sums
 
-template <class CF>
+// Gated read (G): before a chunk's keys are added the state decays by the
+// chunk's gate product 2^beta_C (beta_C / 2 read from the gate sums at the
+// chunk's last token; every chunk of a summed span is whole), and the staged
+// key rows carry their key factors.  The ones-column tile is not updated.
+template <class CF, bool G = false>
 __device__ __forceinline__ void span_state_mfma_body(const MfmaArgs& a) {
   constexpr int C = CF::C, DK = CF::DK;
   // two LDS tile buffers: chunk i is staged into buffer i % 2 while the
@@ -884,22 +908,28 @@ __device__ __forceinline__ void span_state_mfma_body(const MfmaArgs& a) {
     const int64_t first = sp * a.G * C;
     int64_t end = first + a.G * C;
     if (end > a.T) end = a.T;
-    Stage<CF, false> st;
-    st.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, first, a.T), tid);
+    Stage<CF, false, G> st;
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, a.T, a.gb, a.gk); };
+    st.load(src(first), tid);
     int buf = 0;
     for (int64_t c0 = first; c0 < end; c0 += C, buf ^= 1) {
       st.store(sm[buf], tid);
-      if (c0 + C < end) st.load(chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c0 + C, a.T), tid);
+      if (c0 + C < end) st.load(src(c0 + C), tid);
       __syncthreads();
-      state_update<CF>(acc, sm[buf], W, lane, kp);
+      if constexpr (G) {
+        gate_decay(acc, __builtin_amdgcn_exp2f(2.f * a.gb[tok0 + c0 + C - 1]));
+        state_update<CF, Smem<CF>, NDT - 1>(acc, sm[buf], W, lane, kp);
+      } else {
+        state_update<CF>(acc, sm[buf], W, lane, kp);
+      }
     }
     store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
   });
 }
 
-template <class CF>
+template <class CF, bool G = false>
 __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
-  span_state_mfma_body<CF>(a);
+  span_state_mfma_body<CF, G>(a);
 }
 
 // ------------------------------------------------------------ span sums, d = 16, LDS DMA
@@ -979,14 +1009,6 @@ __device__ __forceinline__ void dma_chunk16(DmaTile16<C, G>& b, const ChunkSrc& 
 // 2^((beta_C - beta_s) / 2) (computed once per token by gate_prep_kernel);
 // the lane's 8 tokens are those of its transposed K operand (32 ks + 4g + m
 // and 32 ks + 16 + 4g + m).
-template <int NA, int NB>
-__device__ __forceinline__ void gate_decay(f32x4 (&acc)[NA][NB], float f) {
-#pragma unroll
-  for (int m = 0; m < NA; ++m) {
-#pragma unroll
-    for (int dt = 0; dt < NB - 1; ++dt) acc[m][dt] *= f;  // the ones-column tile is unused
-  }
-}
 
 __device__ __forceinline__ void gate_keys(float (&kr)[8], const float* gk, int ks) {
   const int g = __lane_id() >> 4;
@@ -1284,6 +1306,14 @@ struct TileSrc {
   }
 };
 
+// the register-staged tiles of the gated read: the chunk's gate row beta_t / 2
+template <class CF>
+struct TileSrcG : TileSrc<CF> {
+  const float* gb;
+  __device__ __forceinline__ float gate(int row) const { return gb[row]; }
+  __device__ __forceinline__ float4 gate4(int row) const { return *reinterpret_cast<const float4*>(&gb[row]); }
+};
+
 // fp32 partial reads of a sliced feature map: rows of PART_LD floats (64
 // value columns, the denominator, padding) for the chunk's tokens
 constexpr int PART_LD = 68;
@@ -1310,7 +1340,7 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
                                               const H& after_q = H{}, const P& part = P{}) {
   constexpr int C = CF::C, DK = CF::DK, FM = CF::FM, NSLOT = CF::NSLOT, NDW = CF::NDW;
   constexpr int SB_LD = CF::SB_LD;
-  static_assert(!G || NDW == NDT, "the gated read uses whole output rows");
+  static_assert(!G || CF::NSL == 1, "the gated read uses the full map");
   // denominators from the key Gram matrix (see below) instead of the ones-column tile
   constexpr bool ZD = S::kGramDen;
   static_assert(!ZD || (DK == 16 && NDW == NDT && !G && CF::NSL == 1), "Gram denominators: d = 16, whole rows");
@@ -1571,10 +1601,14 @@ __device__ __forceinline__ void readout_chunk(const S& src, const uint16_t* __re
 }
 
 // every wave reads out and carries its share of the state
-template <class CF>
+// (G: the gated read -- gate row in LDS, query and score factors in the
+// readout, the chunk decay and key factors in the state carry, no
+// denominator)
+template <class CF, bool G = false>
 __device__ __forceinline__ void readout_mfma_body(const MfmaArgs& a) {
   constexpr int C = CF::C, DK = CF::DK, SB_LD = CF::SB_LD;
   __shared__ SmemOut<CF> sm;
+  __shared__ alignas(16) float gbs[G ? C : 4];
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index is uniform across the wave: keep it scalar so every
   // wave-dependent branch is a scalar branch, not an exec-mask region
@@ -1605,18 +1639,23 @@ __device__ __forceinline__ void readout_mfma_body(const MfmaArgs& a) {
     // chunk i is read from LDS while chunk i+1 arrives in registers; after
     // the chunk's reads a single phase writes the next state copy and stages
     // the next chunk (disjoint LDS regions), so each chunk costs two barriers
-    Stage<CF, true> st;
+    Stage<CF, true, G> st;
     const int64_t first = sp * a.G * C;
     int64_t end = first + a.G * C;
     if (end > a.T) end = a.T;
-    st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, first, a.T), tid);
-    st.store(sm, tid);
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, a.T, a.gb, a.gk); };
+    st.load(src(first), tid);
+    st.store(sm, tid, gbs);
     __syncthreads();
     for (int64_t c0 = first; c0 < end; c0 += C) {
       // the next chunk's loads go out first, to overlap this chunk's compute
-      if (c0 + C < end) st.load(chunk_src<DK, C>(a.q, a.k, a.v, tok0, c0 + C, a.T), tid);
+      if (c0 + C < end) st.load(src(c0 + C), tid);
       const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
-      if constexpr (CF::NSL > 1) {
+      if constexpr (G) {
+        readout_chunk<CF, TileSrcG<CF>, NoHook, true>(TileSrcG<CF>{{sm}, gbs}, sm.Sb, L, lane, a.eps,
+                                                      rows_rsrc(a.out, tok0 + c0, n, 2 * DV),
+                                                      sm.Ob[CF::NDW == NDT ? W : 0]);
+      } else if constexpr (CF::NSL > 1) {
         readout_chunk<CF, TileSrc<CF>, NoHook, false, PartRows>(
             TileSrc<CF>{sm}, sm.Sb, L, lane, a.eps, rows_rsrc(a.out, tok0 + c0, n, 2 * DV), sm.Ob[0], NoHook{},
             PartRows{rows_rsrc(a.part, tok0 + c0, n, PART_LD * 4)});
@@ -1626,18 +1665,23 @@ __device__ __forceinline__ void readout_mfma_body(const MfmaArgs& a) {
       }
       if (c0 + C >= end) break;
       // carry the state across the chunk
-      state_update<CF>(acc, sm, W, lane, kp);
+      if constexpr (G) {
+        gate_decay(acc, __builtin_amdgcn_exp2f(2.f * gbs[C - 1]));  // a whole chunk: beta_C / 2
+        state_update<CF, SmemOut<CF>, NDT - 1>(acc, sm, W, lane, kp);
+      } else {
+        state_update<CF>(acc, sm, W, lane, kp);
+      }
       __syncthreads();  // every wave done reading the tiles and Sb of this chunk
       write_sb<CF>(sm.Sb, acc, W, lane);
-      st.store(sm, tid);
+      st.store(sm, tid, gbs);
       __syncthreads();
     }
   });
 }
 
-template <class CF>
+template <class CF, bool G = false>
 __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
-  readout_mfma_body<CF>(a);
+  readout_mfma_body<CF, G>(a);
 }
 
 // ------------------------------------------------------------ readout, d = 16, LDS DMA
@@ -1917,6 +1961,10 @@ hipError_t launch_span_state_gated(const MfmaArgs& a, hipStream_t stream) {
     span_state_dma16_kernel<64, true><<<grid, 256, 0, stream>>>(a);
   } else if (a.d == 16 && a.chunk == 128) {
     span_state_dma16_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 32 && a.chunk == 64) {
+    span_state_mfma_kernel<Cfg<32, 64>, true><<<grid, Cfg<32, 64>::NT, 0, stream>>>(a);
+  } else if (a.d == 32 && a.chunk == 128) {
+    span_state_mfma_kernel<Cfg<32, 128>, true><<<grid, Cfg<32, 128>::NT, 0, stream>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
@@ -1929,6 +1977,10 @@ hipError_t launch_readout_gated(const MfmaArgs& a, hipStream_t stream) {
     readout_dma16_kernel<64, true><<<grid, 256, 0, stream>>>(a);
   } else if (a.d == 16 && a.chunk == 128) {
     readout_dma16_kernel<128, true><<<grid, 256, 0, stream>>>(a);
+  } else if (a.d == 32 && a.chunk == 64) {
+    readout_mfma_kernel<Cfg<32, 64>, true><<<grid, Cfg<32, 64>::NT, 0, stream>>>(a);
+  } else if (a.d == 32 && a.chunk == 128) {
+    readout_mfma_kernel<Cfg<32, 128>, true><<<grid, Cfg<32, 128>::NT, 0, stream>>>(a);
   } else {
     return hipErrorInvalidValue;
   }

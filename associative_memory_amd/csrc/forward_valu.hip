@@ -18,13 +18,18 @@ constexpr int TT = 32;   // tokens per LDS tile in the state kernel
 // grid.x enumerates (bh, span, dv tile).  Thread e-slots own elements
 // (f, c) = (e / DVT, e % DVT) of the D x DVT block; z is summed by the dv
 // tile 0 workgroup.
-template <int DK, bool BF16>
+//
+// GATED (a.log_gamma != nullptr, one span per head): the GatedKATA state of
+// the span, S <- gamma_t S + phi(k_t) v_t^T token by token (the page, App.
+// F.4), with gamma_t = exp(log_gamma_t); no z.
+template <int DK, bool BF16, bool GATED = false>
 __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
   constexpr int D = feature_dim(DK);
   constexpr int M = (D * DVT + kThreads - 1) / kThreads;
   constexpr int MZ = (D + kThreads - 1) / kThreads;
   __shared__ float ks[TT][DK];
   __shared__ float vs[TT][DVT];
+  __shared__ float gs[GATED ? TT : 1];
 
   const int n_tiles = a.dv / DVT;
   int64_t id = blockIdx.x;
@@ -75,8 +80,18 @@ __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
       const int64_t t = t0 + r;
       vs[r][c] = (t < t_end) ? load_elem<BF16>(a.v, (tok0 + t) * a.dv + tile * DVT + c) : 0.f;
     }
+    if (GATED && tid < TT) {
+      const int64_t t = t0 + tid;
+      gs[tid] = (t < t_end) ? __expf(a.log_gamma[tok0 + t]) : 1.f;  // padding: no decay, no key
+    }
     __syncthreads();
     for (int r = 0; r < TT; ++r) {
+      if constexpr (GATED) {
+        const float g = gs[r];
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(acc[m], g, ks[r][fi[m]] * ks[r][fj[m]] * vs[r][fc[m]]);
+        continue;
+      }
 #pragma unroll
       for (int m = 0; m < M; ++m) acc[m] += ks[r][fi[m]] * ks[r][fj[m]] * vs[r][fc[m]];
       if (tile == 0) {
@@ -97,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
       So[f * a.dv + tile * DVT + fc[m]] = w * acc[m];
     }
   }
-  if (tile == 0) {
+  if (!GATED && tile == 0) {
     float* zo = a.z_out + (bh * a.n_spans + sp) * a.z_stride;
 #pragma unroll
     for (int m = 0; m < MZ; ++m) {
@@ -260,7 +275,13 @@ template <int DK>
 hipError_t launch_state_d(const StateArgs& a, hipStream_t s) {
   const int64_t blocks = a.BH * a.n_spans * (a.dv / DVT);
   dim3 grid(static_cast<unsigned>(blocks));
-  if (a.bf16) {
+  if (a.log_gamma != nullptr) {
+    if (a.bf16) {
+      state_valu_kernel<DK, true, true><<<grid, kThreads, 0, s>>>(a);
+    } else {
+      state_valu_kernel<DK, false, true><<<grid, kThreads, 0, s>>>(a);
+    }
+  } else if (a.bf16) {
     state_valu_kernel<DK, true><<<grid, kThreads, 0, s>>>(a);
   } else {
     state_valu_kernel<DK, false><<<grid, kThreads, 0, s>>>(a);

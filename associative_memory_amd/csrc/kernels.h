@@ -44,6 +44,9 @@ struct StateArgs {
   bool bf16;
   bool sym;
   bool skip_last;
+  // gated state (one span per head): S <- exp(log_gamma_t) S + phi(k_t) v_t^T
+  // token by token, log_gamma [BH*T]; z_out is not written
+  const float* log_gamma = nullptr;
 };
 hipError_t launch_state_valu(const StateArgs& a, hipStream_t stream);
 

@@ -126,10 +126,11 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream);
 // readout of every span, starting from the exclusive prefix in ws
 hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream);
 
-// The gated read (GatedKATA) on the d = 16 path, chunk 64 or 128: span sums
-// and readout with the running gate sums a.gb (no denominator).
+// The gated read (GatedKATA) on the d = 16 and d = 32 paths, chunk 64 or 128:
+// span sums and readout with the running gate sums a.gb and key factors a.gk
+// (no denominator).
 inline bool gated_supported(bool bf16, int d, int dv, int chunk) {
-  return bf16 && d == 16 && dv == 64 && (chunk == 64 || chunk == 128);
+  return bf16 && (d == 16 || d == 32) && dv == 64 && (chunk == 64 || chunk == 128);
 }
 hipError_t launch_span_state_gated(const MfmaArgs& a, hipStream_t stream);
 hipError_t launch_readout_gated(const MfmaArgs& a, hipStream_t stream);

@@ -441,13 +441,14 @@ def bench_linear(args, hip, am, ki, torch):
 
 
 def bench_gated(args, hip, am, ki, torch):
-    """The gated read (GatedKATA, d = 16) on the T = 131072 and T = 2048
-    forward shapes at both chunk lengths, gates from the seeded recipe.
+    """The gated read (GatedKATA) on the T = 131072 and T = 2048 (d = 16)
+    and T = 8192 (d = 32) forward shapes at both chunk lengths, gates from the
+    seeded recipe.
     Algorithmic bytes: q, k, v, the fp32 gate read and out written,
     2 (2d + dv) + 4 + 2 dv = 324 B per token-head."""
     res = {}
     stream = torch.cuda.current_stream().cuda_stream
-    for w in (ki.LONG, ki.MEDIUM):
+    for w in (ki.LONG, ki.MEDIUM, ki.WIDE):
         q, k, v = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")
         lg = torch.from_numpy(ki.draw_log_gamma(w.B, w.H, w.T, w.seed)).cuda()
         out = torch.empty_like(v)

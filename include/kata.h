@@ -181,8 +181,8 @@ kata_status_t kata_forward_quadratic(const void* q, const void* k, const void* v
  *   chunk     : chunk length, 64 or 128
  * Arithmetic: gate sums in fp32 (log2 units), bf16 operands, fp32 scores,
  * states and accumulation, bf16 output.
- * Supported: KATA_BF16, d = 16, dv = 64, T >= 1 (other shapes and KATA_F32
- * return KATA_ERR_UNSUPPORTED).  The workspace is always needed:
+ * Supported: KATA_BF16, d in {16, 32}, dv = 64, T >= 1 (other shapes and
+ * KATA_F32 return KATA_ERR_UNSUPPORTED).  The workspace is always needed:
  * workspace_bytes >= kata_forward_gated_workspace_bytes(...).  Pointers
  * 16-byte aligned; out and the workspace must not overlap each other or the
  * inputs.  Deterministic for fixed arguments and device.
@@ -299,6 +299,22 @@ kata_status_t kata_forward_chunked_profiled(const void* q, const void* k, const 
 kata_status_t kata_prefill_state(const void* k, const void* v, float* S,
                                  float* z, int B, int H, int64_t T, int d,
                                  int dv, kata_dtype_t dtype, void* stream);
+
+/*
+ * kata_prefill_state_gated -- GatedKATA state of a history, for continuing
+ * it with kata_decode_step_gated (the KATA page, App. F.4: S_t = gamma_t
+ * S_{t-1} + psi(k_t) v_t^T from S_0 = 0; unrolled, Sec. 5.2):
+ *   S = sum_t (prod_{r=t+1..T} gamma_r) phi(k_t) v_t^T   [B*H, D, dv] fp32
+ * in the layout of kata_prefill_state (no z: the gated read has no
+ * denominator), taken token by token in fp32.
+ *   k : [B, H, T, d], v : [B, H, T, dv] in dtype
+ *   log_gamma : [B, H, T] fp32, log of the gate per token (4-byte aligned)
+ * S is overwritten.  Supported: d in {16, 32}; dv in {16, 32, 64}; T >= 1.
+ * S must not overlap the inputs.
+ */
+kata_status_t kata_prefill_state_gated(const void* k, const void* v, const float* log_gamma,
+                                       float* S, int B, int H, int64_t T, int d, int dv,
+                                       kata_dtype_t dtype, void* stream);
 
 /*
  * kata_decode_step -- one token of the additive recurrence (the KATA page,

@@ -231,7 +231,7 @@ def gated(q=P[0], k=P[1], v=P[2], lg=P[4], out=P[3], B=1, H=1, T=300, d=16, dv=6
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=NULL), INVALID), (dict(lg=NULL), INVALID), (dict(out=NULL), INVALID), (dict(H=0), INVALID),
-    (dict(dt=5), INVALID), (dict(dt=F32), UNSUPPORTED), (dict(d=32), UNSUPPORTED), (dict(dv=16), UNSUPPORTED),
+    (dict(dt=5), INVALID), (dict(dt=F32), UNSUPPORTED), (dict(d=64), UNSUPPORTED), (dict(dv=16), UNSUPPORTED),
     (dict(chunk=32), UNSUPPORTED),
     (dict(lg=ctypes.c_void_p(P[4].value + 4)), INVALID),   # misaligned
     (dict(out=P[4]), INVALID),                              # out overlaps log_gamma
@@ -255,7 +255,29 @@ def test_gated_workspace_sizes():
     assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 16, 64, 128) == ctot_off + 3 * 4
     # 64 heads of one chunk: a single span, no states
     assert L.kata_forward_gated_workspace_bytes(8, 8, 100, 16, 64, 128) == 2 * 25600 + 64 * 4
-    assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 32, 64, 128) == 0  # unsupported
+    # d = 32: 33 feature tiles per span state (3 spans of one chunk)
+    states = 3 * (33 * 4 * 256 + 33 * 16) * 4
+    gb_off = (states + 255) // 256 * 256
+    gk_off = (gb_off + 300 * 4 + 255) // 256 * 256
+    ctot_off = (gk_off + 300 * 4 + 255) // 256 * 256
+    assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 32, 64, 128) == ctot_off + 3 * 4
+    assert L.kata_forward_gated_workspace_bytes(1, 1, 300, 64, 64, 128) == 0  # unsupported
+
+
+def test_gated_prefill_error_paths():
+    L = am.lib()
+    pre = lambda k=P[0], v=P[1], lg=P[2], S=P[3], B=1, H=1, T=10, d=16, dv=64, dt=F32: \
+        L.kata_prefill_state_gated(k, v, lg, S, B, H, T, d, dv, dt, None)
+    assert pre(k=NULL) == INVALID
+    assert pre(lg=NULL) == INVALID
+    assert pre(S=NULL) == INVALID
+    assert pre(T=0) == INVALID
+    assert pre(dt=4) == INVALID
+    assert pre(d=24) == UNSUPPORTED
+    assert pre(dv=48) == UNSUPPORTED
+    assert pre(lg=ctypes.c_void_p(P[2].value + 2)) == INVALID   # misaligned
+    assert pre(S=P[1]) == INVALID                               # S overlaps v
+    assert pre(S=ctypes.c_void_p(P[2].value + 16)) == INVALID   # S overlaps log_gamma
 
 
 def test_gated_decode_error_paths():

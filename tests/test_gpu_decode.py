@@ -214,16 +214,24 @@ def test_decode_graph_replay_matches_eager():
 @pytest.mark.parametrize("d,dv,dtype", [(16, 64, ki.F32), (16, 16, ki.F32), (32, 64, ki.F32),
                                         (16, 64, ki.BF16)])
 def test_gated_decode_steps_match_oracle(d, dv, dtype):
-    # GatedKATA steps from a prefilled state (the additive prefill is a valid
-    # starting state).  No denominator: row bars scale with the decayed score
-    # mass A = phi(q)^T z_gated, tracked by running the oracle with v = 1.
+    # GatedKATA steps from the gated state of a history (kata_prefill_state_gated).
+    # No denominator: row bars scale with the decayed score mass A =
+    # phi(q)^T z_gated, tracked by running the oracle with v = 1.
     say(f"gated decode d={d} dv={dv} dtype={dtype}")
     heads, prefill, steps = 9, 200, 24
-    di, S, z, S_ref, z_ref = _decode_case(heads, prefill, steps, d, dv, seed=13)
+    di = ki.decode_inputs(13, heads, prefill, steps, d, dv)
     rng = np.random.Generator(np.random.PCG64(14))
+    lg_pre = (-np.log1p(np.exp(-(rng.standard_normal((heads, prefill)) + 3.0)))).astype(np.float32)
     lg = (-np.log1p(np.exp(-(rng.standard_normal((steps, heads)) + 2.0)))).astype(np.float32)
+    S = am.kata_prefill_state_gated(to_dev(di.pk[:, None], ki.F32), to_dev(di.pv[:, None], ki.F32),
+                                    torch.from_numpy(lg_pre[:, None]).cuda())
+    torch.cuda.synchronize()
+    pk, pv, lgp = di.pk.astype(np.float64), di.pv.astype(np.float64), lg_pre.astype(np.float64)
+    S_ref = np.stack([orc.gated_state(pk[h], pv[h], lgp[h]) for h in range(heads)])
+    M_ref = np.stack([orc.gated_state(pk[h], np.ones((prefill, 1)), lgp[h]) for h in range(heads)])
     vmax = max(np.abs(di.pv).max(), np.abs(di.sv).max())
-    M_ref = z_ref[..., None]  # the mass state: v = 1
+    # the prefilled state itself: fp32, prefill terms each at most 2 max|v|
+    assert np.abs(to_host64(S) - S_ref).max() <= prefill * 8 * 2.0 ** -24 * 2 * (1 + vmax)
     tol = 1e-4 if dtype == ki.F32 else 2e-2
     for s in range(steps):
         qs, q64 = ki.as_storage(di.sq[s].astype(np.float64), dtype)
@@ -240,3 +248,45 @@ def test_gated_decode_steps_match_oracle(d, dv, dtype):
     # the state itself, after 24 decays and writes (fp32 throughout)
     Sg = to_host64(S)
     assert np.abs(Sg - S_ref).max() <= 1e-5 * (1 + np.abs(S_ref).max())
+
+
+@pytest.mark.parametrize("d", [16, 32])
+def test_gated_forward_prefill_then_decode(d):
+    # a gated history through the forward and the gated prefill, then gated
+    # decode steps, equals the gated forward over the whole sequence at the
+    # new positions (the unrolled read of Sec. 5.2)
+    B, H, T0, n, dv = 2, 2, 700, 12, 64
+    say(f"gated forward -> prefill -> decode d={d}")
+    inp = ki.forward_inputs(B, H, T0 + n, d, dv, ki.BF16, seed=27 + d)
+    lg = ki.draw_log_gamma(B, H, T0 + n, seed=28)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    g = torch.from_numpy(lg).cuda()
+    full = am.kata_forward_gated(q, k, v, g)
+    S = am.kata_prefill_state_gated(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(),
+                                    g[:, :, :T0].contiguous())
+    outs = []
+    for t in range(T0, T0 + n):
+        o = am.kata_decode_step_gated(S, q[:, :, t].reshape(B * H, d).contiguous(),
+                                      k[:, :, t].reshape(B * H, d).contiguous(),
+                                      v[:, :, t].reshape(B * H, dv).contiguous(),
+                                      g[:, :, t].reshape(B * H).contiguous())
+        outs.append(o.reshape(B, H, dv))
+    torch.cuda.synchronize()
+    dec = to_host64(torch.stack(outs, dim=2))
+    lg64 = lg.astype(np.float64)
+    ref = orc.forward_gated_quadratic(inp.q64, inp.k64, inp.v64, lg64)[:, :, T0:]
+    mass = orc.forward_gated_quadratic(inp.q64, inp.k64, np.ones((B, H, T0 + n, 1)), lg64)[:, :, T0:, 0]
+    vmax = np.abs(inp.v64).max()
+    # bf16 inputs and outputs (fp32 state and arithmetic): the bf16 bar on the mass scale
+    err = np.abs(dec - ref).max(axis=-1)
+    assert (err <= 2e-2 * vmax * np.maximum(1.0, mass)).all(), f"decode after gated prefill: {err.max()}"
+    # the gated prefill itself against the unrolled state (fp32 sums of bf16 products)
+    S_ref = np.stack([orc.gated_state(inp.k64[b, h, :T0], inp.v64[b, h, :T0], lg64[b, h, :T0])
+                      for b in range(B) for h in range(H)])
+    S0 = am.kata_prefill_state_gated(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(),
+                                     g[:, :, :T0].contiguous())
+    torch.cuda.synchronize()
+    assert np.abs(to_host64(S0) - S_ref).max() <= T0 * 8 * 2.0 ** -24 * 2 * (1 + vmax)
+    # the forward itself (bf16 path) at the same positions
+    errf = np.abs(to_host64(full)[:, :, T0:] - ref).max(axis=-1)
+    assert (errf <= 2e-2 * vmax * np.maximum(1.0, mass)).all(), f"gated forward tail: {errf.max()}"

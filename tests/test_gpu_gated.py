@@ -1,7 +1,9 @@
-"""GPU parity of the gated read (GatedKATA, d = 16, dv = 64) against the fp64
-oracle, through the C ABI: full outputs on ragged and multi-span shapes at
-both chunk lengths, gates without decay (the unnormalised KATA numerator) and
-with strong decay, sampled rows at T = 131072, and determinism.
+"""GPU parity of the gated read (GatedKATA, d = 16 and d = 32, dv = 64)
+against the fp64 oracle, through the C ABI: full outputs on ragged and
+multi-span shapes at both chunk lengths, gates without decay (the
+unnormalised KATA numerator) and with strong decay, sampled rows at
+T = 131072 (d = 16) and every row of two heads at T = 8192 (d = 32), guard
+bands, and determinism.
 
 Tolerance.  The gated read has no denominator, so |o_t| grows with the
 decayed score mass A_t = sum_{s<=t} (prod gamma) (q_t.k_s)^2.  The bf16
@@ -58,32 +60,52 @@ GATED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("d", [16, 32])
 @pytest.mark.parametrize("case", GATED_CASES, ids=lambda c: "B{}H{}T{}C{}".format(*c))
-def test_ragged_and_multispan(case):
+def test_ragged_and_multispan(case, d):
     B, H, T, C = case
-    say(f"gated {case}")
-    inp = ki.forward_inputs(B, H, T, 16, 64, ki.BF16, seed=T + C)
+    say(f"gated d={d} {case}")
+    inp = ki.forward_inputs(B, H, T, d, 64, ki.BF16, seed=T + C + d)
     lg = ki.draw_log_gamma(B, H, T, seed=T + C)
-    full_check(inp, lg, C, f"gated {case}")
+    full_check(inp, lg, C, f"gated d={d} {case}")
 
 
+@pytest.mark.parametrize("d", [16, 32])
 @pytest.mark.parametrize("C", [64, 128])
-def test_no_decay_is_the_numerator(C):
+def test_no_decay_is_the_numerator(C, d):
     # gamma = 1: o_t = sum_{s<=t} (q_t.k_s)^2 v_s, the unnormalised KATA read
     B, H, T = 1, 2, 3000
-    inp = ki.forward_inputs(B, H, T, 16, 64, ki.BF16, seed=90)
+    inp = ki.forward_inputs(B, H, T, d, 64, ki.BF16, seed=90 + d)
     lg = np.zeros((B, H, T), dtype=np.float32)
-    full_check(inp, lg, C, f"gated no decay C{C}")
+    full_check(inp, lg, C, f"gated d={d} no decay C{C}")
+
+
+@pytest.mark.parametrize("d", [16, 32])
+@pytest.mark.parametrize("C", [64, 128])
+def test_strong_decay(C, d):
+    # gates around 0.5: a memory of a few tokens, far below one chunk
+    B, H, T = 2, 2, 2500
+    inp = ki.forward_inputs(B, H, T, d, 64, ki.BF16, seed=91 + d)
+    rng = np.random.Generator(np.random.PCG64(92))
+    lg = (-np.log1p(np.exp(-rng.standard_normal((B, H, T))))).astype(np.float32)
+    full_check(inp, lg, C, f"gated d={d} strong decay C{C}")
 
 
 @pytest.mark.parametrize("C", [64, 128])
-def test_strong_decay(C):
-    # gates around 0.5: a memory of a few tokens, far below one chunk
-    B, H, T = 2, 2, 2500
-    inp = ki.forward_inputs(B, H, T, 16, 64, ki.BF16, seed=91)
-    rng = np.random.Generator(np.random.PCG64(92))
-    lg = (-np.log1p(np.exp(-rng.standard_normal((B, H, T))))).astype(np.float32)
-    full_check(inp, lg, C, f"gated strong decay C{C}")
+def test_d32_workload_shape_two_heads(C):
+    # B = 2, H = 16, T = 8192, d = 32 (the d = 32 forward workload's shape and
+    # plan): every row of the first and last head
+    w = ki.WIDE
+    say(f"gated {w.name} C{C}: every row of two heads")
+    inp = ki.workload_inputs(w)
+    lg = ki.draw_log_gamma(w.B, w.H, w.T, seed=w.seed)
+    got = run(inp, lg, C)
+    vmax = np.abs(inp.v64).max()
+    for (b, h) in ((0, 0), (w.B - 1, w.H - 1)):
+        q, k, v, g = inp.q64[b, h], inp.k64[b, h], inp.v64[b, h], lg[b, h].astype(np.float64)
+        ref = orc.forward_gated_quadratic(q, k, v, g)
+        mass = orc.forward_gated_quadratic(q, k, np.ones((w.T, 1)), g)[..., 0]
+        check_gated(got[b, h], ref, mass, vmax, f"gated {w.name} C{C} head ({b},{h})")
 
 
 def test_long_sequence_sampled_rows():
@@ -120,8 +142,9 @@ def test_many_spans_sampled_rows():
     check_gated(got[0, 0, rows], ref, mass, np.abs(inp.v64).max(), "gated many spans")
 
 
-def test_deterministic():
-    inp = ki.forward_inputs(1, 4, 7000, 16, 64, ki.BF16, seed=94)
+@pytest.mark.parametrize("d", [16, 32])
+def test_deterministic(d):
+    inp = ki.forward_inputs(1, 4, 7000, d, 64, ki.BF16, seed=94)
     lg = torch.from_numpy(ki.draw_log_gamma(1, 4, 7000, seed=94)).cuda()
     q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
     x = am.kata_forward_gated(q, k, v, lg)
@@ -130,16 +153,17 @@ def test_deterministic():
     assert torch.equal(x.view(torch.int16), y.view(torch.int16))
 
 
+@pytest.mark.parametrize("d", [16, 32])
 @pytest.mark.parametrize("C", [64, 128])
 @pytest.mark.parametrize("case", [(1, 2, 1000), (2, 1, 20000)], ids=lambda c: "B{}H{}T{}".format(*c))
-def test_guard_bands(case, C):
+def test_guard_bands(case, C, d):
     B, H, T = case
-    say(f"gated guard bands {case} C{C}")
-    inp = ki.forward_inputs(B, H, T, 16, 64, ki.BF16, seed=T + C + 1)
+    say(f"gated d={d} guard bands {case} C{C}")
+    inp = ki.forward_inputs(B, H, T, d, 64, ki.BF16, seed=T + C + 1)
     lg = ki.draw_log_gamma(B, H, T, seed=T + C + 1)
     q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
     buf, out = guarded((B, H, T, 64), torch.bfloat16)
-    need = am.kata_forward_gated_workspace_bytes(B, H, T, 16, 64, C)
+    need = am.kata_forward_gated_workspace_bytes(B, H, T, d, 64, C)
     wbuf, ws = guarded_workspace(need)
     am.kata_forward_gated(q, k, v, torch.from_numpy(lg).cuda(), chunk=C, out=out, workspace=ws)
     torch.cuda.synchronize()
