@@ -219,6 +219,20 @@ constexpr Schedule<DK> make_schedule() {
         s.pair2[4 * j + x] = (j == 8);
       }
     }
+  } else if constexpr (DK == 32) {
+    // entry 8 j + x is the pair (x, x + j), j = 0 .. 16: k-step j then holds
+    // on feature tile 2 j row R the pair (R, R + j) and on tile 2 j + 1 row R
+    // the pair (16 + R, 16 + R + j mod 32), which the state update builds by
+    // lane rotation (lane R holds dimensions R and 16 + R of its tokens and
+    // takes the partner from lane R + j of its row).  j = 16 is the size-2
+    // orbit (tile 33 stays empty).
+    for (int j = 0; j <= 16; ++j) {
+      for (int x = 0; x < 8; ++x) {
+        s.a[8 * j + x] = static_cast<int8_t>(x);
+        s.b[8 * j + x] = static_cast<int8_t>(x + j);
+        s.pair2[8 * j + x] = (j == 16);
+      }
+    }
   } else {
     bool used[DK][DK] = {};
     int n4 = 0, n2 = (DK * (DK + 1) / 2 - DK / 2) / 4;
@@ -1684,6 +1698,439 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
   readout_mfma_body<CF, G>(a);
 }
 
+// ------------------------------------------------------------ readout, d = 32, wave-specialised
+//
+// The d = 32 chunked readout at chunk 64 with the 8 waves split by role.
+// Waves 0..3 read out one query tile each (all four value tiles, inter term
+// phi_q(Q_c) S from the state copy plus the squared causal block); waves
+// 4..7 carry the state across the chunk (state wave u owns feature tiles
+// u, u + 4, ..., u + 32 of the 33) while the readout runs, so every query
+// feature and every key feature is built exactly once per chunk.  The
+// denominators take the key Gram matrix Z = sum_s k_s k_s^T (32 x 32, on
+// state wave 3, one product per 16 x 16 tile and 32 keys from the
+// transposing read of the bf16 K rows): phi_q(q) . z = q^T Z q, from two
+// 16x16x32 products E = Z Q^T per query tile and a dot with q; the chunk part
+// is the vector sum of the query's bf16 weights.  No ones-column tile.
+// Key features by lane rotation: the same transposing read gives lane (g, R)
+// dimensions R and 16 + R of its 8 tokens; feature tile (j, h) of the
+// schedule holds on row R the pair (R + 16 h, R + 16 h + j mod 32), whose
+// partner sits in lane R + j of the row, in the register h or 1 - h
+// depending on whether R + j wraps: the source lane selects the register, a
+// row rotation delivers it, and the product is one multiply.  No fp32 K copy.
+// The key features carry weight 1 (the products of bf16 k are exact), so the
+// state waves hold half the state (halved on load) and the state copy is
+// read with query features of weight 1 on the diagonal and 2 off it.
+// Staging splits the same way: readout waves bring V (transposed) and Q,
+// state waves bring the bf16 K rows.  The span state in the workspace keeps
+// the layout of the other d = 32 kernels: its z column holds 2 Z[a][b] on
+// the position of the pair (a, b), the sum of the key features.
+using CfgWs32 = Cfg<32, 64, 8>;   // tiles and strides
+constexpr int ZB_LD = 40;         // bf16 row stride of the Gram copy
+
+// feature position of every pair (a, b) of the d = 32 schedule (symmetric)
+struct PairPos32 {
+  int16_t p[32][32];
+};
+constexpr PairPos32 make_pair_pos32() {
+  PairPos32 t{};
+  for (int a = 0; a < 32; ++a)
+    for (int b = 0; b < 32; ++b) t.p[a][b] = -1;
+  for (int p = 0; p < Schedule<32>::NPOS; ++p) {
+    const int ks = p >> 5, o = p & 31, g = o >> 3, i = o & 7, e = 8 * ks + i;
+    if (e >= Schedule<32>::NE || (kSched<32>.pair2[e] && g >= 2)) continue;
+    const int a = (kSched<32>.a[e] + Schedule<32>::SH * g) % 32, b = (kSched<32>.b[e] + Schedule<32>::SH * g) % 32;
+    t.p[a][b] = static_cast<int16_t>(p);
+    t.p[b][a] = static_cast<int16_t>(p);
+  }
+  return t;
+}
+constexpr bool pair_pos32_ok() {
+  constexpr PairPos32 t = make_pair_pos32();
+  for (int a = 0; a < 32; ++a)
+    for (int b = 0; b < 32; ++b)
+      if (t.p[a][b] < 0 || t.p[a][b] >= 16 * mfma_feature_tiles(32)) return false;
+  return true;
+}
+static_assert(pair_pos32_ok(), "every d = 32 pair has a feature position");
+__constant__ PairPos32 kPairPos32 = make_pair_pos32();
+
+// The bf16 state copy in the order the inter-term products read it: for
+// k-step j and value tile i, the 64 lanes' 16-byte A operands (lane (g, r):
+// value row 16 i + r, feature positions 32 j + 8 g .. + 7) lie contiguous,
+// so each operand read is one contiguous 1 KB.
+constexpr int kSbo32Elems = Schedule<32>::NKS * (NDT - 1) * 64 * 8;
+__device__ __forceinline__ int sbo32(int ks, int vt, int lane) { return ((ks * (NDT - 1) + vt) * 64 + lane) * 8; }
+
+struct alignas(16) SmemWs32 : Tiles<CfgWs32> {
+  alignas(16) uint16_t Sb[kSbo32Elems];   // bf16 state copy, operand order
+  alignas(16) uint16_t Zb[32 * ZB_LD];    // bf16 Gram matrix, row-major
+  alignas(16) uint16_t Ob[4][16 * OB_LD]; // per readout wave output tile
+};
+
+// Staging of one chunk by the readout waves (threads 0..255): V (transposed),
+// Q (fp32 rows) and the bf16 K rows; the state waves stage nothing.  Tokens
+// at or past the end read as zero.
+struct StageWs32 {
+  static constexpr int C = 64, DK = 32;
+  uint4 x[4];  // V: 4 tokens x 16 bytes; Q or K: one 64-byte row
+
+  __device__ __forceinline__ void load(const ChunkSrc& src, int tid) {
+    if (tid < 128) {  // V: token group tid % 16, column group tid / 16
+      const int tg = tid % (C / 4), cg = tid / (C / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = buf_load16(src.v, (4 * tg + r) * (2 * DV) + 16 * cg);
+    } else if (tid < 192) {  // Q row
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = buf_load16(src.q, (tid - 128) * (2 * DK) + 16 * u);
+    } else if (tid < 256) {  // K row
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = buf_load16(src.k, (tid - 192) * (2 * DK) + 16 * u);
+    }
+  }
+
+  __device__ __forceinline__ void store(SmemWs32& sm, int tid) const {
+    using CF = CfgWs32;
+    if (tid < 128) {
+      const int tg = tid % (C / 4), cg = tid / (C / 4);
+      const int pos = group_pos(tg);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int w = c >> 1;
+        const uint32_t w0 = w == 0 ? x[0].x : w == 1 ? x[0].y : w == 2 ? x[0].z : x[0].w;
+        const uint32_t w1 = w == 0 ? x[1].x : w == 1 ? x[1].y : w == 2 ? x[1].z : x[1].w;
+        const uint32_t w2 = w == 0 ? x[2].x : w == 1 ? x[2].y : w == 2 ? x[2].z : x[2].w;
+        const uint32_t w3 = w == 0 ? x[3].x : w == 1 ? x[3].y : w == 2 ? x[3].z : x[3].w;
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        uint2 o;
+        o.x = __builtin_amdgcn_perm(w1, w0, sel);
+        o.y = __builtin_amdgcn_perm(w3, w2, sel);
+        *reinterpret_cast<uint2*>(&sm.Vt[(8 * cg + c) * CF::LDT + pos]) = o;
+      }
+    } else if (tid < 192) {
+      const int t = tid - 128;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t v[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float4 f;
+          f.x = lo_bf16(v[2 * h]);
+          f.y = hi_bf16(v[2 * h]);
+          f.z = lo_bf16(v[2 * h + 1]);
+          f.w = hi_bf16(v[2 * h + 1]);
+          *reinterpret_cast<float4*>(&sm.Qf[t * CF::QF_LD + 8 * u + 4 * h]) = f;
+        }
+      }
+    } else if (tid < 256) {
+      const int t = tid - 192;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(&sm.Kb[t * CF::KB_LD + 8 * u]) = x[u];
+    }
+  }
+};
+
+// transposing read of the bf16 K rows for the Gram matrix: lane (g, s) gets
+// dimension 16 I + s of the 8 tokens 32 ks + 4g + m, 32 ks + 16 + 4g + m
+__device__ __forceinline__ u32x4 gram_operand32(const uint16_t* Kb, int I, int ks, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int off = (4 * g + (s >> 2)) * CfgWs32::KB_LD + 16 * I + 4 * (s & 3);
+  u32x4 out;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint2 v = tr_read(&Kb[off + (32 * ks + 16 * h) * CfgWs32::KB_LD]);
+    out[2 * h] = v.x;
+    out[2 * h + 1] = v.y;
+  }
+  return out;
+}
+
+// feature tile ft = 2 j + h of the d = 32 schedule for the lane's 8 tokens:
+// row R (= lane r of the row) pairs dimension R + 16 h (own register h) with
+// R + 16 h + j mod 32, found in lane (R + j) mod 16 of the row, register h
+// when that lane is at or past j (no wrap) and 1 - h otherwise
+// (weight 1 on every pair: the state waves keep half the state)
+template <int FT>
+__device__ __forceinline__ void ws32_key_tile(f32x4 (&acc)[NDT - 1], const float (&x)[2][8],
+                                              const u32x4 (&bv)[NDT - 1], int r) {
+  constexpr int J = FT >> 1, H = FT & 1;
+  float f[8];
+  if constexpr (J == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = x[H][i] * x[H][i];
+  } else if constexpr (J == 16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = x[H][i] * x[1 - H][i];
+  } else {
+    const bool own = r >= J;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = x[H][i] * row_rotate<J>(own ? x[H][i] : x[1 - H][i]);
+  }
+  const u32x4 af = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+#pragma unroll
+  for (int dt = 0; dt < NDT - 1; ++dt) acc[dt] = mfma(af, bv[dt], acc[dt]);
+}
+
+template <int U, int MT, int... M>
+__device__ __forceinline__ void ws32_key_tiles(f32x4 (&acc)[MT][NDT - 1], const float (&x)[2][8],
+                                               const u32x4 (&bv)[NDT - 1], int r,
+                                               std::integer_sequence<int, M...>) {
+  (ws32_key_tile<U + 4 * M>(acc[M], x, bv, r), ...);
+}
+
+template <int U>
+struct Ws32State {
+  static constexpr int MT = (mfma_feature_tiles(32) - U + 3) / 4;  // feature tiles owned
+  static constexpr bool GRAM = U == 3;
+};
+
+template <int DUMMY = 0>
+__device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
+  using CF = CfgWs32;
+  constexpr int C = 64, DK = 32, NT = 512;
+  __shared__ SmemWs32 sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int g = lane >> 4, r = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t bh = blockIdx.x / a.n_spans;
+  const int64_t sp = blockIdx.x - bh * a.n_spans;
+  const int64_t tok0 = bh * a.T;
+  const int64_t first = sp * a.G * C;
+  int64_t end = first + a.G * C;
+  if (end > a.T) end = a.T;
+  const float* prefix = a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
+
+  // feature positions no tile writes hold no feature (tile 33: lane groups
+  // 2 and 3 of the last k-step): zero once
+  for (int e = tid; e < (NDT - 1) * 32 * 8; e += NT) {
+    const int vt = e / 256, l = 32 + (e / 8) % 32, j = e % 8;
+    sm.Sb[sbo32(Schedule<32>::NKS - 1, vt, l) + j] = 0;
+  }
+
+  auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, a.T); };
+
+  with_wave<8>(w, [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    if constexpr (W < 4) {
+      StageWs32 st;
+      st.load(src(first), tid);
+      // ---------------------------------------------------------------- readout wave
+      constexpr int QT = W;
+      bool keep[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) keep[j] = 4 * g + j <= r;
+      st.store(sm, tid);
+      __syncthreads();  // state copy, Gram copy and chunk 0 in place
+      for (int64_t c0 = first; c0 < end; c0 += C) {
+        const bool more = c0 + C < end;
+        if (more) st.load(src(c0 + C), tid);
+        const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
+        // the query row, rotated by 8 g (the lane group's share of the pairs)
+        float qr[DK];
+#pragma unroll
+        for (int c = 0; c < DK / 4; ++c) {
+          const float4 x = *reinterpret_cast<const float4*>(&sm.Qf[(16 * QT + r) * CF::QF_LD + 4 * ((c + 2 * g) % 8)]);
+          qr[4 * c + 0] = x.x;
+          qr[4 * c + 1] = x.y;
+          qr[4 * c + 2] = x.z;
+          qr[4 * c + 3] = x.w;
+        }
+        f32x4 o[NDT - 1];
+#pragma unroll
+        for (int i = 0; i < NDT - 1; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // inter term phi_q(Q_c) S against the state copy, which holds half the
+        // state: query features at weight 1 on the diagonal and 2 off it
+        float qr2[DK];
+#pragma unroll
+        for (int c = 0; c < DK; ++c) qr2[c] = 2.f * qr[c];
+#pragma unroll
+        for (int ks = 0; ks < Schedule<32>::NKS; ++ks) {
+          u32x4 bs[NDT - 1];
+#pragma unroll
+          for (int i = 0; i < NDT - 1; ++i) bs[i] = *reinterpret_cast<const u32x4*>(&sm.Sb[sbo32(ks, i, lane)]);
+          float f[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int e = 8 * ks + i;
+            if (e >= Schedule<32>::NE) {
+              f[i] = 0.f;
+            } else {
+              const int pa = kSched<32>.a[e], pb = kSched<32>.b[e];
+              f[i] = pa == pb ? qr[pa] * qr[pa] : qr2[pa] * qr[pb];
+            }
+          }
+          const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
+#pragma unroll
+          for (int i = 0; i < NDT - 1; ++i) o[i] = mfma(bs[i], qfeat, o[i]);
+        }
+        // prefix denominator q^T Z q: E = Z Q^T (two products), dotted with q
+        const u32x4 qf = score_operand<CF>(sm.Qf, 16 * QT + r, g);
+        float den = 0.f;
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+          const u32x4 zr = *reinterpret_cast<const u32x4*>(&sm.Zb[(16 * I + r) * ZB_LD + 8 * g]);
+          const f32x4 e4 = mfma(zr, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+          const float4 qa = *reinterpret_cast<const float4*>(&sm.Qf[(16 * QT + r) * CF::QF_LD + 16 * I + 4 * g]);
+          den = __builtin_fmaf(qa.x, e4[0], den);
+          den = __builtin_fmaf(qa.y, e4[1], den);
+          den = __builtin_fmaf(qa.z, e4[2], den);
+          den = __builtin_fmaf(qa.w, e4[3], den);
+        }
+        // intra-chunk term: squared causal scores times V, their sum
+#pragma unroll
+        for (int s = 0; s <= QT / 2; ++s) {
+          float p[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int kt = 2 * s + h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
+            if (kt > QT) continue;
+            const u32x4 kf = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * kt + r) * CF::KB_LD + 8 * g]);
+            const f32x4 sc = mfma(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[h][j] = (kt < QT || keep[j]) ? sc[j] * sc[j] : 0.f;
+          }
+          const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
+                            pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
+#pragma unroll
+          for (int i = 0; i < NDT - 1; ++i) {
+            const u32x4 bv = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * i + r) * CF::LDT + 32 * s + 8 * g]);
+            o[i] = mfma(bv, pf, o[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) den = dot2_bf16(pf[i], kOnesBf16x2, den);
+        }
+        // the four 16-lane rows hold parts of the query's denominator
+        {
+          const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(den), __float_as_uint(den), false, false);
+          const float d2 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+          const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d2), __float_as_uint(d2), false, false);
+          den = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+        }
+        const float inv = __builtin_amdgcn_rcpf(den + a.eps);
+        uint16_t* ob = sm.Ob[W];
+#pragma unroll
+        for (int i = 0; i < NDT - 1; ++i) {
+          uint2 x;
+          x.x = pack2(o[i][0] * inv, o[i][1] * inv);
+          x.y = pack2(o[i][2] * inv, o[i][3] * inv);
+          *reinterpret_cast<uint2*>(&ob[r * OB_LD + 16 * i + 4 * g]) = x;
+        }
+        const __amdgpu_buffer_rsrc_t dst = rows_rsrc(a.out, tok0 + c0, n, 2 * DV);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 8 * h + (lane >> 3);
+          const uint4 x = *reinterpret_cast<const uint4*>(&ob[row * OB_LD + 8 * (lane & 7)]);
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, dst,
+                                                 (16 * QT + row) * (2 * DV) + 16 * (lane & 7), 0, 0);
+        }
+        __syncthreads();  // every wave done with the chunk and the state copy
+        if (more) st.store(sm, tid);
+        __syncthreads();
+      }
+    } else {
+      // ---------------------------------------------------------------- state wave
+      constexpr int U = W - 4;
+      constexpr int MT = Ws32State<U>::MT;
+      constexpr bool GRAM = Ws32State<U>::GRAM;
+      f32x4 acc[MT][NDT - 1];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int ft = U + 4 * m;
+#pragma unroll
+        for (int dt = 0; dt < NDT - 1; ++dt) {
+          acc[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (prefix != nullptr) {
+            // the state waves keep half the state (key features at weight 1)
+            const float4 x = *reinterpret_cast<const float4*>(prefix + ((ft * (NDT - 1) + dt) * 64 + lane) * 4);
+            acc[m][dt] = 0.5f * f32x4{x.x, x.y, x.z, x.w};
+          }
+        }
+      }
+      // Gram tiles (I, J): lane (g, r) holds Z[16 I + 4 g + i][16 J + r]; from
+      // the prefix's z column, 2 Z[a][b] on the position of (a, b)
+      f32x4 zt[GRAM ? 4 : 1];
+      if constexpr (GRAM) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int I = t >> 1, J = t & 1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ra = 16 * I + 4 * g + i, cb = 16 * J + r;
+            zt[t][i] = prefix != nullptr ? 0.5f * prefix[CF::ZOFF + kPairPos32.p[ra][cb]] : 0.f;
+          }
+        }
+      }
+      // the state copy of the owned tiles, and the Gram copy
+      auto publish = [&]() {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const int ft = U + 4 * m;
+#pragma unroll
+          for (int dt = 0; dt < NDT - 1; ++dt) {
+            uint2 x;
+            x.x = pack2(acc[m][dt][0], acc[m][dt][1]);
+            x.y = pack2(acc[m][dt][2], acc[m][dt][3]);
+            // positions 32 j + 16 h + 4 g .. + 3 of value row 16 dt + r: half
+            // g & 1 of the operand of lane (2 h + g / 2, r)
+            *reinterpret_cast<uint2*>(&sm.Sb[sbo32(ft >> 1, dt, 16 * (2 * (ft & 1) + (g >> 1)) + r) + 4 * (g & 1)]) = x;
+          }
+        }
+        if constexpr (GRAM) {
+          // Z is symmetric: lane (g, r) writes row 16 J + r, columns 16 I + 4 g ..
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int I = t >> 1, J = t & 1;
+            *reinterpret_cast<uint2*>(&sm.Zb[(16 * J + r) * ZB_LD + 16 * I + 4 * g]) =
+                make_uint2(pack2(zt[t][0], zt[t][1]), pack2(zt[t][2], zt[t][3]));
+          }
+        }
+      };
+      publish();
+      __syncthreads();  // state copy, Gram copy and chunk 0 in place
+      for (int64_t c0 = first; c0 < end; c0 += C) {
+        const bool more = c0 + C < end;
+        if (more) {
+          // carry the state across the chunk: phi_k(K_c)^T V_c and K_c^T K_c
+#pragma unroll
+          for (int ks = 0; ks < C / 32; ++ks) {
+            u32x4 bv[NDT - 1];
+#pragma unroll
+            for (int dt = 0; dt < NDT - 1; ++dt) {
+              bv[dt] = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * dt + r) * CF::LDT + 32 * ks + 8 * g]);
+            }
+            // dimensions r and 16 + r of the lane's 8 tokens
+            const u32x4 k0 = gram_operand32(sm.Kb, 0, ks, lane);
+            const u32x4 k1 = gram_operand32(sm.Kb, 1, ks, lane);
+            if constexpr (GRAM) {
+              zt[0] = mfma(k0, k0, zt[0]);
+              zt[1] = mfma(k0, k1, zt[1]);
+              zt[2] = mfma(k1, k0, zt[2]);
+              zt[3] = mfma(k1, k1, zt[3]);
+            }
+            float x[2][8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[0][2 * i] = lo_bf16(k0[i]);
+              x[0][2 * i + 1] = hi_bf16(k0[i]);
+              x[1][2 * i] = lo_bf16(k1[i]);
+              x[1][2 * i + 1] = hi_bf16(k1[i]);
+            }
+            ws32_key_tiles<U>(acc, x, bv, r, std::make_integer_sequence<int, MT>{});
+          }
+        }
+        __syncthreads();  // every wave done with the chunk and the state copy
+        if (more) publish();
+        __syncthreads();
+      }
+    }
+  });
+}
+
+__global__ __launch_bounds__(512, 2) void readout_ws32_kernel(MfmaArgs a) {
+  readout_ws32(a);
+}
+
 // ------------------------------------------------------------ readout, d = 16, LDS DMA
 //
 // The chunk's V, K and Q arrive raw by LDS DMA into one of two buffers while
@@ -2001,7 +2448,10 @@ hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream) {
   }
   if (a.d == 16 && a.chunk == 64) return launch_readout<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_readout<16, 128>(a, stream);
-  if (a.d == 32 && a.chunk == 64) return launch_readout<32, 64>(a, stream);
+  if (a.d == 32 && a.chunk == 64) {
+    readout_ws32_kernel<<<dim3(static_cast<unsigned>(a.BH * a.n_spans)), 512, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   if (a.d == 32 && a.chunk == 128) return launch_readout<32, 128>(a, stream);
   if (a.d == 64 && a.chunk == 64) return launch_readout<64, 64>(a, stream);
   return hipErrorInvalidValue;
