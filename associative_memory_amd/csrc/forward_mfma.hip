@@ -1870,11 +1870,12 @@ __device__ __forceinline__ void ws32_key_tile(f32x4 (&acc)[NDT - 1], const float
   for (int dt = 0; dt < NDT - 1; ++dt) acc[dt] = mfma(af, bv[dt], acc[dt]);
 }
 
-template <int U, int MT, int... M>
+// the feature tiles U, U + STRIDE, ... of one wave
+template <int U, int STRIDE = 4, int MT, int... M>
 __device__ __forceinline__ void ws32_key_tiles(f32x4 (&acc)[MT][NDT - 1], const float (&x)[2][8],
                                                const u32x4 (&bv)[NDT - 1], int r,
                                                std::integer_sequence<int, M...>) {
-  (ws32_key_tile<U + 4 * M>(acc[M], x, bv, r), ...);
+  (ws32_key_tile<U + STRIDE * M>(acc[M], x, bv, r), ...);
 }
 
 template <int U>
@@ -2129,6 +2130,158 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
 
 __global__ __launch_bounds__(512, 2) void readout_ws32_kernel(MfmaArgs a) {
   readout_ws32(a);
+}
+
+
+// ------------------------------------------------------------ span sums, d = 32, chunk 64
+//
+// The span sums of the wave-specialised d = 32 readout's plan: 8 waves, wave W
+// owning feature tiles W, W + 8, ... (5 or 4 of the 33), key features built by
+// lane rotation (as in the readout's state waves), the key Gram matrix on
+// wave 7.  The chunk goes from HBM straight into LDS by DMA (raw V rows with
+// 16-byte pieces swizzled by (row >> 1) & 7, raw K rows with pieces swizzled
+// by row & 2 against bank conflicts of the transposing reads), three buffers
+// deep, each chunk's transfer issued two chunks ahead; the MFMA operands come
+// from transposing reads.  The span state is stored in the layout the readout
+// loads: value tiles at full scale (key features of weight 2, the products
+// here carry 1: stored doubled) and the z column as 2 Z[a][b] on the
+// position of each pair.
+struct alignas(16) DmaTile32 {
+  alignas(16) uint16_t v[64 * DV];  // [token][value column], pieces swizzled by vswz
+  alignas(16) uint16_t k[64 * 32];  // [token][dimension], pieces swizzled by row & 2
+};
+
+// wave W's share of a chunk's transfer: V rows 8 W .. 8 W + 7; waves 4..7
+// also K rows 16 (W - 4) .. + 15.  Rows past the end arrive as zero.
+template <int W>
+__device__ __forceinline__ void dma_chunk32(DmaTile32& b, const ChunkSrc& src, int lane) {
+  {
+    const int t = 8 * W + (lane >> 3);
+    const int cg = (lane & 7) ^ vswz(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, KATA_LDS(&b.v[8 * W * DV]), 16, t * (2 * DV) + 16 * cg, 0, 0, 0);
+  }
+  if constexpr (W >= 4) {
+    const int t = 16 * (W - 4) + (lane >> 2);
+    const int c = (lane & 3) ^ (t & 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[16 * (W - 4) * 32]), 16, t * 64 + 16 * c, 0, 0, 0);
+  }
+}
+
+// offsets of the transposing K reads: lane (g, s) gets dimension 16 I + s of
+// its 8 tokens (rows 4 g + s / 4 of each 16-token half of the k-step)
+__device__ __forceinline__ int tr_offset_k32(int I, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = 4 * g + (s >> 2);
+  const int c = (2 * I + ((s & 3) >> 1)) ^ ((s >> 2) & 2);
+  return row * 32 + 8 * c + 4 * (s & 1);
+}
+
+__global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
+  using CF = CfgWs32;
+  constexpr int C = 64;
+  __shared__ DmaTile32 b0;
+  __shared__ DmaTile32 b1;
+  __shared__ DmaTile32 b2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t nsp_work = a.n_spans - 1;  // the last span's sum is never read
+  const int64_t bh = blockIdx.x / nsp_work;
+  const int64_t sp = blockIdx.x - bh * nsp_work;
+  const int64_t tok0 = bh * a.T;
+  const int64_t first = sp * a.G * C;
+  int64_t end = first + a.G * C;
+  if (end > a.T) end = a.T;
+  auto src = [&](int64_t c) { return chunk_src<32, C>(nullptr, a.k, a.v, tok0, c, end); };
+
+  with_wave<8>(w, [&](auto wc) {
+    constexpr int W = decltype(wc)::value;
+    constexpr int NPC = W >= 4 ? 2 : 1;  // this wave's transfers per chunk
+    constexpr int NFT = mfma_feature_tiles(32);
+    constexpr int MT = (NFT - W + 7) / 8;
+    constexpr bool GRAM = W == 7;
+    const TrOffsets to = tr_offsets(lane);
+    const int ok0 = tr_offset_k32(0, lane), ok1 = tr_offset_k32(1, lane);
+    f32x4 acc[MT][NDT - 1];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+#pragma unroll
+      for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4 zt[GRAM ? 4 : 1];
+#pragma unroll
+    for (int t = 0; t < (GRAM ? 4 : 1); ++t) zt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto reduce = [&](const DmaTile32& b) {
+      // one k-step at a time: interleaving the two would exceed the registers
+#pragma unroll 1
+      for (int ks = 0; ks < C / 32; ++ks) {
+        u32x4 bv[NDT - 1];
+#pragma unroll
+        for (int dt = 0; dt < NDT - 1; ++dt) bv[dt] = tr_operand<DV>(b.v, to.v[dt], ks);
+        const u32x4 k0 = tr_operand<32>(b.k, ok0, ks);
+        const u32x4 k1 = tr_operand<32>(b.k, ok1, ks);
+        if constexpr (GRAM) {
+          zt[0] = mfma(k0, k0, zt[0]);
+          zt[1] = mfma(k0, k1, zt[1]);
+          zt[2] = mfma(k1, k0, zt[2]);
+          zt[3] = mfma(k1, k1, zt[3]);
+        }
+        float x[2][8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[0][2 * i] = lo_bf16(k0[i]);
+          x[0][2 * i + 1] = hi_bf16(k0[i]);
+          x[1][2 * i] = lo_bf16(k1[i]);
+          x[1][2 * i + 1] = hi_bf16(k1[i]);
+        }
+        ws32_key_tiles<W, 8>(acc, x, bv, r, std::make_integer_sequence<int, MT>{});
+      }
+    };
+    dma_chunk32<W>(b0, src(first), lane);
+    dma_chunk32<W>(b1, src(first + C), lane);
+    for (int64_t c0 = first; c0 < end; c0 += 3 * C) {
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
+      barrier_lds();
+      dma_chunk32<W>(b2, src(c0 + 2 * C), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      reduce(b0);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
+      barrier_lds();
+      dma_chunk32<W>(b0, src(c0 + 3 * C), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + C < end) reduce(b1);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
+      barrier_lds();
+      dma_chunk32<W>(b1, src(c0 + 4 * C), lane);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + 2 * C < end) reduce(b2);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+    // store: value tiles doubled (the state's key features carry weight 2),
+    // z as 2 Z[a][b] on the position of each pair a <= b
+    float* P = a.ws + (bh * a.n_spans + sp) * mfma_state_floats(32);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int ft = W + 8 * m;
+#pragma unroll
+      for (int dt = 0; dt < NDT - 1; ++dt) {
+        *reinterpret_cast<float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4) =
+            make_float4(2.f * acc[m][dt][0], 2.f * acc[m][dt][1], 2.f * acc[m][dt][2], 2.f * acc[m][dt][3]);
+      }
+    }
+    if constexpr (GRAM) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int I = t >> 1, J = t & 1;
+        if (I > J) continue;  // the mirror of tile (0, 1)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ra = 16 * I + 4 * g + i, cb = 16 * J + r;
+          if (ra <= cb) P[CF::ZOFF + kPairPos32.p[ra][cb]] = 2.f * zt[t][i];
+        }
+      }
+    }
+  });
 }
 
 // ------------------------------------------------------------ readout, d = 16, LDS DMA
@@ -2395,7 +2548,10 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   }
   if (a.d == 16 && a.chunk == 64) return launch_span<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_span<16, 128>(a, stream);
-  if (a.d == 32 && a.chunk == 64) return launch_span<32, 64>(a, stream);
+  if (a.d == 32 && a.chunk == 64) {
+    span_state_ws32_kernel<<<dim3(static_cast<unsigned>(a.BH * (a.n_spans - 1))), 512, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   if (a.d == 32 && a.chunk == 128) return launch_span<32, 128>(a, stream);
   if (a.d == 64 && a.chunk == 64) return launch_span<64, 64>(a, stream);
   return hipErrorInvalidValue;
