@@ -59,6 +59,8 @@ def parse():
                     help="skip the quadratic block-map timings on the d = 64 shape")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--calib-read", action="store_true",
+                    help="only run a read-only reduction of known size (second counter calibration)")
     return ap.parse_args()
 
 
@@ -644,6 +646,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+    if args.calib_read:
+        # reads 256 MiB once per launch and writes a few bytes
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        for _ in range(5):
+            src.sum()
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_read_bytes": n, "launches": 5}))
         return
 
     def progress(what):
