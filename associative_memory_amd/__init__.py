@@ -15,7 +15,9 @@ import os
 from typing import Optional, Tuple
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkata.so")
+# KATA_LIBRARY names another build of the same library (e.g. one whose host
+# code carries the address and undefined-behaviour sanitizers).
+LIB_PATH = os.environ.get("KATA_LIBRARY") or os.path.join(_HERE, "libkata.so")
 
 KATA_F32 = 0
 KATA_BF16 = 1

@@ -37,18 +37,28 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations below are int-sized.  A C caller may pass any int where
+ * one is expected (C allows values outside the enumerators); the C++
+ * implementation gives them a fixed `int` base so that such a value is read
+ * without undefined behaviour and rejected by validation. */
+#ifdef __cplusplus
+#define KATA_ENUM_BASE : int
+#else
+#define KATA_ENUM_BASE
+#endif
+
+typedef enum KATA_ENUM_BASE {
   KATA_F32 = 0,  /* IEEE binary32 */
   KATA_BF16 = 1  /* bfloat16 (upper half of binary32), round-to-nearest-even */
 } kata_dtype_t;
 
-typedef enum {
+typedef enum KATA_ENUM_BASE {
   KATA_SCAN_AUTO = 0,        /* library picks (measured default per shape) */
   KATA_SCAN_SEQUENTIAL = 1,  /* linear-depth pass over chunk states */
   KATA_SCAN_ASSOCIATIVE = 2  /* log-depth parallel scan over chunk states */
 } kata_scan_t;
 
-typedef enum {
+typedef enum KATA_ENUM_BASE {
   KATA_OK = 0,
   KATA_ERR_INVALID_VALUE = 1, /* null pointer, non-positive size, bad eps, aliasing, misalignment */
   KATA_ERR_UNSUPPORTED = 2,   /* valid but outside the supported set (d, dv, chunk, dtype) */
@@ -219,7 +229,7 @@ kata_status_t kata_forward_chunked_blocks(const void* q, const void* k, const vo
                                           void* stream);
 
 /* Linear (D = d) features of kata_forward_linear. */
-typedef enum {
+typedef enum KATA_ENUM_BASE {
   KATA_FEATURE_ORTHANT = 0,  /* psi(x) = ReLU(x) + shift, every coordinate */
   KATA_FEATURE_LORENTZ = 1,  /* psi(x) = (y, |y|_2 (1 + s^2)), y = x_{1..d-1}, s = x_d */
   KATA_FEATURE_IDENTITY = 2  /* psi(x) = x; read without a denominator (see below) */
