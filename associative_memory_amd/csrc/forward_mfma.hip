@@ -2297,7 +2297,8 @@ struct alignas(16) DmaTileQ16 : GateRows<C, G, false> {
   alignas(16) uint16_t q[C * 16];  // [token][dimension]
 };
 
-template <int C, int W, int NW, bool G = false>
+// (WQ false: V and K only, for a chunk whose queries are not read out)
+template <int C, int W, int NW, bool G = false, bool WQ = true>
 __device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C, G>& b, const ChunkSrc& src, int lane) {
 #pragma unroll
   for (int j = W; j < C / 8; j += NW) {
@@ -2309,7 +2310,8 @@ __device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C, G>& b, const ChunkSrc
   for (int j = W; j < C / 32; j += NW) {
     const int t = 32 * j + (lane >> 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.q, KATA_LDS(&b.q[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
+    if constexpr (WQ)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.q, KATA_LDS(&b.q[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
   }
   dma_gate<G, W, NW>(b, src, lane);
 }
@@ -2403,6 +2405,14 @@ __device__ __forceinline__ void write_gram16(uint16_t* __restrict__ zb, const f3
   *reinterpret_cast<uint2*>(&zb[16 * r + 4 * g]) = make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3]));
 }
 
+// Span of a workgroup that forms its prefix itself (RC): the latest spans,
+// which carry the most chunks before them, take the lowest block indices and
+// start first; consecutive blocks are different heads.
+__device__ inline SpanOf recompute_span(const MfmaArgs& a) {
+  const int64_t b = blockIdx.x;
+  return {b % a.BH, a.n_spans - 1 - b / a.BH};
+}
+
 // The kernel body, a device function taking the arguments by reference (this
 // form compiles to slightly fewer registers and branches than the body in the
 // kernel itself, and measured 2% faster at T = 131072).
@@ -2410,11 +2420,19 @@ __device__ __forceinline__ void write_gram16(uint16_t* __restrict__ zb, const f3
 // Denominators (ungated read): no ones-column tile.  Wave 0 carries the key
 // Gram matrix Z (one 16x16x32 product per 32 keys, against 9 for a ones
 // column over the feature tiles) and publishes its bf16 copy with Sb.
-template <int C, bool G>
+//
+// RC (prefix formed in the workgroup, for heads of few spans): no prefix
+// state is read.  The workgroup starts at the head's first chunk and carries
+// the state from zero over every chunk before its span (keys and values
+// only, nothing read out), then reads out its span as usual.  The exclusive
+// prefix of Eqs. 17-20 is then summed chunk by chunk in one workgroup, with
+// no span-sum or prefix launch; every span of a head repeats that sum.
+template <int C, bool G, bool RC = false>
 __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   using CF = Cfg<16, C>;
   constexpr int DK = 16, SB_LD = CF::SB_LD;
   static_assert(CF::NDW == NDT, "whole output rows per wave");
+  static_assert(!(G && RC), "the gated read takes its prefix from the affine scan");
   __shared__ DmaTileQ16<C, G> x0;
   __shared__ DmaTileQ16<C, G> x1;
   // bf16 Z (the gated read has no denominator)
@@ -2423,7 +2441,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   __shared__ alignas(16) uint16_t Ob[CF::STAGE_OUT ? CF::NW : 1][16 * OB_LD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const SpanOf span = readout_span(a);
+  const SpanOf span = RC ? recompute_span(a) : readout_span(a);
   const int64_t bh = span.bh, sp = span.sp;
   const int64_t tok0 = bh * a.T;
 
@@ -2440,7 +2458,8 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     const ReadoutLane<CF> L = readout_lane<CF>(W, lane);
     const TrOffsets to = tr_offsets(lane);
     f32x4 acc[CF::MFT][NDT];
-    const float* prefix = a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
+    const float* prefix =
+        (!RC && a.n_spans > 1) ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
     load_state<CF>(acc, prefix, W, lane);
     // the d = 16 span sums store the value tiles at kSpanValueScale
 #pragma unroll
@@ -2458,7 +2477,8 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
     auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb, a.gk); };
-    dma_chunkq16<C, W, CF::NW, G>(x0, src(first), lane);
+    const int64_t start = RC ? 0 : first;
+    dma_chunkq16<C, W, CF::NW, G>(x0, src(start), lane);
     // the state loads and the first chunk; an unconditional vmcnt(0) also
     // retires the state loads for the compiler's wait-count analysis
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -2467,6 +2487,28 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     // one chunk: prefetch the next into the other buffer, read out, and
     // (unless it is the span's last) carry the state and refresh Sb
     auto chunk = [&](DmaTileQ16<C, G>& cur, DmaTileQ16<C, G>& nxt, int64_t c) {
+      if constexpr (RC) {
+        if (c < first) {
+          // a chunk before the span: fetch the next (its queries only if it
+          // is read out), carry the state, and publish it before the span
+          __builtin_amdgcn_sched_barrier(0);
+          if (c + C < first) {
+            dma_chunkq16<C, W, CF::NW, G, false>(nxt, src(c + C), lane);
+          } else {
+            dma_chunkq16<C, W, CF::NW, G>(nxt, src(c + C), lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          state_update_ro16<CF, W, G>(acc, gram, cur, to);
+          __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+          barrier_lds();
+          if (c + C == first) {
+            write_sb<CF, NDT - 1, DmaSrc16<C, G>::kHalfDiag>(Sb, acc, W, lane);
+            if constexpr (!G && W == 0) write_gram16(Zb, gram, lane);
+            barrier_lds();
+          }
+          return;
+        }
+      }
       const int64_t n = (a.T - c < C) ? a.T - c : C;
       // the next chunk's transfer goes out right after the query rows are
       // read (zeros past the span's end); issued any earlier, the compiler's
@@ -2494,7 +2536,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
         barrier_lds();
       }
     };
-    for (int64_t c0 = first; c0 < end; c0 += 2 * C) {
+    for (int64_t c0 = start; c0 < end; c0 += 2 * C) {
       chunk(x0, x1, c0);
       if (c0 + C < end) chunk(x1, x0, c0 + C);
     }
@@ -2502,9 +2544,9 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   });
 }
 
-template <int C, bool G = false>
+template <int C, bool G = false, bool RC = false>
 __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
-  readout_dma16_body<C, G>(a);
+  readout_dma16_body<C, G, RC>(a);
 }
 
 template <int DK, int C>
@@ -2524,7 +2566,11 @@ hipError_t launch_readout(const MfmaArgs& a, hipStream_t stream) {
   using CF = Cfg<DK, C>;
   dim3 grid(static_cast<unsigned>(a.BH * a.n_spans));
   if constexpr (DK == 16) {
-    readout_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
+    if (a.recompute) {
+      readout_dma16_kernel<C, false, true><<<grid, CF::NT, 0, stream>>>(a);
+    } else {
+      readout_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
+    }
   } else {
     readout_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
   }

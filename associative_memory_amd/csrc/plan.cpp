@@ -26,6 +26,16 @@ constexpr int64_t kPairSkewDiv = 8;
 // target already gives spans of 256 tokens or more.
 constexpr int64_t kMinSpanTokens16 = 256;
 constexpr int64_t kMinReadoutWorkgroups16 = 256;
+// prefix formed in the readout workgroups: about this many workgroups, and
+// the automatic choice only while the latest span carries at most this many
+// tokens before it (measured, step us, sequential prefix / recompute:
+// B=4 H=8 d=16 bf16, T=512 C=64 21.4 / 10.4, T=1024 C=64 29.1 / 17.0,
+// T=1024 C=128 23.5 / 14.8; B=16 H=16 T=1024 C=64 46.6 / 30.3; at 1,800 to
+// 1,900 tokens before the latest span the two are within 10% either way:
+// B=4 H=8 T=2048 C=128 28.0 / 26.0, C=64 27.7 / 29.8, B=1 H=8 T=2048 C=128
+// 18.4 / 22.5; beyond, the recompute loses: B=4 H=8 T=4096 C=128 37.1 / 48.9)
+constexpr int64_t kRecomputeWorkgroups = 512;
+constexpr int64_t kRecomputeMaxPrefixTokens = 1024;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -51,6 +61,21 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.path = mfma ? Path::Mfma : Path::Valu;
   p.E = mfma ? mfma_state_floats(d) : static_cast<int64_t>(p.D) * dv + p.D;
 
+  if (scan == KATA_SCAN_RECOMPUTE || scan == KATA_SCAN_AUTO) {
+    // every readout workgroup sums the chunks before its span itself
+    int64_t spans = ceil_div(kRecomputeWorkgroups, p.BH);
+    if (spans > p.n_chunks) spans = p.n_chunks;
+    const int64_t G = ceil_div(p.n_chunks, spans);
+    const bool short_prefix = (p.n_chunks - G) * chunk <= kRecomputeMaxPrefixTokens;
+    if (scan == KATA_SCAN_RECOMPUTE ||
+        (short_prefix && recompute_supported(p.bf16, d, dv, chunk) && g == 1)) {
+      p.scan = KATA_SCAN_RECOMPUTE;
+      p.G = G;
+      p.n_spans = ceil_div(p.n_chunks, p.G);
+      p.wg_output = p.BH * p.n_spans;
+      return p;
+    }
+  }
   const int64_t tiles = mfma ? 1 : dv / kValuDvTile;
   // enough spans to give the readout about the target number of workgroups
   int64_t spans = ceil_div(mfma ? mfma_target_workgroups(d) : kTargetWorkgroups, p.BH * tiles);
@@ -92,7 +117,10 @@ void describe_plan(const ForwardPlan& p, char* buf, size_t len) {
                 "paired_even_span=%lld n_spans=%lld wg_state=%lld wg_output=%lld "
                 "workspace_bytes=%zu",
                 p.path == Path::Mfma ? "mfma" : "valu",
-                p.scan == KATA_SCAN_ASSOCIATIVE ? "associative" : "sequential", p.D, p.chunk,
+                p.scan == KATA_SCAN_ASSOCIATIVE ? "associative"
+                : p.scan == KATA_SCAN_RECOMPUTE ? "recompute"
+                                                : "sequential",
+                p.D, p.chunk,
                 static_cast<long long>(p.n_chunks), static_cast<long long>(p.G),
                 static_cast<long long>(p.GL),
                 static_cast<long long>(p.n_spans), static_cast<long long>(p.wg_state),
@@ -170,10 +198,11 @@ hipError_t run_forward(const ForwardPlan& p, const void* q, const void* k, const
     m.GL = p.GL;
     m.n_spans = p.n_spans;
     m.eps = eps;
-    if (p.n_spans > 1) KATA_TRY(launch_span_state_mfma(m, stream));
+    m.recompute = p.scan == KATA_SCAN_RECOMPUTE;
+    if (p.n_spans > 1 && !m.recompute) KATA_TRY(launch_span_state_mfma(m, stream));
     KATA_TRY(mark(ev, false, 0, stream));
     KATA_TRY(mark(ev, true, 1, stream));
-    if (p.n_spans > 1) {
+    if (p.n_spans > 1 && !m.recompute) {
       KATA_TRY((p.scan == KATA_SCAN_ASSOCIATIVE)
                    ? launch_scan_associative(ws, p.BH, p.n_spans, p.E, stream)
                    : launch_scan_sequential(ws, p.BH, p.n_spans, p.E, stream));

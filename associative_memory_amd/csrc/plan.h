@@ -28,7 +28,7 @@ struct ForwardPlan {
   int chunk = 0;
   int D = 0;
   bool bf16 = false;
-  kata_scan_t scan = KATA_SCAN_SEQUENTIAL;  // resolved: SEQUENTIAL or ASSOCIATIVE
+  kata_scan_t scan = KATA_SCAN_SEQUENTIAL;  // resolved: SEQUENTIAL, ASSOCIATIVE or RECOMPUTE
   Path path = Path::Valu;
   int64_t n_chunks = 0;  // ceil(T / chunk)
   int64_t G = 1;         // chunks per span

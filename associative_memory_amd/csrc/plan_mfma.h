@@ -46,6 +46,9 @@ struct MfmaArgs {
   const float* gk = nullptr;  // gated read: key factors 2^((beta_C - beta_t) / 2) per token
   float* part = nullptr;      // sliced maps: fp32 partial reads [BH*T][68]
   int fm = 0;                 // sliced maps: 100 + slice (KATA-M1), 200 + slice (KATA-M2)
+  // d = 16, ungated: each readout workgroup forms its span's prefix from the
+  // head's earlier chunks (no span sums, no prefix, no workspace)
+  bool recompute = false;
 };
 
 struct QuadArgs {
@@ -111,6 +114,11 @@ hipError_t launch_linear_readout(const LinArgs& a, hipStream_t stream);
 
 inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
   return bf16 && (d == 16 || d == 32) && dv == 64 && (chunk == 64 || chunk == 128);
+}
+
+// readout workgroups that form their span's prefix themselves (KATA_SCAN_RECOMPUTE)
+inline bool recompute_supported(bool bf16, int d, int dv, int chunk) {
+  return mfma_supported(bf16, d, dv, chunk) && d == 16;
 }
 
 // the chunked reads at d = 64: KATA-M4 (g = 4, blocks of 16), KATA-M2 (g = 2,

@@ -285,6 +285,25 @@ def bench_other_workloads(args, hip, am, ki, torch):
         }
         if w.dtype == ki.BF16 and w.dv == 64:
             res[w.name]["quadratic"] = bench_quadratic(args, hip, am, torch, w, q, k, v, out)
+        if w.dtype == ki.BF16 and w.d == 16 and w.dv == 64:
+            # the prefix formed inside the readout workgroups (one launch, no workspace)
+            for _ in range(args.warmup):
+                am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan="recompute", out=out)
+            torch.cuda.synchronize()
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(args.steps):
+                am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan="recompute", out=out)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            rms = hip.ms(e0, e1) / args.steps
+            hip.destroy(e0)
+            hip.destroy(e1)
+            res[w.name]["recompute"] = {
+                "ms_per_step": round(rms, 4),
+                "tokens_per_s": round(w.B * w.T / (rms * 1e-3), 1),
+                "plan": am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk, am.KATA_BF16, "recompute"),
+            }
     return res
 
 

@@ -55,7 +55,10 @@ typedef enum KATA_ENUM_BASE {
 typedef enum KATA_ENUM_BASE {
   KATA_SCAN_AUTO = 0,        /* library picks (measured default per shape) */
   KATA_SCAN_SEQUENTIAL = 1,  /* linear-depth pass over chunk states */
-  KATA_SCAN_ASSOCIATIVE = 2  /* log-depth parallel scan over chunk states */
+  KATA_SCAN_ASSOCIATIVE = 2, /* log-depth parallel scan over chunk states */
+  KATA_SCAN_RECOMPUTE = 3    /* no prefix pass: each readout workgroup sums the chunk
+                                states before its span itself (kata_forward_chunked,
+                                bf16, d = 16, dv = 64 only; no workspace) */
 } kata_scan_t;
 
 typedef enum KATA_ENUM_BASE {

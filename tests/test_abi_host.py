@@ -94,6 +94,9 @@ def fwd(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=64, d=16, dv=16, C=32, eps
     (dict(C=16), UNSUPPORTED), (dict(C=256), UNSUPPORTED),
     (dict(eps=-1e-6), INVALID), (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID),
     (dict(dt=7), INVALID), (dict(scan=5), INVALID),
+    # the prefix formed in the readout (scan 3): bf16, d = 16, dv = 64, chunk 64 / 128 only
+    (dict(scan=3), UNSUPPORTED), (dict(scan=3, dv=64, dt=F32), UNSUPPORTED),
+    (dict(scan=3, d=32, dv=64, C=64), UNSUPPORTED), (dict(scan=3, dv=64, C=32), UNSUPPORTED),
     (dict(q=ctypes.c_void_p(P[0].value + 4)), INVALID),     # misaligned
     (dict(out=P[0]), INVALID),                                # out aliases q
     (dict(out=ctypes.c_void_p(P[2].value + 16)), INVALID),   # out overlaps v
@@ -343,3 +346,21 @@ def test_probe_rejects_bad_arguments():
     assert L.kata_probe_mfma_bf16(256, 8, 0, None) == -1          # no rounds
     assert L.kata_probe_mfma_bf16(256, (1 << 20) + 1, 1, None) == -1
     assert L.kata_probe_mfma_bf16(256, 1, (1 << 24) + 1, None) == -1
+
+
+def test_recompute_plan():
+    """Scan 3: no span sums, no prefix, no workspace; every chunk of a head
+    belongs to exactly one readout workgroup's span."""
+    L = am.lib()
+    for (B, H, T, C) in [(4, 8, 2048, 64), (4, 8, 2048, 128), (1, 2, 77, 128), (1, 3, 40000, 128),
+                         (1, 8, 131072, 128)]:
+        assert L.kata_forward_workspace_bytes(B, H, T, 16, 64, C, 3) == 0
+        plan = am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "recompute")
+        f = dict(kv.split("=") for kv in plan.split())
+        assert f["scan"] == "recompute" and f["wg_state"] == "0" and f["workspace_bytes"] == "0"
+        G, n_spans, n_chunks = int(f["chunks_per_span"]), int(f["n_spans"]), int(f["n_chunks"])
+        assert n_chunks == -(-T // C) and G * n_spans >= n_chunks > G * (n_spans - 1)
+        assert int(f["wg_output"]) == B * H * n_spans and f["paired_even_span"] == "0"
+    # the other forwards take no scan 3
+    assert L.kata_forward_workspace_bytes(1, 1, 64, 32, 64, 64, 3) == 0
+    assert L.kata_forward_chunked_blocks_workspace_bytes(1, 1, 64, 64, 64, 4, 64, 3) == 0

@@ -327,3 +327,44 @@ def test_guard_bands_bf16(case, scan):
     ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6) if T <= 9000 else None
     if ref is not None:
         check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"guarded {case}")
+
+
+RECOMPUTE_CASES = [
+    # (B, H, T, chunk), d = 16, dv = 64, bf16: the T = 2048 workload at both
+    # chunk sizes, a single ragged chunk, ragged spans and last chunks, heads
+    # of many spans (the latest workgroup sums 60 spans before its own)
+    (4, 8, 2048, 64),
+    (4, 8, 2048, 128),
+    (1, 2, 77, 128),
+    (2, 3, 1000, 64),
+    (1, 1, 5000, 128),
+    (3, 5, 2500, 128),
+    (2, 2, 8191, 64),
+    (1, 3, 40000, 128),
+]
+
+
+@pytest.mark.parametrize("case", RECOMPUTE_CASES, ids=lambda c: "B{}H{}T{}C{}".format(*c))
+def test_recompute_prefix(case):
+    """Prefix formed inside the readout workgroups (no span sums, no prefix
+    launch, no workspace): every output against the oracle, guard bands
+    around the output, and run-to-run bitwise determinism."""
+    B, H, T, chunk = case
+    d, dv = 16, 64
+    plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, "recompute")
+    say(f"forward recompute {case} plan: {plan}")
+    assert "scan=recompute" in plan and "wg_state=0" in plan and "workspace_bytes=0" in plan
+    assert am.kata_forward_workspace_bytes(B, H, T, d, dv, chunk, "recompute") == 0
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.BF16, seed=T + 11 * chunk)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    buf, out = guarded((B, H, T, dv), torch.bfloat16)
+    am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="recompute", out=out)
+    again = am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="recompute")
+    torch.cuda.synchronize()
+    assert_guards(buf, f"out {case}")
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "run-to-run bits"
+    if T <= 9000:
+        ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6)
+    else:
+        ref = orc.forward_chunked(inp.q64, inp.k64, inp.v64, chunk, 1e-6)
+    check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"recompute {case}")
