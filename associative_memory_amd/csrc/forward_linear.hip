@@ -18,7 +18,7 @@ namespace {
 // where psi is applied in fp32 (orthant: ReLU(x) + shift per coordinate;
 // Lorentz: (y, |y| (1 + s^2)), |y| summed over the 4 lanes that hold a row;
 // identity: the bf16 rows as they are), and land in LDS as bf16 rows in the V
-// layout (16-byte pieces swizzled by (row >> 1) & 7); V arrives by DMA into
+// layout (16-byte pieces swizzled by vswz(row)); V arrives by DMA into
 // two buffers.  The fp32 state [S | z] (64 features x 65; S alone for the
 // identity map) is one feature tile per wave; psi(K)^T and [V | 1] operands
 // of its update both come from transposing LDS reads.  The readout computes

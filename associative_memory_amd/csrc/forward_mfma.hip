@@ -397,7 +397,10 @@ struct Cfg {
   static constexpr int NPOS = Schedule<FM>::NPOS;
   static constexpr int NFT = FM_ < 100 ? mfma_feature_tiles(DK) : feature_tiles<FM_>();
   static constexpr int MFT = (NFT + NW - 1) / NW;   // feature tiles per wave (max)
-  static constexpr int SB_LD = NPOS + 8;            // bf16 row stride of the state copy
+  // bf16 row stride of the state copy; at d = 16 (160 positions) rows of
+  // 352 bytes keep the 16-byte operand reads of 16 rows x 4 lane groups free
+  // of bank conflicts (7.4 cycles per read per CU against 10.9 at 336 bytes)
+  static constexpr int SB_LD = DK == 16 ? NPOS + 16 : NPOS + 8;
   static constexpr int QF_LD = DK + 4;              // fp32 row stride of Q
   static constexpr int KB_LD = DK + 8;              // bf16 row stride of K
   static constexpr int LDT = C + 8;                 // bf16 row stride of V^T
@@ -949,8 +952,9 @@ __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
 // ------------------------------------------------------------ span sums, d = 16, LDS DMA
 //
 // The chunk goes from HBM straight into LDS (`buffer_load ... lds`, no
-// registers, no VALU): raw V rows (128 B, 16-byte chunks XOR-swizzled by
-// (row >> 1) & 7 against bank conflicts) and raw K rows (32 B).  The MFMA
+// registers, no VALU): raw V rows (128 B, 16-byte pieces XOR-swizzled by
+// vswz(row) against bank conflicts) and raw K rows (32 B, pieces swizzled by
+// ksw16(row)).  The MFMA
 // operands are read back with the transposing LDS read `ds_read_b64_tr_b16`:
 // in each 16-lane group, lane i receives element i % 4 of the 8 bytes
 // addressed by lanes 4m + i/4 (m = 0..3), so when lane s addresses row m = s/4,
@@ -1011,7 +1015,8 @@ __device__ __forceinline__ void dma_chunk16(DmaTile16<C, G>& b, const ChunkSrc& 
 #pragma unroll
   for (int j = W; j < C / 32; j += NW) {
     const int t = 32 * j + (lane >> 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
+    const int pc = (lane & 1) ^ ksw16(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * pc, 0, 0, 0);
   }
   dma_gate<G, W, NW>(b, src, lane);
 }
@@ -2139,7 +2144,7 @@ __global__ __launch_bounds__(512, 2) void readout_ws32_kernel(MfmaArgs a) {
 // owning feature tiles W, W + 8, ... (5 or 4 of the 33), key features built by
 // lane rotation (as in the readout's state waves), the key Gram matrix on
 // wave 7.  The chunk goes from HBM straight into LDS by DMA (raw V rows with
-// 16-byte pieces swizzled by (row >> 1) & 7, raw K rows with pieces swizzled
+// 16-byte pieces swizzled by vswz(row), raw K rows with pieces swizzled
 // by row & 2 against bank conflicts of the transposing reads), three buffers
 // deep, each chunk's transfer issued two chunks ahead; the MFMA operands come
 // from transposing reads.  The span state is stored in the layout the readout
@@ -2309,9 +2314,10 @@ __device__ __forceinline__ void dma_chunkq16(DmaTileQ16<C, G>& b, const ChunkSrc
 #pragma unroll
   for (int j = W; j < C / 32; j += NW) {
     const int t = 32 * j + (lane >> 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
+    const int pc = (lane & 1) ^ ksw16(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[32 * j * 16]), 16, t * 32 + 16 * pc, 0, 0, 0);
     if constexpr (WQ)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.q, KATA_LDS(&b.q[32 * j * 16]), 16, t * 32 + 16 * (lane & 1), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src.q, KATA_LDS(&b.q[32 * j * 16]), 16, t * 32 + 16 * pc, 0, 0, 0);
   }
   dma_gate<G, W, NW>(b, src, lane);
 }
@@ -2323,22 +2329,23 @@ struct DmaSrc16 {
   const DmaTileQ16<C, G>& b;
   const TrOffsets& to;
   const uint16_t* gram;  // bf16 Z, 16 x 16 row-major (ungated read)
+  // rows of 32 bytes with their 16-byte pieces swizzled by ksw16(row)
   __device__ __forceinline__ float4 qrow4(int row, int c4) const {
-    const uint2 x = *reinterpret_cast<const uint2*>(&b.q[row * 16 + 4 * c4]);
+    const uint2 x = *reinterpret_cast<const uint2*>(&b.q[row * 16 + 4 * (c4 ^ (2 * ksw16(row)))]);
     return make_float4(lo_bf16(x.x), hi_bf16(x.x), lo_bf16(x.y), hi_bf16(x.y));
   }
   __device__ __forceinline__ uint2 score_q(int row, int g) const {
-    return *reinterpret_cast<const uint2*>(&b.q[row * 16 + 4 * g]);
+    return *reinterpret_cast<const uint2*>(&b.q[row * 16 + 4 * (g ^ (2 * ksw16(row)))]);
   }
   __device__ __forceinline__ uint2 score_k(int row, int g) const {
-    return *reinterpret_cast<const uint2*>(&b.k[row * 16 + 4 * g]);
+    return *reinterpret_cast<const uint2*>(&b.k[row * 16 + 4 * (g ^ (2 * ksw16(row)))]);
   }
   __device__ __forceinline__ u32x4 v_op(int vt, int s, int lane) const {
     return tr_operand<DV>(b.v, to.v[vt], s);
   }
-  // Z[r][4g .. 4g + 3], the A operand of E = Z Q^T
+  // Z[r][4g .. 4g + 3], the A operand of E = Z Q^T (rows swizzled as K)
   __device__ __forceinline__ uint2 gram_op(int r, int g) const {
-    return *reinterpret_cast<const uint2*>(&gram[r * 16 + 4 * g]);
+    return *reinterpret_cast<const uint2*>(&gram[r * 16 + 4 * (g ^ (2 * ksw16(r)))]);
   }
   __device__ __forceinline__ float gate(int row) const { return b.gb[row]; }
   __device__ __forceinline__ float4 gate4(int row) const {
@@ -2399,10 +2406,11 @@ __device__ __forceinline__ f32x4 load_gram16(const float* __restrict__ P, int la
   return z;
 }
 
-// bf16 copy of Z, row-major: lane (g, r) holds Z[4g + i][r] = Z[r][4g + i]
+// bf16 copy of Z, row-major with the 16-byte pieces of row r swizzled by
+// ksw16(r): lane (g, r) holds Z[4g + i][r] = Z[r][4g + i]
 __device__ __forceinline__ void write_gram16(uint16_t* __restrict__ zb, const f32x4& z, int lane) {
   const int g = lane >> 4, r = lane & 15;
-  *reinterpret_cast<uint2*>(&zb[16 * r + 4 * g]) = make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3]));
+  *reinterpret_cast<uint2*>(&zb[16 * r + 4 * (g ^ (2 * ksw16(r)))]) = make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3]));
 }
 
 // Span of a workgroup that forms its prefix itself (RC): the latest spans,
@@ -2437,7 +2445,8 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   __shared__ DmaTileQ16<C, G> x1;
   // bf16 Z (the gated read has no denominator)
   __shared__ alignas(16) uint16_t Zb[G ? 4 : 256];
-  __shared__ alignas(16) uint16_t Sb[VROWS * SB_LD];
+  // value rows only: this readout keeps no z column in Sb
+  __shared__ alignas(16) uint16_t Sb[DV * SB_LD];
   __shared__ alignas(16) uint16_t Ob[CF::STAGE_OUT ? CF::NW : 1][16 * OB_LD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2446,7 +2455,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   const int64_t tok0 = bh * a.T;
 
   // feature positions no tile writes hold no feature: zero once
-  for (int e = tid; e < VROWS * CF::NPOS; e += CF::NT) {
+  for (int e = tid; e < DV * CF::NPOS; e += CF::NT) {
     const int c = e % CF::NPOS;
     if (sb_col_unused<CF>(c)) Sb[(e / CF::NPOS) * SB_LD + c] = 0;
   }

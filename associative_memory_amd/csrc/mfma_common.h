@@ -148,7 +148,20 @@ __device__ __forceinline__ ChunkSrc chunk_src(const void* q, const void* k, cons
 
 #define KATA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-__device__ __forceinline__ int vswz(int row) { return (row >> 1) & 7; }
+// Swizzles of the LDS tiles against bank conflicts (measured on gfx950 with
+// per-pattern read loops and SQ_LDS_BANK_CONFLICT):
+//  - 128-byte rows (V, and the linear map's feature rows): the 32-byte piece
+//    pair of row t is XORed with (t >> 1) & 3, i.e. 16-byte piece p is stored
+//    at p ^ vswz(t).  A transposing read (4 rows x 32 bytes per 16 lanes) then
+//    reaches 4 distinct pair positions and no bank twice: 4.5 cycles per read
+//    per CU against 5.3 with the former (t >> 1) & 7 on 16-byte pieces; row
+//    reads of 16 bytes per lane stay conflict-free.
+//  - 32-byte rows (K and Q at d = 16, the key Gram matrix): the two 16-byte
+//    pieces of row t are exchanged when ksw16(t) = (t >> 3) & 1 is set, so the
+//    8-byte operand reads of 16 consecutive rows (score operands, query rows)
+//    do not pair rows t and t + 8 on one bank: 4.8 cycles per read against 5.9.
+__device__ __forceinline__ int vswz(int row) { return 2 * ((row >> 1) & 3); }
+__device__ __forceinline__ int ksw16(int row) { return (row >> 3) & 1; }
 
 __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
   const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -158,9 +171,9 @@ __device__ __forceinline__ uint2 tr_read(const uint16_t* p) {
 
 // Per-lane element offsets of the transposing reads.  Lane (g, s) addresses
 // row 4g + s/4 (+ 32 ks + 16 h), columns 4(s % 4)..+3 of the 16-column block;
-// within a 32-row k-step the V swizzle (row >> 1) & 7 reduces to
-// (2g + s/8) & 7, so the offsets are lane constants and k-step / half are
-// immediate offsets.
+// within a 32-row k-step the V swizzle vswz(row) reduces to 2 ((2g + s/8) & 3)
+// and the K swizzle ksw16(row) to (g >> 1) & 1, so the offsets are lane
+// constants and k-step / half are immediate offsets.
 struct TrOffsets {
   int v[NDT - 1];  // V, per value tile
   int k;           // K
@@ -169,14 +182,14 @@ struct TrOffsets {
 __device__ __forceinline__ TrOffsets tr_offsets(int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int row = 4 * g + (s >> 2);
-  const int z = (2 * g + (s >> 3)) & 7;
+  const int z = 2 * ((2 * g + (s >> 3)) & 3);
   TrOffsets o;
 #pragma unroll
   for (int dt = 0; dt < NDT - 1; ++dt) {
     const int chunk = (2 * dt + ((s & 3) >> 1)) ^ z;
     o.v[dt] = row * DV + 8 * chunk + 4 * (s & 1);
   }
-  o.k = row * 16 + 4 * (s & 3);
+  o.k = row * 16 + 4 * ((s & 3) ^ (2 * ((g >> 1) & 1)));
   return o;
 }
 
