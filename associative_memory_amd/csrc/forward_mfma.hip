@@ -402,8 +402,12 @@ struct Cfg {
   // of bank conflicts (7.4 cycles per read per CU against 10.9 at 336 bytes)
   static constexpr int SB_LD = DK == 16 ? NPOS + 16 : NPOS + 8;
   static constexpr int QF_LD = DK + 4;              // fp32 row stride of Q
-  static constexpr int KB_LD = DK + 8;              // bf16 row stride of K
-  static constexpr int LDT = C + 8;                 // bf16 row stride of V^T
+  // bf16 row strides of K and V^T: a multiple of 16 bytes that is 2 mod 4 in
+  // 16-byte units, so 16-byte reads of 16 consecutive rows by 4 lane groups
+  // hit no bank twice (measured 7.2-7.4 cycles per read per CU against 10.2-10.6
+  // at the next strides either side)
+  static constexpr int KB_LD = DK == 16 ? 48 : DK == 32 ? 48 : 80;
+  static constexpr int LDT = C == 64 ? 80 : 144;
   static constexpr int LDK = C + 4;                 // fp32 row stride of K^T
   // readout split: 4 waves take 1 or 2 query tiles each with all value tiles;
   // 8 waves take one query tile each, at chunk 64 sharing it between two
