@@ -1774,6 +1774,8 @@ struct alignas(16) SmemWs32 : Tiles<CfgWs32> {
   alignas(16) uint16_t Sb[kSbo32Elems];   // bf16 state copy, operand order
   alignas(16) uint16_t Zb[32 * ZB_LD];    // bf16 Gram matrix, row-major
   alignas(16) uint16_t Ob[4][16 * OB_LD]; // per readout wave output tile
+  alignas(16) float gbs[64];              // gated read: beta_t / 2 of the chunk
+  alignas(16) float gks[64];              // gated read: key factors 2^((beta_C - beta_t) / 2)
 };
 
 // Staging of one chunk by the readout waves (threads 0..255): V (transposed),
@@ -1838,6 +1840,27 @@ struct StageWs32 {
   }
 };
 
+// Gated read: the chunk's gate sums (state-wave threads u = 0..15) and key
+// factors (u = 16..31), 16 bytes each, staged by the state waves (whose
+// registers have room; the readout waves' have none).
+struct GateStageWs32 {
+  uint4 x;
+  __device__ __forceinline__ void load(const ChunkSrc& src, int u) {
+    if (u < 16) {
+      x = buf_load16(src.g, 16 * u);
+    } else if (u < 32) {
+      x = buf_load16(src.gk, 16 * (u - 16));
+    }
+  }
+  __device__ __forceinline__ void store(SmemWs32& sm, int u) const {
+    if (u < 16) {
+      *reinterpret_cast<uint4*>(&sm.gbs[4 * u]) = x;
+    } else if (u < 32) {
+      *reinterpret_cast<uint4*>(&sm.gks[4 * (u - 16)]) = x;
+    }
+  }
+};
+
 // transposing read of the bf16 K rows for the Gram matrix: lane (g, s) gets
 // dimension 16 I + s of the 8 tokens 32 ks + 4g + m, 32 ks + 16 + 4g + m
 __device__ __forceinline__ u32x4 gram_operand32(const uint16_t* Kb, int I, int ks, int lane) {
@@ -1887,13 +1910,31 @@ __device__ __forceinline__ void ws32_key_tiles(f32x4 (&acc)[MT][NDT - 1], const 
   (ws32_key_tile<U + STRIDE * M>(acc[M], x, bv, r), ...);
 }
 
+// gated read: the key factors 2^((beta_C - beta_t) / 2) of the lane's 8
+// tokens (32 ks + 4 g + m and 32 ks + 16 + 4 g + m) on both halves' values
+__device__ __forceinline__ void ws32_gate_keys(float (&x)[2][8], const float* gk, int ks, int g) {
+  const float4 f0 = *reinterpret_cast<const float4*>(&gk[32 * ks + 4 * g]);
+  const float4 f1 = *reinterpret_cast<const float4*>(&gk[32 * ks + 16 + 4 * g]);
+  const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[0][i] *= f[i];
+    x[1][i] *= f[i];
+  }
+}
+
 template <int U>
 struct Ws32State {
   static constexpr int MT = (mfma_feature_tiles(32) - U + 3) / 4;  // feature tiles owned
   static constexpr bool GRAM = U == 3;
 };
 
-template <int DUMMY = 0>
+// G: the gated read (GatedKATA).  The readout waves scale the query row by
+// 2^(beta_q / 2) (the inter term carries 2^beta_q), weight each squared score
+// by 2^(beta_q - beta_k) and keep no denominator; the state waves decay the
+// state by 2^beta_C per chunk and scale the keys by 2^((beta_C - beta_t) / 2);
+// there is no Gram matrix.
+template <bool G = false>
 __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
   using CF = CfgWs32;
   constexpr int C = 64, DK = 32, NT = 512;
@@ -1916,7 +1957,7 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
     sm.Sb[sbo32(Schedule<32>::NKS - 1, vt, l) + j] = 0;
   }
 
-  auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, a.T); };
+  auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, a.T, a.gb, a.gk); };
 
   with_wave<8>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
@@ -1943,6 +1984,13 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
           qr[4 * c + 1] = x.y;
           qr[4 * c + 2] = x.z;
           qr[4 * c + 3] = x.w;
+        }
+        float bq = 0.f;  // gated read: beta_q / 2
+        if constexpr (G) {
+          bq = sm.gbs[16 * QT + r];
+          const float f = __builtin_amdgcn_exp2f(bq);
+#pragma unroll
+          for (int c = 0; c < DK; ++c) qr[c] *= f;
         }
         f32x4 o[NDT - 1];
 #pragma unroll
@@ -1976,7 +2024,7 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
         const u32x4 qf = score_operand<CF>(sm.Qf, 16 * QT + r, g);
         float den = 0.f;
 #pragma unroll
-        for (int I = 0; I < 2; ++I) {
+        for (int I = 0; I < (G ? 0 : 2); ++I) {
           const u32x4 zr = *reinterpret_cast<const u32x4*>(&sm.Zb[(16 * I + r) * ZB_LD + 8 * g]);
           const f32x4 e4 = mfma(zr, qf, f32x4{0.f, 0.f, 0.f, 0.f});
           const float4 qa = *reinterpret_cast<const float4*>(&sm.Qf[(16 * QT + r) * CF::QF_LD + 16 * I + 4 * g]);
@@ -1996,7 +2044,15 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
             for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
             if (kt > QT) continue;
             const u32x4 kf = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * kt + r) * CF::KB_LD + 8 * g]);
-            const f32x4 sc = mfma(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 sc = mfma(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+            if constexpr (G) {
+              // p = sc^2 2^(beta_q - beta_k): the root of the weight into sc
+              const float4 bk = *reinterpret_cast<const float4*>(&sm.gbs[16 * kt + 4 * g]);
+              sc[0] *= __builtin_amdgcn_exp2f(bq - bk.x);
+              sc[1] *= __builtin_amdgcn_exp2f(bq - bk.y);
+              sc[2] *= __builtin_amdgcn_exp2f(bq - bk.z);
+              sc[3] *= __builtin_amdgcn_exp2f(bq - bk.w);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) p[h][j] = (kt < QT || keep[j]) ? sc[j] * sc[j] : 0.f;
           }
@@ -2007,17 +2063,20 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
             const u32x4 bv = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * i + r) * CF::LDT + 32 * s + 8 * g]);
             o[i] = mfma(bv, pf, o[i]);
           }
+          if constexpr (!G) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) den = dot2_bf16(pf[i], kOnesBf16x2, den);
+            for (int i = 0; i < 4; ++i) den = dot2_bf16(pf[i], kOnesBf16x2, den);
+          }
         }
-        // the four 16-lane rows hold parts of the query's denominator
-        {
+        float inv = 1.f;  // the gated read has no denominator
+        if constexpr (!G) {
+          // the four 16-lane rows hold parts of the query's denominator
           const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(den), __float_as_uint(den), false, false);
           const float d2 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
           const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(d2), __float_as_uint(d2), false, false);
           den = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+          inv = __builtin_amdgcn_rcpf(den + a.eps);
         }
-        const float inv = __builtin_amdgcn_rcpf(den + a.eps);
         uint16_t* ob = sm.Ob[W];
 #pragma unroll
         for (int i = 0; i < NDT - 1; ++i) {
@@ -2042,7 +2101,7 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
       // ---------------------------------------------------------------- state wave
       constexpr int U = W - 4;
       constexpr int MT = Ws32State<U>::MT;
-      constexpr bool GRAM = Ws32State<U>::GRAM;
+      constexpr bool GRAM = Ws32State<U>::GRAM && !G;
       f32x4 acc[MT][NDT - 1];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -2096,12 +2155,29 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
           }
         }
       };
+      GateStageWs32 gs;
+      if constexpr (G) {
+        gs.load(src(first), tid - 256);
+        gs.store(sm, tid - 256);
+      }
       publish();
       __syncthreads();  // state copy, Gram copy and chunk 0 in place
       for (int64_t c0 = first; c0 < end; c0 += C) {
         const bool more = c0 + C < end;
+        if constexpr (G) {
+          if (more) gs.load(src(c0 + C), tid - 256);
+        }
         if (more) {
           // carry the state across the chunk: phi_k(K_c)^T V_c and K_c^T K_c
+          // (gated: the state decays by 2^beta_C first)
+          if constexpr (G) {
+            const float f = __builtin_amdgcn_exp2f(2.f * sm.gbs[C - 1]);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+#pragma unroll
+              for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] *= f;
+            }
+          }
 #pragma unroll
           for (int ks = 0; ks < C / 32; ++ks) {
             u32x4 bv[NDT - 1];
@@ -2126,19 +2202,24 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
               x[1][2 * i] = lo_bf16(k1[i]);
               x[1][2 * i + 1] = hi_bf16(k1[i]);
             }
+            if constexpr (G) ws32_gate_keys(x, sm.gks, ks, g);
             ws32_key_tiles<U>(acc, x, bv, r, std::make_integer_sequence<int, MT>{});
           }
         }
         __syncthreads();  // every wave done with the chunk and the state copy
-        if (more) publish();
+        if (more) {
+          publish();
+          if constexpr (G) gs.store(sm, tid - 256);
+        }
         __syncthreads();
       }
     }
   });
 }
 
+template <bool G = false>
 __global__ __launch_bounds__(512, 2) void readout_ws32_kernel(MfmaArgs a) {
-  readout_ws32(a);
+  readout_ws32<G>(a);
 }
 
 
@@ -2158,11 +2239,13 @@ __global__ __launch_bounds__(512, 2) void readout_ws32_kernel(MfmaArgs a) {
 struct alignas(16) DmaTile32 {
   alignas(16) uint16_t v[64 * DV];  // [token][value column], pieces swizzled by vswz
   alignas(16) uint16_t k[64 * 32];  // [token][dimension], pieces swizzled by row & 2
+  alignas(16) float gk[64];         // gated read: key factors 2^((beta_C - beta_t) / 2)
 };
 
 // wave W's share of a chunk's transfer: V rows 8 W .. 8 W + 7; waves 4..7
-// also K rows 16 (W - 4) .. + 15.  Rows past the end arrive as zero.
-template <int W>
+// also K rows 16 (W - 4) .. + 15; gated, wave 0 also the key factors (16
+// lanes).  Rows past the end arrive as zero.
+template <int W, bool G = false>
 __device__ __forceinline__ void dma_chunk32(DmaTile32& b, const ChunkSrc& src, int lane) {
   {
     const int t = 8 * W + (lane >> 3);
@@ -2173,6 +2256,9 @@ __device__ __forceinline__ void dma_chunk32(DmaTile32& b, const ChunkSrc& src, i
     const int t = 16 * (W - 4) + (lane >> 2);
     const int c = (lane & 3) ^ (t & 2);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, KATA_LDS(&b.k[16 * (W - 4) * 32]), 16, t * 64 + 16 * c, 0, 0, 0);
+  }
+  if constexpr (G && W == 0) {
+    if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(src.gk, KATA_LDS(&b.gk[0]), 16, 16 * lane, 0, 0, 0);
   }
 }
 
@@ -2185,6 +2271,9 @@ __device__ __forceinline__ int tr_offset_k32(int I, int lane) {
   return row * 32 + 8 * c + 4 * (s & 1);
 }
 
+// G: the gated span sums (the state decays by 2^beta_C per chunk, keys scaled
+// by the key factors, no Gram matrix; the z column is stored as zeros).
+template <bool G = false>
 __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
   using CF = CfgWs32;
   constexpr int C = 64;
@@ -2201,14 +2290,14 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
   const int64_t first = sp * a.G * C;
   int64_t end = first + a.G * C;
   if (end > a.T) end = a.T;
-  auto src = [&](int64_t c) { return chunk_src<32, C>(nullptr, a.k, a.v, tok0, c, end); };
+  auto src = [&](int64_t c) { return chunk_src<32, C>(nullptr, a.k, a.v, tok0, c, end, a.gb, a.gk); };
 
   with_wave<8>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
-    constexpr int NPC = W >= 4 ? 2 : 1;  // this wave's transfers per chunk
+    constexpr int NPC = (W >= 4 ? 2 : 1) + (G && W == 0 ? 1 : 0);  // this wave's transfers per chunk
     constexpr int NFT = mfma_feature_tiles(32);
     constexpr int MT = (NFT - W + 7) / 8;
-    constexpr bool GRAM = W == 7;
+    constexpr bool GRAM = W == 7 && !G;
     const TrOffsets to = tr_offsets(lane);
     const int ok0 = tr_offset_k32(0, lane), ok1 = tr_offset_k32(1, lane);
     f32x4 acc[MT][NDT - 1];
@@ -2220,7 +2309,16 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
     f32x4 zt[GRAM ? 4 : 1];
 #pragma unroll
     for (int t = 0; t < (GRAM ? 4 : 1); ++t) zt[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto reduce = [&](const DmaTile32& b) {
+    auto reduce = [&](const DmaTile32& b, int64_t c) {
+      if constexpr (G) {
+        // the state decays by 2^beta_C over the chunk (a whole chunk: beta_C / 2 stored)
+        const float f = __builtin_amdgcn_exp2f(2.f * a.gb[tok0 + c + C - 1]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] *= f;
+        }
+      }
       // one k-step at a time: interleaving the two would exceed the registers
 #pragma unroll 1
       for (int ks = 0; ks < C / 32; ++ks) {
@@ -2243,27 +2341,28 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
           x[1][2 * i] = lo_bf16(k1[i]);
           x[1][2 * i + 1] = hi_bf16(k1[i]);
         }
+        if constexpr (G) ws32_gate_keys(x, b.gk, ks, g);
         ws32_key_tiles<W, 8>(acc, x, bv, r, std::make_integer_sequence<int, MT>{});
       }
     };
-    dma_chunk32<W>(b0, src(first), lane);
-    dma_chunk32<W>(b1, src(first + C), lane);
+    dma_chunk32<W, G>(b0, src(first), lane);
+    dma_chunk32<W, G>(b1, src(first + C), lane);
     for (int64_t c0 = first; c0 < end; c0 += 3 * C) {
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
-      dma_chunk32<W>(b2, src(c0 + 2 * C), lane);
+      dma_chunk32<W, G>(b2, src(c0 + 2 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      reduce(b0);
+      reduce(b0, c0);
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
-      dma_chunk32<W>(b0, src(c0 + 3 * C), lane);
+      dma_chunk32<W, G>(b0, src(c0 + 3 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (c0 + C < end) reduce(b1);
+      if (c0 + C < end) reduce(b1, c0 + C);
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
-      dma_chunk32<W>(b1, src(c0 + 4 * C), lane);
+      dma_chunk32<W, G>(b1, src(c0 + 4 * C), lane);
       __builtin_amdgcn_sched_barrier(0);
-      if (c0 + 2 * C < end) reduce(b2);
+      if (c0 + 2 * C < end) reduce(b2, c0 + 2 * C);
     }
     __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
     // store: value tiles doubled (the state's key features carry weight 2),
@@ -2289,6 +2388,10 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
           if (ra <= cb) P[CF::ZOFF + kPairPos32.p[ra][cb]] = 2.f * zt[t][i];
         }
       }
+    }
+    if constexpr (G && W == 7) {
+      // no denominator: the z column holds zeros
+      for (int i = lane; i < 16 * NFT; i += 64) P[CF::ZOFF + i] = 0.f;
     }
   });
 }
@@ -2608,7 +2711,7 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 16 && a.chunk == 64) return launch_span<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_span<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) {
-    span_state_ws32_kernel<<<dim3(static_cast<unsigned>(a.BH * (a.n_spans - 1))), 512, 0, stream>>>(a);
+    span_state_ws32_kernel<false><<<dim3(static_cast<unsigned>(a.BH * (a.n_spans - 1))), 512, 0, stream>>>(a);
     return hipGetLastError();
   }
   if (a.d == 32 && a.chunk == 128) return launch_span<32, 128>(a, stream);
@@ -2624,7 +2727,7 @@ hipError_t launch_span_state_gated(const MfmaArgs& a, hipStream_t stream) {
   } else if (a.d == 16 && a.chunk == 128) {
     span_state_dma16_kernel<128, true><<<grid, 256, 0, stream>>>(a);
   } else if (a.d == 32 && a.chunk == 64) {
-    span_state_mfma_kernel<Cfg<32, 64>, true><<<grid, Cfg<32, 64>::NT, 0, stream>>>(a);
+    span_state_ws32_kernel<true><<<grid, 512, 0, stream>>>(a);
   } else if (a.d == 32 && a.chunk == 128) {
     span_state_mfma_kernel<Cfg<32, 128>, true><<<grid, Cfg<32, 128>::NT, 0, stream>>>(a);
   } else {
@@ -2640,7 +2743,7 @@ hipError_t launch_readout_gated(const MfmaArgs& a, hipStream_t stream) {
   } else if (a.d == 16 && a.chunk == 128) {
     readout_dma16_kernel<128, true><<<grid, 256, 0, stream>>>(a);
   } else if (a.d == 32 && a.chunk == 64) {
-    readout_mfma_kernel<Cfg<32, 64>, true><<<grid, Cfg<32, 64>::NT, 0, stream>>>(a);
+    readout_ws32_kernel<true><<<grid, 512, 0, stream>>>(a);
   } else if (a.d == 32 && a.chunk == 128) {
     readout_mfma_kernel<Cfg<32, 128>, true><<<grid, Cfg<32, 128>::NT, 0, stream>>>(a);
   } else {
@@ -2664,7 +2767,7 @@ hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 16 && a.chunk == 64) return launch_readout<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_readout<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) {
-    readout_ws32_kernel<<<dim3(static_cast<unsigned>(a.BH * a.n_spans)), 512, 0, stream>>>(a);
+    readout_ws32_kernel<false><<<dim3(static_cast<unsigned>(a.BH * a.n_spans)), 512, 0, stream>>>(a);
     return hipGetLastError();
   }
   if (a.d == 32 && a.chunk == 128) return launch_readout<32, 128>(a, stream);
