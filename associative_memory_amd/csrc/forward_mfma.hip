@@ -2520,6 +2520,23 @@ __device__ __forceinline__ void write_gram16(uint16_t* __restrict__ zb, const f3
   *reinterpret_cast<uint2*>(&zb[16 * r + 4 * (g ^ (2 * ksw16(r)))]) = make_uint2(pack2(z[0], z[1]), pack2(z[2], z[3]));
 }
 
+// DMA instructions one readout wave issues per chunk (ungated; WQ: with Q)
+template <int C, int W, int NW, bool WQ>
+constexpr int dma_count_q16() {
+  int n = 0;
+  for (int j = W; j < C / 8; j += NW) ++n;
+  for (int j = W; j < C / 32; j += NW) n += WQ ? 2 : 1;
+  return n;
+}
+
+// a tile that exists only when E holds (an empty struct otherwise)
+template <bool E, class T>
+struct MaybeTile {
+  T t;
+};
+template <class T>
+struct MaybeTile<false, T> {};
+
 // Span of a workgroup that forms its prefix itself (RC): the latest spans,
 // which carry the most chunks before them, take the lowest block indices and
 // start first; consecutive blocks are different heads.
@@ -2550,6 +2567,9 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   static_assert(!(G && RC), "the gated read takes its prefix from the affine scan");
   __shared__ DmaTileQ16<C, G> x0;
   __shared__ DmaTileQ16<C, G> x1;
+  // the third buffer of the deep warm-up (prefix formed in the workgroup, chunk 64)
+  constexpr bool DEEP = RC && C == 64;
+  __shared__ MaybeTile<DEEP, DmaTileQ16<C, G>> x2h;
   // bf16 Z (the gated read has no denominator)
   __shared__ alignas(16) uint16_t Zb[G ? 4 : 256];
   // value rows only: this readout keeps no z column in Sb
@@ -2593,12 +2613,61 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     int64_t end = span_first_chunk(a, sp + 1) * C;
     if (end > a.T) end = a.T;
     auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb, a.gk); };
-    const int64_t start = RC ? 0 : first;
-    dma_chunkq16<C, W, CF::NW, G>(x0, src(start), lane);
-    // the state loads and the first chunk; an unconditional vmcnt(0) also
-    // retires the state loads for the compiler's wait-count analysis
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
+    const int64_t start = (RC && !DEEP) ? 0 : first;
+    bool staged = false;  // chunk `first` already in x0
+    if constexpr (DEEP) {
+      // The chunks before the span, three buffers deep: step i waits for its
+      // own share of chunk i, meets the other waves at a barrier (after which
+      // nobody reads chunk i - 1's buffer), sends chunk i + 2 into that
+      // buffer (queries only for the span's first chunk) and adds chunk i to
+      // the state.  Chunk i sits in buffer (i - nf) mod 3 of (x0, x1, x2), so
+      // the span's first chunk (index nf) arrives in x0.  Steps before chunk 0
+      // only issue the first two transfers.
+      const int64_t nf = first / C;
+      if (nf > 0) {
+        constexpr int NK = dma_count_q16<C, W, CF::NW, false>();
+        constexpr int NQ = dma_count_q16<C, W, CF::NW, true>();
+        auto wstep = [&](int64_t i, const DmaTileQ16<C, G>& cur, DmaTileQ16<C, G>& pre) {
+          if (i >= 0 && i < nf) {
+            if (i + 1 == nf) {
+              __builtin_amdgcn_s_waitcnt(wait_vmcnt(NQ));
+            } else {
+              __builtin_amdgcn_s_waitcnt(wait_vmcnt(NK));
+            }
+            barrier_lds();
+          }
+          if (i + 2 >= 0 && i + 2 <= nf) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i + 2 == nf) {
+              dma_chunkq16<C, W, CF::NW, G>(pre, src((i + 2) * C), lane);
+            } else {
+              dma_chunkq16<C, W, CF::NW, G, false>(pre, src((i + 2) * C), lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (i >= 0 && i < nf) state_update_ro16<CF, W, G>(acc, gram, cur, to);
+        };
+        const int64_t s0 = nf - 3 * ((nf + 2) / 3 + 1);  // <= -3, s0 = nf (mod 3)
+        for (int64_t i = s0; i < nf; i += 3) {
+          wstep(i, x0, x2h.t);
+          wstep(i + 1, x1, x0);
+          wstep(i + 2, x2h.t, x1);
+        }
+        // the span's first chunk has landed (the last transfer issued)
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        write_sb<CF, NDT - 1, DmaSrc16<C, G>::kHalfDiag>(Sb, acc, W, lane);
+        if constexpr (!G && W == 0) write_gram16(Zb, gram, lane);
+        __syncthreads();
+        staged = true;
+      }
+    }
+    if (!staged) {
+      dma_chunkq16<C, W, CF::NW, G>(x0, src(start), lane);
+      // the state loads and the first chunk; an unconditional vmcnt(0) also
+      // retires the state loads for the compiler's wait-count analysis
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      __syncthreads();
+    }
 
     // one chunk: prefetch the next into the other buffer, read out, and
     // (unless it is the span's last) carry the state and refresh Sb
