@@ -341,6 +341,9 @@ RECOMPUTE_CASES = [
     (3, 5, 2500, 128),
     (2, 2, 8191, 64),
     (1, 3, 40000, 128),
+    (1, 1, 1, 64),        # one token, one span
+    (7, 9, 65, 64),       # 63 heads of two chunks, the second a single token
+    (40, 16, 300, 64),    # more heads than workgroups: one span per head
 ]
 
 
