@@ -723,6 +723,31 @@ __device__ __forceinline__ float row_rotate(float x) {
   }
 }
 
+// f[i] = a[i] * (b[i] of lane (r + J) mod 16 of the row), J = 1..15, as eight
+// v_mul_f32 with the row rotation in the DPP field of the first operand.  The
+// compiler only folds a rotation into its multiply when the two sit within a
+// few instructions of each other, which its instruction order does not keep
+// for products whose operands come from different registers; written out, the
+// rotation costs nothing.  DPP reads a VGPR two wait states after a VALU
+// write at the earliest, hence the leading s_nop (the inputs may have been
+// written by the instructions just before).
+template <int J>
+__device__ __forceinline__ void mul_row_rotated(float (&f)[8], const float (&a)[8], const float (&b)[8]) {
+  static_assert(J > 0 && J < 16, "row rotation by 1..15 lanes");
+  asm("s_nop 1\n\t"
+      "v_mul_f32_dpp %0, %16, %8 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %17, %9 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %2, %18, %10 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %3, %19, %11 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %4, %20, %12 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %5, %21, %13 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %6, %22, %14 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %7, %23, %15 row_ror:%24 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=&v"(f[0]), "=&v"(f[1]), "=&v"(f[2]), "=&v"(f[3]), "=&v"(f[4]), "=&v"(f[5]), "=&v"(f[6]), "=&v"(f[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]), "v"(b[6]), "v"(b[7]), "n"(16 - J));
+}
+
 // d = 16: key-feature tile J (J = 0..8) holds on row R the pair (R, R + J mod
 // 16).  Lane (g, r) loads its own dimension r of its 8 tokens once per
 // k-step and takes the partner dimension from lane r + J of its row, so the
@@ -1710,33 +1735,122 @@ __global__ __launch_bounds__(CF::NT, 2) void readout_mfma_kernel(MfmaArgs a) {
 // ------------------------------------------------------------ readout, d = 32, wave-specialised
 //
 // The d = 32 chunked readout at chunk 64 with the 8 waves split by role.
-// Waves 0..3 read out one query tile each (all four value tiles, inter term
-// phi_q(Q_c) S from the state copy plus the squared causal block); waves
+// Waves 0..3 read out one query tile each (all four value tiles): the inter
+// term phi_q(Q_c) S from the state copy and the prefix denominator.  Waves
 // 4..7 carry the state across the chunk (state wave u owns feature tiles
-// u, u + 4, ..., u + 32 of the 33) while the readout runs, so every query
-// feature and every key feature is built exactly once per chunk.  The
-// denominators take the key Gram matrix Z = sum_s k_s k_s^T (32 x 32, on
-// state wave 3, one product per 16 x 16 tile and 32 keys from the
-// transposing read of the bf16 K rows): phi_q(q) . z = q^T Z q, from two
-// 16x16x32 products E = Z Q^T per query tile and a dot with q; the chunk part
-// is the vector sum of the query's bf16 weights.  No ones-column tile.
-// Key features by lane rotation: the same transposing read gives lane (g, R)
-// dimensions R and 16 + R of its 8 tokens; feature tile (j, h) of the
-// schedule holds on row R the pair (R + 16 h, R + 16 h + j mod 32), whose
-// partner sits in lane R + j of the row, in the register h or 1 - h
-// depending on whether R + j wraps: the source lane selects the register, a
-// row rotation delivers it, and the product is one multiply.  No fp32 K copy.
-// The key features carry weight 1 (the products of bf16 k are exact), so the
-// state waves hold half the state (halved on load) and the state copy is
-// read with query features of weight 1 on the diagonal and 2 off it.
-// Staging splits the same way: readout waves bring V (transposed) and Q,
-// state waves bring the bf16 K rows.  The span state in the workspace keeps
-// the layout of the other d = 32 kernels: its z column holds 2 Z[a][b] on
-// the position of the pair (a, b), the sum of the key features.
+// u, u + 4, ..., u + 32 of the 33) and form the squared causal block of one
+// query tile each, which they hand to its readout wave through LDS; so every
+// query feature and every key feature is built exactly once per chunk.  Per
+// chunk the readout waves run the inter term while the state waves run the
+// intra-chunk blocks and the state update; after the barrier the readout
+// waves add the block, normalise and store while the state waves publish the
+// new state copy.  The denominators take the key Gram matrix
+// Z = sum_s k_s k_s^T (32 x 32, on state wave 3, one product per 16 x 16 tile
+// and 32 keys from the transposing read of the bf16 K rows): phi_q(q) . z =
+// q^T Z q, from two 16x16x32 products E = Z Q^T per query tile and a dot with
+// q; the chunk part is the vector sum of the query's bf16 weights.  No
+// ones-column tile.  Feature positions follow the rotation schedule below:
+// the transposing read gives lane (g, R) dimensions R and 16 + R of its 8
+// tokens, and every key feature is one multiply of one of them by one of
+// lane R + j's, the rotation folded in.  No fp32 K copy.  The key features
+// carry weight 1 (the products of bf16 k are exact), so the state waves hold
+// half the state (halved on load) and the state copy is read with query
+// features of weight 1 on the diagonal and 2 off it.  The readout waves stage
+// the chunk (V transposed, Q as fp32 rows, the bf16 K rows); the state waves
+// stage the gate sums of the gated read.  The span state in the workspace
+// holds the value tiles at full scale and the z column as 2 Z[a][b] on the
+// position of the pair (a, b), the sum of the key features.
 using CfgWs32 = Cfg<32, 64, 8>;   // tiles and strides
 constexpr int ZB_LD = 40;         // bf16 row stride of the Gram copy
 
-// feature position of every pair (a, b) of the d = 32 schedule (symmetric)
+// The feature schedule of the wave-specialised d = 32 kernels (17 k-steps of
+// 32 positions, feature tile ft = 2 ks + h, row R = position 32 ks + 16 h + R).
+// Every tile is a row rotation: row R holds the pair (R + 16 h1,
+// (R + j) mod 16 + 16 h2), which the key side builds as x_h1 times x_h2 of
+// lane R + j of its 16-lane row (x0, x1: dimensions r and 16 + r of the
+// lane's tokens), one multiply with the rotation folded in and no select:
+//   ks = 0..7,  j = ks:     h = 0: (0, 0, j)   h = 1: (1, 1, j)   pairs inside each half
+//   ks = 8..14, j = ks - 7: h = 0: (0, 1, j)   h = 1: (1, 0, j)   cross pairs at offsets j, 16 - j
+//   ks = 15:                h = 0: (0, 1, 0)   h = 1: (0, 1, 8)   cross pairs at offsets 0, 8
+//   ks = 16:                h = 0: rows 0..7 (R, R + 8) and rows 8..15 (R + 8, R + 16)
+//                           (offset 8 inside each half); h = 1 holds nothing.
+// The query side: lane group g holds positions 8 g + i of each k-step, the
+// pair (pi_g(A), pi_g(B)) of a compile-time pattern (A, B) of entry i, where
+// pi_g exchanges the halves of the dimensions for g >= 2 and rotates each
+// half by 8 for odd g.  The lane reads its query row permuted by pi_g once
+// per chunk and indexes it at compile time; k-steps 15 and 16 take a second
+// pattern on lane groups 2 and 3 (k-step 15) or 1 (k-step 16), and k-step
+// 16 nothing on groups 2 and 3.
+struct Ws32Pair {
+  int a, b;
+};
+__host__ __device__ constexpr int ws32_pi(int dim, int g) {
+  return 16 * ((dim >> 4) ^ (g >> 1)) + (((dim & 15) + 8 * (g & 1)) & 15);
+}
+// pattern of entry i of k-step ks (alt: the second pattern)
+__host__ __device__ constexpr Ws32Pair ws32_pattern(int ks, bool alt, int i) {
+  if (ks < 8) return {i, (i + ks) & 15};
+  if (ks < 15) return {i, 16 + ((i + ks - 7) & 15)};
+  if (ks == 15) return alt ? Ws32Pair{16 + i, 8 + i} : Ws32Pair{i, 16 + i};
+  return alt ? Ws32Pair{24 + i, 16 + i} : Ws32Pair{i, 8 + i};
+}
+// the pattern lane group g of k-step ks uses: 0, 1 (the second) or -1 (none)
+__host__ __device__ constexpr int ws32_variant(int ks, int g) {
+  if (ks < 15) return 0;
+  if (ks == 15) return g >= 2 ? 1 : 0;
+  return g == 0 ? 0 : g == 1 ? 1 : -1;
+}
+// the pair the query side places at feature position p (a < 0: none)
+constexpr Ws32Pair ws32_pair_at(int p) {
+  const int ks = p >> 5, g = (p >> 3) & 3, i = p & 7;
+  const int var = ks < 17 ? ws32_variant(ks, g) : -1;
+  if (var < 0) return {-1, -1};
+  const Ws32Pair e = ws32_pattern(ks, var == 1, i);
+  return {ws32_pi(e.a, g), ws32_pi(e.b, g)};
+}
+// key tile ft: row R pairs R + 16 h1 with (R + j) mod 16 + 16 h2; h1 < 0 for
+// the mixed tile 32, h1 = -2 for the empty tile 33
+struct Ws32Key {
+  int h1, h2, j;
+};
+constexpr Ws32Key ws32_key(int ft) {
+  const int ks = ft >> 1, h = ft & 1;
+  if (ks < 8) return {h, h, ks};
+  if (ks < 15) return {h, 1 - h, ks - 7};
+  if (ks == 15) return {0, 1, h ? 8 : 0};
+  return {h ? -2 : -1, 0, 8};
+}
+// both sides place the same pair on every position, and every pair a <= b
+// has exactly one position
+constexpr bool ws32_schedule_ok() {
+  bool seen[32][32] = {};
+  int n = 0;
+  for (int p = 0; p < 17 * 32; ++p) {
+    const Ws32Pair q = ws32_pair_at(p);
+    const int R = p & 15;
+    const Ws32Key k = ws32_key(p >> 4);
+    int ka = -1, kb = -1;
+    if (k.h1 == -1) {
+      ka = R < 8 ? R : 16 + R;
+      kb = R < 8 ? R + 8 : R + 8;
+    } else if (k.h1 >= 0) {
+      ka = R + 16 * k.h1;
+      kb = ((R + k.j) & 15) + 16 * k.h2;
+    }
+    if ((q.a < 0) != (ka < 0)) return false;
+    if (q.a < 0) continue;
+    if (!((q.a == ka && q.b == kb) || (q.a == kb && q.b == ka))) return false;
+    const int x = q.a < q.b ? q.a : q.b, y = q.a < q.b ? q.b : q.a;
+    if (seen[x][y]) return false;
+    seen[x][y] = true;
+    ++n;
+  }
+  return n == 32 * 33 / 2;
+}
+static_assert(ws32_schedule_ok(), "the wave-specialised d = 32 schedule covers every pair once");
+static_assert(Schedule<32>::NKS == 17, "the wave-specialised d = 32 kernels use 17 k-steps");
+
+// feature position of every pair (a, b) of that schedule (symmetric)
 struct PairPos32 {
   int16_t p[32][32];
 };
@@ -1744,12 +1858,11 @@ constexpr PairPos32 make_pair_pos32() {
   PairPos32 t{};
   for (int a = 0; a < 32; ++a)
     for (int b = 0; b < 32; ++b) t.p[a][b] = -1;
-  for (int p = 0; p < Schedule<32>::NPOS; ++p) {
-    const int ks = p >> 5, o = p & 31, g = o >> 3, i = o & 7, e = 8 * ks + i;
-    if (e >= Schedule<32>::NE || (kSched<32>.pair2[e] && g >= 2)) continue;
-    const int a = (kSched<32>.a[e] + Schedule<32>::SH * g) % 32, b = (kSched<32>.b[e] + Schedule<32>::SH * g) % 32;
-    t.p[a][b] = static_cast<int16_t>(p);
-    t.p[b][a] = static_cast<int16_t>(p);
+  for (int p = 0; p < 17 * 32; ++p) {
+    const Ws32Pair q = ws32_pair_at(p);
+    if (q.a < 0) continue;
+    t.p[q.a][q.b] = static_cast<int16_t>(p);
+    t.p[q.b][q.a] = static_cast<int16_t>(p);
   }
   return t;
 }
@@ -1776,7 +1889,13 @@ struct alignas(16) SmemWs32 : Tiles<CfgWs32> {
   alignas(16) uint16_t Ob[4][16 * OB_LD]; // per readout wave output tile
   alignas(16) float gbs[64];              // gated read: beta_t / 2 of the chunk
   alignas(16) float gks[64];              // gated read: key factors 2^((beta_C - beta_t) / 2)
+  // the intra-chunk term of each query tile, from the state waves to the
+  // readout waves: the four fp32 accumulator tiles in lane order, and each
+  // lane's part of the denominator
+  alignas(16) float Xo[4][(NDT - 1) * 64 * 4];
+  alignas(16) float Xd[4][64];
 };
+static_assert(sizeof(SmemWs32) <= 160 * 1024, "the d = 32 readout's LDS fits one CU");
 
 // Staging of one chunk by the readout waves (threads 0..255): V (transposed),
 // Q (fp32 rows) and the bf16 K rows; the state waves stage nothing.  Tokens
@@ -1876,26 +1995,29 @@ __device__ __forceinline__ u32x4 gram_operand32(const uint16_t* Kb, int I, int k
   return out;
 }
 
-// feature tile ft = 2 j + h of the d = 32 schedule for the lane's 8 tokens:
-// row R (= lane r of the row) pairs dimension R + 16 h (own register h) with
-// R + 16 h + j mod 32, found in lane (R + j) mod 16 of the row, register h
-// when that lane is at or past j (no wrap) and 1 - h otherwise
-// (weight 1 on every pair: the state waves keep half the state)
+// feature tile ft of the wave-specialised d = 32 schedule for the lane's 8
+// tokens: row R (= lane r of the row) takes x_h1 times x_h2 of lane
+// (R + j) mod 16; tile 32 takes offset 8 inside the first half on rows 0..7
+// and inside the second on rows 8..15 (weight 1 on every pair: the state
+// waves keep half the state)
 template <int FT>
 __device__ __forceinline__ void ws32_key_tile(f32x4 (&acc)[NDT - 1], const float (&x)[2][8],
                                               const u32x4 (&bv)[NDT - 1], int r) {
-  constexpr int J = FT >> 1, H = FT & 1;
+  constexpr Ws32Key K = ws32_key(FT);
+  static_assert(K.h1 != -2, "tile 33 holds no feature");
   float f[8];
-  if constexpr (J == 0) {
+  if constexpr (K.h1 < 0) {
+    const bool lo = r < 8;
+    float f0[8], f1[8];
+    mul_row_rotated<8>(f0, x[0], x[0]);
+    mul_row_rotated<8>(f1, x[1], x[1]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = x[H][i] * x[H][i];
-  } else if constexpr (J == 16) {
+    for (int i = 0; i < 8; ++i) f[i] = lo ? f0[i] : f1[i];
+  } else if constexpr (K.j == 0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = x[H][i] * x[1 - H][i];
+    for (int i = 0; i < 8; ++i) f[i] = x[K.h1][i] * x[K.h2][i];
   } else {
-    const bool own = r >= J;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = x[H][i] * row_rotate<J>(own ? x[H][i] : x[1 - H][i]);
+    mul_row_rotated<K.j>(f, x[K.h1], x[K.h2]);
   }
   const u32x4 af = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
 #pragma unroll
@@ -1923,10 +2045,15 @@ __device__ __forceinline__ void ws32_gate_keys(float (&x)[2][8], const float* gk
   }
 }
 
+// state wave U: the feature tiles it owns, whether it keeps the key Gram
+// matrix, and the query tile whose intra-chunk term it forms (the heavier
+// blocks, 11 and 12 products, on the waves with 8 tiles and no Gram matrix;
+// 5 and 6 products on the waves with 72 state products)
 template <int U>
 struct Ws32State {
   static constexpr int MT = (mfma_feature_tiles(32) - U + 3) / 4;  // feature tiles owned
   static constexpr bool GRAM = U == 3;
+  static constexpr int QI = U == 0 ? 0 : U == 1 ? 3 : U == 2 ? 2 : 1;
 };
 
 // G: the gated read (GatedKATA).  The readout waves scale the query row by
@@ -1966,29 +2093,27 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
       st.load(src(first), tid);
       // ---------------------------------------------------------------- readout wave
       constexpr int QT = W;
-      bool keep[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) keep[j] = 4 * g + j <= r;
       st.store(sm, tid);
       __syncthreads();  // state copy, Gram copy and chunk 0 in place
       for (int64_t c0 = first; c0 < end; c0 += C) {
         const bool more = c0 + C < end;
         if (more) st.load(src(c0 + C), tid);
         const int64_t n = (a.T - c0 < C) ? a.T - c0 : C;
-        // the query row, rotated by 8 g (the lane group's share of the pairs)
+        // the query row permuted by pi_g (the lane group's share of the pairs):
+        // 4-dimension block c holds block pi_g(4 c) / 4 of the row
         float qr[DK];
 #pragma unroll
         for (int c = 0; c < DK / 4; ++c) {
-          const float4 x = *reinterpret_cast<const float4*>(&sm.Qf[(16 * QT + r) * CF::QF_LD + 4 * ((c + 2 * g) % 8)]);
+          const int blk = ((c & 4) ^ (4 * (g >> 1))) | ((c + 2 * (g & 1)) & 3);
+          const float4 x = *reinterpret_cast<const float4*>(&sm.Qf[(16 * QT + r) * CF::QF_LD + 4 * blk]);
           qr[4 * c + 0] = x.x;
           qr[4 * c + 1] = x.y;
           qr[4 * c + 2] = x.z;
           qr[4 * c + 3] = x.w;
         }
-        float bq = 0.f;  // gated read: beta_q / 2
         if constexpr (G) {
-          bq = sm.gbs[16 * QT + r];
-          const float f = __builtin_amdgcn_exp2f(bq);
+          // beta_q / 2 of the query into its row
+          const float f = __builtin_amdgcn_exp2f(sm.gbs[16 * QT + r]);
 #pragma unroll
           for (int c = 0; c < DK; ++c) qr[c] *= f;
         }
@@ -2008,12 +2133,15 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
           float f[8];
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const int e = 8 * ks + i;
-            if (e >= Schedule<32>::NE) {
-              f[i] = 0.f;
+            constexpr auto feat = [](const float* q, const float* q2, Ws32Pair e) {
+              return e.a == e.b ? q[e.a] * q[e.a] : q2[e.a] * q[e.b];
+            };
+            const float f0 = feat(qr, qr2, ws32_pattern(ks, false, i));
+            if (ks < 15) {
+              f[i] = f0;
             } else {
-              const int pa = kSched<32>.a[e], pb = kSched<32>.b[e];
-              f[i] = pa == pb ? qr[pa] * qr[pa] : qr2[pa] * qr[pb];
+              const float f1 = feat(qr, qr2, ws32_pattern(ks, true, i));
+              f[i] = ks == 15 ? (g >= 2 ? f1 : f0) : (g == 0 ? f0 : g == 1 ? f1 : 0.f);
             }
           }
           const u32x4 qfeat = {pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])};
@@ -2021,55 +2149,28 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
           for (int i = 0; i < NDT - 1; ++i) o[i] = mfma(bs[i], qfeat, o[i]);
         }
         // prefix denominator q^T Z q: E = Z Q^T (two products), dotted with q
-        const u32x4 qf = score_operand<CF>(sm.Qf, 16 * QT + r, g);
         float den = 0.f;
+        if constexpr (!G) {
+          const u32x4 qf = score_operand<CF>(sm.Qf, 16 * QT + r, g);
 #pragma unroll
-        for (int I = 0; I < (G ? 0 : 2); ++I) {
-          const u32x4 zr = *reinterpret_cast<const u32x4*>(&sm.Zb[(16 * I + r) * ZB_LD + 8 * g]);
-          const f32x4 e4 = mfma(zr, qf, f32x4{0.f, 0.f, 0.f, 0.f});
-          const float4 qa = *reinterpret_cast<const float4*>(&sm.Qf[(16 * QT + r) * CF::QF_LD + 16 * I + 4 * g]);
-          den = __builtin_fmaf(qa.x, e4[0], den);
-          den = __builtin_fmaf(qa.y, e4[1], den);
-          den = __builtin_fmaf(qa.z, e4[2], den);
-          den = __builtin_fmaf(qa.w, e4[3], den);
-        }
-        // intra-chunk term: squared causal scores times V, their sum
-#pragma unroll
-        for (int s = 0; s <= QT / 2; ++s) {
-          float p[2][4];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int kt = 2 * s + h;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
-            if (kt > QT) continue;
-            const u32x4 kf = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * kt + r) * CF::KB_LD + 8 * g]);
-            f32x4 sc = mfma(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
-            if constexpr (G) {
-              // p = sc^2 2^(beta_q - beta_k): the root of the weight into sc
-              const float4 bk = *reinterpret_cast<const float4*>(&sm.gbs[16 * kt + 4 * g]);
-              sc[0] *= __builtin_amdgcn_exp2f(bq - bk.x);
-              sc[1] *= __builtin_amdgcn_exp2f(bq - bk.y);
-              sc[2] *= __builtin_amdgcn_exp2f(bq - bk.z);
-              sc[3] *= __builtin_amdgcn_exp2f(bq - bk.w);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) p[h][j] = (kt < QT || keep[j]) ? sc[j] * sc[j] : 0.f;
-          }
-          const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
-                            pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
-#pragma unroll
-          for (int i = 0; i < NDT - 1; ++i) {
-            const u32x4 bv = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * i + r) * CF::LDT + 32 * s + 8 * g]);
-            o[i] = mfma(bv, pf, o[i]);
-          }
-          if constexpr (!G) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) den = dot2_bf16(pf[i], kOnesBf16x2, den);
+          for (int I = 0; I < 2; ++I) {
+            const u32x4 zr = *reinterpret_cast<const u32x4*>(&sm.Zb[(16 * I + r) * ZB_LD + 8 * g]);
+            const f32x4 e4 = mfma(zr, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+            const float4 qa = *reinterpret_cast<const float4*>(&sm.Qf[(16 * QT + r) * CF::QF_LD + 16 * I + 4 * g]);
+            den = __builtin_fmaf(qa.x, e4[0], den);
+            den = __builtin_fmaf(qa.y, e4[1], den);
+            den = __builtin_fmaf(qa.z, e4[2], den);
+            den = __builtin_fmaf(qa.w, e4[3], den);
           }
         }
+        __syncthreads();  // intra-chunk terms in place; every wave done with the chunk, Sb and Zb
+        // the intra-chunk term a state wave formed for this query tile (same
+        // lane layout as o)
+#pragma unroll
+        for (int i = 0; i < NDT - 1; ++i) o[i] += *reinterpret_cast<const f32x4*>(&sm.Xo[QT][(64 * i + lane) * 4]);
         float inv = 1.f;  // the gated read has no denominator
         if constexpr (!G) {
+          den += sm.Xd[QT][lane];
           // the four 16-lane rows hold parts of the query's denominator
           const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(den), __float_as_uint(den), false, false);
           const float d2 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
@@ -2093,15 +2194,18 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
           __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, dst,
                                                  (16 * QT + row) * (2 * DV) + 16 * (lane & 7), 0, 0);
         }
-        __syncthreads();  // every wave done with the chunk and the state copy
         if (more) st.store(sm, tid);
-        __syncthreads();
+        __syncthreads();  // next chunk, state copy and Gram copy in place
       }
     } else {
       // ---------------------------------------------------------------- state wave
       constexpr int U = W - 4;
       constexpr int MT = Ws32State<U>::MT;
       constexpr bool GRAM = Ws32State<U>::GRAM && !G;
+      constexpr int QI = Ws32State<U>::QI;
+      bool keep[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) keep[j] = 4 * g + j <= r;
       f32x4 acc[MT][NDT - 1];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -2167,6 +2271,55 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
         if constexpr (G) {
           if (more) gs.load(src(c0 + C), tid - 256);
         }
+        {
+          // intra-chunk term of query tile QI: squared causal scores times V,
+          // and (ungated) each lane's part of their sum, for the readout wave
+          // of that tile
+          const u32x4 qf = score_operand<CF>(sm.Qf, 16 * QI + r, g);
+          float bq = 0.f;  // gated read: beta_q / 2
+          if constexpr (G) bq = sm.gbs[16 * QI + r];
+          f32x4 o[NDT - 1];
+#pragma unroll
+          for (int i = 0; i < NDT - 1; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+          float den = 0.f;
+#pragma unroll
+          for (int s = 0; s <= QI / 2; ++s) {
+            float p[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int kt = 2 * s + h;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) p[h][j] = 0.f;
+              if (kt > QI) continue;
+              const u32x4 kf = *reinterpret_cast<const u32x4*>(&sm.Kb[(16 * kt + r) * CF::KB_LD + 8 * g]);
+              f32x4 sc = mfma(kf, qf, f32x4{0.f, 0.f, 0.f, 0.f});
+              if constexpr (G) {
+                // p = sc^2 2^(beta_q - beta_k): the root of the weight into sc
+                const float4 bk = *reinterpret_cast<const float4*>(&sm.gbs[16 * kt + 4 * g]);
+                sc[0] *= __builtin_amdgcn_exp2f(bq - bk.x);
+                sc[1] *= __builtin_amdgcn_exp2f(bq - bk.y);
+                sc[2] *= __builtin_amdgcn_exp2f(bq - bk.z);
+                sc[3] *= __builtin_amdgcn_exp2f(bq - bk.w);
+              }
+#pragma unroll
+              for (int j = 0; j < 4; ++j) p[h][j] = (kt < QI || keep[j]) ? sc[j] * sc[j] : 0.f;
+            }
+            const u32x4 pf = {pack2(p[0][0], p[0][1]), pack2(p[0][2], p[0][3]),
+                              pack2(p[1][0], p[1][1]), pack2(p[1][2], p[1][3])};
+#pragma unroll
+            for (int i = 0; i < NDT - 1; ++i) {
+              const u32x4 bv = *reinterpret_cast<const u32x4*>(&sm.Vt[(16 * i + r) * CF::LDT + 32 * s + 8 * g]);
+              o[i] = mfma(bv, pf, o[i]);
+            }
+            if constexpr (!G) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) den = dot2_bf16(pf[i], kOnesBf16x2, den);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < NDT - 1; ++i) *reinterpret_cast<f32x4*>(&sm.Xo[QI][(64 * i + lane) * 4]) = o[i];
+          if constexpr (!G) sm.Xd[QI][lane] = den;
+        }
         if (more) {
           // carry the state across the chunk: phi_k(K_c)^T V_c and K_c^T K_c
           // (gated: the state decays by 2^beta_C first)
@@ -2206,12 +2359,12 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
             ws32_key_tiles<U>(acc, x, bv, r, std::make_integer_sequence<int, MT>{});
           }
         }
-        __syncthreads();  // every wave done with the chunk and the state copy
+        __syncthreads();  // intra-chunk terms in place; every wave done with the chunk, Sb and Zb
         if (more) {
           publish();
           if constexpr (G) gs.store(sm, tid - 256);
         }
-        __syncthreads();
+        __syncthreads();  // next chunk, state copy and Gram copy in place
       }
     }
   });
