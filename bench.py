@@ -242,8 +242,37 @@ def bench_forward(args, hip, am, ki, torch):
     return w, inp, results
 
 
+def _interleaved_ms(args, hip, torch, calls):
+    """Median milliseconds per call of each named callable: after `warmup`
+    calls of each, `repeats` rounds each time `steps` back-to-back calls of
+    every callable (HIP events on the current stream), the order rotated per
+    round so no variant always runs first."""
+    stream = torch.cuda.current_stream().cuda_stream
+    names = list(calls)
+    for f in calls.values():
+        for _ in range(args.warmup):
+            f()
+    torch.cuda.synchronize()
+    samples = {n: [] for n in names}
+    for r in range(args.repeats):
+        shift = r % len(names)
+        for n in names[shift:] + names[:shift]:
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(args.steps):
+                calls[n]()
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            samples[n].append(hip.ms(e0, e1) / args.steps)
+            hip.destroy(e0)
+            hip.destroy(e1)
+    return {n: (statistics.median(x), x) for n, x in samples.items()}
+
+
 def bench_other_workloads(args, hip, am, ki, torch):
-    """The other forward workloads (parity-test shapes), library default plan."""
+    """The other forward workloads (parity-test shapes), library default plan,
+    timed interleaved with the quadratic form and (d = 16) the plan that forms
+    the prefix in the readout."""
     res = {}
     for w in (ki.MEDIUM, ki.WIDE, ki.TINY):
         inp = ki.workload_inputs(w)
@@ -255,19 +284,16 @@ def bench_other_workloads(args, hip, am, ki, torch):
         out = torch.empty((w.B, w.H, w.T, w.dv), dtype=q.dtype, device="cuda")
         ws_bytes = am.kata_forward_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, w.chunk, "auto")
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-        stream = torch.cuda.current_stream().cuda_stream
-        for _ in range(args.warmup):
-            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, out=out, workspace=ws)
-        torch.cuda.synchronize()
-        e0, e1 = hip.event(), hip.event()
-        hip.record(e0, stream)
-        for _ in range(args.steps):
-            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, out=out, workspace=ws)
-        hip.record(e1, stream)
-        torch.cuda.synchronize()
-        ms = hip.ms(e0, e1) / args.steps
-        hip.destroy(e0)
-        hip.destroy(e1)
+        calls = {"chunked": lambda: am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, out=out, workspace=ws)}
+        quad = w.dtype == ki.BF16 and w.dv == 64
+        rc = w.dtype == ki.BF16 and w.d == 16 and w.dv == 64
+        if quad:
+            calls["quadratic"] = lambda: am.kata_forward_quadratic(q, k, v, eps=w.eps, g=w.g, out=out)
+        if rc:
+            # the prefix formed inside the readout workgroups (one launch, no workspace)
+            calls["recompute"] = lambda: am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan="recompute", out=out)
+        t = _interleaved_ms(args, hip, torch, calls)
+        ms = t["chunked"][0]
         D = w.d * (w.d + 1) // 2
         BHT = w.B * w.H * w.T
         es = 2 if w.dtype == ki.BF16 else 4
@@ -275,6 +301,7 @@ def bench_other_workloads(args, hip, am, ki, torch):
         bytes_ = (es * (2 * w.d + w.dv) + es * w.dv) * BHT
         res[w.name] = {
             "ms_per_step": round(ms, 4),
+            "ms_per_step_samples": [round(x, 5) for x in t["chunked"][1]],
             "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
             "useful_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -283,22 +310,15 @@ def bench_other_workloads(args, hip, am, ki, torch):
             "plan": am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk,
                                          am.KATA_BF16 if w.dtype == ki.BF16 else am.KATA_F32, "auto"),
         }
-        if w.dtype == ki.BF16 and w.dv == 64:
-            res[w.name]["quadratic"] = bench_quadratic(args, hip, am, torch, w, q, k, v, out)
-        if w.dtype == ki.BF16 and w.d == 16 and w.dv == 64:
-            # the prefix formed inside the readout workgroups (one launch, no workspace)
-            for _ in range(args.warmup):
-                am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan="recompute", out=out)
-            torch.cuda.synchronize()
-            e0, e1 = hip.event(), hip.event()
-            hip.record(e0, stream)
-            for _ in range(args.steps):
-                am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan="recompute", out=out)
-            hip.record(e1, stream)
-            torch.cuda.synchronize()
-            rms = hip.ms(e0, e1) / args.steps
-            hip.destroy(e0)
-            hip.destroy(e1)
+        if quad:
+            qms = t["quadratic"][0]
+            qflops = 2 * (w.T + 1) / 2 * (w.d + w.dv) * w.B * w.H * w.T
+            res[w.name]["quadratic"] = {
+                "ms_per_step": round(qms, 4), "tokens_per_s": round(w.B * w.T / (qms * 1e-3), 1),
+                "useful_tflops": round(qflops / (qms * 1e-3) / 1e12, 2),
+                "mfma_frac": round(qflops / (qms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        if rc:
+            rms = t["recompute"][0]
             res[w.name]["recompute"] = {
                 "ms_per_step": round(rms, 4),
                 "tokens_per_s": round(w.B * w.T / (rms * 1e-3), 1),
@@ -722,7 +742,8 @@ def main():
                               flop_per_tok * BHT / (BF16_PEAK_TFLOPS * 1e12))
                           / (main_r["ms_per_step"] * 1e-3), 4)},
         "timing": f"median over {args.repeats} regions of exactly {args.steps} forwards each, the three "
-                  "prefix variants interleaved (rotating order), HIP events on the library's stream",
+                  "prefix variants interleaved (rotating order), HIP events on the library's stream; "
+                  "other_workloads the same way, each workload's plans interleaved",
         "scan_variants": {s: {"tokens_per_s": round(fwd[s]["tokens_per_s"], 1),
                               "ms_per_step": round(fwd[s]["ms_per_step"], 4),
                               "ms_per_step_samples": fwd[s]["ms_per_step_samples"],
