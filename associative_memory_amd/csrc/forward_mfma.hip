@@ -884,6 +884,18 @@ __host__ __device__ constexpr bool sb_col_unused(int c) {
     return c >= 16 * CF::NFT;
   }
 }
+// d = 16: the unused columns are 128 + 8 i + 4 + m (i, m = 0..3), the
+// positions the DMA readout zeroes directly
+constexpr bool sb_unused16_ok() {
+  int n = 0;
+  for (int c = 0; c < Schedule<16>::NPOS; ++c) {
+    const bool listed = c >= 128 && (c & 4) != 0;
+    if (sb_col_unused<Cfg<16, 64>>(c) != listed) return false;
+    n += listed;
+  }
+  return n == 16;
+}
+static_assert(sb_unused16_ok(), "unused state-copy columns at d = 16");
 
 // bf16 copy of the owned state tiles into Sb[value row][feature position]
 // (ND: value tiles copied; the d = 16 DMA readout keeps no z column in Sb.
@@ -2734,11 +2746,6 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   const int64_t bh = span.bh, sp = span.sp;
   const int64_t tok0 = bh * a.T;
 
-  // feature positions no tile writes hold no feature: zero once
-  for (int e = tid; e < DV * CF::NPOS; e += CF::NT) {
-    const int c = e % CF::NPOS;
-    if (sb_col_unused<CF>(c)) Sb[(e / CF::NPOS) * SB_LD + c] = 0;
-  }
   with_wave<CF::NW>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
     // output stores a wave issues per chunk: two 1 KB stores per query tile,
@@ -2746,10 +2753,24 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     constexpr int NSTORE = (CF::STAGE_OUT ? 2 : NDT - 1) * CF::NSLOT;
     const ReadoutLane<CF> L = readout_lane<CF>(W, lane);
     const TrOffsets to = tr_offsets(lane);
+    const int64_t first = span_first_chunk(a, sp) * C;
+    int64_t end = span_first_chunk(a, sp + 1) * C;
+    if (end > a.T) end = a.T;
+    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb, a.gk); };
+    const int64_t start = (RC && !DEEP) ? 0 : first;
+    // the first chunk's transfer goes out before the prefix state is read,
+    // so the two HBM latencies overlap (the warm-up of DEEP issues its own)
+    if constexpr (!DEEP) dma_chunkq16<C, W, CF::NW, G>(x0, src(start), lane);
     f32x4 acc[CF::MFT][NDT];
     const float* prefix =
         (!RC && a.n_spans > 1) ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
     load_state<CF>(acc, prefix, W, lane);
+    // feature positions no tile writes hold no feature: zero once (the 16
+    // positions of tile 8 in lane groups 2 and 3, below)
+    for (int e = tid; e < DV * 16; e += CF::NT) {
+      const int j = e & 15;
+      Sb[(e >> 4) * SB_LD + 128 + 8 * (j >> 2) + 4 + (j & 3)] = 0;
+    }
     // the d = 16 span sums store the value tiles at kSpanValueScale
 #pragma unroll
     for (int m = 0; m < CF::MFT; ++m) {
@@ -2762,12 +2783,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
       gram = load_gram16<CF>(prefix, lane);
       write_gram16(Zb, gram, lane);
     }
-    const int64_t first = span_first_chunk(a, sp) * C;
-    int64_t end = span_first_chunk(a, sp + 1) * C;
-    if (end > a.T) end = a.T;
-    auto src = [&](int64_t c) { return chunk_src<DK, C>(a.q, a.k, a.v, tok0, c, end, a.gb, a.gk); };
-    const int64_t start = (RC && !DEEP) ? 0 : first;
-    bool staged = false;  // chunk `first` already in x0
+    bool staged = !DEEP;  // chunk `start` already on its way into x0
     if constexpr (DEEP) {
       // The chunks before the span, three buffers deep: step i waits for its
       // own share of chunk i, meets the other waves at a barrier (after which
@@ -2814,8 +2830,8 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
         staged = true;
       }
     }
-    if (!staged) {
-      dma_chunkq16<C, W, CF::NW, G>(x0, src(start), lane);
+    if (!DEEP || !staged) {
+      if (!staged) dma_chunkq16<C, W, CF::NW, G>(x0, src(start), lane);
       // the state loads and the first chunk; an unconditional vmcnt(0) also
       // retires the state loads for the compiler's wait-count analysis
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
