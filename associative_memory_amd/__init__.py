@@ -25,11 +25,12 @@ KATA_SCAN_AUTO = 0
 KATA_SCAN_SEQUENTIAL = 1
 KATA_SCAN_ASSOCIATIVE = 2
 KATA_SCAN_RECOMPUTE = 3
+KATA_SCAN_FUSED = 4
 KATA_OK = 0
 
 _SCANS = {"auto": KATA_SCAN_AUTO, "sequential": KATA_SCAN_SEQUENTIAL, "seq": KATA_SCAN_SEQUENTIAL,
           "associative": KATA_SCAN_ASSOCIATIVE, "assoc": KATA_SCAN_ASSOCIATIVE,
-          "recompute": KATA_SCAN_RECOMPUTE}
+          "recompute": KATA_SCAN_RECOMPUTE, "fused": KATA_SCAN_FUSED}
 
 EXPORTED = (
     "kata_status_string",

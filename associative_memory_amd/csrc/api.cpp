@@ -40,11 +40,13 @@ kata_status_t check_forward_shape(int B, int H, int64_t T, int d, int dv, int ch
                                   kata_dtype_t dtype, kata_scan_t scan) {
   if (B <= 0 || H <= 0 || T <= 0) return KATA_ERR_INVALID_VALUE;
   if (scan != KATA_SCAN_AUTO && scan != KATA_SCAN_SEQUENTIAL && scan != KATA_SCAN_ASSOCIATIVE &&
-      scan != KATA_SCAN_RECOMPUTE)
+      scan != KATA_SCAN_RECOMPUTE && scan != KATA_SCAN_FUSED)
     return KATA_ERR_INVALID_VALUE;
   if (!dtype_ok(dtype)) return KATA_ERR_INVALID_VALUE;
   if (!head_dim_ok(d) || !value_dim_ok(dv) || !chunk_ok(chunk)) return KATA_ERR_UNSUPPORTED;
   if (scan == KATA_SCAN_RECOMPUTE && !kata::recompute_supported(dtype == KATA_BF16, d, dv, chunk))
+    return KATA_ERR_UNSUPPORTED;
+  if (scan == KATA_SCAN_FUSED && !kata::fused_supported(dtype == KATA_BF16, d, dv, chunk))
     return KATA_ERR_UNSUPPORTED;
   // every element index must fit comfortably in int64 and every grid in 2^31
   const int64_t BH = static_cast<int64_t>(B) * H;

@@ -844,6 +844,33 @@ __device__ __forceinline__ void load_state(f32x4 (&acc)[CF::MFT][NDT], const flo
   }
 }
 
+// The value tiles of the wave's feature tiles summed over the n span sums at
+// P0, P0 + E, ... in span order: the sums the sequential prefix forms, bit
+// for bit (the z column is not read)
+template <class CF>
+__device__ __forceinline__ void sum_states(f32x4 (&acc)[CF::MFT][NDT], const float* __restrict__ P0,
+                                           int64_t n, int w, int lane) {
+#pragma unroll
+  for (int m = 0; m < CF::MFT; ++m) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[m][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll 2
+  for (int64_t s = 0; s < n; ++s) {
+    const float* P = P0 + s * mfma_state_floats(CF::DK);
+#pragma unroll
+    for (int m = 0; m < CF::MFT; ++m) {
+      const int ft = w + CF::NW * m;
+      if (ft >= CF::NFT) continue;
+#pragma unroll
+      for (int dt = 0; dt < NDT - 1; ++dt) {
+        const float4 x = *reinterpret_cast<const float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4);
+        acc[m][dt] += f32x4{x.x, x.y, x.z, x.w};
+      }
+    }
+  }
+}
+
 // (WITH_Z false: the z column is written elsewhere)
 template <class CF, bool WITH_Z = true>
 __device__ __forceinline__ void store_state(const f32x4 (&acc)[CF::MFT][NDT], float* __restrict__ P,
@@ -1175,6 +1202,15 @@ __device__ inline SpanOf readout_span(const MfmaArgs& a) {
   const int64_t odd = b >= half ? 1 : 0;
   const int64_t r = b - odd * half;
   return {r / per, 2 * (r % per) + odd};
+}
+
+// Span of a readout workgroup that adds the span sums before its span
+// (a.fused): consecutive blocks are different heads, so with a multiple of 8
+// heads every span of a head runs on one XCD and the head's span sums, read
+// by each of its later spans, stay in that XCD's L2.
+__device__ inline SpanOf fused_span(const MfmaArgs& a) {
+  const int64_t b = blockIdx.x;
+  return {b % a.BH, b / a.BH};
 }
 
 // Span of a span-sum workgroup: spans 0 .. n_spans - 2 of every head (the
@@ -2678,6 +2714,29 @@ __device__ __forceinline__ f32x4 load_gram16(const float* __restrict__ P, int la
   return z;
 }
 
+// load_gram16 of the sum of the n span sums at P0, P0 + E, ... (summed in
+// span order, then halved, as the sequential prefix and load_gram16 do)
+template <class CF>
+__device__ __forceinline__ f32x4 sum_gram16(const float* __restrict__ P0, int64_t n, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  int off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * g + i, j = (r - row) & 15;
+    off[i] = CF::ZOFF + (j <= 8 ? 16 * j + row : 16 * (16 - j) + r);
+  }
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int64_t s = 0; s < n; ++s) {
+    const float* P = P0 + s * mfma_state_floats(CF::DK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] += P[off[i]];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] *= 0.5f;
+  return z;
+}
+
 // bf16 copy of Z, row-major with the 16-byte pieces of row r swizzled by
 // ksw16(r): lane (g, r) holds Z[4g + i][r] = Z[r][4g + i]
 __device__ __forceinline__ void write_gram16(uint16_t* __restrict__ zb, const f32x4& z, int lane) {
@@ -2724,12 +2783,14 @@ __device__ inline SpanOf recompute_span(const MfmaArgs& a) {
 // only, nothing read out), then reads out its span as usual.  The exclusive
 // prefix of Eqs. 17-20 is then summed chunk by chunk in one workgroup, with
 // no span-sum or prefix launch; every span of a head repeats that sum.
-template <int C, bool G, bool RC = false>
+// FP (a.fused): the span sums of the spans before this one are stored
+// unscanned; the workgroup adds them in span order in its prologue.
+template <int C, bool G, bool RC = false, bool FP = false>
 __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   using CF = Cfg<16, C>;
   constexpr int DK = 16, SB_LD = CF::SB_LD;
   static_assert(CF::NDW == NDT, "whole output rows per wave");
-  static_assert(!(G && RC), "the gated read takes its prefix from the affine scan");
+  static_assert(!(G && RC) && !(G && FP) && !(RC && FP), "one prefix source per readout");
   __shared__ DmaTileQ16<C, G> x0;
   __shared__ DmaTileQ16<C, G> x1;
   // the third buffer of the deep warm-up (prefix formed in the workgroup, chunk 64)
@@ -2742,7 +2803,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   __shared__ alignas(16) uint16_t Ob[CF::STAGE_OUT ? CF::NW : 1][16 * OB_LD];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const SpanOf span = RC ? recompute_span(a) : readout_span(a);
+  const SpanOf span = RC ? recompute_span(a) : FP ? fused_span(a) : readout_span(a);
   const int64_t bh = span.bh, sp = span.sp;
   const int64_t tok0 = bh * a.T;
 
@@ -2763,8 +2824,13 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     if constexpr (!DEEP) dma_chunkq16<C, W, CF::NW, G>(x0, src(start), lane);
     f32x4 acc[CF::MFT][NDT];
     const float* prefix =
-        (!RC && a.n_spans > 1) ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
-    load_state<CF>(acc, prefix, W, lane);
+        (!RC && !FP && a.n_spans > 1) ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
+    const float* sums = FP ? a.ws + bh * a.n_spans * mfma_state_floats(DK) : nullptr;
+    if constexpr (FP) {
+      sum_states<CF>(acc, sums, sp, W, lane);
+    } else {
+      load_state<CF>(acc, prefix, W, lane);
+    }
     // feature positions no tile writes hold no feature: zero once (the 16
     // positions of tile 8 in lane groups 2 and 3, below)
     for (int e = tid; e < DV * 16; e += CF::NT) {
@@ -2780,7 +2846,7 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
     write_sb<CF, NDT - 1, DmaSrc16<C, G>::kHalfDiag>(Sb, acc, W, lane);
     f32x4 gram = {0.f, 0.f, 0.f, 0.f};
     if constexpr (!G && W == 0) {
-      gram = load_gram16<CF>(prefix, lane);
+      gram = FP ? sum_gram16<CF>(sums, sp, lane) : load_gram16<CF>(prefix, lane);
       write_gram16(Zb, gram, lane);
     }
     bool staged = !DEEP;  // chunk `start` already on its way into x0
@@ -2898,9 +2964,9 @@ __device__ __forceinline__ void readout_dma16_body(const MfmaArgs& a) {
   });
 }
 
-template <int C, bool G = false, bool RC = false>
+template <int C, bool G = false, bool RC = false, bool FP = false>
 __global__ __launch_bounds__(256, 2) void readout_dma16_kernel(MfmaArgs a) {
-  readout_dma16_body<C, G, RC>(a);
+  readout_dma16_body<C, G, RC, FP>(a);
 }
 
 template <int DK, int C>
@@ -2922,6 +2988,8 @@ hipError_t launch_readout(const MfmaArgs& a, hipStream_t stream) {
   if constexpr (DK == 16) {
     if (a.recompute) {
       readout_dma16_kernel<C, false, true><<<grid, CF::NT, 0, stream>>>(a);
+    } else if (a.fused) {
+      readout_dma16_kernel<C, false, false, true><<<grid, CF::NT, 0, stream>>>(a);
     } else {
       readout_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
     }

@@ -36,6 +36,14 @@ constexpr int64_t kMinReadoutWorkgroups16 = 256;
 // 18.4 / 22.5; beyond, the recompute loses: B=4 H=8 T=4096 C=128 37.1 / 48.9)
 constexpr int64_t kRecomputeWorkgroups = 512;
 constexpr int64_t kRecomputeMaxPrefixTokens = 1024;
+// prefix added in the readout workgroups from the stored span sums (no
+// prefix launch): the automatic choice at d = 16 up to this many spans per
+// head (measured, step us, sequential / recompute / fused, d = 16 bf16
+// chunk 64: B=4 H=8 T=2048 (8 spans) 26.8 / 26.2 / 22.6, B=8 H=8 T=2048
+// 33.6 / 28.7 / 27.3, B=4 H=8 T=4096 (16 spans) 34.2 / 47.6 / 30.9;
+// B=2 H=8 T=8192 (32 spans) 34.7 / 85.7 / 39.7, B=1 H=8 T=16384 (64)
+// 34.9 / 161.6 / 57.6)
+constexpr int64_t kFusedMaxSpans = 16;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -88,16 +96,20 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.G = ceil_div(p.n_chunks, spans);
   if (ceil_div(p.n_chunks, p.G) > kMaxSpans) p.G = ceil_div(p.n_chunks, kMaxSpans);
   p.n_spans = ceil_div(p.n_chunks, p.G);
-  if (mfma && d == 16 && p.n_spans % 2 == 0 && p.n_chunks == p.n_spans * p.G &&
-      p.G >= kPairSkewDiv && p.n_spans * p.BH == mfma_target_workgroups(d))
-    p.GL = p.G + p.G / kPairSkewDiv;
-
   if (scan == KATA_SCAN_AUTO) {
     // measured on MI355X at 9,360-float span states (prefix stage, us,
     // sequential / associative): 8 heads x 64 spans 11.2 / 11.7, 4 x 128
     // 12.7 / 12.4, 1 x 512 29.8 / 19.6; d = 32, 32 x 8 spans 14.4 / 15.1
-    scan = p.n_spans >= 128 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;
+    if (p.n_spans > 1 && p.n_spans <= kFusedMaxSpans && g == 1 && fused_supported(p.bf16, d, dv, chunk)) {
+      scan = KATA_SCAN_FUSED;
+    } else {
+      scan = p.n_spans >= 128 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;
+    }
   }
+  // (the fused prefix maps spans to workgroups by head, without pairs)
+  if (mfma && d == 16 && p.n_spans % 2 == 0 && p.n_chunks == p.n_spans * p.G &&
+      p.G >= kPairSkewDiv && p.n_spans * p.BH == mfma_target_workgroups(d) && scan != KATA_SCAN_FUSED)
+    p.GL = p.G + p.G / kPairSkewDiv;
   p.scan = scan;
   p.wg_output = p.BH * p.n_spans * tiles;
   if (p.n_spans > 1) {
@@ -119,6 +131,7 @@ void describe_plan(const ForwardPlan& p, char* buf, size_t len) {
                 p.path == Path::Mfma ? "mfma" : "valu",
                 p.scan == KATA_SCAN_ASSOCIATIVE ? "associative"
                 : p.scan == KATA_SCAN_RECOMPUTE ? "recompute"
+                : p.scan == KATA_SCAN_FUSED     ? "fused"
                                                 : "sequential",
                 p.D, p.chunk,
                 static_cast<long long>(p.n_chunks), static_cast<long long>(p.G),
@@ -199,10 +212,11 @@ hipError_t run_forward(const ForwardPlan& p, const void* q, const void* k, const
     m.n_spans = p.n_spans;
     m.eps = eps;
     m.recompute = p.scan == KATA_SCAN_RECOMPUTE;
+    m.fused = p.scan == KATA_SCAN_FUSED;
     if (p.n_spans > 1 && !m.recompute) KATA_TRY(launch_span_state_mfma(m, stream));
     KATA_TRY(mark(ev, false, 0, stream));
     KATA_TRY(mark(ev, true, 1, stream));
-    if (p.n_spans > 1 && !m.recompute) {
+    if (p.n_spans > 1 && !m.recompute && !m.fused) {
       KATA_TRY((p.scan == KATA_SCAN_ASSOCIATIVE)
                    ? launch_scan_associative(ws, p.BH, p.n_spans, p.E, stream)
                    : launch_scan_sequential(ws, p.BH, p.n_spans, p.E, stream));

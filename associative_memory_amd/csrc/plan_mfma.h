@@ -49,6 +49,9 @@ struct MfmaArgs {
   // d = 16, ungated: each readout workgroup forms its span's prefix from the
   // head's earlier chunks (no span sums, no prefix, no workspace)
   bool recompute = false;
+  // d = 16, ungated: the readout workgroup of span j adds the stored span
+  // sums of spans 0 .. j - 1 itself (no prefix launch)
+  bool fused = false;
 };
 
 struct QuadArgs {
@@ -118,6 +121,11 @@ inline bool mfma_supported(bool bf16, int d, int dv, int chunk) {
 
 // readout workgroups that form their span's prefix themselves (KATA_SCAN_RECOMPUTE)
 inline bool recompute_supported(bool bf16, int d, int dv, int chunk) {
+  return mfma_supported(bf16, d, dv, chunk) && d == 16;
+}
+
+// readout workgroups that add the stored span sums before their span (KATA_SCAN_FUSED)
+inline bool fused_supported(bool bf16, int d, int dv, int chunk) {
   return mfma_supported(bf16, d, dv, chunk) && d == 16;
 }
 

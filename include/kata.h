@@ -56,9 +56,14 @@ typedef enum KATA_ENUM_BASE {
   KATA_SCAN_AUTO = 0,        /* library picks (measured default per shape) */
   KATA_SCAN_SEQUENTIAL = 1,  /* linear-depth pass over chunk states */
   KATA_SCAN_ASSOCIATIVE = 2, /* log-depth parallel scan over chunk states */
-  KATA_SCAN_RECOMPUTE = 3    /* no prefix pass: each readout workgroup sums the chunk
+  KATA_SCAN_RECOMPUTE = 3,   /* no prefix pass: each readout workgroup sums the chunk
                                 states before its span itself (kata_forward_chunked,
                                 bf16, d = 16, dv = 64 only; no workspace) */
+  KATA_SCAN_FUSED = 4        /* no prefix pass: the span sums are stored as by the
+                                sequential pass and each readout workgroup adds
+                                those of the spans before its own, in span order
+                                (the sequential pass's sums, bit for bit);
+                                kata_forward_chunked, bf16, d = 16, dv = 64 only */
 } kata_scan_t;
 
 typedef enum KATA_ENUM_BASE {

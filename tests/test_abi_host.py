@@ -97,6 +97,9 @@ def fwd(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=64, d=16, dv=16, C=32, eps
     # the prefix formed in the readout (scan 3): bf16, d = 16, dv = 64, chunk 64 / 128 only
     (dict(scan=3), UNSUPPORTED), (dict(scan=3, dv=64, dt=F32), UNSUPPORTED),
     (dict(scan=3, d=32, dv=64, C=64), UNSUPPORTED), (dict(scan=3, dv=64, C=32), UNSUPPORTED),
+    # the prefix added in the readout from stored span sums (scan 4): the same shapes
+    (dict(scan=4), UNSUPPORTED), (dict(scan=4, dv=64, dt=F32), UNSUPPORTED),
+    (dict(scan=4, d=32, dv=64, C=64), UNSUPPORTED), (dict(scan=4, dv=64, C=32), UNSUPPORTED),
     (dict(q=ctypes.c_void_p(P[0].value + 4)), INVALID),     # misaligned
     (dict(out=P[0]), INVALID),                                # out aliases q
     (dict(out=ctypes.c_void_p(P[2].value + 16)), INVALID),   # out overlaps v
@@ -364,3 +367,29 @@ def test_recompute_plan():
     # the other forwards take no scan 3
     assert L.kata_forward_workspace_bytes(1, 1, 64, 32, 64, 64, 3) == 0
     assert L.kata_forward_chunked_blocks_workspace_bytes(1, 1, 64, 64, 64, 4, 64, 3) == 0
+
+
+def test_fused_plan():
+    """Scan 4: span sums stored unscanned, no prefix launch, the workspace of
+    the sequential plan; the automatic choice at d = 16 up to 16 spans per
+    head, without paired spans."""
+    L = am.lib()
+    for (B, H, T, C) in [(4, 8, 2048, 64), (4, 8, 2048, 128), (4, 8, 4096, 64), (8, 8, 2048, 64)]:
+        plan = am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "auto")
+        f = dict(kv.split("=") for kv in plan.split())
+        assert f["scan"] == "fused" and f["paired_even_span"] == "0", plan
+        assert 1 < int(f["n_spans"]) <= 16
+        assert int(f["wg_state"]) == B * H * (int(f["n_spans"]) - 1)
+        assert L.kata_forward_workspace_bytes(B, H, T, 16, 64, C, 0) == \
+            L.kata_forward_workspace_bytes(B, H, T, 16, 64, C, 1) == \
+            L.kata_forward_workspace_bytes(B, H, T, 16, 64, C, 4) > 0
+    for (B, H, T, C) in [(1, 8, 131072, 128), (2, 8, 8192, 64)]:
+        auto = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "auto").split())
+        assert auto["scan"] == "sequential" and int(auto["n_spans"]) > 16
+        fused = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "fused").split())
+        assert fused["scan"] == "fused" and fused["paired_even_span"] == "0"
+        assert fused["n_spans"] == auto["n_spans"] and fused["workspace_bytes"] == auto["workspace_bytes"]
+    # d = 32, fp32 and the block maps keep their prefix launch
+    assert "scan=sequential" in am.kata_forward_plan(2, 16, 8192, 32, 64, 64, BF16, "auto")
+    assert "scan=fused" not in am.kata_forward_plan(4, 8, 2048, 16, 64, 64, F32, "auto")
+    assert L.kata_forward_chunked_blocks_workspace_bytes(1, 1, 64, 64, 64, 4, 64, 4) == 0

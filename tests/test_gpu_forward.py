@@ -371,3 +371,51 @@ def test_recompute_prefix(case):
     else:
         ref = orc.forward_chunked(inp.q64, inp.k64, inp.v64, chunk, 1e-6)
     check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"recompute {case}")
+
+
+FUSED_CASES = [
+    # (B, H, T, chunk), d = 16, dv = 64, bf16: the T = 2048 workload at both
+    # chunk sizes (the automatic plan there), ragged spans and last chunks,
+    # head counts that are not a multiple of the 8 XCDs, many spans per head
+    # (the latest workgroup adds 63 span sums), one token, one span per head
+    (4, 8, 2048, 64),
+    (4, 8, 2048, 128),
+    (2, 3, 1000, 64),
+    (3, 5, 2500, 128),
+    (1, 1, 5000, 128),
+    (2, 2, 8191, 64),
+    (1, 3, 40000, 128),
+    (1, 1, 1, 64),
+    (7, 9, 65, 64),
+    (40, 16, 300, 64),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B{}H{}T{}C{}".format(*c))
+def test_fused_prefix(case):
+    """Prefix added in the readout from the stored span sums: every output
+    against the oracle, guard bands around the output, run-to-run bitwise
+    determinism, and the same bits as the sequential prefix whenever the two
+    plans cut the same spans (the sums are added in the same order)."""
+    B, H, T, chunk = case
+    d, dv = 16, 64
+    plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, "fused")
+    seq_plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, "sequential")
+    say(f"forward fused {case} plan: {plan}")
+    assert "scan=fused" in plan and "paired_even_span=0" in plan
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.BF16, seed=T + 13 * chunk)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    buf, out = guarded((B, H, T, dv), torch.bfloat16)
+    am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="fused", out=out)
+    again = am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="fused")
+    seq = am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="sequential")
+    torch.cuda.synchronize()
+    assert_guards(buf, f"out {case}")
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "run-to-run bits"
+    if plan.replace("scan=fused", "") == seq_plan.replace("scan=sequential", ""):
+        assert torch.equal(out.view(torch.int16), seq.view(torch.int16)), "fused vs sequential bits"
+    if T <= 9000:
+        ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6)
+    else:
+        ref = orc.forward_chunked(inp.q64, inp.k64, inp.v64, chunk, 1e-6)
+    check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"fused {case}")
