@@ -2109,21 +2109,28 @@ struct Ws32State {
 // by 2^(beta_q - beta_k) and keep no denominator; the state waves decay the
 // state by 2^beta_C per chunk and scale the keys by 2^((beta_C - beta_t) / 2);
 // there is no Gram matrix.
-template <bool G = false>
+// FP (a.fused): the span sums are stored unscanned and the state waves add
+// those of the spans before this one in span order (blocks mapped to spans
+// by head first, as for the d = 16 readout).
+template <bool G = false, bool FP = false>
 __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
+  static_assert(!(G && FP), "the gated read takes its prefix from the affine scan");
   using CF = CfgWs32;
   constexpr int C = 64, DK = 32, NT = 512;
   __shared__ SmemWs32 sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int g = lane >> 4, r = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t bh = blockIdx.x / a.n_spans;
-  const int64_t sp = blockIdx.x - bh * a.n_spans;
+  const SpanOf span = FP ? fused_span(a) : SpanOf{blockIdx.x / a.n_spans, blockIdx.x % a.n_spans};
+  const int64_t bh = span.bh, sp = span.sp;
   const int64_t tok0 = bh * a.T;
   const int64_t first = sp * a.G * C;
   int64_t end = first + a.G * C;
   if (end > a.T) end = a.T;
-  const float* prefix = a.n_spans > 1 ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
+  const float* prefix =
+      (!FP && a.n_spans > 1) ? a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK) : nullptr;
+  // FP: the head's span sums, sp of them before this span
+  const float* sums = FP ? a.ws + bh * a.n_spans * mfma_state_floats(DK) : nullptr;
 
   // feature positions no tile writes hold no feature (tile 33: lane groups
   // 2 and 3 of the last k-step): zero once
@@ -2268,6 +2275,27 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
           }
         }
       }
+      if constexpr (FP) {
+        // the prefix the sequential pass would form, summed in span order
+#pragma unroll 2
+        for (int64_t s = 0; s < sp; ++s) {
+          const float* P = sums + s * mfma_state_floats(DK);
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const int ft = U + 4 * m;
+#pragma unroll
+            for (int dt = 0; dt < NDT - 1; ++dt) {
+              const float4 x = *reinterpret_cast<const float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4);
+              acc[m][dt] += f32x4{x.x, x.y, x.z, x.w};
+            }
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+#pragma unroll
+          for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] *= 0.5f;
+        }
+      }
       // Gram tiles (I, J): lane (g, r) holds Z[16 I + 4 g + i][16 J + r]; from
       // the prefix's z column, 2 Z[a][b] on the position of (a, b)
       f32x4 zt[GRAM ? 4 : 1];
@@ -2278,7 +2306,14 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int ra = 16 * I + 4 * g + i, cb = 16 * J + r;
-            zt[t][i] = prefix != nullptr ? 0.5f * prefix[CF::ZOFF + kPairPos32.p[ra][cb]] : 0.f;
+            const int off = CF::ZOFF + kPairPos32.p[ra][cb];
+            if constexpr (FP) {
+              float z = 0.f;
+              for (int64_t s = 0; s < sp; ++s) z += sums[s * mfma_state_floats(DK) + off];
+              zt[t][i] = 0.5f * z;
+            } else {
+              zt[t][i] = prefix != nullptr ? 0.5f * prefix[off] : 0.f;
+            }
           }
         }
       }
@@ -2418,9 +2453,9 @@ __device__ __forceinline__ void readout_ws32(const MfmaArgs& a) {
   });
 }
 
-template <bool G = false>
+template <bool G = false, bool FP = false>
 __global__ __launch_bounds__(512, 2) void readout_ws32_kernel(MfmaArgs a) {
-  readout_ws32<G>(a);
+  readout_ws32<G, FP>(a);
 }
 
 
@@ -3073,7 +3108,11 @@ hipError_t launch_readout_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 16 && a.chunk == 64) return launch_readout<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_readout<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) {
-    readout_ws32_kernel<false><<<dim3(static_cast<unsigned>(a.BH * a.n_spans)), 512, 0, stream>>>(a);
+    if (a.fused) {
+      readout_ws32_kernel<false, true><<<dim3(static_cast<unsigned>(a.BH * a.n_spans)), 512, 0, stream>>>(a);
+    } else {
+      readout_ws32_kernel<false><<<dim3(static_cast<unsigned>(a.BH * a.n_spans)), 512, 0, stream>>>(a);
+    }
     return hipGetLastError();
   }
   if (a.d == 32 && a.chunk == 128) return launch_readout<32, 128>(a, stream);

@@ -44,6 +44,11 @@ constexpr int64_t kRecomputeMaxPrefixTokens = 1024;
 // B=2 H=8 T=8192 (32 spans) 34.7 / 85.7 / 39.7, B=1 H=8 T=16384 (64)
 // 34.9 / 161.6 / 57.6)
 constexpr int64_t kFusedMaxSpans = 16;
+// the same at d = 32 (137 KB span states; step us, sequential / fused,
+// B x H x T, chunk 64: 8 x 16 x 2048 (2 spans) 103.4 / 84.9, 8 x 16 x 4096
+// (2) 167.0 / 148.3, 4 x 16 x 2048 (4) 73.3 / 65.7, 4 x 16 x 4096 (4)
+// 106.3 / 98.1; 4 x 8 x 4096 (8) 74.5 / 91.3, 2 x 16 x 8192 (8) 106.9 / 122.7)
+constexpr int64_t kFusedMaxSpans32 = 4;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -100,7 +105,8 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
     // measured on MI355X at 9,360-float span states (prefix stage, us,
     // sequential / associative): 8 heads x 64 spans 11.2 / 11.7, 4 x 128
     // 12.7 / 12.4, 1 x 512 29.8 / 19.6; d = 32, 32 x 8 spans 14.4 / 15.1
-    if (p.n_spans > 1 && p.n_spans <= kFusedMaxSpans && g == 1 && fused_supported(p.bf16, d, dv, chunk)) {
+    if (p.n_spans > 1 && p.n_spans <= (d == 16 ? kFusedMaxSpans : kFusedMaxSpans32) && g == 1 &&
+        fused_supported(p.bf16, d, dv, chunk)) {
       scan = KATA_SCAN_FUSED;
     } else {
       scan = p.n_spans >= 128 ? KATA_SCAN_ASSOCIATIVE : KATA_SCAN_SEQUENTIAL;

@@ -124,9 +124,10 @@ inline bool recompute_supported(bool bf16, int d, int dv, int chunk) {
   return mfma_supported(bf16, d, dv, chunk) && d == 16;
 }
 
-// readout workgroups that add the stored span sums before their span (KATA_SCAN_FUSED)
+// readout workgroups that add the stored span sums before their span
+// (KATA_SCAN_FUSED): the d = 16 readout and the wave-specialised d = 32 one
 inline bool fused_supported(bool bf16, int d, int dv, int chunk) {
-  return mfma_supported(bf16, d, dv, chunk) && d == 16;
+  return mfma_supported(bf16, d, dv, chunk) && (d == 16 || chunk == 64);
 }
 
 // the chunked reads at d = 64: KATA-M4 (g = 4, blocks of 16), KATA-M2 (g = 2,

@@ -63,7 +63,8 @@ typedef enum KATA_ENUM_BASE {
                                 sequential pass and each readout workgroup adds
                                 those of the spans before its own, in span order
                                 (the sequential pass's sums, bit for bit);
-                                kata_forward_chunked, bf16, d = 16, dv = 64 only */
+                                kata_forward_chunked, bf16, dv = 64, d = 16 at
+                                chunk 64 or 128, d = 32 at chunk 64 only */
 } kata_scan_t;
 
 typedef enum KATA_ENUM_BASE {

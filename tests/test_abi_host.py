@@ -99,7 +99,7 @@ def fwd(q=P[0], k=P[1], v=P[2], out=P[3], B=1, H=1, T=64, d=16, dv=16, C=32, eps
     (dict(scan=3, d=32, dv=64, C=64), UNSUPPORTED), (dict(scan=3, dv=64, C=32), UNSUPPORTED),
     # the prefix added in the readout from stored span sums (scan 4): the same shapes
     (dict(scan=4), UNSUPPORTED), (dict(scan=4, dv=64, dt=F32), UNSUPPORTED),
-    (dict(scan=4, d=32, dv=64, C=64), UNSUPPORTED), (dict(scan=4, dv=64, C=32), UNSUPPORTED),
+    (dict(scan=4, d=32, dv=64, C=128), UNSUPPORTED), (dict(scan=4, dv=64, C=32), UNSUPPORTED),
     (dict(q=ctypes.c_void_p(P[0].value + 4)), INVALID),     # misaligned
     (dict(out=P[0]), INVALID),                                # out aliases q
     (dict(out=ctypes.c_void_p(P[2].value + 16)), INVALID),   # out overlaps v
@@ -389,7 +389,12 @@ def test_fused_plan():
         fused = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "fused").split())
         assert fused["scan"] == "fused" and fused["paired_even_span"] == "0"
         assert fused["n_spans"] == auto["n_spans"] and fused["workspace_bytes"] == auto["workspace_bytes"]
-    # d = 32, fp32 and the block maps keep their prefix launch
+    # d = 32 (chunk 64) takes it up to 4 spans per head
+    for (B, H, T, n) in [(8, 16, 2048, 2), (4, 16, 4096, 4)]:
+        f = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 32, 64, 64, BF16, "auto").split())
+        assert f["scan"] == "fused" and f["n_spans"] == str(n)
+    assert "scan=fused" in am.kata_forward_plan(2, 16, 8192, 32, 64, 64, BF16, "fused")
+    # d = 32 at 8 spans per head, fp32 and the block maps keep their prefix launch
     assert "scan=sequential" in am.kata_forward_plan(2, 16, 8192, 32, 64, 64, BF16, "auto")
     assert "scan=fused" not in am.kata_forward_plan(4, 8, 2048, 16, 64, 64, F32, "auto")
     assert L.kata_forward_chunked_blocks_workspace_bytes(1, 1, 64, 64, 64, 4, 64, 4) == 0

@@ -419,3 +419,44 @@ def test_fused_prefix(case):
     else:
         ref = orc.forward_chunked(inp.q64, inp.k64, inp.v64, chunk, 1e-6)
     check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"fused {case}")
+
+
+FUSED32_CASES = [
+    # (B, H, T), d = 32, dv = 64, chunk 64, bf16: 2 and 4 spans per head (the
+    # automatic plan there), the d = 32 workload's 8 spans, ragged spans and a
+    # head count that is not a multiple of 8
+    (8, 16, 2048),
+    (4, 16, 2048),
+    (2, 16, 8192),
+    (3, 5, 2500),
+    (1, 1, 1),
+]
+
+
+@pytest.mark.parametrize("case", FUSED32_CASES, ids=lambda c: "B{}H{}T{}".format(*c))
+def test_fused_prefix_d32(case):
+    """The wave-specialised d = 32 readout with the prefix added from the
+    stored span sums: the sequential prefix's bits (same spans, same order),
+    guard bands, and sampled rows of every head against the oracle."""
+    B, H, T = case
+    d, dv, chunk = 32, 64, 64
+    plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, "fused")
+    say(f"forward fused d=32 {case} plan: {plan}")
+    assert "scan=fused" in plan
+    q, k, v = ki.forward_inputs_torch(B, H, T, d, dv, seed=T + 5, device="cuda")
+    buf, out = guarded((B, H, T, dv), torch.bfloat16)
+    am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="fused", out=out)
+    seq = am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="sequential")
+    torch.cuda.synchronize()
+    assert_guards(buf, f"out {case}")
+    assert torch.equal(out.view(torch.int16), seq.view(torch.int16)), "fused vs sequential bits"
+    g = np.random.Generator(np.random.PCG64(T))
+    vmax = float(v.float().abs().max())
+    refs, gots = [], []
+    for b in range(B):
+        for h in range(H):
+            rows = sorted({0, T - 1} | {int(x) for x in g.integers(0, T, 3)})
+            qh, kh, vh = (to_host64(x[b, h]) for x in (q, k, v))
+            refs.append(orc.forward_rows(qh, kh, vh, rows, 1e-6))
+            gots.append(to_host64(out[b, h, rows]))
+    check(np.concatenate(gots), np.concatenate(refs), ki.BF16, vmax, f"fused d=32 {case} rows")
