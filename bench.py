@@ -269,6 +269,12 @@ def _interleaved_ms(args, hip, torch, calls):
     return {n: (statistics.median(x), x) for n, x in samples.items()}
 
 
+def res_plan(am, ki, w):
+    """The library's plan string for workload w (AUTO prefix)."""
+    return am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk,
+                                am.KATA_BF16 if w.dtype == ki.BF16 else am.KATA_F32, "auto")
+
+
 def bench_other_workloads(args, hip, am, ki, torch):
     """The other forward workloads (parity-test shapes), library default plan,
     timed interleaved with the quadratic form and (d = 16) the plan that forms
@@ -292,6 +298,10 @@ def bench_other_workloads(args, hip, am, ki, torch):
         if rc:
             # the prefix formed inside the readout workgroups (one launch, no workspace)
             calls["recompute"] = lambda: am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan="recompute", out=out)
+        if w.dtype == ki.BF16 and "scan=sequential" not in res_plan(am, ki, w):
+            # the three-launch plan beside the library's choice
+            calls["sequential"] = lambda: am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan="sequential",
+                                                                  out=out, workspace=ws)
         t = _interleaved_ms(args, hip, torch, calls)
         ms = t["chunked"][0]
         D = w.d * (w.d + 1) // 2
@@ -317,6 +327,13 @@ def bench_other_workloads(args, hip, am, ki, torch):
                 "ms_per_step": round(qms, 4), "tokens_per_s": round(w.B * w.T / (qms * 1e-3), 1),
                 "useful_tflops": round(qflops / (qms * 1e-3) / 1e12, 2),
                 "mfma_frac": round(qflops / (qms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        if "sequential" in t:
+            sms = t["sequential"][0]
+            res[w.name]["sequential"] = {
+                "ms_per_step": round(sms, 4),
+                "tokens_per_s": round(w.B * w.T / (sms * 1e-3), 1),
+                "plan": am.kata_forward_plan(w.B, w.H, w.T, w.d, w.dv, w.chunk, am.KATA_BF16, "sequential"),
+            }
         if rc:
             rms = t["recompute"][0]
             res[w.name]["recompute"] = {
