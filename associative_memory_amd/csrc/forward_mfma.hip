@@ -2555,8 +2555,7 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
           for (int dt = 0; dt < NDT - 1; ++dt) acc[m][dt] *= f;
         }
       }
-      // one k-step at a time: interleaving the two would exceed the registers
-#pragma unroll 1
+#pragma unroll
       for (int ks = 0; ks < C / 32; ++ks) {
         u32x4 bv[NDT - 1];
 #pragma unroll
