@@ -225,7 +225,8 @@ def kata_forward_chunked(q, k, v, chunk: int, eps: float = 1e-6, scan="auto", ou
     """Causal normalised read o_t = sum_{s<=t}(q_t.k_s)^2 v_s / (sum + eps).
 
     q, k: [B, H, T, d]; v: [B, H, T, dv]; float32 or bfloat16, contiguous,
-    on the device.  Returns out [B, H, T, dv] (same dtype).
+    on the device.  scan: "auto", "sequential", "associative", "recompute"
+    or "fused" (kata_scan_t).  Returns out [B, H, T, dv] (same dtype).
     """
     torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):

@@ -107,8 +107,9 @@ size_t kata_forward_workspace_bytes(int B, int H, int64_t T, int d, int dv,
  * Eqs. 17-20 (per-chunk states phi(K_c)^T V_c and phi(K_c)^T 1, an exclusive
  * prefix over chunks, and per chunk the readout phi(Q_c) S_prefix plus the
  * causally masked (Q_c K_c^T)^2 block times V_c, normalised).  The prefix over
- * chunk states is the vector-space cumulative sum of Sec. 4.2, taken either
- * sequentially or as a log-depth associative scan (`scan`).
+ * chunk states is the vector-space cumulative sum of Sec. 4.2, taken
+ * sequentially, as a log-depth associative scan, or for heads of few spans
+ * inside the readout (`scan`: KATA_SCAN_RECOMPUTE, KATA_SCAN_FUSED).
  *   q, k : [B, H, T, d] in dtype;  v, out : [B, H, T, dv] in dtype
  *   eps  : finite, >= 0; added once to the accumulated denominator
  *   chunk: chunk length C; a final partial chunk is zero-padded (App. D.2)
