@@ -23,7 +23,7 @@ def _case(B, H, T, d, chunk, seed):
     return inp, q, k, v
 
 
-@pytest.mark.parametrize("scan", ["sequential", "associative"])
+@pytest.mark.parametrize("scan", ["sequential", "associative", "fused"])
 def test_noalloc_matches_workspace_entry_point(scan):
     cases = [(4, 8, 2048, 16, 64, 1), (1, 2, 1000, 16, 128, 2), (1, 3, 3000, 32, 64, 3)]
     outs = []
