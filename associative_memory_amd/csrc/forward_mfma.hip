@@ -724,13 +724,13 @@ __device__ __forceinline__ float row_rotate(float x) {
 }
 
 // f[i] = a[i] * (b[i] of lane (r + J) mod 16 of the row), J = 1..15, as eight
-// v_mul_f32 with the row rotation in the DPP field of the first operand.  The
-// compiler only folds a rotation into its multiply when the two sit within a
-// few instructions of each other, which its instruction order does not keep
-// for products whose operands come from different registers; written out, the
-// rotation costs nothing.  DPP reads a VGPR two wait states after a VALU
-// write at the earliest, hence the leading s_nop (the inputs may have been
-// written by the instructions just before).
+// v_mul_f32 with the row rotation in the DPP field of the first operand.
+// Written with a rotating move and a multiply, about half of the d = 32
+// products compiled to the two separate instructions (the compiler's folding
+// of the move into its user did not take where the move was emitted far from
+// the multiply); written out, the rotation costs nothing.  DPP reads a VGPR
+// two wait states after a VALU write at the earliest, hence the leading s_nop
+// (the inputs may have been written by the instructions just before).
 template <int J>
 __device__ __forceinline__ void mul_row_rotated(float (&f)[8], const float (&a)[8], const float (&b)[8]) {
   static_assert(J > 0 && J < 16, "row rotation by 1..15 lanes");
