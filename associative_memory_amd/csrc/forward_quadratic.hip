@@ -149,6 +149,9 @@ __device__ __forceinline__ void quad_block(f32x4 (&o)[2][NDT], const QuadTile<DK
   }
 }
 
+// query blocks per group of heads in the grid order (two per CU)
+constexpr int64_t kQuadGroupWorkgroups = 512;
+
 template <int DK, int M>
 __device__ __forceinline__ void quad_body(const QuadArgs& a) {
   using Op = QkOp<DK, M>;
@@ -159,8 +162,21 @@ __device__ __forceinline__ void quad_body(const QuadArgs& a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nqb = (a.T + QB - 1) / QB;
-  const int64_t bh = blockIdx.x / nqb;
-  const int64_t qb = nqb - 1 - (blockIdx.x - bh * nqb);  // the longest rows of blocks first
+  // Heads go in groups of about kQuadGroupWorkgroups query blocks (one
+  // round of two workgroups per CU), so the resident workgroups share the
+  // K and V of few heads.  Within a group the query blocks are ranked by
+  // length (rank r: block nqb - 1 - r / hg of the group's head r mod hg);
+  // the first half of the group takes ranks ascending, the second half
+  // descending from the shortest, so the two workgroups a CU receives (j and
+  // j + half) carry about the same number of key blocks together.
+  const int64_t hpg = nqb >= kQuadGroupWorkgroups ? 1 : kQuadGroupWorkgroups / nqb;
+  const int64_t idx = blockIdx.x;
+  const int64_t grp = idx / (hpg * nqb), j = idx - grp * hpg * nqb;
+  const int64_t hg = a.BH - grp * hpg < hpg ? a.BH - grp * hpg : hpg;  // heads in this group
+  const int64_t nwg = hg * nqb, half = (nwg + 1) / 2;
+  const int64_t rank = j < half ? j : nwg - 1 - (j - half);
+  const int64_t bh = grp * hpg + rank % hg;
+  const int64_t qb = nqb - 1 - rank / hg;
   const int64_t tok0 = bh * a.T;
   const int64_t q0 = qb * QB;
   const int64_t kend = (a.T < q0 + QB) ? a.T : q0 + QB;  // keys [0, kend) are read
