@@ -1205,12 +1205,17 @@ __device__ inline SpanOf readout_span(const MfmaArgs& a) {
 }
 
 // Span of a readout workgroup that adds the span sums before its span
-// (a.fused): consecutive blocks are different heads, so with a multiple of 8
-// heads every span of a head runs on one XCD and the head's span sums, read
-// by each of its later spans, stay in that XCD's L2.
+// (a.fused).  Consecutive blocks are different heads, so with a multiple of
+// 8 heads every span of a head runs on one XCD and the head's span sums,
+// read by each of its later spans, stay in that XCD's L2.  The spans go
+// latest first in the first half of the grid and earliest first in the
+// second, so when the grid is one round of two workgroups per CU the two a
+// CU receives (blocks b and b + half) add about the same number of sums
+// together.
 __device__ inline SpanOf fused_span(const MfmaArgs& a) {
   const int64_t b = blockIdx.x;
-  return {b % a.BH, b / a.BH};
+  const int64_t k = b / a.BH, n = a.n_spans, first = (n + 1) / 2;
+  return {b % a.BH, k < first ? n - 1 - k : k - first};
 }
 
 // Span of a span-sum workgroup: spans 0 .. n_spans - 2 of every head (the
