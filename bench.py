@@ -18,7 +18,7 @@ The fp64 oracle's timing on the host is reported as cpu_baseline: its chunked
 form over the whole T = 131072 workload, with the plain definition on one head
 and per-workload timings beside it.  A baseline, not the target.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warmup-ms MS] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup-ms", type=float, default=200.0,
+                    help="untimed warm-up continues past --warmup calls until this much wall time "
+                         "has passed, so the timed regions start at the clocks the GPU holds under load")
     ap.add_argument("--repeats", type=int, default=5,
                     help="interleaved timed regions of K steps per prefix variant (median reported)")
     ap.add_argument("--decode-steps", type=int, default=1024)
@@ -188,9 +191,9 @@ def bench_forward(args, hip, am, ki, torch):
     for scan in scans:
         ws_bytes = am.kata_forward_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, w.chunk, scan)
         ws[scan] = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-        for _ in range(args.warmup):
-            am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=scan, out=out, workspace=ws[scan])
-    torch.cuda.synchronize()
+    _warm(args, torch, *[
+        (lambda sc=scan: am.kata_forward_chunked(q, k, v, w.chunk, eps=w.eps, scan=sc, out=out,
+                                                 workspace=ws[sc])) for scan in scans])
     samples = {scan: [] for scan in scans}
     walls = {scan: [] for scan in scans}
     for r in range(args.repeats):
@@ -242,17 +245,30 @@ def bench_forward(args, hip, am, ki, torch):
     return w, inp, results
 
 
+def _warm(args, torch, *fns):
+    """Untimed warm-up: every callable in turn, at least `warmup` rounds and
+    until `warmup_ms` of wall time has passed (the GPU leaves its idle clocks
+    over tens of milliseconds of work; a handful of calls does not get it
+    there)."""
+    t0 = time.perf_counter()
+    rounds = 0
+    while rounds < args.warmup or 1e3 * (time.perf_counter() - t0) < args.warmup_ms:
+        for f in fns:
+            f()
+        rounds += 1
+        if rounds % 8 == 0 or rounds >= args.warmup:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def _interleaved_ms(args, hip, torch, calls):
-    """Median milliseconds per call of each named callable: after `warmup`
-    calls of each, `repeats` rounds each time `steps` back-to-back calls of
+    """Median milliseconds per call of each named callable: after the warm-up
+    (`_warm`), `repeats` rounds each time `steps` back-to-back calls of
     every callable (HIP events on the current stream), the order rotated per
     round so no variant always runs first."""
     stream = torch.cuda.current_stream().cuda_stream
     names = list(calls)
-    for f in calls.values():
-        for _ in range(args.warmup):
-            f()
-    torch.cuda.synchronize()
+    _warm(args, torch, *calls.values())
     samples = {n: [] for n in names}
     for r in range(args.repeats):
         shift = r % len(names)
@@ -350,9 +366,7 @@ def bench_quadratic(args, hip, am, torch, w, q, k, v, out):
     token-head as for the intra-chunk block, with the chunk as long as the
     sequence (the KATA-Mg score costs the same 2d per pair for any g)."""
     stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(args.warmup):
-        am.kata_forward_quadratic(q, k, v, eps=w.eps, g=w.g, out=out)
-    torch.cuda.synchronize()
+    _warm(args, torch, lambda: am.kata_forward_quadratic(q, k, v, eps=w.eps, g=w.g, out=out))
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, stream)
     for _ in range(args.steps):
@@ -401,9 +415,7 @@ def bench_table8(args, hip, am, ki, torch):
         out = torch.empty_like(v)
         need = am.lib().kata_forward_chunked_blocks_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, g, C, 0)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-        for _ in range(args.warmup):
-            am.kata_forward_chunked_blocks(q, k, v, g, chunk=C, out=out, workspace=ws)
-        torch.cuda.synchronize()
+        _warm(args, torch, lambda: am.kata_forward_chunked_blocks(q, k, v, g, chunk=C, out=out, workspace=ws))
         e0, e1 = hip.event(), hip.event()
         hip.record(e0, stream)
         for _ in range(args.steps):
@@ -439,9 +451,8 @@ PAGE_E1_MTOKS = {(1024, "orthant"): (24.1, 25.6), (1024, "lorentz"): (24.1, 25.6
 
 def _time_linear(args, hip, am, torch, q, k, v, out, ws, feature, chunk, scan):
     stream = torch.cuda.current_stream().cuda_stream
-    for _ in range(args.warmup):
-        am.kata_forward_linear(q, k, v, feature=feature, chunk=chunk, scan=scan, out=out, workspace=ws)
-    torch.cuda.synchronize()
+    _warm(args, torch, lambda: am.kata_forward_linear(q, k, v, feature=feature, chunk=chunk, scan=scan,
+                                                      out=out, workspace=ws))
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, stream)
     for _ in range(args.steps):
@@ -513,9 +524,7 @@ def bench_gated(args, hip, am, ki, torch):
         for C in (64, 128):
             need = am.kata_forward_gated_workspace_bytes(w.B, w.H, w.T, w.d, w.dv, C)
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-            for _ in range(args.warmup):
-                am.kata_forward_gated(q, k, v, lg, chunk=C, out=out, workspace=ws)
-            torch.cuda.synchronize()
+            _warm(args, torch, lambda: am.kata_forward_gated(q, k, v, lg, chunk=C, out=out, workspace=ws))
             e0, e1 = hip.event(), hip.event()
             hip.record(e0, stream)
             for _ in range(args.steps):
@@ -551,9 +560,10 @@ def bench_decode(args, hip, am, ki, torch, w):
     del pk, pv
     out = torch.empty((w.heads, w.dv), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    for s in range(min(args.warmup, steps)):
-        am.kata_decode_step(S, z, sq[s], sk[s], sv[s], eps=w.eps, out=out)
-    torch.cuda.synchronize()
+    # warm-up steps on a copy of the state, so the timed loop starts from the prefill
+    S_w, z_w = S.clone(), z.clone()
+    _warm(args, torch, lambda: am.kata_decode_step(S_w, z_w, sq[0], sk[0], sv[0], eps=w.eps, out=out))
+    del S_w, z_w
     e0, e1 = hip.event(), hip.event()
     hip.record(e0, stream)
     for s in range(steps):
@@ -732,6 +742,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_ms": args.warmup_ms,
         "ms_per_step": round(main_r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -758,7 +769,9 @@ def main():
             "frac": round(max(bytes_per_tok * BHT / (HBM_PEAK_GBS * 1e9),
                               flop_per_tok * BHT / (BF16_PEAK_TFLOPS * 1e12))
                           / (main_r["ms_per_step"] * 1e-3), 4)},
-        "timing": f"median over {args.repeats} regions of exactly {args.steps} forwards each, the three "
+        "timing": f"after an untimed warm-up of at least {args.warmup} forwards per variant and "
+                  f"{args.warmup_ms:g} ms, median over {args.repeats} regions of exactly {args.steps} "
+                  "forwards each, the three "
                   "prefix variants interleaved (rotating order), HIP events on the library's stream; "
                   "other_workloads the same way, each workload's plans interleaved",
         "scan_variants": {s: {"tokens_per_s": round(fwd[s]["tokens_per_s"], 1),
