@@ -101,6 +101,18 @@ ForwardPlan plan_forward(int B, int H, int64_t T, int d, int dv, int chunk,
   p.G = ceil_div(p.n_chunks, spans);
   if (ceil_div(p.n_chunks, p.G) > kMaxSpans) p.G = ceil_div(p.n_chunks, kMaxSpans);
   p.n_spans = ceil_div(p.n_chunks, p.G);
+  // few heads at short T: rather than more spans than the fused prefix takes
+  // (and a prefix launch), kFusedMaxSpans spans of at most kMinSpanTokens16
+  // tokens (measured, step us, B x H x T chunk, as planned before / capped:
+  // 2x8x2048 C64 (32 spans) 28.5 / 21.8, 1x8x4096 C64 (64) 28.6 / 24.0,
+  // 2x8x4096 C64 and 1x16x4096 C64 (32) equal; with longer capped spans the
+  // cap loses: 1x8x8192 C128 27.5 / 29.9, 1x8x16384 C128 36.3 / 44.3)
+  if (scan == KATA_SCAN_AUTO && mfma && d == 16 && g == 1 && p.n_spans > kFusedMaxSpans &&
+      ceil_div(p.n_chunks, kFusedMaxSpans) * chunk <= kMinSpanTokens16 &&
+      fused_supported(p.bf16, d, dv, chunk)) {
+    p.G = ceil_div(p.n_chunks, kFusedMaxSpans);
+    p.n_spans = ceil_div(p.n_chunks, p.G);
+  }
   if (scan == KATA_SCAN_AUTO) {
     // measured on MI355X at 9,360-float span states (prefix stage, us,
     // sequential / associative): 8 heads x 64 spans 11.2 / 11.7, 4 x 128

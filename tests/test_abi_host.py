@@ -389,6 +389,15 @@ def test_fused_plan():
         fused = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "fused").split())
         assert fused["scan"] == "fused" and fused["paired_even_span"] == "0"
         assert fused["n_spans"] == auto["n_spans"] and fused["workspace_bytes"] == auto["workspace_bytes"]
+    # few heads at short T: 16 spans of at most 256 tokens in place of more spans and a prefix launch
+    for (B, H, T, C, n_seq) in [(2, 8, 2048, 64, 32), (1, 8, 4096, 64, 64), (1, 1, 2048, 64, 32)]:
+        auto = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "auto").split())
+        seq = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 16, 64, C, BF16, "sequential").split())
+        assert auto["scan"] == "fused" and auto["n_spans"] == "16", auto
+        assert int(auto["chunks_per_span"]) * C <= 256
+        assert seq["n_spans"] == str(n_seq)
+        assert L.kata_forward_workspace_bytes(B, H, T, 16, 64, C, 0) < L.kata_forward_workspace_bytes(B, H, T, 16, 64, C, 1)
+    assert "scan=sequential" in am.kata_forward_plan(1, 8, 8192, 16, 64, 128, BF16, "auto")
     # d = 32 (chunk 64) takes it up to 4 spans per head
     for (B, H, T, n) in [(8, 16, 2048, 2), (4, 16, 4096, 4)]:
         f = dict(kv.split("=") for kv in am.kata_forward_plan(B, H, T, 32, 64, 64, BF16, "auto").split())

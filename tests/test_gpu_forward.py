@@ -421,6 +421,38 @@ def test_fused_prefix(case):
     check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"fused {case}")
 
 
+FUSED_CAPPED_CASES = [
+    # (B, H, T, chunk), d = 16: few heads at short T, where the automatic
+    # plan takes 16 spans of at most 256 tokens with the fused prefix; a
+    # ragged last span and last chunk
+    (2, 8, 2048, 64),
+    (1, 8, 4096, 64),
+    (1, 1, 2048, 64),
+    (1, 3, 3001, 64),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CAPPED_CASES, ids=lambda c: "B{}H{}T{}C{}".format(*c))
+def test_fused_prefix_capped_spans(case):
+    """The automatic plan's 16 short spans with the fused prefix: every output
+    against the oracle, guard bands and run-to-run bitwise determinism."""
+    B, H, T, chunk = case
+    d, dv = 16, 64
+    plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, "auto")
+    say(f"forward auto {case} plan: {plan}")
+    assert "scan=fused" in plan and "n_spans=16 " in plan
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.BF16, seed=T + 7 * chunk)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    buf, out = guarded((B, H, T, dv), torch.bfloat16)
+    am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="auto", out=out)
+    again = am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan="auto")
+    torch.cuda.synchronize()
+    assert_guards(buf, f"out {case}")
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "run-to-run bits"
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6)
+    check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"fused capped {case}")
+
+
 FUSED32_CASES = [
     # (B, H, T), d = 32, dv = 64, chunk 64, bf16: 2 and 4 spans per head (the
     # automatic plan there), the d = 32 workload's 8 spans, ragged spans and a
