@@ -15,9 +15,11 @@ constexpr int TT = 32;   // tokens per LDS tile in the state kernel
 
 // ---------------------------------------------------------------- span states
 //
-// grid.x enumerates (bh, span, dv tile).  Thread e-slots own elements
-// (f, c) = (e / DVT, e % DVT) of the D x DVT block; z is summed by the dv
-// tile 0 workgroup.
+// grid.x enumerates (bh, span, dv tile).  Thread slot m owns feature
+// f = tid + m * kThreads with all DVT columns of the tile: per token it reads
+// its two key coordinates and the token's DVT values (one broadcast row), so
+// the product k_i k_j is formed once per feature and token.  z is summed by
+// the dv tile 0 workgroup.
 //
 // GATED (a.log_gamma != nullptr, one span per head): the GatedKATA state of
 // the span, S <- gamma_t S + phi(k_t) v_t^T token by token (the page, App.
@@ -25,10 +27,9 @@ constexpr int TT = 32;   // tokens per LDS tile in the state kernel
 template <int DK, bool BF16, bool GATED = false>
 __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
   constexpr int D = feature_dim(DK);
-  constexpr int M = (D * DVT + kThreads - 1) / kThreads;
-  constexpr int MZ = (D + kThreads - 1) / kThreads;
+  constexpr int MF = (D + kThreads - 1) / kThreads;  // features per thread
   __shared__ float ks[TT][DK];
-  __shared__ float vs[TT][DVT];
+  __shared__ alignas(16) float vs[TT][DVT];
   __shared__ float gs[GATED ? TT : 1];
 
   const int n_tiles = a.dv / DVT;
@@ -40,29 +41,19 @@ __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
   if (a.skip_last && sp == a.n_spans - 1) return;
   const int tid = threadIdx.x;
 
-  int fi[M], fj[M], fc[M];
-  float acc[M];
+  int fi[MF], fj[MF];
+  float acc[MF][DVT];
+  float zacc[MF];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = tid + m * kThreads;
-    const int f = e / DVT;
-    fc[m] = e % DVT;
+  for (int m = 0; m < MF; ++m) {
+    const int f = tid + m * kThreads;
     int i = 0, j = 0;
     if (f < D) pair_of(f, DK, i, j);
     fi[m] = i;
     fj[m] = j;
-    acc[m] = 0.f;
-  }
-  int zi[MZ], zj[MZ];
-  float zacc[MZ];
-#pragma unroll
-  for (int m = 0; m < MZ; ++m) {
-    const int f = tid + m * kThreads;
-    int i = 0, j = 0;
-    if (f < D) pair_of(f, DK, i, j);
-    zi[m] = i;
-    zj[m] = j;
     zacc[m] = 0.f;
+#pragma unroll
+    for (int c = 0; c < DVT; ++c) acc[m][c] = 0.f;
   }
 
   const int64_t t_begin = sp * a.span;
@@ -86,17 +77,30 @@ __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
     }
     __syncthreads();
     for (int r = 0; r < TT; ++r) {
-      if constexpr (GATED) {
-        const float g = gs[r];
+      float vr[DVT];
 #pragma unroll
-        for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(acc[m], g, ks[r][fi[m]] * ks[r][fj[m]] * vs[r][fc[m]]);
-        continue;
+      for (int c4 = 0; c4 < DVT / 4; ++c4) {
+        const float4 x = reinterpret_cast<const float4*>(vs[r])[c4];
+        vr[4 * c4] = x.x;
+        vr[4 * c4 + 1] = x.y;
+        vr[4 * c4 + 2] = x.z;
+        vr[4 * c4 + 3] = x.w;
       }
+      const float g = GATED ? gs[r] : 1.f;
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[m] += ks[r][fi[m]] * ks[r][fj[m]] * vs[r][fc[m]];
-      if (tile == 0) {
+      for (int m = 0; m < MF; ++m) {
+        if (m + 1 < MF || tid + m * kThreads < D) {
+          const float p = ks[r][fi[m]] * ks[r][fj[m]];
 #pragma unroll
-        for (int m = 0; m < MZ; ++m) zacc[m] += ks[r][zi[m]] * ks[r][zj[m]];
+          for (int c = 0; c < DVT; ++c) {
+            if constexpr (GATED) {
+              acc[m][c] = __builtin_fmaf(acc[m][c], g, p * vr[c]);
+            } else {
+              acc[m][c] = __builtin_fmaf(p, vr[c], acc[m][c]);
+            }
+          }
+          zacc[m] += p;
+        }
       }
     }
     __syncthreads();
@@ -104,21 +108,21 @@ __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
 
   float* So = a.S_out + (bh * a.n_spans + sp) * a.s_stride;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = tid + m * kThreads;
-    const int f = e / DVT;
+  for (int m = 0; m < MF; ++m) {
+    const int f = tid + m * kThreads;
     if (f < D) {
       const float w = (a.sym && fi[m] != fj[m]) ? kSqrt2 : 1.0f;
-      So[f * a.dv + tile * DVT + fc[m]] = w * acc[m];
+#pragma unroll
+      for (int c = 0; c < DVT; ++c) So[static_cast<int64_t>(f) * a.dv + tile * DVT + c] = w * acc[m][c];
     }
   }
   if (!GATED && tile == 0) {
     float* zo = a.z_out + (bh * a.n_spans + sp) * a.z_stride;
 #pragma unroll
-    for (int m = 0; m < MZ; ++m) {
+    for (int m = 0; m < MF; ++m) {
       const int f = tid + m * kThreads;
       if (f < D) {
-        const float w = (a.sym && zi[m] != zj[m]) ? kSqrt2 : 1.0f;
+        const float w = (a.sym && fi[m] != fj[m]) ? kSqrt2 : 1.0f;
         zo[f] = w * zacc[m];
       }
     }
@@ -131,20 +135,29 @@ __global__ __launch_bounds__(kThreads) void state_valu_kernel(StateArgs a) {
 // live in LDS.  The forward keeps its private state with weight 1 on every
 // k_i k_j and puts the off-diagonal factor 2 on the query side, so
 // phi_q . phi_k = (q.k)^2 needs no sqrt(2) rounding.
+//
+// The TPQ threads of a query row split its work and add their partial reads
+// by a butterfly over their lanes (each ends with the same sums): thread cg
+// takes the packed feature rows p and DK - 1 - p (DK + 1 features together)
+// for p = cg, cg + TPQ, ... in the inter-chunk term, and the keys s = cg,
+// cg + TPQ, ... of the chunk in the intra-chunk term; it stores value columns
+// cg * CPT .. + CPT - 1.  The state update gives each thread whole feature
+// rows (all DVT columns), so k_i k_j is formed once per feature and token.
 template <int DK, int C, bool BF16>
 __global__ __launch_bounds__(kThreads) void output_valu_kernel(OutputArgs a) {
   constexpr int D = feature_dim(DK);
   constexpr int TPQ = kThreads / C;   // threads per query row
-  constexpr int CPT = DVT / TPQ;      // value columns per thread
-  constexpr int M = (D * DVT + kThreads - 1) / kThreads;
-  constexpr int MZ = (D + kThreads - 1) / kThreads;
+  constexpr int CPT = DVT / TPQ;      // value columns each thread stores
+  constexpr int KP = DK + 4;          // q / k row stride (16-byte rows)
+  constexpr int MF = (D + kThreads - 1) / kThreads;  // feature rows per thread in the update
   static_assert(TPQ * C == kThreads && CPT * TPQ == DVT, "bad tiling");
+  static_assert((DK / 2) % TPQ == 0, "row pairs split evenly over a query's threads");
 
-  __shared__ float Ss[D][DVT];
+  __shared__ alignas(16) float Ss[D][DVT];
   __shared__ float zs[D];
-  __shared__ float qs[C][DK + 1];
-  __shared__ float ks[C][DK + 1];
-  __shared__ float vs[C][DVT];
+  __shared__ alignas(16) float qs[C][KP];
+  __shared__ alignas(16) float ks[C][KP];
+  __shared__ alignas(16) float vs[C][DVT];
 
   const int n_tiles = a.dv / DVT;
   int64_t id = blockIdx.x;
@@ -159,33 +172,22 @@ __global__ __launch_bounds__(kThreads) void output_valu_kernel(OutputArgs a) {
   const float* P = a.prefix ? a.prefix + (bh * a.n_spans + sp) * E : nullptr;
   for (int e = tid; e < D * DVT; e += kThreads) {
     const int f = e / DVT, c = e - f * DVT;
-    Ss[f][c] = P ? P[f * a.dv + tile * DVT + c] : 0.f;
+    Ss[f][c] = P ? P[static_cast<int64_t>(f) * a.dv + tile * DVT + c] : 0.f;
   }
   for (int f = tid; f < D; f += kThreads) zs[f] = P ? P[static_cast<int64_t>(D) * a.dv + f] : 0.f;
 
-  int fi[M], fj[M], fc[M];
+  int fi[MF], fj[MF];
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int e = tid + m * kThreads;
-    const int f = e / DVT;
-    fc[m] = e % DVT;
+  for (int m = 0; m < MF; ++m) {
+    const int f = tid + m * kThreads;
     int i = 0, j = 0;
     if (f < D) pair_of(f, DK, i, j);
     fi[m] = i;
     fj[m] = j;
   }
-  int zi[MZ], zj[MZ];
-#pragma unroll
-  for (int m = 0; m < MZ; ++m) {
-    const int f = tid + m * kThreads;
-    int i = 0, j = 0;
-    if (f < D) pair_of(f, DK, i, j);
-    zi[m] = i;
-    zj[m] = j;
-  }
 
   const int tq = tid / TPQ;          // query row within the chunk
-  const int cg = tid - tq * TPQ;     // column group
+  const int cg = tid - tq * TPQ;     // thread within the row's group
   const int64_t tok0 = bh * a.T;
 
   for (int64_t g = 0; g < a.G; ++g) {
@@ -206,65 +208,107 @@ __global__ __launch_bounds__(kThreads) void output_valu_kernel(OutputArgs a) {
     }
     __syncthreads();
 
-    float xq[DK];
+    float num[DVT];
 #pragma unroll
-    for (int i = 0; i < DK; ++i) xq[i] = qs[tq][i];
-    float num[CPT];
-#pragma unroll
-    for (int cc = 0; cc < CPT; ++cc) num[cc] = 0.f;
+    for (int c = 0; c < DVT; ++c) num[c] = 0.f;
     float den = 0.f;
-    // inter-chunk term: phi_q(q_t) . S and phi_q(q_t) . z
-    {
-      int f = 0;
+    // inter-chunk term: phi_q(q_t) . S and phi_q(q_t) . z over this thread's
+    // feature rows
+    for (int pp = cg; pp < DK / 2; pp += TPQ) {
+      const int i0 = pp, i1 = DK - 1 - pp;
+      const float qa = qs[tq][i0], qb = qs[tq][i1];
+      const int f0 = i0 * DK - i0 * (i0 - 1) / 2;  // first packed feature of row i0
+      const int f1 = i1 * DK - i1 * (i1 - 1) / 2;
+      for (int n = 0; n <= DK; ++n) {
+        const bool row0 = n < DK - i0;
+        const int j = row0 ? i0 + n : n - 1;
+        const int f = row0 ? f0 + n : f1 + (n - (DK - i0));
+        const bool diag = j == (row0 ? i0 : i1);
+        const float pf = (diag ? 1.0f : 2.0f) * (row0 ? qa : qb) * qs[tq][j];
 #pragma unroll
-      for (int i = 0; i < DK; ++i) {
-#pragma unroll
-        for (int j = i; j < DK; ++j, ++f) {
-          const float pf = (i == j ? 1.0f : 2.0f) * xq[i] * xq[j];
-#pragma unroll
-          for (int cc = 0; cc < CPT; ++cc) num[cc] += pf * Ss[f][cg * CPT + cc];
-          den += pf * zs[f];
+        for (int c4 = 0; c4 < DVT / 4; ++c4) {
+          const float4 x = reinterpret_cast<const float4*>(Ss[f])[c4];
+          num[4 * c4] = __builtin_fmaf(pf, x.x, num[4 * c4]);
+          num[4 * c4 + 1] = __builtin_fmaf(pf, x.y, num[4 * c4 + 1]);
+          num[4 * c4 + 2] = __builtin_fmaf(pf, x.z, num[4 * c4 + 2]);
+          num[4 * c4 + 3] = __builtin_fmaf(pf, x.w, num[4 * c4 + 3]);
         }
+        den = __builtin_fmaf(pf, zs[f], den);
       }
     }
-    // intra-chunk term: (q_t . k_s)^2 for s <= t within the chunk
-    for (int s = 0; s <= tq; ++s) {
+    // intra-chunk term: (q_t . k_s)^2 for this thread's keys s <= t
+    float xq[DK];
+#pragma unroll
+    for (int i4 = 0; i4 < DK / 4; ++i4) {
+      const float4 x = reinterpret_cast<const float4*>(qs[tq])[i4];
+      xq[4 * i4] = x.x;
+      xq[4 * i4 + 1] = x.y;
+      xq[4 * i4 + 2] = x.z;
+      xq[4 * i4 + 3] = x.w;
+    }
+    for (int s = cg; s <= tq; s += TPQ) {
       float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < DK; ++i) dot += xq[i] * ks[s][i];
+      for (int i4 = 0; i4 < DK / 4; ++i4) {
+        const float4 x = reinterpret_cast<const float4*>(ks[s])[i4];
+        dot = __builtin_fmaf(xq[4 * i4], x.x, dot);
+        dot = __builtin_fmaf(xq[4 * i4 + 1], x.y, dot);
+        dot = __builtin_fmaf(xq[4 * i4 + 2], x.z, dot);
+        dot = __builtin_fmaf(xq[4 * i4 + 3], x.w, dot);
+      }
       const float sc = dot * dot;
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) num[cc] += sc * vs[s][cg * CPT + cc];
+      for (int c4 = 0; c4 < DVT / 4; ++c4) {
+        const float4 x = reinterpret_cast<const float4*>(vs[s])[c4];
+        num[4 * c4] = __builtin_fmaf(sc, x.x, num[4 * c4]);
+        num[4 * c4 + 1] = __builtin_fmaf(sc, x.y, num[4 * c4 + 1]);
+        num[4 * c4 + 2] = __builtin_fmaf(sc, x.z, num[4 * c4 + 2]);
+        num[4 * c4 + 3] = __builtin_fmaf(sc, x.w, num[4 * c4 + 3]);
+      }
       den += sc;
+    }
+    // the row's TPQ partial reads, added over lanes tq * TPQ .. + TPQ - 1
+#pragma unroll
+    for (int off = 1; off < TPQ; off <<= 1) {
+#pragma unroll
+      for (int c = 0; c < DVT; ++c) num[c] += __shfl_xor(num[c], off);
+      den += __shfl_xor(den, off);
     }
     const int64_t t = c0 + tq;
     if (t < a.T) {
       const float inv = 1.0f / (den + a.eps);
+      const int64_t o = (tok0 + t) * a.dv + tile * DVT;
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc) {
-        store_elem<BF16>(a.out, (tok0 + t) * a.dv + tile * DVT + cg * CPT + cc, num[cc] * inv);
+      for (int c = 0; c < DVT; ++c) {
+        if (c / CPT == cg) store_elem<BF16>(a.out, o + c, num[c] * inv);
       }
     }
 
     if (g + 1 < a.G) {
       __syncthreads();  // all readouts of this chunk done before S changes
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int e = tid + m * kThreads;
-        const int f = e / DVT;
-        if (f < D) {
-          float s = 0.f;
-          for (int r = 0; r < C; ++r) s += ks[r][fi[m]] * ks[r][fj[m]] * vs[r][fc[m]];
-          Ss[f][fc[m]] += s;
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MZ; ++m) {
+      for (int m = 0; m < MF; ++m) {
         const int f = tid + m * kThreads;
-        if (f < D) {
-          float s = 0.f;
-          for (int r = 0; r < C; ++r) s += ks[r][zi[m]] * ks[r][zj[m]];
-          zs[f] += s;
+        if (m + 1 < MF || f < D) {
+          float su[DVT];
+#pragma unroll
+          for (int c = 0; c < DVT; ++c) su[c] = 0.f;
+          float sz = 0.f;
+          for (int r = 0; r < C; ++r) {
+            const float p = ks[r][fi[m]] * ks[r][fj[m]];
+#pragma unroll
+            for (int c4 = 0; c4 < DVT / 4; ++c4) {
+              const float4 x = reinterpret_cast<const float4*>(vs[r])[c4];
+              su[4 * c4] = __builtin_fmaf(p, x.x, su[4 * c4]);
+              su[4 * c4 + 1] = __builtin_fmaf(p, x.y, su[4 * c4 + 1]);
+              su[4 * c4 + 2] = __builtin_fmaf(p, x.z, su[4 * c4 + 2]);
+              su[4 * c4 + 3] = __builtin_fmaf(p, x.w, su[4 * c4 + 3]);
+            }
+            sz += p;
+          }
+#pragma unroll
+          for (int c = 0; c < DVT; ++c) Ss[f][c] += su[c];
+          zs[f] += sz;
         }
       }
     }
