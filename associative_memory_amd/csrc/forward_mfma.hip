@@ -35,6 +35,8 @@
 //    the readout, which is split across waves by query tile (and, for d = 32,
 //    by value tiles) and computed transposed, O^T = [S|z]^T phi_q^T + [V|1]^T P^T,
 //    so a lane holds 4 consecutive value columns of one query.
+#include <type_traits>
+
 #include "kernels.h"
 #include "mfma_common.h"
 
@@ -1257,13 +1259,17 @@ __device__ __forceinline__ void store_gram16(const f32x4& z, float* __restrict__
 // (vmcnt: the later chunk's transfers may stay outstanding) and the barrier
 // then publishes every wave's share.  Chunks at or past the span's end read
 // as zero; their reduction is skipped.
-template <int C, bool G>
+// SHORT (spans of at most four chunks, uniform layout): a fourth buffer, and
+// all four chunks' transfers issued before the first reduction, so a short
+// span waits for one memory latency instead of one per two chunks.
+template <int C, bool G, bool SHORT = false>
 __device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
   using CF = Cfg<16, C>;
   constexpr int DK = 16;
   __shared__ DmaTile16<C, G> b0;
   __shared__ DmaTile16<C, G> b1;
   __shared__ DmaTile16<C, G> b2;
+  __shared__ std::conditional_t<SHORT, DmaTile16<C, G>, char> b3;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const SpanOf span = sum_span(a);
@@ -1285,7 +1291,27 @@ __device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
     auto src = [&](int64_t c) { return chunk_src<DK, C>(nullptr, a.k, a.v, tok0, c, end, a.gb, a.gk); };
     dma_chunk16<C, W, CF::NW, G>(b0, src(first), lane);
     dma_chunk16<C, W, CF::NW, G>(b1, src(first + C), lane);
-    for (int64_t c0 = first; c0 < end; c0 += 3 * C) {
+    if constexpr (SHORT) {
+      dma_chunk16<C, W, CF::NW, G>(b2, src(first + 2 * C), lane);
+      dma_chunk16<C, W, CF::NW, G>(b3, src(first + 3 * C), lane);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(3 * NPC));
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      state_update_dma16<CF, W, G>(acc, acc8, b0, to);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(2 * NPC));
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      if (first + C < end) state_update_dma16<CF, W, G>(acc, acc8, b1, to);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      if (first + 2 * C < end) state_update_dma16<CF, W, G>(acc, acc8, b2, to);
+      __builtin_amdgcn_s_waitcnt(wait_vmcnt(0));
+      barrier_lds();
+      __builtin_amdgcn_sched_barrier(0);
+      if (first + 3 * C < end) state_update_dma16<CF, W, G>(acc, acc8, b3, to);
+    }
+    for (int64_t c0 = first; !SHORT && c0 < end; c0 += 3 * C) {
       __builtin_amdgcn_s_waitcnt(wait_vmcnt(NPC));
       barrier_lds();
       dma_chunk16<C, W, CF::NW, G>(b2, src(c0 + 2 * C), lane);
@@ -1350,9 +1376,9 @@ __device__ __forceinline__ void span_state_dma16_body(const MfmaArgs& a) {
   });
 }
 
-template <int C, bool G = false>
+template <int C, bool G = false, bool SHORT = false>
 __global__ __launch_bounds__(256) void span_state_dma16_kernel(MfmaArgs a) {
-  span_state_dma16_body<C, G>(a);
+  span_state_dma16_body<C, G, SHORT>(a);
 }
 
 // ------------------------------------------------------------ readout
@@ -3013,7 +3039,14 @@ hipError_t launch_span(const MfmaArgs& a, hipStream_t stream) {
   using CF = Cfg<DK, C>;
   dim3 grid(static_cast<unsigned>(a.BH * (a.n_spans - 1)));
   if constexpr (DK == 16) {
-    span_state_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
+    // four chunk buffers: 43 KB at chunk 64; at chunk 128 (86 KB, one
+    // workgroup per CU) the short form measured slower (B=4 H=8 T=2048 step
+    // 21.5 -> 22.1 us; chunk 64: 23.1 -> 22.5 us, B=4 H=8 T=4096 31.7 -> 30.9)
+    if (C == 64 && a.GL == 0 && a.G <= 4) {
+      span_state_dma16_kernel<C, false, C == 64><<<grid, CF::NT, 0, stream>>>(a);
+    } else {
+      span_state_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
+    }
   } else {
     span_state_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
   }
