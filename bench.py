@@ -549,6 +549,39 @@ def bench_gated(args, hip, am, ki, torch):
 
 # ------------------------------------------------------------------ decode
 
+def bench_feature_map(args, hip, am, ki, torch):
+    """The standalone feature map on the query rows of two forward workloads
+    (bf16 in, bf16 out): HBM-bound, bytes = rows * (d + D) * 2."""
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    for w in (ki.LONG, ki.WIDE):
+        x = ki.forward_inputs_torch(w.B, w.H, w.T, w.d, w.dv, w.seed, "cuda")[0].reshape(-1, w.d)
+        rows, D = x.shape[0], w.d * (w.d + 1) // 2
+        phi = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
+        _warm(args, torch, lambda: am.kata_feature_map(x, out=phi))
+        samples = []
+        for _ in range(args.repeats):
+            e0, e1 = hip.event(), hip.event()
+            hip.record(e0, stream)
+            for _ in range(args.steps):
+                am.kata_feature_map(x, out=phi)
+            hip.record(e1, stream)
+            torch.cuda.synchronize()
+            samples.append(hip.ms(e0, e1) / args.steps)
+            hip.destroy(e0)
+            hip.destroy(e1)
+        ms = statistics.median(samples)
+        nbytes = rows * (w.d + D) * 2
+        res[f"rows{rows}_d{w.d}_bf16"] = {
+            "ms_per_call": round(ms, 5), "ms_per_call_samples": [round(t, 5) for t in samples],
+            "rows_per_s": round(rows / (ms * 1e-3), 1), "bytes_per_call": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        del x, phi
+    return res
+
+
 def bench_decode(args, hip, am, ki, torch, w):
     """Recurrent decode: `steps` consecutive kata_decode_step launches over
     every head, timed three ways on the library's stream: the eager launch
@@ -799,6 +832,8 @@ def main():
     if not args.no_gated:
         progress("gated read")
         rec["gated"] = bench_gated(args, hip, am, ki, torch)
+    progress("feature map")
+    rec["feature_map"] = bench_feature_map(args, hip, am, ki, torch)
     if not args.no_decode:
         progress("decode")
         rec["decode"] = bench_decode(args, hip, am, ki, torch, ki.DECODE)
