@@ -2540,8 +2540,12 @@ __device__ __forceinline__ int tr_offset_k32(int I, int lane) {
 
 // G: the gated span sums (the state decays by 2^beta_C per chunk, keys scaled
 // by the key factors, no Gram matrix; the z column is stored as zeros).
-template <bool G = false>
-__global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
+// NH = 2 (fewer spans than CUs): two workgroups per span, each reading the
+// whole chunk and reducing every other feature tile of each wave (half h
+// takes tiles W + 8 (2 m + h)); blocks b and b + BH (n_spans - 1) hold the
+// two halves of a span, on the same XCD when that count is a multiple of 8.
+template <bool G, int NH>
+__device__ __forceinline__ void span_state_ws32_body(const MfmaArgs& a) {
   using CF = CfgWs32;
   constexpr int C = 64;
   __shared__ DmaTile32 b0;
@@ -2551,20 +2555,26 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
   const int r = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nsp_work = a.n_spans - 1;  // the last span's sum is never read
-  const int64_t bh = blockIdx.x / nsp_work;
-  const int64_t sp = blockIdx.x - bh * nsp_work;
+  const int64_t nwork = a.BH * nsp_work;
+  const int h = static_cast<int>(blockIdx.x / nwork);
+  const int64_t blk = blockIdx.x - h * nwork;
+  const int64_t bh = blk / nsp_work;
+  const int64_t sp = blk - bh * nsp_work;
   const int64_t tok0 = bh * a.T;
   const int64_t first = sp * a.G * C;
   int64_t end = first + a.G * C;
   if (end > a.T) end = a.T;
   auto src = [&](int64_t c) { return chunk_src<32, C>(nullptr, a.k, a.v, tok0, c, end, a.gb, a.gk); };
 
+  auto half = [&](auto hc) {
   with_wave<8>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
+    constexpr int H = decltype(hc)::value;
     constexpr int NPC = (W >= 4 ? 2 : 1) + (G && W == 0 ? 1 : 0);  // this wave's transfers per chunk
     constexpr int NFT = mfma_feature_tiles(32);
-    constexpr int MT = (NFT - W + 7) / 8;
-    constexpr bool GRAM = W == 7 && !G;
+    constexpr int T0 = W + 8 * H, TS = 8 * NH;  // tiles T0, T0 + TS, ...
+    constexpr int MT = (NFT - T0 + TS - 1) / TS;
+    constexpr bool GRAM = W == 7 && H == 0 && !G;
     const TrOffsets to = tr_offsets(lane);
     const int ok0 = tr_offset_k32(0, lane), ok1 = tr_offset_k32(1, lane);
     f32x4 acc[MT][NDT - 1];
@@ -2608,7 +2618,7 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
           x[1][2 * i + 1] = hi_bf16(k1[i]);
         }
         if constexpr (G) ws32_gate_keys(x, b.gk, ks, g);
-        ws32_key_tiles<W, 8>(acc, x, bv, r, std::make_integer_sequence<int, MT>{});
+        ws32_key_tiles<T0, TS>(acc, x, bv, r, std::make_integer_sequence<int, MT>{});
       }
     };
     dma_chunk32<W, G>(b0, src(first), lane);
@@ -2636,7 +2646,7 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
     float* P = a.ws + (bh * a.n_spans + sp) * mfma_state_floats(32);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int ft = W + 8 * m;
+      const int ft = T0 + TS * m;
 #pragma unroll
       for (int dt = 0; dt < NDT - 1; ++dt) {
         *reinterpret_cast<float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4) =
@@ -2655,11 +2665,28 @@ __global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
         }
       }
     }
-    if constexpr (G && W == 7) {
+    if constexpr (G && W == 7 && H == 0) {
       // no denominator: the z column holds zeros
       for (int i = lane; i < 16 * NFT; i += 64) P[CF::ZOFF + i] = 0.f;
     }
   });
+  };
+  if (NH == 1 || h == 0) {
+    half(std::integral_constant<int, 0>{});
+  } else if constexpr (NH == 2) {
+    half(std::integral_constant<int, 1>{});
+  }
+}
+
+// the d = 32 span sums split over two workgroups per span while the spans do
+// not fill the CUs (B=2 H=16 T=8192: span stage 30.0 -> 28.3 us, step 103.2
+// -> 101.2 us; B=8 H=16 T=2048 83.3 -> 78.1 us; a fourth and fifth chunk
+// buffer instead, or as well, measured slower)
+constexpr int64_t kSplitSpanSums32 = 256;
+
+template <bool G = false, int NH = 1>
+__global__ __launch_bounds__(512, 2) void span_state_ws32_kernel(MfmaArgs a) {
+  span_state_ws32_body<G, NH>(a);
 }
 
 // ------------------------------------------------------------ readout, d = 16, LDS DMA
@@ -3089,7 +3116,12 @@ hipError_t launch_span_state_mfma(const MfmaArgs& a, hipStream_t stream) {
   if (a.d == 16 && a.chunk == 64) return launch_span<16, 64>(a, stream);
   if (a.d == 16 && a.chunk == 128) return launch_span<16, 128>(a, stream);
   if (a.d == 32 && a.chunk == 64) {
-    span_state_ws32_kernel<false><<<dim3(static_cast<unsigned>(a.BH * (a.n_spans - 1))), 512, 0, stream>>>(a);
+    const int64_t spans = a.BH * (a.n_spans - 1);
+    if (spans <= kSplitSpanSums32) {
+      span_state_ws32_kernel<false, 2><<<dim3(static_cast<unsigned>(2 * spans)), 512, 0, stream>>>(a);
+    } else {
+      span_state_ws32_kernel<false><<<dim3(static_cast<unsigned>(spans)), 512, 0, stream>>>(a);
+    }
     return hipGetLastError();
   }
   if (a.d == 32 && a.chunk == 128) return launch_span<32, 128>(a, stream);
