@@ -780,8 +780,10 @@ __device__ __forceinline__ void state_tiles16(f32x4 (&acc)[CF::MFT][NDT], const 
   (state_tile16<CF, J>(acc, kr, bv, w), ...);
 }
 
-// (N: value tiles updated; the gated read leaves out the ones-column tile)
-template <class CF, class S, int N = NDT>
+// (N: value tiles updated; the gated read leaves out the ones-column tile.
+// HS, HO: at d >= 32 only the wave's tiles m with m % HS == HO, for span sums
+// split over HS workgroups)
+template <class CF, class S, int N = NDT, int HS = 1, int HO = 0>
 __device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S& sm, int w, int lane,
                                              const KeyPairs<CF>& kp) {
   constexpr int LDT = CF::LDT, LDK = CF::LDK;
@@ -802,6 +804,7 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[CF::MFT][NDT], const S
     } else {
 #pragma unroll
       for (int m = 0; m < CF::MFT; ++m) {
+        if (m % HS != HO) continue;                // this workgroup's half (compile time)
         if (w + CF::NW * m >= CF::NFT) continue;  // uniform per wave
         const float* ra = &sm.Kt[kp.a[m] * LDK + 32 * ks + 8 * g];
         const float* rb = &sm.Kt[kp.b[m] * LDK + 32 * ks + 8 * g];
@@ -874,14 +877,15 @@ __device__ __forceinline__ void sum_states(f32x4 (&acc)[CF::MFT][NDT], const flo
 }
 
 // (WITH_Z false: the z column is written elsewhere)
-template <class CF, bool WITH_Z = true>
+// (HS, HO: only the tiles m with m % HS == HO)
+template <class CF, bool WITH_Z = true, int HS = 1, int HO = 0>
 __device__ __forceinline__ void store_state(const f32x4 (&acc)[CF::MFT][NDT], float* __restrict__ P,
                                             int w, int lane) {
   const int g = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int m = 0; m < CF::MFT; ++m) {
     const int ft = w + CF::NW * m;
-    if (ft >= CF::NFT) continue;
+    if (ft >= CF::NFT || m % HS != HO) continue;
 #pragma unroll
     for (int dt = 0; dt < NDT - 1; ++dt) {
       *reinterpret_cast<float4*>(P + ((ft * (NDT - 1) + dt) * 64 + lane) * 4) =
@@ -969,7 +973,10 @@ __device__ __forceinline__ void gate_decay(f32x4 (&acc)[NA][NB], float f) {
 // chunk's gate product 2^beta_C (beta_C / 2 read from the gate sums at the
 // chunk's last token; every chunk of a summed span is whole), and the staged
 // key rows carry their key factors.  The ones-column tile is not updated.
-template <class CF, bool G = false>
+// NH = 2 (fewer spans than CUs): two workgroups per span, both staging the
+// whole chunk; half h reduces the wave's tiles m with m % 2 == h.  Blocks b
+// and b + BH (n_spans - 1) hold the two halves of a span.
+template <class CF, bool G = false, int NH = 1>
 __device__ __forceinline__ void span_state_mfma_body(const MfmaArgs& a) {
   constexpr int C = CF::C, DK = CF::DK;
   // two LDS tile buffers: chunk i is staged into buffer i % 2 while the
@@ -980,12 +987,17 @@ __device__ __forceinline__ void span_state_mfma_body(const MfmaArgs& a) {
   // wave-dependent branch is a scalar branch, not an exec-mask region
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nsp_work = a.n_spans - 1;  // the last span's sum is never read
-  const int64_t bh = blockIdx.x / nsp_work;
-  const int64_t sp = blockIdx.x - bh * nsp_work;
+  const int64_t nwork = a.BH * nsp_work;
+  const int hh = NH == 1 ? 0 : static_cast<int>(blockIdx.x / nwork);
+  const int64_t blk = blockIdx.x - hh * nwork;
+  const int64_t bh = blk / nsp_work;
+  const int64_t sp = blk - bh * nsp_work;
   const int64_t tok0 = bh * a.T;
 
   init_const_rows<CF>(sm[0], tid);
   init_const_rows<CF>(sm[1], tid);
+  auto half = [&](auto hc) {
+  constexpr int H = decltype(hc)::value;
   with_wave<CF::NW>(w, [&](auto wc) {
     constexpr int W = decltype(wc)::value;
     const KeyPairs<CF> kp = key_pairs<CF>(W, lane & 15);
@@ -1005,18 +1017,24 @@ __device__ __forceinline__ void span_state_mfma_body(const MfmaArgs& a) {
       __syncthreads();
       if constexpr (G) {
         gate_decay(acc, __builtin_amdgcn_exp2f(2.f * a.gb[tok0 + c0 + C - 1]));
-        state_update<CF, Smem<CF>, NDT - 1>(acc, sm[buf], W, lane, kp);
+        state_update<CF, Smem<CF>, NDT - 1, NH, H>(acc, sm[buf], W, lane, kp);
       } else {
-        state_update<CF>(acc, sm[buf], W, lane, kp);
+        state_update<CF, Smem<CF>, NDT, NH, H>(acc, sm[buf], W, lane, kp);
       }
     }
-    store_state<CF>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
+    store_state<CF, true, NH, H>(acc, a.ws + (bh * a.n_spans + sp) * mfma_state_floats(DK), W, lane);
   });
+  };
+  if (NH == 1 || hh == 0) {
+    half(std::integral_constant<int, 0>{});
+  } else if constexpr (NH == 2) {
+    half(std::integral_constant<int, 1>{});
+  }
 }
 
-template <class CF, bool G = false>
+template <class CF, bool G = false, int NH = 1>
 __global__ __launch_bounds__(CF::NT) void span_state_mfma_kernel(MfmaArgs a) {
-  span_state_mfma_body<CF, G>(a);
+  span_state_mfma_body<CF, G, NH>(a);
 }
 
 // ------------------------------------------------------------ span sums, d = 16, LDS DMA
@@ -3074,6 +3092,12 @@ hipError_t launch_span(const MfmaArgs& a, hipStream_t stream) {
     } else {
       span_state_dma16_kernel<C><<<grid, CF::NT, 0, stream>>>(a);
     }
+  } else if (DK >= 64 && grid.x <= kSplitSpanSums32) {
+    // the d = 64 maps: two workgroups per span while the spans do not fill
+    // the CUs (B=8 H=16, T=4096: KATA-M4 step 0.265 -> 0.252 ms, M1 1.068
+    // -> 1.015 ms; T=131072: M4 7.68 -> 7.20 ms, M1 31.3 -> 29.0 ms); at
+    // d = 32, chunk 128 it measured slower (B=2 H=16 T=8192 116.8 -> 122.7 us)
+    span_state_mfma_kernel<CF, false, 2><<<dim3(2 * grid.x), CF::NT, 0, stream>>>(a);
   } else {
     span_state_mfma_kernel<CF><<<grid, CF::NT, 0, stream>>>(a);
   }
