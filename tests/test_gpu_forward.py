@@ -492,3 +492,46 @@ def test_fused_prefix_d32(case):
             refs.append(orc.forward_rows(qh, kh, vh, rows, 1e-6))
             gots.append(to_host64(out[b, h, rows]))
     check(np.concatenate(gots), np.concatenate(refs), ki.BF16, vmax, f"fused d=32 {case} rows")
+
+
+def _random_cases(n=36, seed=2026):
+    """Seeded shapes across every plan the forward can take: both head
+    widths, both chunk lengths, every prefix mode, lengths from one token to
+    a few thousand (ragged last chunks and spans), head counts that are and
+    are not multiples of the 8 XCDs."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    scans = ["auto", "sequential", "associative", "recompute", "fused"]
+    out = []
+    while len(out) < n:
+        d = int(g.choice([16, 32]))
+        chunk = int(g.choice([64, 128]))
+        scan = str(g.choice(scans))
+        if scan == "recompute" and d != 16:
+            continue
+        if scan == "fused" and d == 32 and chunk == 128:
+            continue
+        B, H = int(g.integers(1, 4)), int(g.integers(1, 9))
+        T = int(g.choice([1, 2, 63, 64, 65, 127, 129, 500, 1000, 2047, 2048, 2049, 3000, 4100]))
+        out.append((B, H, T, d, chunk, scan))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: "B{}H{}T{}d{}C{}-{}".format(*c))
+def test_random_shapes_every_plan(case):
+    """Every output against the definition, guard bands around the output
+    and past the workspace, on seeded shapes across the plans."""
+    B, H, T, d, chunk, scan = case
+    dv = 64
+    plan = am.kata_forward_plan(B, H, T, d, dv, chunk, am.KATA_BF16, scan)
+    say(f"forward random {case} plan: {plan}")
+    inp = ki.forward_inputs(B, H, T, d, dv, ki.BF16, seed=7 * T + B + 3 * H + d + chunk)
+    q, k, v = (to_dev(a, ki.BF16) for a in (inp.q, inp.k, inp.v))
+    need = am.kata_forward_workspace_bytes(B, H, T, d, dv, chunk, scan)
+    wbuf, ws = guarded_workspace(need)
+    buf, out = guarded((B, H, T, dv), torch.bfloat16)
+    am.kata_forward_chunked(q, k, v, chunk, eps=1e-6, scan=scan, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert_guards(buf, f"out {case}")
+    assert_workspace_guard(wbuf, need, f"workspace {case}")
+    ref = orc.forward_quadratic(inp.q64, inp.k64, inp.v64, 1e-6)
+    check(to_host64(out), ref, ki.BF16, np.abs(inp.v64).max(), f"random {case}")
